@@ -1,0 +1,441 @@
+"""Plain, slow CPU oracle of the FlashLoop lazy-update loop step.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the HIP path.  It shares no code with
+the HIP library (no kernels, headers, tables or helpers); only the seeded input
+generator is common to both sides.
+
+Source ("[FL]"): the page "FlashLoop: Fast and Memory-Efficient Looped
+Transformers via Lazy Updates" (rit.work blog).  Its sections are cited as
+  [FL/late]    "Later loops change only part of the state"
+  [FL/savings] "FlashLoop combines three kinds of savings"
+with the paragraph number inside the section (par. 1 = first paragraph).
+
+Precision.  The pages fix none.  Attention, softmax statistics and the
+token-change score are evaluated in float64.  The int4 codec and the KV
+reconstruction chain are evaluated in float32, because their results decide
+integers (the 4-bit codes) and the HIP path takes those decisions in float32;
+both sides therefore take the same decision in the same precision.
+
+Readings of points the page leaves open (all listed in the design doc):
+  R1 tokens are ranked at loop l by the change of the previous loop,
+     ||h_eff^(l-1) - h_eff^(l-2)||^2 (a loop cannot know its own change before
+     computing it); squared L2 over the whole hidden row, float64.
+  R2 ties in any top-k go to the lower index; results are returned ascending.
+  R3 keys are selected per (sequence, head) by the previous loop's column mass
+     c_j = sum_{i>=j} p_ij; the causal limit is applied per row.
+  R4 mass-corrected attention (the "column update" reading):
+        o_i = m_i * otilde_i + (o_prev_i - a_i)
+     m_i = previous-loop probability mass of the row on the selected keys,
+     a_i = those keys' previous contribution to the row's output,
+     otilde_i = softmax over the selected keys with the current Q, K, V.
+  R5 previous-loop probabilities are exp(s' - lse_prev), where a lazy loop's
+     lse is the implied normaliser M + log Z - log m.
+  R6 a row whose selected set (after the causal limit) is empty, or whose mass
+     m is 0, keeps o, lse and contributes nothing to c.
+  R7 int4 codec: symmetric codes -7..7, one float16 scale per group of 32
+     consecutive elements of a head row, s = f16_rne(min(absmax/7, 65504)),
+     code = rint(delta/s) clamped to [-7, 7] (0 when s == 0), low nibble =
+     even element; delta is taken against the previous reconstruction.
+  R8 loop 1 stores the base (working dtype); every later loop, full or lazy,
+     appends one delta layer holding records of that loop's active tokens.
+  R9 all attention reads the reconstructed K^, V^ of every key; queries are
+     exact.
+Parity unpinned: the page prints no worked example of the mass-corrected
+formula (R4), so its exact form is pinned only by invariants (full attention
+when all keys are selected, fixed point when nothing changed, mass
+preservation) and by brute force; see tests/test_oracle_attention.py.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+__all__ = [
+    "token_scores", "topk_ascending", "select_keys", "f16_rne", "quantize_groups",
+    "dequantize_groups", "pack_int4", "unpack_int4", "KVStore", "full_attention",
+    "lazy_attention", "LoopState", "run_prefill", "run_decode_seq",
+]
+
+F32 = np.float32
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------- #
+# Step 1: token selection  ([FL/savings] par. 1; [FL/late] par. 3)
+# --------------------------------------------------------------------------- #
+def token_scores(h_cur: np.ndarray, h_prev: np.ndarray) -> np.ndarray:
+    """u_i = sum_k (h_cur[i,k] - h_prev[i,k])^2 in float64 (reading R1).
+
+    [FL/savings] par. 1: tokens are ranked by how much their hidden state
+    changed; rows that were carried unchanged score exactly 0.
+    """
+    diff = h_cur.astype(F64) - h_prev.astype(F64)
+    return np.einsum("ik,ik->i", diff, diff)
+
+
+def topk_ascending(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores; ties to the lower index; ascending (R2)."""
+    scores = np.asarray(scores)
+    n = scores.shape[0]
+    if not 0 <= k <= n:
+        raise ValueError("k out of range")
+    if np.isnan(scores).any():
+        raise ValueError("NaN score")
+    order = np.lexsort((np.arange(n), -scores.astype(F64)))
+    return np.sort(order[:k]).astype(np.int32)
+
+
+def select_keys(colmass: np.ndarray, k: int) -> np.ndarray:
+    """Per-head key selection from the previous loop's column mass (R3).
+
+    [FL/savings] par. 2: keys are chosen from the previous loop's attention
+    statistics.  colmass [H, N] -> [H, k] ascending int32.
+    """
+    return np.stack([topk_ascending(colmass[h], k) for h in range(colmass.shape[0])])
+
+
+# --------------------------------------------------------------------------- #
+# Step 4: the int4 delta codec  ([FL/savings] par. 3)
+# --------------------------------------------------------------------------- #
+def f16_rne(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16, nearest-even (numpy's own conversion)."""
+    return np.asarray(x, dtype=F32).astype(np.float16)
+
+
+def quantize_groups(delta: np.ndarray, group: int = 32):
+    """float32 delta [..., d] -> (codes int8 [..., d], scales float16 [..., d/group]).
+
+    Reading R7; all arithmetic in float32 (correctly rounded division, rint
+    half-to-even), so the codes are a pure function of the float32 delta.
+    """
+    delta = np.asarray(delta, dtype=F32)
+    d = delta.shape[-1]
+    g = delta.reshape(delta.shape[:-1] + (d // group, group))
+    absmax = np.max(np.abs(g), axis=-1)
+    q = np.minimum(absmax / F32(7.0), F32(65504.0))
+    scales = f16_rne(q)
+    sf = scales.astype(F32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(sf == 0, F32(0), g / np.where(sf == 0, F32(1), sf))
+    codes = np.clip(np.rint(ratio), -7, 7).astype(np.int8)
+    return codes.reshape(delta.shape), scales
+
+
+def dequantize_groups(codes: np.ndarray, scales: np.ndarray, group: int = 32) -> np.ndarray:
+    """code * float(scale) in float32 (the product is exact)."""
+    d = codes.shape[-1]
+    c = codes.astype(F32).reshape(codes.shape[:-1] + (d // group, group))
+    return (c * scales.astype(F32)[..., None]).reshape(codes.shape)
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles, low nibble = even element -> uint8 [..., d/2]."""
+    c = (codes.astype(np.int16) & 0xF).astype(np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    lo = (packed & 0xF).astype(np.int16)
+    hi = (packed >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+@dataclass
+class _Records:
+    idx: np.ndarray        # [n] token positions
+    codes: np.ndarray      # [n, H, d] int8
+    scales: np.ndarray     # [n, H, d/group] float16
+
+
+class KVStore:
+    """One sequence's KV cache: a base plus a chain of int4 delta layers (R8).
+
+    [FL/savings] par. 3: the cache is a compressed base and a sequence of
+    compressed corrections; active tokens write a low-bit difference from
+    their previous state, inactive tokens write no entry.
+    """
+
+    def __init__(self, n_tokens: int, n_heads: int, head_dim: int, group: int = 32):
+        self.n, self.h, self.d, self.group = n_tokens, n_heads, head_dim, group
+        self.base = {"k": np.zeros((n_tokens, n_heads, head_dim), F32),
+                     "v": np.zeros((n_tokens, n_heads, head_dim), F32)}
+        self.layers: Dict[int, Dict[str, List[_Records]]] = {}
+
+    def reconstruct(self, which: str, version: int, tokens: Optional[np.ndarray] = None) -> np.ndarray:
+        """X^(version) = float(base) + sum of the token's deltas in layers 2..version,
+        accumulated in float32 in increasing layer order."""
+        sel = np.arange(self.n) if tokens is None else np.asarray(tokens)
+        x = self.base[which][sel].astype(F32).copy()
+        pos = np.full(self.n, -1, np.int64)
+        pos[sel] = np.arange(sel.shape[0])
+        for l in range(2, version + 1):
+            for rec in self.layers.get(l, {}).get(which, []):
+                rows = pos[rec.idx]
+                hit = rows >= 0
+                if hit.any():
+                    deq = dequantize_groups(rec.codes[hit], rec.scales[hit], self.group)
+                    x[rows[hit]] = x[rows[hit]] + deq
+        return x
+
+    def commit(self, version: int, idx: np.ndarray, k_new: np.ndarray, v_new: np.ndarray):
+        """Write loop ``version``'s K/V rows of tokens ``idx`` (O-1).
+
+        version 1 stores the base; later versions store int4 deltas against the
+        version-1 reconstruction of the same tokens.  Returns the records.
+        """
+        idx = np.asarray(idx, np.int64)
+        out = {}
+        for which, new in (("k", k_new), ("v", v_new)):
+            new = np.asarray(new, F32)
+            if version == 1:
+                self.base[which][idx] = new
+                continue
+            prev = self.reconstruct(which, version - 1, idx)
+            delta = new - prev                      # float32 subtraction
+            codes, scales = quantize_groups(delta, self.group)
+            rec = _Records(idx.copy(), codes, scales)
+            self.layers.setdefault(version, {"k": [], "v": []})[which].append(rec)
+            out[which] = rec
+        return out
+
+    def bytes_stored(self, base_elem_bytes: int) -> int:
+        b = 2 * self.n * self.h * self.d * base_elem_bytes
+        for layer in self.layers.values():
+            for recs in layer.values():
+                for r in recs:
+                    b += r.idx.shape[0] * self.h * (self.d // 2 + 2 * (self.d // self.group))
+        return b
+
+
+# --------------------------------------------------------------------------- #
+# Step 0 / Step 3: attention
+# --------------------------------------------------------------------------- #
+def full_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray,
+                   chunk: int = 1024):
+    """Causal softmax attention of rows ``rows`` over keys 0..i (O-2), float64.
+
+    q [n_rows, H, d] (the queries of ``rows``), k, v [N, H, d].
+    Returns o [n_rows, H, d], lse [n_rows, H], colmass [H, N] with
+    colmass[h, j] = sum over the given rows i >= j of p_ij.
+    """
+    rows = np.asarray(rows, np.int64)
+    n_rows, n_heads, d = q.shape
+    n = k.shape[0]
+    scale = 1.0 / math.sqrt(d)
+    o = np.zeros((n_rows, n_heads, d), F64)
+    lse = np.zeros((n_rows, n_heads), F64)
+    colmass = np.zeros((n_heads, n), F64)
+    for h in range(n_heads):
+        kh = k[:, h, :].astype(F64)
+        vh = v[:, h, :].astype(F64)
+        for r0 in range(0, n_rows, chunk):
+            r1 = min(n_rows, r0 + chunk)
+            rr = rows[r0:r1]
+            nk = int(rr.max()) + 1          # keys past the last row are masked for all
+            s = (q[r0:r1, h, :].astype(F64) @ kh[:nk].T) * scale
+            mask = np.arange(nk)[None, :] <= rr[:, None]
+            s = np.where(mask, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            z = e.sum(axis=1, keepdims=True)
+            l = m + np.log(z)
+            p = np.exp(s - l)
+            o[r0:r1, h, :] = p @ vh[:nk]
+            lse[r0:r1, h] = l[:, 0]
+            colmass[h, :nk] += p.sum(axis=0)
+    return o, lse, colmass
+
+
+def lazy_attention(q_cur, q_prev, k_prev, v_prev, k_cur, v_cur, o_prev, lse_prev, colmass_prev,
+                   rows: np.ndarray, keys: np.ndarray, chunk: int = 1024):
+    """Mass-corrected attention on the selected keys (O-5, readings R4-R6), float64.
+
+    [FL/savings] par. 2: keys are selected from the previous loop's
+    statistics; the selected group keeps the previous loop's probability mass
+    instead of being renormalised to 1, so the result approximates full
+    attention.  [FL/late] par. 4: the change between adjacent loops is carried
+    by a small, stable group of keys ("updating 10% of attention columns").
+
+    q_cur, q_prev, o_prev: [n_rows, H, d] for the active rows ``rows``;
+    lse_prev [n_rows, H]; k_*, v_* [N, H, d] reconstructions at versions l-1
+    and l; colmass_prev [H, N]; keys [H, nS] ascending.
+    Returns (o [n_rows,H,d], lse [n_rows,H], colmass [H,N], m [n_rows,H],
+    updated [n_rows,H] bool).
+    """
+    rows = np.asarray(rows, np.int64)
+    n_rows, n_heads, d = q_cur.shape
+    scale = 1.0 / math.sqrt(d)
+    o = np.array(o_prev, F64, copy=True)
+    lse = np.array(lse_prev, F64, copy=True)
+    colmass = np.array(colmass_prev, F64, copy=True)
+    mass = np.zeros((n_rows, n_heads), F64)
+    updated = np.zeros((n_rows, n_heads), bool)
+    for h in range(n_heads):
+        sel = np.asarray(keys[h], np.int64)
+        kp = k_prev[sel, h, :].astype(F64)
+        vp = v_prev[sel, h, :].astype(F64)
+        kc = k_cur[sel, h, :].astype(F64)
+        vc = v_cur[sel, h, :].astype(F64)
+        dcol = np.zeros(sel.shape[0], F64)
+        for r0 in range(0, n_rows, chunk):
+            r1 = min(n_rows, r0 + chunk)
+            rr = rows[r0:r1]
+            mask = sel[None, :] <= rr[:, None]
+            # previous loop's probabilities on the selected keys
+            sp = (q_prev[r0:r1, h, :].astype(F64) @ kp.T) * scale
+            pp = np.where(mask, np.exp(sp - lse_prev[r0:r1, h].astype(F64)[:, None]), 0.0)
+            m = pp.sum(axis=1)
+            a = pp @ vp
+            # current softmax restricted to the selected keys
+            sc = np.where(mask, (q_cur[r0:r1, h, :].astype(F64) @ kc.T) * scale, -np.inf)
+            any_key = mask.any(axis=1)
+            mx = np.where(any_key, sc.max(axis=1), 0.0)
+            e = np.where(mask, np.exp(sc - mx[:, None]), 0.0)
+            z = e.sum(axis=1)
+            ok = any_key & (m > 0)
+            zs = np.where(ok, z, 1.0)
+            otil = (e @ vc) / zs[:, None]
+            o_new = m[:, None] * otil + (o_prev[r0:r1, h, :].astype(F64) - a)
+            lse_new = mx + np.log(zs) - np.log(np.where(ok, m, 1.0))
+            p = (m / zs)[:, None] * e
+            o[r0:r1, h, :] = np.where(ok[:, None], o_new, o[r0:r1, h, :])
+            lse[r0:r1, h] = np.where(ok, lse_new, lse[r0:r1, h])
+            dcol += np.where(ok[:, None], p - pp, 0.0).sum(axis=0)
+            mass[r0:r1, h] = m
+            updated[r0:r1, h] = ok
+        colmass[h, sel] += dcol
+    return o, lse, colmass, mass, updated
+
+
+# --------------------------------------------------------------------------- #
+# Loop drivers
+# --------------------------------------------------------------------------- #
+@dataclass
+class LoopState:
+    """Per-sequence state after a loop (everything carried for inactive rows)."""
+    loop: int
+    h: Optional[np.ndarray]        # [N, D] effective hidden state (prefill only)
+    q: np.ndarray                  # [Nq, H, d] effective queries
+    o: np.ndarray                  # [Nq, H, d] float64
+    lse: np.ndarray                # [Nq, H] float64
+    colmass: np.ndarray            # [H, N] float64
+    store: KVStore
+    records: Dict[int, dict] = field(default_factory=dict)   # loop -> details
+
+
+def _copy_state(st: LoopState) -> LoopState:
+    import copy
+    return copy.deepcopy(st)
+
+
+def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: int = 0):
+    """Run loops 1..T of a prefill workload on one sequence.
+
+    ``loops`` yields (l, dict(h, q, k, v)) with l = 0..T, arrays shaped
+    [S, N, ...] (sequence ``seq`` is used); values are already in the
+    working dtype.  Early loops run in full; later loops select tokens and
+    keys, commit deltas of the active tokens and run mass-corrected attention
+    ([FL/savings] par. 1-3).  Returns the final LoopState (and, with
+    keep=True, the list of states after every loop).
+    """
+    n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
+    T = wl.n_loops if upto is None else upto
+    store = KVStore(n, H, d, wl.group)
+    h_eff = h_prev_eff = q_eff = None
+    o = lse = colmass = None
+    history = []
+    st = None
+    for l, x in loops:
+        if l > T:
+            break
+        if l == 0:
+            h_eff = x["h"][seq].copy()
+            continue
+        rec = {}
+        if l <= wl.n_full:
+            rows = np.arange(n, dtype=np.int32)
+            h_prev_eff, h_eff = h_eff, x["h"][seq].copy()
+            q_eff = x["q"][seq].copy()
+            store.commit(l, rows, x["k"][seq], x["v"][seq])
+            kh = store.reconstruct("k", l)
+            vh = store.reconstruct("v", l)
+            o, lse, colmass = full_attention(q_eff, kh, vh, rows)
+            rec.update(rows=rows)
+        else:
+            u = token_scores(h_eff, h_prev_eff)
+            rows = topk_ascending(u, wl.n_active(l))
+            keys = select_keys(colmass, wl.n_keys)
+            # the shared block recomputes only the active rows; others carry
+            h_prev_eff = h_eff.copy()
+            h_eff[rows] = x["h"][seq][rows]
+            q_prev_rows = q_eff[rows].copy()
+            q_eff[rows] = x["q"][seq][rows]
+            k_prev_hat = store.reconstruct("k", l - 1)
+            v_prev_hat = store.reconstruct("v", l - 1)
+            recs = store.commit(l, rows, x["k"][seq][rows], x["v"][seq][rows])
+            k_hat = store.reconstruct("k", l)
+            v_hat = store.reconstruct("v", l)
+            o_r, lse_r, colmass, m, upd = lazy_attention(
+                q_eff[rows], q_prev_rows, k_prev_hat, v_prev_hat, k_hat, v_hat,
+                o[rows], lse[rows], colmass, rows, keys)
+            o[rows] = o_r
+            lse[rows] = lse_r
+            rec.update(rows=rows, keys=keys, scores=u, mass=m, updated=upd, records=recs)
+        st = LoopState(l, h_eff, q_eff, o, lse, colmass, store, {l: rec})
+        if keep:
+            history.append(_copy_state(st))
+    return (st, history) if keep else st
+
+
+def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], loops_data):
+    """Decode workload, one sequence (O-6).
+
+    The stored context (positions 0..N-2) is committed first: the base from
+    loop 1 and one delta layer per later loop for the positions in
+    ``ctx_sets[l]``.  Then the new token at position N-1 runs T loops: loop 1
+    attends in full over version 1, loops l >= 2 select keys from that row's
+    column mass, commit the token's own delta and run mass-corrected
+    attention over version l.  ``loops_data[l]`` holds dict(q [S,1,H,d],
+    k [S,N,H,d], v [S,N,H,d]).  Returns a list of per-loop dicts.
+    """
+    n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
+    si = seq_index
+    store = KVStore(n, H, d, wl.group)
+    ctx = np.arange(n - 1)
+    last = np.array([n - 1])
+    for l in range(1, wl.n_loops + 1):
+        x = loops_data[l]
+        sel = ctx if l == 1 else np.asarray(ctx_sets[l], np.int64)
+        store.commit(l, sel, x["k"][si][sel], x["v"][si][sel])
+    out = []
+    o = lse = colmass = None
+    q_prev = None
+    for l in range(1, wl.n_loops + 1):
+        x = loops_data[l]
+        q = x["q"][si]                       # [1, H, d]
+        store.commit(l, last, x["k"][si][last], x["v"][si][last])
+        if l == 1:
+            kh = store.reconstruct("k", 1)
+            vh = store.reconstruct("v", 1)
+            o, lse, colmass = full_attention(q, kh, vh, last)
+            out.append(dict(o=o.copy(), lse=lse.copy(), colmass=colmass.copy()))
+        else:
+            keys = select_keys(colmass, wl.n_keys)
+            kp = store.reconstruct("k", l - 1)
+            vp = store.reconstruct("v", l - 1)
+            kc = store.reconstruct("k", l)
+            vc = store.reconstruct("v", l)
+            o, lse, colmass, m, upd = lazy_attention(q, q_prev, kp, vp, kc, vc, o, lse, colmass,
+                                                     last, keys)
+            out.append(dict(o=o.copy(), lse=lse.copy(), colmass=colmass.copy(), keys=keys, mass=m))
+        q_prev = q.copy()
+    return out, store

@@ -1,0 +1,167 @@
+"""Pins for the oracle's int4 delta codec and base+delta chain (CPU only).
+
+Page "FlashLoop: Fast and Memory-Efficient Looped Transformers via Lazy
+Updates", section "FlashLoop combines three kinds of savings", paragraph 3:
+the KV cache is a base plus low-bit corrections, written only for active
+tokens, 4 bits in the main setting.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import (KVStore, dequantize_groups, f16_rne, pack_int4, quantize_groups,
+                    unpack_int4)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "int4_group_examples.json")
+
+
+def _all_finite_halves():
+    """Every finite binary16 value as an exact Fraction, decoded from its bits."""
+    out = []
+    for bits in range(0x7C00):                     # positive finite halves
+        e, m = bits >> 10, bits & 0x3FF
+        if e == 0:
+            v = Fraction(m, 1 << 24)
+        else:
+            v = Fraction(1024 + m, 1 << 10) * (Fraction(2) ** (e - 15))
+        out.append((v, bits))
+    return out
+
+
+def test_f16_rne_against_exhaustive_table():
+    halves = _all_finite_halves()
+    vals = [v for v, _ in halves]
+    import bisect
+    rng = np.random.default_rng(0)
+    xs = np.concatenate([
+        (rng.random(3000) * 2.0 ** rng.integers(-26, 16, 3000)).astype(np.float32),
+        np.array([v for v, _ in halves[::97]], dtype=np.float64).astype(np.float32),
+        # exact midpoints between neighbouring halves (ties -> even mantissa)
+        np.array([float((halves[i][0] + halves[i + 1][0]) / 2) for i in range(0, 0x7BFF, 131)],
+                 np.float32),
+    ])
+    got = f16_rne(xs).view(np.uint16)
+    for x, g in zip(xs, got):
+        fx = Fraction(float(x))
+        if fx > vals[-1] + (vals[-1] - vals[-2]) / 2:
+            continue                               # overflow range, not used by the codec
+        j = bisect.bisect_left(vals, fx)
+        cands = [c for c in (j - 1, j) if 0 <= c < len(vals)]
+        best = min(cands, key=lambda c: (abs(vals[c] - fx), halves[c][1] & 1))
+        assert int(g) == halves[best][1], (float(x), hex(int(g)), hex(halves[best][1]))
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        data = json.load(f)
+    return data["group"], data["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases()[1], ids=lambda c: c["name"])
+def test_golden_int4_examples(case):
+    group = _golden_cases()[0]
+    delta = np.zeros(group, np.float32)
+    for i, s in enumerate(case["delta"]):
+        delta[i] = np.float32(s)
+    codes, scales = quantize_groups(delta[None], group)
+    assert int(scales.view(np.uint16)[0, 0]) == int(case["scale_bits"], 16)
+    want = np.zeros(group, np.int8)
+    want[:len(case["codes"])] = case["codes"]
+    assert codes[0].tolist() == want.tolist()
+    packed = np.zeros(group // 2, np.uint8)
+    hexes = case["packed"].split()
+    packed[:len(hexes)] = [int(h, 16) for h in hexes]
+    assert pack_int4(codes[0]).tolist() == packed.tolist()
+    assert unpack_int4(packed).tolist() == want.tolist()
+
+
+def test_lattice_round_trip_is_exact():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        s = np.float16(rng.random() * 2.0 ** rng.integers(-14, 8))
+        if s == 0:
+            continue
+        codes = rng.integers(-7, 8, 32)
+        codes[rng.integers(0, 32)] = rng.choice([-7, 7])        # absmax = 7 s
+        delta = (codes.astype(np.float32) * np.float32(s)).astype(np.float32)
+        c, sc = quantize_groups(delta[None])
+        assert sc[0, 0] == s
+        assert c[0].tolist() == codes.tolist()
+        assert np.array_equal(dequantize_groups(c, sc)[0], delta)
+
+
+def test_odd_symmetry_and_error_bound():
+    rng = np.random.default_rng(6)
+    delta = (rng.standard_normal((500, 4, 96)) * 10.0 ** rng.uniform(-4, 2, (500, 4, 1))).astype(np.float32)
+    c, s = quantize_groups(delta)
+    cn, sn = quantize_groups(-delta)
+    assert np.array_equal(cn, -c) and np.array_equal(sn, s)
+    assert c.min() >= -7 and c.max() <= 7
+    deq = dequantize_groups(c, s)
+    g = delta.reshape(500, 4, 3, 32)
+    a = np.abs(g).max(-1)
+    sf = s.astype(np.float64)
+    bound = sf / 2 + np.maximum(0.0, a - 7 * sf) + 1e-6 * a
+    err = np.abs(g - deq.reshape(500, 4, 3, 32)).max(-1)
+    assert np.all(err <= bound)
+    # the scale is the nearest half to absmax/7
+    assert np.all(np.abs(sf - a / 7.0) <= np.maximum(2.0 ** -25, np.abs(a / 7.0) * 2.0 ** -11) + 1e-12)
+
+
+def test_pack_nibble_order():
+    codes = np.array([1, -1, 7, -7, 0, -8 + 1, 3, 4], np.int8)
+    p = pack_int4(codes)
+    assert p.tolist() == [0xF1, 0x97, 0x90, 0x43]
+    assert unpack_int4(p).tolist() == codes.tolist()
+
+
+def test_chain_lattice_deltas_reconstruct_exactly():
+    """Deltas chosen on the int4 lattice make every version exact (reading of
+    'a base plus a sequence of corrections'); inactive tokens carry."""
+    rng = np.random.default_rng(7)
+    n, H, d = 12, 2, 64
+    st = KVStore(n, H, d)
+    k1 = rng.standard_normal((n, H, d)).astype(np.float32)
+    v1 = rng.standard_normal((n, H, d)).astype(np.float32)
+    st.commit(1, np.arange(n), k1, v1)
+    truth = {"k": k1.copy(), "v": v1.copy()}
+    history = {1: {"k": k1.copy(), "v": v1.copy()}}
+    for l, act in ((2, np.arange(n)), (3, np.array([1, 4, 5, 9])), (4, np.array([4, 9]))):
+        new = {}
+        for w in ("k", "v"):
+            s = np.float16(2.0 ** rng.integers(-6, 0))
+            codes = rng.integers(-7, 8, (act.size, H, d))
+            codes[..., 0] = 7
+            codes[..., 32] = -7
+            new[w] = truth[w][act] + codes.astype(np.float32) * np.float32(s)
+        st.commit(l, act, new["k"], new["v"])
+        for w in ("k", "v"):
+            truth[w][act] = new[w]
+        history[l] = {w: truth[w].copy() for w in ("k", "v")}
+    for l in range(1, 5):
+        for w in ("k", "v"):
+            assert np.array_equal(st.reconstruct(w, l), history[l][w]), (l, w)
+    # token 0 is inactive after loop 2: versions 2..4 agree
+    assert np.array_equal(st.reconstruct("k", 4)[0], st.reconstruct("k", 2)[0])
+    assert np.array_equal(st.reconstruct("k", 3, np.array([4, 0])), history[3]["k"][[4, 0]])
+
+
+def test_chain_delta_is_against_previous_reconstruction():
+    rng = np.random.default_rng(8)
+    n, H, d = 6, 1, 32
+    st = KVStore(n, H, d)
+    k1 = rng.standard_normal((n, H, d)).astype(np.float32)
+    st.commit(1, np.arange(n), k1, k1)
+    k2 = k1 + rng.standard_normal((n, H, d)).astype(np.float32)
+    st.commit(2, np.arange(n), k2, k2)
+    rec2 = st.reconstruct("k", 2)
+    k3 = k2 + 0.01 * rng.standard_normal((n, H, d)).astype(np.float32)
+    recs = st.commit(3, np.arange(n), k3, k3)
+    # closed loop: the layer-3 codes quantise k3 - khat2, not k3 - k2
+    c, s = quantize_groups(k3 - rec2)
+    assert np.array_equal(recs["k"].codes, c) and np.array_equal(recs["k"].scales, s)
+    err3 = np.abs(st.reconstruct("k", 3) - k3).max()
+    assert err3 <= np.abs(k3 - rec2).max() / 7 / 2 * 1.01 + 1e-7
