@@ -1,0 +1,204 @@
+/*
+ * flashloop.h -- C ABI of the FlashLoop lazy-update loop step for MI355X (gfx950).
+ *
+ * Source of the method: the page "FlashLoop: Fast and Memory-Efficient Looped
+ * Transformers via Lazy Updates" (rit.work blog), section "FlashLoop combines
+ * three kinds of savings".  Paragraph 1: early loops run in full; later loops
+ * rank tokens by the change of their hidden state and recompute only the
+ * active ones, the others reuse their state and KV entries.  Paragraph 2: keys
+ * are chosen from the previous loop's attention statistics and the chosen group
+ * keeps the previous loop's probability mass.  Paragraph 3: the KV cache is a
+ * compressed base plus a chain of 4-bit corrections written only for active
+ * tokens.  Paragraph 4: the selected data is gathered into dense buffers and
+ * the KV update and compression are fused with the compute.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a HIP device pointer owned by the caller.  The
+ *    library never allocates, frees or copies to the host, never synchronises,
+ *    and launches only on the stream it is given (`stream` is a hipStream_t;
+ *    NULL is the default stream).  All calls are asynchronous.
+ *  - Layouts are row-major and contiguous.  bf16 tensors hold raw bfloat16
+ *    bits (uint16); fp32 tensors hold IEEE binary32.
+ *  - Index lists are int32, ascending and unique, each value in [0, N).  The
+ *    caller guarantees this (the library cannot check device contents without
+ *    synchronising); violating it gives unspecified results but never writes
+ *    outside the buffers the descriptor and the arguments describe.
+ *  - Arguments are validated on the host before any launch.  On failure the
+ *    call returns a non-zero fl_status, launches nothing, and
+ *    flashloop_last_error() describes the problem.  A failed launch returns
+ *    FL_ERR_HIP.  No C++ exception crosses this boundary.
+ *  - The library holds no state besides a thread-local error message; calls
+ *    from several threads are safe.  Calls that write the same buffers on
+ *    different streams race, as any two kernels would.
+ */
+#ifndef FLASHLOOP_H
+#define FLASHLOOP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLASHLOOP_ABI_VERSION 1
+#define FL_MAX_VERSIONS 32          /* versions 1..FL_MAX_VERSIONS */
+
+typedef enum {
+  FL_OK = 0,
+  FL_ERR_ARG = 1,          /* a null pointer, a size out of range, an inconsistent argument */
+  FL_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. head_dim outside {64, 96, 128}) */
+  FL_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_bytes query */
+  FL_ERR_HIP = 4           /* a HIP launch failed; the message holds hipGetErrorString */
+} fl_status;
+
+typedef enum { FL_F32 = 0, FL_BF16 = 1 } fl_dtype;
+typedef enum { FL_SEL_TOKENS = 0, FL_SEL_KEYS = 1 } fl_select_mode;
+typedef enum { FL_ATTEND_FULL = 0, FL_ATTEND_LAZY = 1 } fl_attend_mode;
+typedef enum { FL_ROWS_BY_TOKEN = 0, FL_ROWS_COMPACT = 1 } fl_row_layout;
+
+/* ------------------------------------------------------------------------ */
+/* KV store: a base (version 1) plus int4 delta layers 2..n_versions.        */
+/* (section "FlashLoop combines three kinds of savings", paragraph 3)        */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t n_seq;        /* independent sequences (decode batch); 1 for prefill */
+  int32_t n_heads;      /* H */
+  int32_t head_dim;     /* d in {64, 96, 128} */
+  int32_t n_tokens;     /* N positions per sequence */
+  int32_t n_versions;   /* T >= 1; delta layers 2..T */
+  int32_t base_dtype;   /* fl_dtype of the base, and of every K/V/Q/h input */
+  int32_t group;        /* quantisation group; must be 32 */
+  int32_t layer_cap[FL_MAX_VERSIONS + 1]; /* [l], l in 2..T: record slots per sequence in layer l */
+  void* arena;          /* device memory of flashloop_kv_arena_bytes() bytes, caller-owned */
+  uint64_t arena_bytes;
+} fl_kv_desc;
+
+/* Byte offsets inside the arena (every array 256-byte aligned):
+ *   base_k, base_v        [n_seq][H][N][d]          base_dtype
+ *   slot_map[l]           [n_seq][N]                int32: record slot of token j in layer l, or -1
+ *   codes_k[l], codes_v[l][n_seq][H][cap_l][d/2]    uint8: two int4 codes per byte, low nibble = even element
+ *   scales_k[l],scales_v[l][n_seq][H][cap_l][d/32]  binary16 bits: one scale per group of 32
+ * The reconstruction of token j at version v is
+ *   float(base[j]) + sum_{l=2..v, slot_map[l][j] >= 0} code * float(scale), added in float32 in increasing l. */
+typedef struct {
+  uint64_t base_k, base_v;
+  uint64_t slot_map[FL_MAX_VERSIONS + 1];
+  uint64_t codes_k[FL_MAX_VERSIONS + 1], codes_v[FL_MAX_VERSIONS + 1];
+  uint64_t scales_k[FL_MAX_VERSIONS + 1], scales_v[FL_MAX_VERSIONS + 1];
+  uint64_t total_bytes;
+} fl_kv_layout;
+
+/* Fills *out with the arena layout of *desc (arena pointer not needed).
+ * Returns FL_ERR_ARG / FL_ERR_UNSUPPORTED for an invalid descriptor. */
+fl_status flashloop_kv_layout(const fl_kv_desc* desc, fl_kv_layout* out);
+
+/* Bytes the caller must allocate for desc->arena; 0 if the descriptor is invalid. */
+uint64_t flashloop_kv_arena_bytes(const fl_kv_desc* desc);
+
+/* ------------------------------------------------------------------------ */
+/* flashloop_kv_commit -- write one loop's K/V rows into the store.          */
+/* (section "FlashLoop combines three kinds of savings", paragraph 3)        */
+/* version 1: copies the rows into the base.  version l >= 2: for each active */
+/* token j, head h and X in {K, V}: delta = X_new - X^(l-1) in float32, per   */
+/* group of 32: s = f16_rne(min(absmax/7, 65504)), code = clamp(rint(delta/s),*/
+/* -7, 7) (0 when s == 0); records go to slots slot_base + r (r = position in */
+/* active_idx) and slot_map[l][j] is set to that slot.  With reset_map != 0   */
+/* every other slot_map[l] entry of the sequence is set to -1; with 0 they    */
+/* are left as they are (to add rows to a layer written by an earlier call).  */
+/* Inactive tokens get no entry.                                              */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const fl_kv_desc* kv;
+  int32_t version;              /* 1..n_versions */
+  const int32_t* active_idx;    /* [n_seq][n_active] ascending token positions */
+  int32_t n_active;             /* 0..N; slot_base + n_active <= layer_cap[version] */
+  int32_t slot_base;
+  int32_t reset_map;
+  const void* k_new;            /* [n_seq][R][H][d] base_dtype, R = N (rows by token) or n_active */
+  const void* v_new;
+  int32_t src_layout;           /* fl_row_layout of k_new / v_new */
+} fl_commit_args;
+
+fl_status flashloop_kv_commit(const fl_commit_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* flashloop_select -- token ranking and key selection.                      */
+/* (section "FlashLoop combines three kinds of savings", paragraphs 1 and 2) */
+/* TOKENS: scores[i] = sum_k (h_cur[i,k] - h_prev[i,k])^2 accumulated in     */
+/*   float64; rows outside cand_idx (when given) are written as 0 without    */
+/*   being read (they were carried unchanged).  Then out_idx = the k rows    */
+/*   with the largest score, ties to the lower index, ascending.             */
+/* KEYS: for each of n_seg segments of key_scores (float32, e.g. column mass */
+/*   [n_seq*H][N]), out_idx[seg] = its top-k positions by the same rule.     */
+/* -0.0 and +0.0 compare equal; NaN scores give unspecified (in-range) sets. */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t mode;                 /* fl_select_mode */
+  /* TOKENS */
+  const void* h_cur;            /* [n_rows][hidden] h_dtype */
+  const void* h_prev;
+  int32_t h_dtype;
+  int64_t n_rows;               /* 1..65536 */
+  int64_t hidden;
+  const int32_t* cand_idx;      /* optional, ascending; NULL = all rows */
+  int32_t n_cand;
+  double* scores;               /* [n_rows] output (float64), required in TOKENS mode */
+  /* KEYS */
+  const float* key_scores;      /* [n_seg][seg_len] */
+  int32_t n_seg;
+  int64_t seg_len;              /* 1..65536 */
+  /* both */
+  int32_t k;                    /* 0..n_rows (TOKENS) or 0..seg_len (KEYS) */
+  int32_t* out_idx;             /* [n_seg][k] (TOKENS: [k]) */
+} fl_select_args;
+
+fl_status flashloop_select(const fl_select_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* flashloop_attend -- causal attention over the reconstructed K^, V^.       */
+/* (section "FlashLoop combines three kinds of savings", paragraphs 2 and 4) */
+/* FULL, version v: for every active row i and head h, over keys j <= i:     */
+/*   o_i = sum_j p_ij v^_j, lse_i = log sum_j exp(s_ij), s_ij = q_i.k^_j/sqrt(d),*/
+/*   p_ij = exp(s_ij - lse_i); colmass[h][j] = sum over active i >= j of p_ij  */
+/*   (every entry of colmass is overwritten).                                */
+/* LAZY, version v (reads v-1 and v): S_i = selected keys <= i;               */
+/*   p'_ij = exp(q_prev_i.k^(v-1)_j/sqrt(d) - lse_i), m_i = sum p'_ij,         */
+/*   a_i = sum p'_ij v^(v-1)_j; otilde_i = softmax over S_i of the current    */
+/*   logits applied to v^(v)_j; o_i <- m_i*otilde_i + (o_i - a_i);            */
+/*   lse_i <- M + log Z - log m_i; colmass[h][j] += sum_i (p_ij - p'_ij) for   */
+/*   selected j, with p_ij = exp(s_ij - lse_i(new)).  Rows with empty S_i or */
+/*   m_i == 0 keep o and lse and add nothing to colmass.                     */
+/* o, lse and colmass are updated in place; rows that are not active are not */
+/* read or written.  Any key tensor entry not described above is untouched.  */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t mode;                 /* fl_attend_mode */
+  const fl_kv_desc* kv;
+  int32_t version;              /* FULL: 1..T; LAZY: 2..T */
+  const void* q_cur;            /* [n_seq][R][H][d] base_dtype */
+  const void* q_prev;           /* LAZY only; same layout */
+  int32_t q_layout;             /* fl_row_layout: R = N, or R = n_active */
+  const int32_t* active_idx;    /* [n_seq][n_active] ascending; FULL may pass NULL = all rows */
+  int32_t n_active;
+  const int32_t* key_idx;       /* LAZY: [n_seq][H][n_keys] ascending */
+  int32_t n_keys;               /* LAZY: 1..N */
+  float* o;                     /* [n_seq][R][H][d] float32, R per o_layout */
+  float* lse;                   /* [n_seq][R][H] float32 */
+  int32_t o_layout;             /* fl_row_layout */
+  float* colmass;               /* [n_seq][H][N] float32 */
+  void* workspace;              /* device, >= flashloop_attend_workspace_bytes(args) */
+  uint64_t workspace_bytes;
+} fl_attend_args;
+
+uint64_t  flashloop_attend_workspace_bytes(const fl_attend_args* args);
+fl_status flashloop_attend(const fl_attend_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+const char* flashloop_last_error(void);  /* thread-local; "" after a successful call */
+int32_t     flashloop_abi_version(void); /* FLASHLOOP_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHLOOP_H */

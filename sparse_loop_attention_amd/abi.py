@@ -1,0 +1,237 @@
+"""ctypes binding of libflashloop.so (include/flashloop.h): argument marshalling only.
+
+Every function takes torch tensors for device memory and launches on torch's
+current stream; all arithmetic happens in the HIP library.  There is no CPU
+fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import torch  # noqa: F401  (loads the HIP runtime that the library binds to)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashloop.so")
+MAX_VERSIONS = 32
+
+FL_OK, FL_ERR_ARG, FL_ERR_UNSUPPORTED, FL_ERR_WORKSPACE, FL_ERR_HIP = range(5)
+FL_F32, FL_BF16 = 0, 1
+FL_SEL_TOKENS, FL_SEL_KEYS = 0, 1
+FL_ATTEND_FULL, FL_ATTEND_LAZY = 0, 1
+FL_ROWS_BY_TOKEN, FL_ROWS_COMPACT = 0, 1
+
+EXPORTS = ("flashloop_kv_layout", "flashloop_kv_arena_bytes", "flashloop_kv_commit", "flashloop_select",
+           "flashloop_attend_workspace_bytes", "flashloop_attend", "flashloop_last_error",
+           "flashloop_abi_version")
+
+
+class fl_kv_desc(C.Structure):
+    _fields_ = [("n_seq", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("n_tokens", C.c_int32), ("n_versions", C.c_int32), ("base_dtype", C.c_int32),
+                ("group", C.c_int32), ("layer_cap", C.c_int32 * (MAX_VERSIONS + 1)),
+                ("arena", C.c_void_p), ("arena_bytes", C.c_uint64)]
+
+
+class fl_kv_layout(C.Structure):
+    _fields_ = [("base_k", C.c_uint64), ("base_v", C.c_uint64),
+                ("slot_map", C.c_uint64 * (MAX_VERSIONS + 1)),
+                ("codes_k", C.c_uint64 * (MAX_VERSIONS + 1)), ("codes_v", C.c_uint64 * (MAX_VERSIONS + 1)),
+                ("scales_k", C.c_uint64 * (MAX_VERSIONS + 1)), ("scales_v", C.c_uint64 * (MAX_VERSIONS + 1)),
+                ("total_bytes", C.c_uint64)]
+
+
+class fl_commit_args(C.Structure):
+    _fields_ = [("kv", C.POINTER(fl_kv_desc)), ("version", C.c_int32), ("active_idx", C.c_void_p),
+                ("n_active", C.c_int32), ("slot_base", C.c_int32), ("reset_map", C.c_int32),
+                ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("src_layout", C.c_int32)]
+
+
+class fl_select_args(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("h_cur", C.c_void_p), ("h_prev", C.c_void_p), ("h_dtype", C.c_int32),
+                ("n_rows", C.c_int64), ("hidden", C.c_int64), ("cand_idx", C.c_void_p), ("n_cand", C.c_int32),
+                ("scores", C.c_void_p), ("key_scores", C.c_void_p), ("n_seg", C.c_int32),
+                ("seg_len", C.c_int64), ("k", C.c_int32), ("out_idx", C.c_void_p)]
+
+
+class fl_attend_args(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("kv", C.POINTER(fl_kv_desc)), ("version", C.c_int32),
+                ("q_cur", C.c_void_p), ("q_prev", C.c_void_p), ("q_layout", C.c_int32),
+                ("active_idx", C.c_void_p), ("n_active", C.c_int32), ("key_idx", C.c_void_p),
+                ("n_keys", C.c_int32), ("o", C.c_void_p), ("lse", C.c_void_p), ("o_layout", C.c_int32),
+                ("colmass", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64)]
+
+
+class FlashLoopError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"flashloop status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m sparse_loop_attention_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        L.flashloop_kv_layout.argtypes = [C.POINTER(fl_kv_desc), C.POINTER(fl_kv_layout)]
+        L.flashloop_kv_arena_bytes.argtypes = [C.POINTER(fl_kv_desc)]
+        L.flashloop_kv_arena_bytes.restype = C.c_uint64
+        L.flashloop_kv_commit.argtypes = [C.POINTER(fl_commit_args), C.c_void_p]
+        L.flashloop_select.argtypes = [C.POINTER(fl_select_args), C.c_void_p]
+        L.flashloop_attend_workspace_bytes.argtypes = [C.POINTER(fl_attend_args)]
+        L.flashloop_attend_workspace_bytes.restype = C.c_uint64
+        L.flashloop_attend.argtypes = [C.POINTER(fl_attend_args), C.c_void_p]
+        L.flashloop_last_error.restype = C.c_char_p
+        L.flashloop_abi_version.restype = C.c_int32
+        for f in ("flashloop_kv_layout", "flashloop_kv_commit", "flashloop_select", "flashloop_attend"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != FL_OK:
+        raise FlashLoopError(status, lib().flashloop_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def dtype_code(t: torch.dtype) -> int:
+    return {torch.float32: FL_F32, torch.bfloat16: FL_BF16}[t]
+
+
+# --------------------------------------------------------------------------- KV
+class KVStore:
+    """A KV arena (torch uint8 tensor) and its descriptor."""
+
+    def __init__(self, n_seq: int, n_heads: int, head_dim: int, n_tokens: int, n_versions: int,
+                 dtype: torch.dtype, layer_caps: Sequence[int], device="cuda", arena: Optional[torch.Tensor] = None):
+        d = fl_kv_desc()
+        d.n_seq, d.n_heads, d.head_dim, d.n_tokens = n_seq, n_heads, head_dim, n_tokens
+        d.n_versions, d.base_dtype, d.group = n_versions, dtype_code(dtype), 32
+        for i, cap in enumerate(layer_caps):
+            d.layer_cap[i + 2] = cap
+        self.desc = d
+        self.dtype = dtype
+        nbytes = kv_arena_bytes(d)
+        if nbytes == 0:
+            raise FlashLoopError(FL_ERR_ARG, lib().flashloop_last_error().decode())
+        self.arena = torch.empty(nbytes, dtype=torch.uint8, device=device) if arena is None else arena
+        d.arena = self.arena.data_ptr()
+        d.arena_bytes = self.arena.numel()
+        self.layout = kv_layout(d)
+
+    def view(self, name: str, layer: int = 0) -> torch.Tensor:
+        """A typed view of one arena array (for tests and checkpoints)."""
+        d, lay = self.desc, self.layout
+        S, H, N, D = d.n_seq, d.n_heads, d.n_tokens, d.head_dim
+        if name in ("base_k", "base_v"):
+            off = getattr(lay, name)
+            es = 2 if self.dtype == torch.bfloat16 else 4
+            n = S * H * N * D
+            t = self.arena[off:off + n * es].view(self.dtype)
+            return t.view(S, H, N, D)
+        cap = d.layer_cap[layer]
+        if name == "slot_map":
+            off = lay.slot_map[layer]
+            return self.arena[off:off + S * N * 4].view(torch.int32).view(S, N)
+        if name in ("codes_k", "codes_v"):
+            off = getattr(lay, name)[layer]
+            return self.arena[off:off + S * H * cap * D // 2].view(S, H, cap, D // 2)
+        if name in ("scales_k", "scales_v"):
+            off = getattr(lay, name)[layer]
+            return self.arena[off:off + S * H * cap * (D // 32) * 2].view(torch.int16).view(S, H, cap, D // 32)
+        raise KeyError(name)
+
+
+def kv_layout(desc: fl_kv_desc) -> fl_kv_layout:
+    out = fl_kv_layout()
+    _check(lib().flashloop_kv_layout(C.byref(desc), C.byref(out)))
+    return out
+
+
+def kv_arena_bytes(desc: fl_kv_desc) -> int:
+    return int(lib().flashloop_kv_arena_bytes(C.byref(desc)))
+
+
+def kv_commit(kv: KVStore, version: int, active_idx: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+              slot_base: int = 0, reset_map: bool = True, compact: bool = False, stream=None) -> None:
+    a = fl_commit_args()
+    a.kv = C.pointer(kv.desc)
+    a.version = version
+    a.active_idx = _ptr(active_idx)
+    a.n_active = active_idx.shape[-1]
+    a.slot_base, a.reset_map = slot_base, int(reset_map)
+    a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
+    a.src_layout = FL_ROWS_COMPACT if compact else FL_ROWS_BY_TOKEN
+    _check(lib().flashloop_kv_commit(C.byref(a), _stream(stream)))
+
+
+# --------------------------------------------------------------------------- select
+def select_tokens(h_cur: torch.Tensor, h_prev: torch.Tensor, k: int, scores: torch.Tensor,
+                  out_idx: torch.Tensor, cand_idx: Optional[torch.Tensor] = None, stream=None) -> None:
+    a = fl_select_args()
+    a.mode = FL_SEL_TOKENS
+    a.h_cur, a.h_prev, a.h_dtype = _ptr(h_cur), _ptr(h_prev), dtype_code(h_cur.dtype)
+    a.n_rows, a.hidden = h_cur.shape[0], h_cur.shape[1]
+    a.cand_idx = _ptr(cand_idx)
+    a.n_cand = 0 if cand_idx is None else cand_idx.numel()
+    a.scores = _ptr(scores)
+    a.k, a.out_idx = k, _ptr(out_idx)
+    _check(lib().flashloop_select(C.byref(a), _stream(stream)))
+
+
+def select_keys(key_scores: torch.Tensor, k: int, out_idx: torch.Tensor, stream=None) -> None:
+    a = fl_select_args()
+    a.mode = FL_SEL_KEYS
+    a.key_scores = _ptr(key_scores)
+    a.seg_len = key_scores.shape[-1]
+    a.n_seg = key_scores.numel() // key_scores.shape[-1]
+    a.k, a.out_idx = k, _ptr(out_idx)
+    _check(lib().flashloop_select(C.byref(a), _stream(stream)))
+
+
+# --------------------------------------------------------------------------- attend
+def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx, n_active: int,
+                key_idx, o, lse, colmass, workspace=None, q_compact=False, o_compact=False) -> fl_attend_args:
+    a = fl_attend_args()
+    a.mode, a.kv, a.version = mode, C.pointer(kv.desc), version
+    a.q_cur, a.q_prev = _ptr(q_cur), _ptr(q_prev)
+    a.q_layout = FL_ROWS_COMPACT if q_compact else FL_ROWS_BY_TOKEN
+    a.active_idx, a.n_active = _ptr(active_idx), n_active
+    a.key_idx = _ptr(key_idx)
+    a.n_keys = 0 if key_idx is None else key_idx.shape[-1]
+    a.o, a.lse, a.colmass = _ptr(o), _ptr(lse), _ptr(colmass)
+    a.o_layout = FL_ROWS_COMPACT if o_compact else FL_ROWS_BY_TOKEN
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    return a
+
+
+def attend_workspace_bytes(a: fl_attend_args) -> int:
+    return int(lib().flashloop_attend_workspace_bytes(C.byref(a)))
+
+
+def attend(a: fl_attend_args, stream=None) -> None:
+    _check(lib().flashloop_attend(C.byref(a), _stream(stream)))
+
+
+def abi_version() -> int:
+    return int(lib().flashloop_abi_version())

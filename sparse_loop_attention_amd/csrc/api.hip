@@ -1,0 +1,226 @@
+// C ABI of the FlashLoop loop step: argument validation, arena layout,
+// workspace planning and dispatch.  Host code only; every step of the path
+// runs in the kernels of select.hip, kv.hip, attn_rows.hip and attn_mfma.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "flashloop.h"
+#include "fl_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fl_status fail(fl_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+fl_status ok() {
+  g_err[0] = '\0';
+  return FL_OK;
+}
+fl_status hip_fail(hipError_t e, const char* what) {
+  return fail(FL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fl_status check_desc(const fl_kv_desc* d, bool need_arena) {
+  if (!d) return fail(FL_ERR_ARG, "kv descriptor is NULL");
+  if (d->n_seq < 1 || d->n_heads < 1 || d->n_tokens < 1)
+    return fail(FL_ERR_ARG, "kv: n_seq, n_heads and n_tokens must be >= 1");
+  if (d->n_tokens > (1 << 24)) return fail(FL_ERR_UNSUPPORTED, "kv: n_tokens > 2^24");
+  if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128)
+    return fail(FL_ERR_UNSUPPORTED, "kv: head_dim %d not in {64, 96, 128}", d->head_dim);
+  if (d->n_versions < 1 || d->n_versions > FL_MAX_VERSIONS)
+    return fail(FL_ERR_ARG, "kv: n_versions %d outside 1..%d", d->n_versions, FL_MAX_VERSIONS);
+  if (d->base_dtype != FL_F32 && d->base_dtype != FL_BF16) return fail(FL_ERR_ARG, "kv: unknown base_dtype");
+  if (d->group != 32) return fail(FL_ERR_UNSUPPORTED, "kv: group must be 32");
+  for (int l = 2; l <= d->n_versions; ++l)
+    if (d->layer_cap[l] < 0 || d->layer_cap[l] > d->n_tokens)
+      return fail(FL_ERR_ARG, "kv: layer_cap[%d] = %d outside 0..n_tokens", l, d->layer_cap[l]);
+  if (need_arena && (!d->arena || !aligned(d->arena, 256)))
+    return fail(FL_ERR_ARG, "kv: arena is NULL or not 256-byte aligned");
+  return FL_OK;
+}
+
+void layout_of(const fl_kv_desc* d, fl_kv_layout* o) {
+  std::memset(o, 0, sizeof(*o));
+  const uint64_t S = d->n_seq, H = d->n_heads, N = d->n_tokens, D = d->head_dim;
+  const uint64_t es = d->base_dtype == FL_BF16 ? 2 : 4;
+  uint64_t off = 0;
+  o->base_k = off; off = align256(off + S * H * N * D * es);
+  o->base_v = off; off = align256(off + S * H * N * D * es);
+  for (int l = 2; l <= d->n_versions; ++l) {
+    const uint64_t cap = d->layer_cap[l];
+    o->slot_map[l] = off; off = align256(off + S * N * 4);
+    o->codes_k[l] = off; off = align256(off + S * H * cap * (D / 2));
+    o->codes_v[l] = off; off = align256(off + S * H * cap * (D / 2));
+    o->scales_k[l] = off; off = align256(off + S * H * cap * (D / 32) * 2);
+    o->scales_v[l] = off; off = align256(off + S * H * cap * (D / 32) * 2);
+  }
+  o->total_bytes = off;
+}
+
+fl_status check_arena(const fl_kv_desc* d, fl_kv_layout* lay) {
+  fl_status st = check_desc(d, true);
+  if (st != FL_OK) return st;
+  layout_of(d, lay);
+  if (d->arena_bytes < lay->total_bytes)
+    return fail(FL_ERR_ARG, "kv: arena_bytes %llu < required %llu", (unsigned long long)d->arena_bytes,
+                (unsigned long long)lay->total_bytes);
+  return FL_OK;
+}
+
+}  // namespace
+
+namespace fl {
+
+KvView make_view(const fl_kv_desc& d, const fl_kv_layout& lay) {
+  KvView v;
+  std::memset(&v, 0, sizeof(v));
+  v.arena = static_cast<const uint8_t*>(d.arena);
+  v.n_seq = d.n_seq; v.H = d.n_heads; v.d = d.head_dim; v.N = d.n_tokens; v.T = d.n_versions;
+  v.dtype = d.base_dtype;
+  v.base[0] = lay.base_k; v.base[1] = lay.base_v;
+  for (int l = 2; l <= d.n_versions; ++l) {
+    v.cap[l] = d.layer_cap[l];
+    v.slot_map[l] = lay.slot_map[l];
+    v.codes[0][l] = lay.codes_k[l]; v.codes[1][l] = lay.codes_v[l];
+    v.scales[0][l] = lay.scales_k[l]; v.scales[1][l] = lay.scales_v[l];
+  }
+  return v;
+}
+
+}  // namespace fl
+
+extern "C" {
+
+int32_t flashloop_abi_version(void) { return FLASHLOOP_ABI_VERSION; }
+const char* flashloop_last_error(void) { return g_err; }
+
+fl_status flashloop_kv_layout(const fl_kv_desc* desc, fl_kv_layout* out) {
+  if (!out) return fail(FL_ERR_ARG, "layout output is NULL");
+  fl_status st = check_desc(desc, false);
+  if (st != FL_OK) return st;
+  layout_of(desc, out);
+  return ok();
+}
+
+uint64_t flashloop_kv_arena_bytes(const fl_kv_desc* desc) {
+  if (check_desc(desc, false) != FL_OK) return 0;
+  fl_kv_layout lay;
+  layout_of(desc, &lay);
+  ok();
+  return lay.total_bytes;
+}
+
+fl_status flashloop_kv_commit(const fl_commit_args* a, void* stream) {
+  if (!a) return fail(FL_ERR_ARG, "commit args are NULL");
+  fl_kv_layout lay;
+  fl_status st = check_arena(a->kv, &lay);
+  if (st != FL_OK) return st;
+  const fl_kv_desc& d = *a->kv;
+  if (a->version < 1 || a->version > d.n_versions)
+    return fail(FL_ERR_ARG, "commit: version %d outside 1..%d", a->version, d.n_versions);
+  if (a->n_active < 0 || a->n_active > d.n_tokens) return fail(FL_ERR_ARG, "commit: n_active out of range");
+  if (a->n_active == 0) return ok();
+  if (!a->active_idx || !a->k_new || !a->v_new) return fail(FL_ERR_ARG, "commit: NULL index or K/V pointer");
+  if (!aligned(a->k_new, 16) || !aligned(a->v_new, 16) || !aligned(a->active_idx, 4))
+    return fail(FL_ERR_ARG, "commit: K/V must be 16-byte aligned");
+  if (a->src_layout != FL_ROWS_BY_TOKEN && a->src_layout != FL_ROWS_COMPACT)
+    return fail(FL_ERR_ARG, "commit: unknown src_layout");
+  if (a->version >= 2) {
+    if (a->slot_base < 0 || static_cast<int64_t>(a->slot_base) + a->n_active > d.layer_cap[a->version])
+      return fail(FL_ERR_ARG, "commit: slots %d..%d exceed layer_cap[%d] = %d", a->slot_base,
+                  a->slot_base + a->n_active, a->version, d.layer_cap[a->version]);
+  }
+  fl::KvView kv = fl::make_view(d, lay);
+  hipError_t e = fl::launch_commit(*a, kv, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "commit launch");
+  return ok();
+}
+
+fl_status flashloop_select(const fl_select_args* a, void* stream) {
+  if (!a) return fail(FL_ERR_ARG, "select args are NULL");
+  if (a->mode == FL_SEL_TOKENS) {
+    if (!a->h_cur || !a->h_prev || !a->scores) return fail(FL_ERR_ARG, "select: NULL h or scores");
+    if (a->h_dtype != FL_F32 && a->h_dtype != FL_BF16) return fail(FL_ERR_ARG, "select: unknown h_dtype");
+    if (a->n_rows < 1 || a->n_rows > 65536) return fail(FL_ERR_UNSUPPORTED, "select: n_rows outside 1..65536");
+    if (a->hidden < 8 || a->hidden % 8) return fail(FL_ERR_UNSUPPORTED, "select: hidden must be a multiple of 8");
+    if (!aligned(a->h_cur, 16) || !aligned(a->h_prev, 16) || !aligned(a->scores, 8))
+      return fail(FL_ERR_ARG, "select: h must be 16-byte aligned");
+    if (a->k < 0 || a->k > a->n_rows) return fail(FL_ERR_ARG, "select: k outside 0..n_rows");
+    if (a->cand_idx && (a->n_cand < 0 || a->n_cand > a->n_rows))
+      return fail(FL_ERR_ARG, "select: n_cand outside 0..n_rows");
+  } else if (a->mode == FL_SEL_KEYS) {
+    if (!a->key_scores) return fail(FL_ERR_ARG, "select: NULL key_scores");
+    if (a->n_seg < 1) return fail(FL_ERR_ARG, "select: n_seg must be >= 1");
+    if (a->seg_len < 1 || a->seg_len > 65536) return fail(FL_ERR_UNSUPPORTED, "select: seg_len outside 1..65536");
+    if (a->k < 0 || a->k > a->seg_len) return fail(FL_ERR_ARG, "select: k outside 0..seg_len");
+  } else {
+    return fail(FL_ERR_ARG, "select: unknown mode %d", a->mode);
+  }
+  if (a->k > 0 && !a->out_idx) return fail(FL_ERR_ARG, "select: NULL out_idx");
+  hipError_t e = fl::launch_select(*a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+static fl_status check_attend(const fl_attend_args* a, fl_kv_layout* lay) {
+  if (!a) return fail(FL_ERR_ARG, "attend args are NULL");
+  fl_status st = check_arena(a->kv, lay);
+  if (st != FL_OK) return st;
+  const fl_kv_desc& d = *a->kv;
+  const bool lazy = a->mode == FL_ATTEND_LAZY;
+  if (a->mode != FL_ATTEND_FULL && !lazy) return fail(FL_ERR_ARG, "attend: unknown mode %d", a->mode);
+  if (a->version < (lazy ? 2 : 1) || a->version > d.n_versions)
+    return fail(FL_ERR_ARG, "attend: version %d invalid for this mode", a->version);
+  if (a->n_active < (lazy ? 0 : 1) || a->n_active > d.n_tokens)
+    return fail(FL_ERR_ARG, "attend: n_active %d out of range", a->n_active);
+  if (!lazy && !a->active_idx && a->n_active != d.n_tokens)
+    return fail(FL_ERR_ARG, "attend: NULL active_idx requires n_active == n_tokens");
+  if (lazy && a->n_active > 0 && !a->active_idx) return fail(FL_ERR_ARG, "attend: LAZY needs active_idx");
+  if (!a->q_cur || (lazy && !a->q_prev)) return fail(FL_ERR_ARG, "attend: NULL query");
+  if (!aligned(a->q_cur, 16) || (lazy && !aligned(a->q_prev, 16)))
+    return fail(FL_ERR_ARG, "attend: queries must be 16-byte aligned");
+  if (lazy && (!a->key_idx || a->n_keys < 1 || a->n_keys > d.n_tokens))
+    return fail(FL_ERR_ARG, "attend: LAZY needs key_idx with 1 <= n_keys <= n_tokens");
+  if (!a->o || !a->lse || !a->colmass) return fail(FL_ERR_ARG, "attend: NULL o, lse or colmass");
+  if (!aligned(a->o, 16)) return fail(FL_ERR_ARG, "attend: o must be 16-byte aligned");
+  if (a->q_layout != FL_ROWS_BY_TOKEN && a->q_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: q_layout");
+  if (a->o_layout != FL_ROWS_BY_TOKEN && a->o_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: o_layout");
+  return FL_OK;
+}
+
+uint64_t flashloop_attend_workspace_bytes(const fl_attend_args* a) {
+  fl_kv_layout lay;
+  if (!a || !a->kv || check_desc(a->kv, false) != FL_OK) return 0;
+  (void)lay;
+  return fl::plan_attend(*a).off_total;
+}
+
+fl_status flashloop_attend(const fl_attend_args* a, void* stream) {
+  fl_kv_layout lay;
+  fl_status st = check_attend(a, &lay);
+  if (st != FL_OK) return st;
+  if (a->n_active == 0) return ok();               // LAZY with no active rows: nothing changes
+  const fl::AttendPlan p = fl::plan_attend(*a);
+  if (p.off_total > 0 && (!a->workspace || a->workspace_bytes < p.off_total || !aligned(a->workspace, 256)))
+    return fail(FL_ERR_WORKSPACE, "attend: workspace needs %llu bytes (256-byte aligned), got %llu",
+                (unsigned long long)p.off_total, (unsigned long long)a->workspace_bytes);
+  fl::KvView kv = fl::make_view(*a->kv, lay);
+  hipError_t e = fl::launch_attend(*a, kv, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attend launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Host-side launch entry points of each kernel family (validated arguments in).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "flashloop.h"
+#include "fl_common.hpp"
+
+namespace fl {
+
+KvView make_view(const fl_kv_desc& d, const fl_kv_layout& lay);
+
+hipError_t launch_select(const fl_select_args& a, hipStream_t st);
+hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t st);
+
+// Workspace layout of an attend call, shared by sizing and launching.
+struct AttendPlan {
+  bool mfma;            // tiled bf16 MFMA path (else the per-row path)
+  int64_t rows;         // active rows per sequence
+  int64_t keys;         // key slots per (sequence, head): n_keys (LAZY) or N (FULL)
+  int splits;           // per-row path: key splits
+  // byte offsets in the workspace
+  uint64_t off_part, off_logit, off_stat, off_gather, off_total;
+};
+AttendPlan plan_attend(const fl_attend_args& a);
+hipError_t launch_attend(const fl_attend_args& a, const KvView& kv, const AttendPlan& p, hipStream_t st);
+
+}  // namespace fl

@@ -1,0 +1,261 @@
+// Token ranking and key selection kernels.
+//
+// Page "FlashLoop: Fast and Memory-Efficient Looped Transformers via Lazy
+// Updates", section "FlashLoop combines three kinds of savings": paragraph 1
+// ranks tokens by how much their hidden state changed (only the top fraction
+// is recomputed); paragraph 2 picks keys from the previous loop's attention
+// statistics.  Both reduce to "k largest, ties to the lower index, ascending".
+#include "fl_common.hpp"
+#include "fl_launch.hpp"
+
+namespace fl {
+
+// ---------------------------------------------------------------------------
+// delta norm: one wave per row, float64 accumulation of (h_cur - h_prev)^2.
+// Each lane streams 8 elements (16 B of bf16) per step, 4 steps in flight.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void k_delta_norm(const void* __restrict__ h_cur,
+                                                    const void* __restrict__ h_prev, int64_t n_rows,
+                                                    int64_t hidden, const int32_t* __restrict__ cand,
+                                                    int32_t n_cand, double* __restrict__ scores) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  if (cand != nullptr) {
+    int lo = 0, hi = n_cand;                      // first index with cand[idx] >= row
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (cand[mid] < row) lo = mid + 1; else hi = mid;
+    }
+    if (lo >= n_cand || cand[lo] != row) {        // carried row: unchanged, scores exactly 0
+      if (lane == 0) scores[row] = 0.0;
+      return;
+    }
+  }
+  const int64_t base = row * hidden;
+  double acc = 0.0;
+  constexpr int kUnroll = 4;
+  int64_t e = static_cast<int64_t>(lane) * 8;
+  for (; e + (kUnroll - 1) * 512 < hidden; e += kUnroll * 512) {
+    float a[kUnroll][8], b[kUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      load8<DT>(h_cur, base + e + u * 512, a[u]);
+      load8<DT>(h_prev, base + e + u * 512, b[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double t = static_cast<double>(a[u][i]) - static_cast<double>(b[u][i]);
+        acc = fma(t, t, acc);
+      }
+  }
+  for (; e < hidden; e += 512) {
+    float a[8], b[8];
+    load8<DT>(h_cur, base + e, a);
+    load8<DT>(h_prev, base + e, b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double t = static_cast<double>(a[i]) - static_cast<double>(b[i]);
+      acc = fma(t, t, acc);
+    }
+  }
+  acc = wave_sum_f64(acc);
+  if (lane == 0) scores[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// top-k by radix select over order-preserving key bits.
+// One 1024-thread workgroup per segment; thread t owns elements
+// [t*EPT, (t+1)*EPT) so that the final compaction is in index order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t order_key(double x) {
+  if (x == 0.0) x = 0.0;                              // -0.0 == +0.0
+  const uint64_t u = __double_as_longlong(x);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ uint32_t order_key(float x) {
+  if (x == 0.0f) x = 0.0f;
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+
+// Exclusive scan of one int per thread across the workgroup; returns the total.
+__device__ __forceinline__ int block_excl_scan(int v, int* lds_waves, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) lds_waves[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kTopkWaves ? lds_waves[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int o = 1; o < kTopkWaves; o <<= 1) {
+      const int t = __shfl_up(wi, o, 64);
+      if (lane >= o) wi += t;
+    }
+    if (lane < kTopkWaves) lds_waves[lane] = wi - w;   // exclusive wave offsets
+    if (lane == kTopkWaves - 1) lds_waves[kTopkWaves] = wi;
+  }
+  __syncthreads();
+  const int res = lds_waves[wave] + incl - v;
+  total = lds_waves[kTopkWaves];
+  __syncthreads();
+  return res;
+}
+
+template <typename ScoreT, int EPT>
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict__ scores,
+                                                       int64_t seg_len, int32_t k,
+                                                       int32_t* __restrict__ out_idx) {
+  using KeyT = decltype(order_key(ScoreT{}));
+  constexpr int kBits = sizeof(KeyT) * 8;
+  __shared__ int hist[256];
+  __shared__ int scan_tmp[kTopkWaves + 1];
+  __shared__ int sel_bin, sel_above;
+
+  const int64_t seg = blockIdx.x;
+  const ScoreT* src = scores + seg * seg_len;
+  int32_t* dst = out_idx + seg * static_cast<int64_t>(k);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t first = static_cast<int64_t>(tid) * EPT;
+
+  if (k == 0) return;
+  if (k >= seg_len) {                                 // everything, already ascending
+    for (int64_t i = tid; i < seg_len; i += kTopkThreads) dst[i] = static_cast<int32_t>(i);
+    return;
+  }
+  KeyT key[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int64_t i = first + e;
+    key[e] = i < seg_len ? order_key(src[i]) : KeyT(0);
+  }
+
+  if (tid == 0) { sel_bin = 0; sel_above = 0; }
+  KeyT prefix = 0, pmask = 0;
+  int k_rem = k;                                      // how many still to take at/below prefix
+  for (int shift = kBits - 8; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const bool act = (first + e < seg_len) && ((key[e] & pmask) == prefix);
+      const int bin = static_cast<int>((key[e] >> shift) & 0xFF);
+      // fast path: every active lane of the wave falls into one bin
+      const uint64_t m = __ballot(act);
+      if (m == 0) continue;
+      const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
+      const int lbin = __shfl(bin, leader, 64);
+      const uint64_t same = __ballot(act && bin == lbin);
+      if (same == m) {
+        if (lane == leader) atomicAdd(&hist[lbin], __popcll(m));
+      } else if (act) {
+        atomicAdd(&hist[bin], 1);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {                                   // one wave finds the crossing bin, top down
+      // lane L owns bins 255-4L .. 252-4L (descending)
+      int c[4], s = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; s += c[i]; }
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      int above = incl - s;                           // count in bins strictly above my 4
+      int found = -1, found_above = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (found < 0 && above < k_rem && above + c[i] >= k_rem) { found = 255 - 4 * lane - i; found_above = above; }
+        above += c[i];
+      }
+      if (found >= 0) { sel_bin = found; sel_above = found_above; }
+    }
+    __syncthreads();
+    const int b = sel_bin;
+    k_rem -= sel_above;
+    prefix |= static_cast<KeyT>(b) << shift;
+    pmask |= static_cast<KeyT>(0xFF) << shift;
+    __syncthreads();
+  }
+  // prefix is now the exact key of the k-th largest; take every key above it and
+  // the first k_rem keys equal to it in index order.
+  int n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) n_eq += (first + e < seg_len && key[e] == prefix) ? 1 : 0;
+  int tot;
+  int eq_before = block_excl_scan(n_eq, scan_tmp, tot);
+  int n_sel = 0;
+  {
+    int eq_rank = eq_before;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (first + e >= seg_len) continue;
+      if (key[e] > prefix) ++n_sel;
+      else if (key[e] == prefix) { if (eq_rank < k_rem) ++n_sel; ++eq_rank; }
+    }
+  }
+  int pos = block_excl_scan(n_sel, scan_tmp, tot);
+  {
+    int eq_rank = eq_before;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (first + e >= seg_len) continue;
+      bool take = false;
+      if (key[e] > prefix) take = true;
+      else if (key[e] == prefix) { take = eq_rank < k_rem; ++eq_rank; }
+      if (take) {
+        if (pos < k) dst[pos] = static_cast<int32_t>(first + e);
+        ++pos;
+      }
+    }
+  }
+}
+
+template <typename ScoreT>
+static hipError_t launch_topk(const ScoreT* scores, int64_t n_seg, int64_t seg_len, int32_t k,
+                              int32_t* out, hipStream_t st) {
+  const int64_t per = (seg_len + kTopkThreads - 1) / kTopkThreads;
+  dim3 grid(static_cast<unsigned>(n_seg)), block(kTopkThreads);
+#define FL_TOPK_CASE(E)                                                                    \
+  if (per <= E) {                                                                          \
+    hipLaunchKernelGGL((k_topk<ScoreT, E>), grid, block, 0, st, scores, seg_len, k, out);  \
+    return hipGetLastError();                                                              \
+  }
+  FL_TOPK_CASE(1) FL_TOPK_CASE(2) FL_TOPK_CASE(4) FL_TOPK_CASE(8) FL_TOPK_CASE(16)
+  FL_TOPK_CASE(32) FL_TOPK_CASE(64)
+#undef FL_TOPK_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_select(const fl_select_args& a, hipStream_t st) {
+  if (a.mode == FL_SEL_TOKENS) {
+    dim3 grid(static_cast<unsigned>((a.n_rows + 3) / 4)), block(256);
+    if (a.h_dtype == FL_BF16)
+      hipLaunchKernelGGL(k_delta_norm<FL_BF16>, grid, block, 0, st, a.h_cur, a.h_prev, a.n_rows,
+                         a.hidden, a.cand_idx, a.n_cand, a.scores);
+    else
+      hipLaunchKernelGGL(k_delta_norm<FL_F32>, grid, block, 0, st, a.h_cur, a.h_prev, a.n_rows,
+                         a.hidden, a.cand_idx, a.n_cand, a.scores);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_topk<double>(a.scores, 1, a.n_rows, a.k, a.out_idx, st);
+  }
+  return launch_topk<float>(a.key_scores, a.n_seg, a.seg_len, a.k, a.out_idx, st);
+}
+
+}  // namespace fl

@@ -1,0 +1,204 @@
+"""Runs the loops of a workload through the C ABI on one GPU.
+
+The sequence follows the page "FlashLoop: Fast and Memory-Efficient Looped
+Transformers via Lazy Updates", section "FlashLoop combines three kinds of
+savings": loops 1..F run in full (commit the base or a dense delta layer, full
+causal attention); each later loop ranks tokens by the change of the previous
+loop, selects keys from the previous loop's column mass, commits int4 deltas
+of the active tokens and runs mass-corrected attention.
+
+The per-loop inputs come from a synthetic stand-in for the shared block (the
+model weights are not available): its new h and Q rows are copied into the
+effective-state buffers only for the active rows, which is how the carried
+rows of a looped model keep their previous state.  That copy is the model's
+work, not the method's, and is done with a torch index copy.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import abi
+from .configs import Workload
+from .synth import SyntheticLoops, to_bf16_bits
+
+
+def torch_dtype(wl: Workload) -> torch.dtype:
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def to_device(x: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
+    """float32 values already representable in `dtype` -> device tensor (exact)."""
+    if dtype == torch.bfloat16:
+        bits = to_bf16_bits(x)
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+
+
+def upload_loops(wl: Workload, loops: SyntheticLoops, device="cuda") -> Dict[int, Dict[str, torch.Tensor]]:
+    dt = torch_dtype(wl)
+    out = {}
+    for l, x in loops:
+        out[l] = {name: to_device(arr, dt, device) for name, arr in x.items()}
+    return out
+
+
+@dataclass
+class LoopRecord:
+    rows: Optional[torch.Tensor] = None
+    keys: Optional[torch.Tensor] = None
+    scores: Optional[torch.Tensor] = None
+    o: Optional[torch.Tensor] = None
+    lse: Optional[torch.Tensor] = None
+    colmass: Optional[torch.Tensor] = None
+    arena: Optional[torch.Tensor] = None
+
+
+class PrefillRun:
+    """GPU state of one prefill workload (n_seq = 1) and its loop sequence."""
+
+    def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], device="cuda"):
+        assert wl.n_seq == 1 and not wl.decode
+        self.wl, self.inp, self.dev = wl, inputs, device
+        n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
+        dt = torch_dtype(wl)
+        self.kv = abi.KVStore(1, H, d, n, wl.n_loops, dt, wl.layer_caps(), device)
+        # effective hidden state (carried rows keep their value) and, at the rows
+        # of the last active set, its value one loop earlier
+        self.h_eff = torch.empty(n, H * d, dtype=dt, device=device)
+        self.h_prev = torch.empty_like(self.h_eff)
+        self.q_eff = torch.empty(n, H, d, dtype=dt, device=device)
+        na_max = max([wl.n_active(l) for l in range(wl.n_full + 1, wl.n_loops + 1)] or [1])
+        self.q_cur_rows = torch.empty(na_max, H, d, dtype=dt, device=device)
+        self.q_prev_rows = torch.empty(na_max, H, d, dtype=dt, device=device)
+        self.o = torch.empty(n, H, d, dtype=torch.float32, device=device)
+        self.lse = torch.empty(n, H, dtype=torch.float32, device=device)
+        self.colmass = torch.empty(H, n, dtype=torch.float32, device=device)
+        self.scores = torch.empty(n, dtype=torch.float64, device=device)
+        self.all_rows = torch.arange(n, dtype=torch.int32, device=device)
+        self.act = {l: torch.empty(wl.n_active(l), dtype=torch.int32, device=device)
+                    for l in range(wl.n_full + 1, wl.n_loops + 1)}
+        self.keys = torch.empty(H, wl.n_keys, dtype=torch.int32, device=device)
+        self.workspace = None
+        ws = 0
+        for l in range(1, wl.n_loops + 1):
+            ws = max(ws, abi.attend_workspace_bytes(self._attend_args(l)))
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+
+    def _attend_args(self, l: int):
+        wl = self.wl
+        if l <= wl.n_full:
+            return abi.attend_args(self.kv, abi.FL_ATTEND_FULL, l, self.inp[l]["q"], None, None, wl.n_tokens,
+                                   None, self.o, self.lse, self.colmass, self.workspace)
+        na = wl.n_active(l)
+        return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, self.q_cur_rows[:na], self.q_prev_rows[:na],
+                               self.act[l], na, self.keys, self.o, self.lse, self.colmass, self.workspace,
+                               q_compact=True)
+
+    # ------------------------------------------------------------------ loops
+    def full_loop(self, l: int) -> None:
+        x = self.inp[l]
+        self.h_prev.copy_(self.inp[0]["h"][0] if l == 1 else self.h_eff)
+        self.h_eff.copy_(x["h"][0])
+        self.q_eff.copy_(x["q"][0])
+        abi.kv_commit(self.kv, l, self.all_rows, x["k"], x["v"])
+        abi.attend(self._attend_args(l))
+
+    def lazy_loop(self, l: int, cand: Optional[torch.Tensor]) -> torch.Tensor:
+        wl, x = self.wl, self.inp[l]
+        act, na = self.act[l], wl.n_active(l)
+        abi.select_tokens(self.h_eff, self.h_prev, na, self.scores, act, cand)
+        abi.select_keys(self.colmass, wl.n_keys, self.keys)
+        # model stand-in: the shared block recomputes the active rows only
+        idx = act.long()
+        self.h_prev.index_copy_(0, idx, self.h_eff.index_select(0, idx))
+        self.h_eff.index_copy_(0, idx, x["h"][0].index_select(0, idx))
+        torch.index_select(self.q_eff, 0, idx, out=self.q_prev_rows[:na])
+        torch.index_select(x["q"][0], 0, idx, out=self.q_cur_rows[:na])
+        self.q_eff.index_copy_(0, idx, self.q_cur_rows[:na])
+        abi.kv_commit(self.kv, l, act, x["k"], x["v"])
+        abi.attend(self._attend_args(l))
+        return act
+
+    def run(self, upto: Optional[int] = None, record: bool = False) -> List[LoopRecord]:
+        wl = self.wl
+        T = wl.n_loops if upto is None else upto
+        recs: List[LoopRecord] = []
+        cand = None
+        for l in range(1, T + 1):
+            if l <= wl.n_full:
+                self.full_loop(l)
+                cand = None
+                rec = LoopRecord()
+            else:
+                act = self.lazy_loop(l, cand)
+                cand = act
+                rec = LoopRecord(rows=act.clone() if record else None,
+                                 keys=self.keys.clone() if record else None,
+                                 scores=self.scores.clone() if record else None)
+            if record:
+                rec.o, rec.lse, rec.colmass = self.o.clone(), self.lse.clone(), self.colmass.clone()
+                rec.arena = self.kv.arena.clone()
+            recs.append(rec)
+        return recs
+
+
+class DecodeRun:
+    """Decode workload: n_seq sequences, one new query per sequence and loop."""
+
+    def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], ctx_sets: Dict[int, List[np.ndarray]],
+                 device="cuda"):
+        assert wl.decode
+        self.wl, self.inp, self.dev = wl, inputs, device
+        S, n, H, d = wl.n_seq, wl.n_tokens, wl.n_heads, wl.head_dim
+        dt = torch_dtype(wl)
+        self.kv = abi.KVStore(S, H, d, n, wl.n_loops, dt, wl.layer_caps(), device)
+        self.ctx = {}
+        for l in range(1, wl.n_loops + 1):
+            if l == 1:
+                idx = np.tile(np.arange(n - 1, dtype=np.int32), (S, 1))
+            else:
+                idx = np.stack(ctx_sets[l]).astype(np.int32)
+            self.ctx[l] = torch.from_numpy(idx).to(device)
+        self.last = torch.full((S, 1), n - 1, dtype=torch.int32, device=device)
+        self.o = torch.empty(S, 1, H, d, dtype=torch.float32, device=device)
+        self.lse = torch.empty(S, 1, H, dtype=torch.float32, device=device)
+        self.colmass = torch.empty(S, H, n, dtype=torch.float32, device=device)
+        self.keys = torch.empty(S, H, wl.n_keys, dtype=torch.int32, device=device)
+        ws = 0
+        for l in range(1, wl.n_loops + 1):
+            ws = max(ws, abi.attend_workspace_bytes(self._args(l, None)))
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+
+    def _args(self, l, ws):
+        x = self.inp[l]
+        if l == 1:
+            return abi.attend_args(self.kv, abi.FL_ATTEND_FULL, 1, x["q"], None, self.last, 1, None,
+                                   self.o, self.lse, self.colmass, ws, q_compact=True, o_compact=True)
+        return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, x["q"], self.inp[l - 1]["q"], self.last, 1,
+                               self.keys, self.o, self.lse, self.colmass, ws, q_compact=True, o_compact=True)
+
+    def build_context(self) -> None:
+        for l in range(1, self.wl.n_loops + 1):
+            x = self.inp[l]
+            abi.kv_commit(self.kv, l, self.ctx[l], x["k"], x["v"], slot_base=0, reset_map=True)
+
+    def loop(self, l: int) -> None:
+        wl, x = self.wl, self.inp[l]
+        slot_base = 0 if l == 1 else self.ctx[l].shape[1]
+        abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False)
+        if l >= 2:
+            abi.select_keys(self.colmass, wl.n_keys, self.keys)
+        abi.attend(self._args(l, self.workspace))
+
+    def run(self, record: bool = False) -> List[LoopRecord]:
+        recs = []
+        for l in range(1, self.wl.n_loops + 1):
+            self.loop(l)
+            if record:
+                recs.append(LoopRecord(keys=self.keys.clone() if l >= 2 else None, o=self.o.clone(),
+                                       lse=self.lse.clone(), colmass=self.colmass.clone()))
+        return recs

@@ -1,0 +1,143 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+computes the arena layout, and rejects invalid arguments before any launch
+(no GPU needed: validation runs before any HIP call)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_loop_attention_amd import abi, configs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "flashloop.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return abi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(flashloop_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(abi.EXPORTS)
+    assert abi.abi_version() == 1
+
+
+def _desc(wl):
+    d = abi.fl_kv_desc()
+    d.n_seq, d.n_heads, d.head_dim, d.n_tokens = wl.n_seq, wl.n_heads, wl.head_dim, wl.n_tokens
+    d.n_versions, d.base_dtype, d.group = wl.n_loops, abi.FL_BF16 if wl.dtype == "bf16" else abi.FL_F32, 32
+    for i, c in enumerate(wl.layer_caps()):
+        d.layer_cap[i + 2] = c
+    return d
+
+
+@pytest.mark.parametrize("name", list(configs.WORKLOADS))
+def test_arena_layout_bytes(L, name):
+    wl = configs.WORKLOADS[name]
+    d = _desc(wl)
+    lay = abi.kv_layout(d)
+    S, H, N, D = wl.n_seq, wl.n_heads, wl.n_tokens, wl.head_dim
+    es = 2 if wl.dtype == "bf16" else 4
+    assert lay.base_v - lay.base_k >= S * H * N * D * es
+    need = 2 * S * H * N * D * es
+    for l, cap in zip(range(2, wl.n_loops + 1), wl.layer_caps()):
+        need += S * N * 4 + 2 * S * H * cap * (D // 2 + 2 * (D // 32))
+        for arr in (lay.slot_map, lay.codes_k, lay.codes_v, lay.scales_k, lay.scales_v):
+            assert arr[l] % 256 == 0
+    assert need <= lay.total_bytes <= need + 256 * (2 + 5 * wl.n_loops)
+    assert abi.kv_arena_bytes(d) == lay.total_bytes
+
+
+def test_compression_ratio_single_layer(L):
+    """base + int4 deltas vs one bf16 cache per loop: 2.87x on the 4-loop,
+    20%-active workload (page: 'up to 6x' KV-cache reduction)."""
+    wl = configs.SINGLE_LAYER
+    lay = abi.kv_layout(_desc(wl))
+    naive = wl.n_loops * 2 * wl.n_heads * wl.n_tokens * wl.head_dim * 2
+    slot_maps = (wl.n_loops - 1) * wl.n_tokens * 4
+    assert naive / (lay.total_bytes - slot_maps) == pytest.approx(2.87, abs=0.01)
+
+
+def test_invalid_descriptors(L):
+    d = _desc(configs.TINY)
+    d.head_dim = 80
+    assert abi.kv_arena_bytes(d) == 0
+    assert b"head_dim" in L.flashloop_last_error()
+    d = _desc(configs.TINY)
+    d.group = 16
+    assert L.flashloop_kv_layout(C.byref(d), C.byref(abi.fl_kv_layout())) == abi.FL_ERR_UNSUPPORTED
+    d = _desc(configs.TINY)
+    d.layer_cap[2] = 10 ** 6
+    assert L.flashloop_kv_layout(C.byref(d), C.byref(abi.fl_kv_layout())) == abi.FL_ERR_ARG
+
+
+def test_commit_validation(L):
+    a = abi.fl_commit_args()
+    assert L.flashloop_kv_commit(C.byref(a), None) == abi.FL_ERR_ARG
+    d = _desc(configs.TINY)
+    a.kv = C.pointer(d)
+    assert L.flashloop_kv_commit(C.byref(a), None) == abi.FL_ERR_ARG      # no arena
+    assert b"arena" in L.flashloop_last_error()
+    d.arena, d.arena_bytes = 256, 16                                        # fake, too small
+    assert L.flashloop_kv_commit(C.byref(a), None) == abi.FL_ERR_ARG
+    d.arena_bytes = abi.kv_arena_bytes(d)
+    a.version = 3                                                           # > n_versions
+    assert L.flashloop_kv_commit(C.byref(a), None) == abi.FL_ERR_ARG
+    a.version, a.n_active = 2, 5
+    assert L.flashloop_kv_commit(C.byref(a), None) == abi.FL_ERR_ARG      # NULL pointers
+    a.active_idx, a.k_new, a.v_new = 256, 256, 256
+    a.slot_base = 62                                                        # 62 + 5 > cap 64
+    assert L.flashloop_kv_commit(C.byref(a), None) == abi.FL_ERR_ARG
+    assert b"layer_cap" in L.flashloop_last_error()
+    a.slot_base, a.n_active = 0, 0
+    assert L.flashloop_kv_commit(C.byref(a), None) == abi.FL_OK          # nothing to do
+
+
+def test_select_validation(L):
+    a = abi.fl_select_args()
+    a.mode = 7
+    assert L.flashloop_select(C.byref(a), None) == abi.FL_ERR_ARG
+    a.mode = abi.FL_SEL_TOKENS
+    assert L.flashloop_select(C.byref(a), None) == abi.FL_ERR_ARG
+    a.h_cur = a.h_prev = a.scores = 256
+    a.h_dtype, a.n_rows, a.hidden = abi.FL_BF16, 100, 12
+    assert L.flashloop_select(C.byref(a), None) == abi.FL_ERR_UNSUPPORTED  # hidden % 8
+    a.hidden, a.k = 64, 101
+    assert L.flashloop_select(C.byref(a), None) == abi.FL_ERR_ARG
+    a.n_rows = 70000
+    assert L.flashloop_select(C.byref(a), None) == abi.FL_ERR_UNSUPPORTED
+    b = abi.fl_select_args()
+    b.mode, b.key_scores, b.n_seg, b.seg_len, b.k = abi.FL_SEL_KEYS, 256, 4, 100, 10
+    assert L.flashloop_select(C.byref(b), None) == abi.FL_ERR_ARG          # NULL out_idx
+    assert b"out_idx" in L.flashloop_last_error()
+
+
+def test_attend_validation(L):
+    d = _desc(configs.TINY)
+    d.arena, d.arena_bytes = 256, abi.kv_arena_bytes(d)
+    a = abi.fl_attend_args()
+    a.kv = C.pointer(d)
+    a.mode = 5
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG
+    a.mode, a.version = abi.FL_ATTEND_LAZY, 1                              # LAZY needs version >= 2
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG
+    a.version, a.n_active = 2, 0
+    a.q_cur = a.q_prev = a.o = a.lse = a.colmass = 256
+    a.key_idx, a.n_keys = 256, 26
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_OK              # A empty: no-op
+    a.n_active, a.active_idx = 64, 256
+    need = L.flashloop_attend_workspace_bytes(C.byref(a))
+    assert need > 0
+    a.workspace, a.workspace_bytes = 256, need - 1
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_WORKSPACE
+    a.mode, a.version, a.active_idx, a.n_active = abi.FL_ATTEND_FULL, 1, None, 10
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG          # NULL rows need n_active == N

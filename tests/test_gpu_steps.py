@@ -1,0 +1,244 @@
+"""GPU parity of each ABI call against the CPU oracle on identical inputs.
+
+Bars: index sets and int4 codes bit-exact; attention outputs within
+2e-2 x RMS (max abs error); float64 token scores within 1e-13 relative.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_loop_attention_amd import abi
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def bf16_round(x):
+    from sparse_loop_attention_amd.synth import round_bf16
+    return round_bf16(np.asarray(x, np.float32))
+
+
+def to_dev(x, dtype):
+    from sparse_loop_attention_amd.driver import to_device
+    return to_device(np.ascontiguousarray(x, np.float32), dtype, DEV)
+
+
+def rel_err_ok(got, want, tol=2e-2):
+    want = np.asarray(want, np.float64)
+    got = np.asarray(got, np.float64)
+    rms = math.sqrt(float(np.mean(want ** 2)))
+    err = float(np.abs(got - want).max()) if want.size else 0.0
+    return err <= tol * rms, err, rms
+
+
+# --------------------------------------------------------------------------- select
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n,hidden,k", [(1, 8, 1), (300, 64, 75), (4096, 2048, 820), (5000, 5280, 1500)])
+def test_select_tokens(dtype, n, hidden, k):
+    rng = np.random.default_rng(n + hidden)
+    h_prev = rng.standard_normal((n, hidden)).astype(np.float32)
+    sig = np.exp(rng.standard_normal(n)).astype(np.float32) * 0.1
+    h_cur = h_prev + sig[:, None] * rng.standard_normal((n, hidden)).astype(np.float32)
+    h_cur[::7] = h_prev[::7]                                       # carried rows: score exactly 0
+    if dtype == torch.bfloat16:
+        h_prev, h_cur = bf16_round(h_prev), bf16_round(h_cur)
+    hc, hp = to_dev(h_cur, dtype), to_dev(h_prev, dtype)
+    scores = torch.empty(n, dtype=torch.float64, device=DEV)
+    out = torch.empty(k, dtype=torch.int32, device=DEV)
+    abi.select_tokens(hc, hp, k, scores, out)
+    torch.cuda.synchronize()
+    u = scores.cpu().numpy()
+    u_ref = oracle.token_scores(h_cur, h_prev)
+    np.testing.assert_allclose(u, u_ref, rtol=1e-13, atol=0)
+    assert np.all(u[::7] == 0.0)
+    got = out.cpu().numpy()
+    assert np.array_equal(got, oracle.topk_ascending(u, k))        # same scores -> identical set
+    assert np.array_equal(got, oracle.topk_ascending(u_ref, k))
+
+
+def test_select_tokens_candidates():
+    rng = np.random.default_rng(3)
+    n, hidden = 2000, 256
+    h_prev = rng.standard_normal((n, hidden)).astype(np.float32)
+    cand = np.sort(rng.choice(n, 300, replace=False)).astype(np.int32)
+    h_cur = h_prev.copy()
+    h_cur[cand] += rng.standard_normal((300, hidden)).astype(np.float32)
+    scores = torch.full((n,), -1.0, dtype=torch.float64, device=DEV)
+    for k in (1, 150, 300, 400):                                   # 400 > candidates: zeros by index
+        out = torch.empty(k, dtype=torch.int32, device=DEV)
+        abi.select_tokens(to_dev(h_cur, torch.float32), to_dev(h_prev, torch.float32), k, scores, out,
+                          torch.from_numpy(cand).to(DEV))
+        torch.cuda.synchronize()
+        u_ref = oracle.token_scores(h_cur, h_prev)
+        np.testing.assert_allclose(scores.cpu().numpy(), u_ref, rtol=1e-13)
+        assert np.array_equal(out.cpu().numpy(), oracle.topk_ascending(u_ref, k))
+
+
+@pytest.mark.parametrize("n_seg,seg_len,k", [(1, 1, 1), (1, 256, 26), (16, 4096, 410), (3, 32768, 3277),
+                                             (512, 8192, 820), (55, 16384, 1639), (2, 1000, 1000), (2, 700, 0)])
+def test_select_keys(n_seg, seg_len, k):
+    rng = np.random.default_rng(seg_len + k)
+    c = rng.random((n_seg, seg_len)).astype(np.float32) * 5
+    c[:, ::5] = np.round(c[:, ::5])                                # exact ties
+    c[:, ::11] = 0.0
+    if seg_len > 3:
+        c[:, 3] = -0.0
+        c[:, 1] = -1.5                                             # negative mass after lazy updates
+    out = torch.empty(n_seg, k, dtype=torch.int32, device=DEV)
+    abi.select_keys(torch.from_numpy(c).to(DEV), k, out)
+    torch.cuda.synchronize()
+    want = oracle.select_keys(c, k) if k else np.zeros((n_seg, 0), np.int32)
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_select_keys_all_equal():
+    c = np.full((4, 3000), 0.25, np.float32)
+    out = torch.empty(4, 100, dtype=torch.int32, device=DEV)
+    abi.select_keys(torch.from_numpy(c).to(DEV), 100, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), np.tile(np.arange(100), (4, 1)))
+
+
+# --------------------------------------------------------------------------- commit
+def _oracle_chain(rng, n, H, d, sets, dtype_np_round):
+    st = oracle.KVStore(n, H, d)
+    inputs = {}
+    k = dtype_np_round(rng.standard_normal((n, H, d)).astype(np.float32))
+    v = dtype_np_round(rng.standard_normal((n, H, d)).astype(np.float32))
+    inputs[1] = (k.copy(), v.copy())
+    st.commit(1, np.arange(n), k, v)
+    for l, act in sets.items():
+        scale = 10.0 ** rng.uniform(-3, 0.5, (n, 1, 1))
+        k = dtype_np_round(k + (scale * rng.standard_normal((n, H, d))).astype(np.float32))
+        v = dtype_np_round(v + (scale * rng.standard_normal((n, H, d))).astype(np.float32))
+        inputs[l] = (k.copy(), v.copy())
+        st.commit(l, act, k[act], v[act])
+    return st, inputs
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 64), (torch.bfloat16, 96), (torch.bfloat16, 128)])
+def test_commit_codes_bit_exact(dtype, d):
+    rng = np.random.default_rng(d)
+    n, H = 300, 3
+    sets = {2: np.arange(n), 3: np.sort(rng.choice(n, 90, replace=False)),
+            4: np.sort(rng.choice(n, 40, replace=False))}
+    rnd = bf16_round if dtype == torch.bfloat16 else (lambda x: x.astype(np.float32))
+    st, inputs = _oracle_chain(rng, n, H, d, sets, rnd)
+    kv = abi.KVStore(1, H, d, n, 4, dtype, [n, 90, 40], DEV)
+    kv.arena.fill_(0xAB)
+    for l in range(1, 5):
+        act = np.arange(n) if l == 1 else sets[l]
+        kk, vv = inputs[l]
+        abi.kv_commit(kv, l, torch.from_numpy(act.astype(np.int32)).to(DEV), to_dev(kk[None], dtype),
+                      to_dev(vv[None], dtype))
+    torch.cuda.synchronize()
+    base_k = kv.view("base_k").float().cpu().numpy()[0]              # [H, N, d]
+    np.testing.assert_array_equal(base_k, inputs[1][0].transpose(1, 0, 2))
+    for l in range(2, 5):
+        slots = kv.view("slot_map", l).cpu().numpy()[0]
+        want_slots = np.full(n, -1)
+        want_slots[sets[l]] = np.arange(len(sets[l]))
+        assert np.array_equal(slots, want_slots)
+        for w in ("k", "v"):
+            rec = st.layers[l][w][0]
+            codes = kv.view(f"codes_{w}", l).cpu().numpy()[0]        # [H, cap, d/2]
+            scales = kv.view(f"scales_{w}", l).cpu().numpy()[0]      # [H, cap, d/32]
+            assert np.array_equal(codes, oracle.pack_int4(rec.codes).transpose(1, 0, 2)), (l, w)
+            assert np.array_equal(scales.view(np.uint16), rec.scales.view(np.uint16).transpose(1, 0, 2)), (l, w)
+
+
+def test_commit_appends_to_layer_without_reset():
+    rng = np.random.default_rng(11)
+    n, H, d = 64, 1, 64
+    kv = abi.KVStore(1, H, d, n, 2, torch.float32, [20], DEV)
+    k1 = rng.standard_normal((1, n, H, d)).astype(np.float32)
+    abi.kv_commit(kv, 1, torch.arange(n, dtype=torch.int32, device=DEV)[None], to_dev(k1, torch.float32),
+                  to_dev(k1, torch.float32))
+    k2 = k1 + 0.1 * rng.standard_normal(k1.shape).astype(np.float32)
+    a = torch.tensor([[3, 9, 40]], dtype=torch.int32, device=DEV)
+    b = torch.tensor([[63]], dtype=torch.int32, device=DEV)
+    abi.kv_commit(kv, 2, a, to_dev(k2, torch.float32), to_dev(k2, torch.float32), slot_base=0, reset_map=True)
+    abi.kv_commit(kv, 2, b, to_dev(k2, torch.float32), to_dev(k2, torch.float32), slot_base=3, reset_map=False)
+    torch.cuda.synchronize()
+    slots = kv.view("slot_map", 2).cpu().numpy()[0]
+    want = np.full(n, -1)
+    want[[3, 9, 40, 63]] = [0, 1, 2, 3]
+    assert np.array_equal(slots, want)
+
+
+# --------------------------------------------------------------------------- attend
+def _setup_attend(rng, n, H, d, dtype, sets, nS=None):
+    rnd = bf16_round if dtype == torch.bfloat16 else (lambda x: x.astype(np.float32))
+    st, inputs = _oracle_chain(rng, n, H, d, sets, rnd)
+    kv = abi.KVStore(1, H, d, n, 1 + len(sets), dtype, [len(sets[l]) for l in sorted(sets)], DEV)
+    for l in range(1, 2 + len(sets)):
+        act = np.arange(n) if l == 1 else sets[l]
+        kk, vv = inputs[l]
+        abi.kv_commit(kv, l, torch.from_numpy(act.astype(np.int32)).to(DEV), to_dev(kk[None], dtype),
+                      to_dev(vv[None], dtype))
+    return st, kv, rnd
+
+
+@pytest.mark.parametrize("dtype,d,n", [(torch.float32, 64, 256), (torch.bfloat16, 128, 300),
+                                       (torch.bfloat16, 96, 200), (torch.float32, 128, 129)])
+def test_attend_full(dtype, d, n):
+    rng = np.random.default_rng(n)
+    H = 2
+    sets = {2: np.arange(n)}
+    st, kv, rnd = _setup_attend(rng, n, H, d, dtype, sets)
+    q = rnd(rng.standard_normal((n, H, d)).astype(np.float32) * 1.5)
+    o = torch.zeros(1, n, H, d, device=DEV)
+    lse = torch.zeros(1, n, H, device=DEV)
+    c = torch.full((1, H, n), 7.0, device=DEV)
+    for version in (1, 2):
+        a = abi.attend_args(kv, abi.FL_ATTEND_FULL, version, to_dev(q[None], dtype), None, None, n, None, o, lse, c)
+        ws = torch.empty(abi.attend_workspace_bytes(a), dtype=torch.uint8, device=DEV)
+        a = abi.attend_args(kv, abi.FL_ATTEND_FULL, version, to_dev(q[None], dtype), None, None, n, None, o, lse, c, ws)
+        abi.attend(a)
+        torch.cuda.synchronize()
+        o_r, lse_r, c_r = oracle.full_attention(q, st.reconstruct("k", version), st.reconstruct("v", version),
+                                                np.arange(n))
+        for got, want in ((o[0], o_r), (lse[0], lse_r), (c[0], c_r)):
+            ok, err, rms = rel_err_ok(got.cpu().numpy(), want)
+            assert ok, (version, err, rms)
+
+
+@pytest.mark.parametrize("dtype,d,n,na,ns", [(torch.float32, 64, 256, 64, 26), (torch.bfloat16, 128, 512, 103, 52),
+                                             (torch.bfloat16, 96, 300, 300, 300), (torch.bfloat16, 128, 700, 1, 70)])
+def test_attend_lazy(dtype, d, n, na, ns):
+    rng = np.random.default_rng(n + na)
+    H = 3
+    act = np.sort(rng.choice(n, na, replace=False)).astype(np.int32)
+    sets = {2: act}
+    st, kv, rnd = _setup_attend(rng, n, H, d, dtype, sets)
+    q0 = rnd(rng.standard_normal((n, H, d)).astype(np.float32))
+    q1 = rnd(q0 + 0.3 * rng.standard_normal((n, H, d)).astype(np.float32))
+    o0, lse0, c0 = oracle.full_attention(q0, st.reconstruct("k", 1), st.reconstruct("v", 1), np.arange(n))
+    keys = oracle.select_keys(c0, ns)
+    o = torch.from_numpy(o0.astype(np.float32)[None]).to(DEV)
+    lse = torch.from_numpy(lse0.astype(np.float32)[None]).to(DEV)
+    c = torch.from_numpy(c0.astype(np.float32)[None]).to(DEV)
+    qc = to_dev(q1[act][None], dtype)
+    qp = to_dev(q0[act][None], dtype)
+    a = abi.attend_args(kv, abi.FL_ATTEND_LAZY, 2, qc, qp, torch.from_numpy(act).to(DEV)[None], na,
+                        torch.from_numpy(keys).to(DEV)[None], o, lse, c, None, q_compact=True)
+    ws = torch.empty(abi.attend_workspace_bytes(a), dtype=torch.uint8, device=DEV)
+    a = abi.attend_args(kv, abi.FL_ATTEND_LAZY, 2, qc, qp, torch.from_numpy(act).to(DEV)[None], na,
+                        torch.from_numpy(keys).to(DEV)[None], o, lse, c, ws, q_compact=True)
+    abi.attend(a)
+    torch.cuda.synchronize()
+    o_r, lse_r, c_r, m, upd = oracle.lazy_attention(
+        q1[act], q0[act], st.reconstruct("k", 1), st.reconstruct("v", 1), st.reconstruct("k", 2),
+        st.reconstruct("v", 2), o0[act], lse0[act], c0, act, keys)
+    got_o = o[0].cpu().numpy()
+    ok, err, rms = rel_err_ok(got_o[act], o_r)
+    assert ok, ("o", err, rms)
+    inactive = np.setdiff1d(np.arange(n), act)
+    assert np.array_equal(got_o[inactive], o0.astype(np.float32)[inactive])      # untouched
+    ok, err, rms = rel_err_ok(lse[0].cpu().numpy()[act], lse_r)
+    assert ok, ("lse", err, rms)
+    ok, err, rms = rel_err_ok(c[0].cpu().numpy(), c_r)
+    assert ok, ("colmass", err, rms)
