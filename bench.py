@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashLoop loop step on one MI355X.
+
+One step = every loop of one workload, in order: the full early loops (commit
+the base or a dense int4 layer, full causal attention with column mass) and
+the lazy loops (token selection, key selection, int4 delta commit of the
+active tokens, mass-corrected attention), i.e. every step of the hot path
+over one batch of synthetic input already resident in HBM.
+
+Metric: active-token loop-steps per second = (sum over the step's loops of the
+rows that loop computes: N in a full loop, n_active in a lazy loop) / step
+time.  The JSON line also carries the lazy-loop rate, KV bytes per second, the
+roofline position of the dominant kernel (per-kernel hipEvent timings taken
+inside the timed region) and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="single_layer",
+                    help="tiny | single_layer | long_prefill | decode | deep")
+    ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the host oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- work model
+def _pairs(rows, keys_sorted):
+    """sum over rows i of |{j in keys : j <= i}| for ascending key lists."""
+    import numpy as np
+    return int(np.searchsorted(keys_sorted, rows, side="right").sum())
+
+
+def work_model(wl, run):
+    """Algorithmic flops / bytes of one step, per kernel family."""
+    import numpy as np
+    H, d, N = wl.n_heads, wl.head_dim, wl.n_tokens
+    es = 2 if wl.dtype == "bf16" else 4
+    rec = d // 2 + 2 * (d // 32)                    # bytes of one int4 record (one head row)
+    w = {"attn_full_flops": 0, "attn_lazy_flops": 0, "colmass_full_flops": 0, "colmass_lazy_flops": 0,
+         "select_bytes": 0, "commit_bytes": 0, "kv_bytes": 0, "lazy_rows": 0, "rows": 0}
+    if wl.decode:
+        S = wl.n_seq
+        for l in range(1, wl.n_loops + 1):
+            w["rows"] += S
+            if l == 1:
+                p = S * H * N
+                w["attn_full_flops"] += 4 * d * p
+                w["kv_bytes"] += S * H * N * d * es * 2
+            else:
+                keys = run.keys.cpu().numpy()
+                p = S * H * wl.n_keys
+                w["attn_lazy_flops"] += 8 * d * p
+                w["lazy_rows"] += S
+                # chain reads of the selected keys: base + one record per present layer, K and V
+                layers_present = 0
+                for s in range(S):
+                    for lp in range(2, l + 1):
+                        present = set(run.ctx[lp][s].cpu().numpy().tolist()) | {N - 1}
+                        layers_present += sum(int(j in present) for j in keys[s, 0])
+                w["kv_bytes"] += 2 * H * (S * wl.n_keys * d * es + layers_present * rec)
+        return w
+    for l in range(1, wl.n_loops + 1):
+        if l <= wl.n_full:
+            p = H * N * (N + 1) // 2
+            w["rows"] += N
+            w["attn_full_flops"] += 4 * d * p
+            w["colmass_full_flops"] += 2 * d * p
+            w["commit_bytes"] += 2 * H * N * (d * es + (d * es + (l - 1) * rec if l > 1 else d * es))
+        else:
+            act = run.act[l].cpu().numpy()
+            keys = run.keys_l[l].cpu().numpy()
+            na = act.size
+            w["rows"] += na
+            w["lazy_rows"] += na
+            p = sum(_pairs(act, keys[h]) for h in range(H))
+            w["attn_lazy_flops"] += 8 * d * p
+            w["colmass_lazy_flops"] += 4 * d * p
+            cand = N if l == wl.n_full + 1 else wl.n_active(l - 1)
+            w["select_bytes"] += cand * H * d * es * 2 + N * 8 + N * 8 + H * N * 4 + H * wl.n_keys * 4
+            chain = 2 * H * na * (d * es + (l - 2) * rec)        # upper bound: every earlier layer present
+            w["commit_bytes"] += 2 * H * na * d * es + chain + 2 * H * na * rec
+            w["kv_bytes"] += chain + 2 * H * na * rec
+    return w
+
+
+KERNEL_WORK = {
+    # kernel name -> (work key, unit, bound)
+    "rows_partial_full": ("attn_full_flops", "TFLOP/s", "alu"),
+    "rows_partial_lazy": ("attn_lazy_flops", "TFLOP/s", "alu"),
+    "mfma_fwd_full": ("attn_full_flops", "TFLOP/s", "mfma"),
+    "mfma_fwd_lazy": ("attn_lazy_flops", "TFLOP/s", "mfma"),
+    "mfma_colmass_full": ("colmass_full_flops", "TFLOP/s", "mfma"),
+    "mfma_colmass_lazy": ("colmass_lazy_flops", "TFLOP/s", "mfma"),
+    "delta_norm": ("select_bytes", "GB/s", "hbm"),
+    "commit_delta": ("commit_bytes", "GB/s", "hbm"),
+    "decode_partial": ("kv_bytes", "GB/s", "hbm"),
+}
+
+
+def roofline(timings, work, steps):
+    name, (ms, launches) = max(timings.items(), key=lambda kv: kv[1][0])
+    avg_ms = ms / max(launches, 1)
+    entry = {"kernel": name, "launches_per_step": launches / steps, "avg_launch_ms": avg_ms}
+    if name in KERNEL_WORK:
+        key, unit, bound = KERNEL_WORK[name]
+        per_step = work[key]
+        secs = ms / 1e3 / steps
+        if unit == "GB/s":
+            achieved = per_step / secs / 1e9
+            peak = HBM_PEAK_GBPS
+        else:
+            achieved = per_step / secs / 1e12
+            peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else FP32_VECTOR_PEAK_TFLOPS
+        entry.update({"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                      "frac": achieved / peak, "traffic": None})
+    else:
+        entry.update({"bound": None, "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None})
+    return entry
+
+
+# --------------------------------------------------------------------------- CPU oracle
+def cpu_baseline(wl, target_s):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle
+    from sparse_loop_attention_amd.synth import SyntheticLoops
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    if wl.decode:
+        syn = SyntheticLoops(wl, seqs=(0,))
+        data = {l: {k: v.copy() for k, v in x.items()} for l, x in syn}
+        ctx = {l: syn.context_active_sets(l)[0] for l in range(2, wl.n_loops + 1)}
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            oracle.run_decode_seq(wl, syn, 0, ctx, data)
+            n += 1
+            if time.perf_counter() - t0 >= target_s:
+                break
+        dt = time.perf_counter() - t0
+        rows = n * wl.n_loops
+        return {"value": rows / dt, "unit": "active-token loop-steps/s", "cores": cores, "kind": "oracle",
+                "sample": f"{n} run(s) of all {wl.n_loops} decode loops of 1 of {wl.n_seq} sequences "
+                          f"(context build included), {dt:.1f} s"}
+    data = [(l, {k: v.copy() for k, v in x.items()}) for l, x in SyntheticLoops(wl)]
+    rows_per_step = sum(wl.n_active(l) for l in range(1, wl.n_loops + 1))
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.run_prefill(wl, iter(data))
+        n += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * rows_per_step / dt, "unit": "active-token loop-steps/s", "cores": cores,
+            "kind": "oracle", "sample": f"{n} whole step(s) of the workload ({wl.n_loops} loops), {dt:.1f} s"}
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(the multi-GPU sharding is a design note, not code)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from sparse_loop_attention_amd import abi, configs, driver
+    from sparse_loop_attention_amd.synth import SyntheticLoops
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    abi.lib()
+    wl = configs.WORKLOADS[args.workload]
+    print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    syn = SyntheticLoops(wl)
+    if wl.decode:
+        ctx_sets = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)}
+        inputs = driver.upload_loops(wl, syn, "cuda")
+        run = driver.DecodeRun(wl, inputs, ctx_sets, "cuda")
+        run.build_context()
+    else:
+        inputs = driver.upload_loops(wl, syn, "cuda")
+        run = driver.PrefillRun(wl, inputs, "cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run.run()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    abi.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run.run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    timings = abi.timing_read()
+    abi.timing_enable(False)
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    work = work_model(wl, run)
+    value = work["rows"] * args.steps / elapsed
+    lazy_ms = sum(ms for name, (ms, _) in timings.items()
+                  if name.endswith("_lazy") or name in ("delta_norm", "topk", "commit_delta", "slot_map",
+                                                        "rows_combine", "rows_colmass")) / args.steps
+    out = {
+        "metric": "active-token loop-steps/sec + KV GB/s; % of HBM / bf16-MFMA roofline",
+        "value": value,
+        "unit": "active-token loop-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes and change/heavy-key structure of the pages' workloads)",
+        "config": {"workload": wl.name, "n_seq": wl.n_seq, "heads": wl.n_heads, "head_dim": wl.head_dim,
+                   "seq_len": wl.n_tokens, "loops": wl.n_loops, "full_loops": wl.n_full,
+                   "active": list(wl.active), "keys": wl.n_keys},
+        "kv_GBps": work["kv_bytes"] / (elapsed / args.steps) / 1e9,
+        "lazy_active_token_steps_per_s": (work["lazy_rows"] / (lazy_ms / 1e3)) if lazy_ms > 0 else None,
+        "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in sorted(timings.items())},
+        "roofline": roofline(timings, work, args.steps),
+    }
+    if args.cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

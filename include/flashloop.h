@@ -27,9 +27,10 @@
  *    call returns a non-zero fl_status, launches nothing, and
  *    flashloop_last_error() describes the problem.  A failed launch returns
  *    FL_ERR_HIP.  No C++ exception crosses this boundary.
- *  - The library holds no state besides a thread-local error message; calls
- *    from several threads are safe.  Calls that write the same buffers on
- *    different streams race, as any two kernels would.
+ *  - The library holds no state besides a thread-local error message and the
+ *    optional kernel-timing registry below; calls from several threads are
+ *    safe.  Calls that write the same buffers on different streams race, as
+ *    any two kernels would.
  */
 #ifndef FLASHLOOP_H
 #define FLASHLOOP_H
@@ -193,6 +194,21 @@ typedef struct {
 
 uint64_t  flashloop_attend_workspace_bytes(const fl_attend_args* args);
 fl_status flashloop_attend(const fl_attend_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing (diagnostics, not part of the method).  While enabled, each  */
+/* kernel the library launches is bracketed by two hipEvents recorded on the */
+/* launch stream.  flashloop_timing_read waits for those events, adds each   */
+/* kernel's elapsed time to a per-kernel-name total and returns the totals:  */
+/* names_out receives max_entries NUL-padded names of 64 bytes each,         */
+/* ms_out the summed milliseconds and launches_out the launch counts.  It    */
+/* returns the number of kernel names (which may exceed max_entries).        */
+/* flashloop_timing_enable(0) stops recording; (1) starts it and clears the  */
+/* totals.  This is the one piece of process-wide state in the library; it   */
+/* is guarded by a mutex.                                                    */
+/* ------------------------------------------------------------------------ */
+fl_status flashloop_timing_enable(int32_t on);
+int32_t   flashloop_timing_read(char* names_out, double* ms_out, int64_t* launches_out, int32_t max_entries);
 
 /* ------------------------------------------------------------------------ */
 const char* flashloop_last_error(void);  /* thread-local; "" after a successful call */

@@ -23,7 +23,7 @@ FL_ROWS_BY_TOKEN, FL_ROWS_COMPACT = 0, 1
 
 EXPORTS = ("flashloop_kv_layout", "flashloop_kv_arena_bytes", "flashloop_kv_commit", "flashloop_select",
            "flashloop_attend_workspace_bytes", "flashloop_attend", "flashloop_last_error",
-           "flashloop_abi_version")
+           "flashloop_abi_version", "flashloop_timing_enable", "flashloop_timing_read")
 
 
 class fl_kv_desc(C.Structure):
@@ -88,6 +88,9 @@ def lib():
         L.flashloop_attend.argtypes = [C.POINTER(fl_attend_args), C.c_void_p]
         L.flashloop_last_error.restype = C.c_char_p
         L.flashloop_abi_version.restype = C.c_int32
+        L.flashloop_timing_enable.argtypes = [C.c_int32]
+        L.flashloop_timing_read.argtypes = [C.c_char_p, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.c_int32]
+        L.flashloop_timing_read.restype = C.c_int32
         for f in ("flashloop_kv_layout", "flashloop_kv_commit", "flashloop_select", "flashloop_attend"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -231,6 +234,20 @@ def attend_workspace_bytes(a: fl_attend_args) -> int:
 
 def attend(a: fl_attend_args, stream=None) -> None:
     _check(lib().flashloop_attend(C.byref(a), _stream(stream)))
+
+
+def timing_enable(on: bool) -> None:
+    _check(lib().flashloop_timing_enable(int(on)))
+
+
+def timing_read() -> dict:
+    """{kernel name: (total ms, launches)} since timing_enable(True)."""
+    n = lib().flashloop_timing_read(None, None, None, 0)
+    names = C.create_string_buffer(64 * max(n, 1))
+    ms = (C.c_double * max(n, 1))()
+    cnt = (C.c_int64 * max(n, 1))()
+    n = lib().flashloop_timing_read(names, ms, cnt, n)
+    return {names.raw[64 * i:64 * (i + 1)].rstrip(b"\0").decode(): (ms[i], cnt[i]) for i in range(n)}
 
 
 def abi_version() -> int:

@@ -17,6 +17,7 @@
 //              row order (deterministic, no atomics).
 #include "fl_common.hpp"
 #include "fl_launch.hpp"
+#include "fl_timing.hpp"
 
 namespace fl {
 
@@ -252,6 +253,8 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
   const bool lazy = x.mode == FL_ATTEND_LAZY;
   const int sh = kv.n_seq * kv.H;
   dim3 g1(p.splits, x.n_active, sh);
+  {
+  TimedLaunch t(st, lazy ? "rows_partial_lazy" : "rows_partial_full");
   if (kv.dtype == FL_BF16) {
     if (lazy) hipLaunchKernelGGL((k_rows_partial<FL_BF16, true>), g1, dim3(64), 0, st, kv, a);
     else hipLaunchKernelGGL((k_rows_partial<FL_BF16, false>), g1, dim3(64), 0, st, kv, a);
@@ -259,13 +262,18 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
     if (lazy) hipLaunchKernelGGL((k_rows_partial<FL_F32, true>), g1, dim3(64), 0, st, kv, a);
     else hipLaunchKernelGGL((k_rows_partial<FL_F32, false>), g1, dim3(64), 0, st, kv, a);
   }
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(x.n_active, sh);
+  {
+  TimedLaunch t(st, "rows_combine");
   if (lazy) hipLaunchKernelGGL(k_rows_combine<true>, g2, dim3(64), 0, st, kv.n_seq, kv.H, kv.d, kv.N, a);
   else hipLaunchKernelGGL(k_rows_combine<false>, g2, dim3(64), 0, st, kv.n_seq, kv.H, kv.d, kv.N, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 g3(static_cast<unsigned>((p.keys + 63) / 64), sh);
+  TimedLaunch t(st, "rows_colmass");
   if (lazy) hipLaunchKernelGGL(k_rows_colmass<true>, g3, dim3(64), 0, st, kv.n_seq, kv.H, kv.N, a);
   else hipLaunchKernelGGL(k_rows_colmass<false>, g3, dim3(64), 0, st, kv.n_seq, kv.H, kv.N, a);
   return hipGetLastError();

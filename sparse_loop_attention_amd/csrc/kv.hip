@@ -7,6 +7,7 @@
 // token writes nothing.
 #include "fl_common.hpp"
 #include "fl_launch.hpp"
+#include "fl_timing.hpp"
 
 namespace fl {
 
@@ -92,6 +93,7 @@ hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t 
   uint8_t* arena = static_cast<uint8_t*>(a.kv->arena);
   if (a.version >= 2) {
     dim3 g((kv.N + 255) / 256, kv.n_seq);
+    TimedLaunch t(st, "slot_map");
     hipLaunchKernelGGL(k_slot_map, g, dim3(256), 0, st,
                        reinterpret_cast<int32_t*>(arena + kv.slot_map[a.version]), kv.N, a.active_idx,
                        a.n_active, a.slot_base, a.reset_map);
@@ -101,6 +103,7 @@ hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t 
   const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_active * kv.H * 2;
   dim3 grid(static_cast<unsigned>((items + 15) / 16)), block(256);
   const int compact = a.src_layout == FL_ROWS_COMPACT;
+  TimedLaunch t(st, a.version == 1 ? "commit_base" : "commit_delta");
   if (kv.dtype == FL_BF16)
     hipLaunchKernelGGL(k_commit<FL_BF16>, grid, block, 0, st, kv, arena, a.version, a.active_idx,
                        a.n_active, a.slot_base, a.k_new, a.v_new, compact);

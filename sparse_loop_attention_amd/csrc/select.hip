@@ -7,6 +7,7 @@
 // statistics.  Both reduce to "k largest, ties to the lower index, ascending".
 #include "fl_common.hpp"
 #include "fl_launch.hpp"
+#include "fl_timing.hpp"
 
 namespace fl {
 
@@ -233,6 +234,7 @@ static hipError_t launch_topk(const ScoreT* scores, int64_t n_seg, int64_t seg_l
   dim3 grid(static_cast<unsigned>(n_seg)), block(kTopkThreads);
 #define FL_TOPK_CASE(E)                                                                    \
   if (per <= E) {                                                                          \
+    TimedLaunch t(st, "topk");                                                             \
     hipLaunchKernelGGL((k_topk<ScoreT, E>), grid, block, 0, st, scores, seg_len, k, out);  \
     return hipGetLastError();                                                              \
   }
@@ -244,13 +246,16 @@ static hipError_t launch_topk(const ScoreT* scores, int64_t n_seg, int64_t seg_l
 
 hipError_t launch_select(const fl_select_args& a, hipStream_t st) {
   if (a.mode == FL_SEL_TOKENS) {
-    dim3 grid(static_cast<unsigned>((a.n_rows + 3) / 4)), block(256);
-    if (a.h_dtype == FL_BF16)
-      hipLaunchKernelGGL(k_delta_norm<FL_BF16>, grid, block, 0, st, a.h_cur, a.h_prev, a.n_rows,
-                         a.hidden, a.cand_idx, a.n_cand, a.scores);
-    else
-      hipLaunchKernelGGL(k_delta_norm<FL_F32>, grid, block, 0, st, a.h_cur, a.h_prev, a.n_rows,
-                         a.hidden, a.cand_idx, a.n_cand, a.scores);
+    {
+      dim3 grid(static_cast<unsigned>((a.n_rows + 3) / 4)), block(256);
+      TimedLaunch t(st, "delta_norm");
+      if (a.h_dtype == FL_BF16)
+        hipLaunchKernelGGL(k_delta_norm<FL_BF16>, grid, block, 0, st, a.h_cur, a.h_prev, a.n_rows,
+                           a.hidden, a.cand_idx, a.n_cand, a.scores);
+      else
+        hipLaunchKernelGGL(k_delta_norm<FL_F32>, grid, block, 0, st, a.h_cur, a.h_prev, a.n_rows,
+                           a.hidden, a.cand_idx, a.n_cand, a.scores);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_topk<double>(a.scores, 1, a.n_rows, a.k, a.out_idx, st);

@@ -81,7 +81,8 @@ class PrefillRun:
         self.all_rows = torch.arange(n, dtype=torch.int32, device=device)
         self.act = {l: torch.empty(wl.n_active(l), dtype=torch.int32, device=device)
                     for l in range(wl.n_full + 1, wl.n_loops + 1)}
-        self.keys = torch.empty(H, wl.n_keys, dtype=torch.int32, device=device)
+        self.keys_l = {l: torch.empty(H, wl.n_keys, dtype=torch.int32, device=device)
+                       for l in range(wl.n_full + 1, wl.n_loops + 1)}
         self.workspace = None
         ws = 0
         for l in range(1, wl.n_loops + 1):
@@ -95,7 +96,7 @@ class PrefillRun:
                                    None, self.o, self.lse, self.colmass, self.workspace)
         na = wl.n_active(l)
         return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, self.q_cur_rows[:na], self.q_prev_rows[:na],
-                               self.act[l], na, self.keys, self.o, self.lse, self.colmass, self.workspace,
+                               self.act[l], na, self.keys_l[l], self.o, self.lse, self.colmass, self.workspace,
                                q_compact=True)
 
     # ------------------------------------------------------------------ loops
@@ -111,7 +112,7 @@ class PrefillRun:
         wl, x = self.wl, self.inp[l]
         act, na = self.act[l], wl.n_active(l)
         abi.select_tokens(self.h_eff, self.h_prev, na, self.scores, act, cand)
-        abi.select_keys(self.colmass, wl.n_keys, self.keys)
+        abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
         # model stand-in: the shared block recomputes the active rows only
         idx = act.long()
         self.h_prev.index_copy_(0, idx, self.h_eff.index_select(0, idx))
@@ -137,7 +138,7 @@ class PrefillRun:
                 act = self.lazy_loop(l, cand)
                 cand = act
                 rec = LoopRecord(rows=act.clone() if record else None,
-                                 keys=self.keys.clone() if record else None,
+                                 keys=self.keys_l[l].clone() if record else None,
                                  scores=self.scores.clone() if record else None)
             if record:
                 rec.o, rec.lse, rec.colmass = self.o.clone(), self.lse.clone(), self.colmass.clone()
@@ -191,7 +192,7 @@ class DecodeRun:
         slot_base = 0 if l == 1 else self.ctx[l].shape[1]
         abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False)
         if l >= 2:
-            abi.select_keys(self.colmass, wl.n_keys, self.keys)
+            abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
         abi.attend(self._args(l, self.workspace))
 
     def run(self, record: bool = False) -> List[LoopRecord]:

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(abi.EXPORTS)
