@@ -39,8 +39,11 @@ Readings of points the page leaves open (all listed in the design doc):
      even element; delta is taken against the previous reconstruction.
   R8 loop 1 stores the base (working dtype); every later loop, full or lazy,
      appends one delta layer holding records of that loop's active tokens.
-  R9 all attention reads the reconstructed K^, V^ of every key; queries are
-     exact.
+  R9 all attention reads the reconstructed K^, V^ of every key, in the
+     working dtype of the workload: the float32 reconstruction is rounded to
+     bfloat16 (nearest-even) for bf16 workloads, as the version-1 base already
+     is; queries are used as given.  The int4 chain itself (R7, R8) stays in
+     float32.
 Parity unpinned: the page prints no worked example of the mass-corrected
 formula (R4), so its exact form is pinned only by invariants (full attention
 when all keys are selected, fixed point when nothing changed, mass
@@ -55,13 +58,29 @@ from typing import Dict, List, Optional
 import numpy as np
 
 __all__ = [
-    "token_scores", "topk_ascending", "select_keys", "f16_rne", "quantize_groups",
+    "to_working_dtype", "token_scores", "topk_ascending", "select_keys", "f16_rne", "quantize_groups",
     "dequantize_groups", "pack_int4", "unpack_int4", "KVStore", "full_attention",
     "lazy_attention", "LoopState", "run_prefill", "run_decode_seq",
 ]
 
 F32 = np.float32
 F64 = np.float64
+
+
+def to_working_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to the workload's dtype (reading R9); float32 out.
+
+    bf16: keep the upper 16 bits of the float32 pattern after adding half an
+    ulp of bf16, with ties to the even bf16 pattern (round-to-nearest-even);
+    values are finite here.  fp32: unchanged.
+    """
+    x = np.ascontiguousarray(x, dtype=F32)
+    if dtype == "fp32":
+        return x
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    rounded = ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    return (rounded & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(F32)
 
 
 # --------------------------------------------------------------------------- #
@@ -366,8 +385,8 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
             h_prev_eff, h_eff = h_eff, x["h"][seq].copy()
             q_eff = x["q"][seq].copy()
             store.commit(l, rows, x["k"][seq], x["v"][seq])
-            kh = store.reconstruct("k", l)
-            vh = store.reconstruct("v", l)
+            kh = to_working_dtype(store.reconstruct("k", l), wl.dtype)
+            vh = to_working_dtype(store.reconstruct("v", l), wl.dtype)
             o, lse, colmass = full_attention(q_eff, kh, vh, rows)
             rec.update(rows=rows)
         else:
@@ -379,11 +398,11 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
             h_eff[rows] = x["h"][seq][rows]
             q_prev_rows = q_eff[rows].copy()
             q_eff[rows] = x["q"][seq][rows]
-            k_prev_hat = store.reconstruct("k", l - 1)
-            v_prev_hat = store.reconstruct("v", l - 1)
+            k_prev_hat = to_working_dtype(store.reconstruct("k", l - 1), wl.dtype)
+            v_prev_hat = to_working_dtype(store.reconstruct("v", l - 1), wl.dtype)
             recs = store.commit(l, rows, x["k"][seq][rows], x["v"][seq][rows])
-            k_hat = store.reconstruct("k", l)
-            v_hat = store.reconstruct("v", l)
+            k_hat = to_working_dtype(store.reconstruct("k", l), wl.dtype)
+            v_hat = to_working_dtype(store.reconstruct("v", l), wl.dtype)
             o_r, lse_r, colmass, m, upd = lazy_attention(
                 q_eff[rows], q_prev_rows, k_prev_hat, v_prev_hat, k_hat, v_hat,
                 o[rows], lse[rows], colmass, rows, keys)
@@ -424,16 +443,16 @@ def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], 
         q = x["q"][si]                       # [1, H, d]
         store.commit(l, last, x["k"][si][last], x["v"][si][last])
         if l == 1:
-            kh = store.reconstruct("k", 1)
-            vh = store.reconstruct("v", 1)
+            kh = to_working_dtype(store.reconstruct("k", 1), wl.dtype)
+            vh = to_working_dtype(store.reconstruct("v", 1), wl.dtype)
             o, lse, colmass = full_attention(q, kh, vh, last)
             out.append(dict(o=o.copy(), lse=lse.copy(), colmass=colmass.copy()))
         else:
             keys = select_keys(colmass, wl.n_keys)
-            kp = store.reconstruct("k", l - 1)
-            vp = store.reconstruct("v", l - 1)
-            kc = store.reconstruct("k", l)
-            vc = store.reconstruct("v", l)
+            kp = to_working_dtype(store.reconstruct("k", l - 1), wl.dtype)
+            vp = to_working_dtype(store.reconstruct("v", l - 1), wl.dtype)
+            kc = to_working_dtype(store.reconstruct("k", l), wl.dtype)
+            vc = to_working_dtype(store.reconstruct("v", l), wl.dtype)
             o, lse, colmass, m, upd = lazy_attention(q, q_prev, kp, vp, kc, vc, o, lse, colmass,
                                                      last, keys)
             out.append(dict(o=o.copy(), lse=lse.copy(), colmass=colmass.copy(), keys=keys, mass=m))

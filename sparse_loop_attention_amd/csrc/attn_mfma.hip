@@ -1,0 +1,520 @@
+// Tiled bf16 MFMA attention on gathered key tiles (prefill: many active rows).
+//
+// Page "FlashLoop: Fast and Memory-Efficient Looped Transformers via Lazy
+// Updates", section "FlashLoop combines three kinds of savings": paragraph 2
+// (attention on the keys chosen from the previous loop's statistics, keeping
+// the chosen group's previous probability mass) and paragraph 4 (the selected
+// data is gathered into dense buffers so that sparsity turns into speed).
+//
+// Three launches per call:
+//   gather   - walks the base+delta chain of every key slot (all N keys in a
+//              full loop, the selected keys in a lazy loop) once, and writes
+//              dense tiles: K^ rows [sh][slot][d] in bf16 and V^ transposed
+//              [sh][d][slot] as fp16 holding the bf16-rounded values (keys
+//              permuted inside each 16-key chunk so that an MFMA operand is
+//              one 16-byte LDS read), plus the key positions; a lazy loop
+//              gathers versions v-1 and v;
+//   fwd      - one workgroup per 128 (full) or 64 (lazy) query rows of one
+//              head.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 keeps every query
+//              in one lane, so the row softmax needs a single cross-half
+//              exchange; P^T feeds the PV product straight from the
+//              accumulators.  In a lazy loop waves pair up: one computes the
+//              current softmax over the selected keys, its partner the
+//              previous loop's probabilities with the fixed normaliser lse_prev
+//              (mass m and contribution a); they combine through LDS into
+//              o = m*otilde + o_prev - a;
+//   colmass  - key-major: one workgroup per 128 key slots, streaming the
+//              query tiles, S = Q K^T with keys in lanes so that the column
+//              sums are lane-local; fixed order, no atomics.
+#include <climits>
+
+#include "fl_common.hpp"
+#include "fl_launch.hpp"
+#include "fl_timing.hpp"
+
+namespace fl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct MfmaArgs {
+  // rows
+  const int32_t* act;       // [n_seq][n_rows] token positions, or null = identity
+  int32_t n_rows;
+  const void* q_cur;        // bf16
+  const void* q_prev;
+  int32_t q_compact, o_compact;
+  float* o;
+  float* lse;
+  float* colmass;
+  // keys
+  const int32_t* key_idx;   // LAZY: [sh][n_keys]; FULL: null (all N keys)
+  int32_t n_keys;           // key slots per head
+  int32_t n_keys_pad;       // multiple of 64
+  int32_t version;
+  float scale;
+  // workspace
+  uint16_t* kc;             // [sh][n_keys_pad][D]
+  uint16_t* kp;
+  uint16_t* vtc;            // [sh][D][n_keys_pad] (permuted keys)
+  uint16_t* vtp;
+  int32_t* kidx;            // [sh][n_keys_pad], INT_MAX for padding
+  float* stat;              // [sh][n_rows][4] = lse_prev, lse_new, valid, token
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// PV runs in fp16: the probabilities need more than bf16's 8 significant bits
+// to keep the output within tolerance; V^ (bf16 values) converts exactly.
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// bf16-rounded V^ as fp16 bits; |v| is saturated at 65504 (the fp16 range).
+__device__ __forceinline__ uint16_t v_operand_bits(float v) {
+  const float b = fminf(fmaxf(round_bf16(v), -65504.0f), 65504.0f);
+  return f32_to_half_bits(b);
+}
+
+__device__ __forceinline__ int row_token(const MfmaArgs& a, int s, int r) {
+  return a.act ? a.act[static_cast<int64_t>(s) * a.n_rows + r] : r;
+}
+
+// position of key offset k16 (0..15) inside its 16-key chunk of V^T:
+// keys 4..7 and 8..11 swap places, so that k-slot i of lane half h
+// (key 8*(i/4) + 4h + i%4) sits at 8h + i.
+__device__ __forceinline__ int vt_pos(int k16) {
+  const int q = k16 >> 2;
+  return ((q == 1) ? 2 : (q == 2) ? 1 : q) * 4 + (k16 & 3);
+}
+
+// --------------------------------------------------------------------------- gather
+template <int DT, int D, bool LAZY>
+__global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a) {
+  __shared__ uint16_t sv[2][64][D + 2];
+  const int sh = blockIdx.y, tile = blockIdx.x;
+  const int s = sh / kv.H, h = sh % kv.H;
+  const int g = threadIdx.x >> 4, p = threadIdx.x & 15;
+  const bool live = 8 * p < D;
+  const int64_t row_kv = static_cast<int64_t>(s) * kv.H + h;
+#pragma unroll 1
+  for (int kk = 0; kk < 4; ++kk) {
+    const int local = g * 4 + kk;
+    const int t = tile * 64 + local;
+    int j = -1;
+    if (t < a.n_keys) j = a.key_idx ? a.key_idx[static_cast<int64_t>(sh) * a.n_keys + t] : t;
+    float x[8] = {}, xp[8] = {};
+    const int64_t krow = (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * p;
+    if (live) {
+      if (j >= 0) recon8<DT>(kv, 0, s, row_kv, j, a.version, p, x, LAZY ? xp : nullptr);
+      store8<FL_BF16>(a.kc, krow, x);
+      if (LAZY) store8<FL_BF16>(a.kp, krow, xp);
+      float y[8] = {}, yp[8] = {};
+      if (j >= 0) recon8<DT>(kv, 1, s, row_kv, j, a.version, p, y, LAZY ? yp : nullptr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sv[0][local][8 * p + e] = v_operand_bits(y[e]);
+        if (LAZY) sv[1][local][8 * p + e] = v_operand_bits(yp[e]);
+      }
+    }
+    if (p == 0) a.kidx[static_cast<int64_t>(sh) * a.n_keys_pad + t] = j >= 0 ? j : INT_MAX;
+  }
+  __syncthreads();
+  // V^T: thread handles (dim, 8 consecutive stored positions)
+  for (int item = threadIdx.x; item < D * 8; item += 256) {
+    const int dim = item >> 3, pos0 = (item & 7) * 8;
+#pragma unroll
+    for (int which = 0; which < (LAZY ? 2 : 1); ++which) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        // stored position pos -> key offset inside the tile
+        int pa = pos0 + e, pb = pos0 + e + 1;
+        int ka = (pa & ~15) + vt_pos(pa & 15), kb = (pb & ~15) + vt_pos(pb & 15);   // vt_pos is an involution
+        w[e / 2] = static_cast<uint32_t>(sv[which][ka][dim]) | (static_cast<uint32_t>(sv[which][kb][dim]) << 16);
+      }
+      uint16_t* dst = (which ? a.vtp : a.vtc) + (static_cast<int64_t>(sh) * D + dim) * a.n_keys_pad + tile * 64 + pos0;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------- fwd
+template <int D, bool LAZY>
+__global__ __launch_bounds__(256) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
+  constexpr int KT = 64;
+  constexpr int DC = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int KS = D + 8;
+  constexpr int VS = KT + 8;
+  constexpr int NR = LAZY ? 2 : 1;
+  constexpr int ROWS = LAZY ? 64 : 128;
+  __shared__ __attribute__((aligned(16))) uint16_t sk[NR][KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[NR][D * VS];
+  __shared__ int skidx[KT];
+  __shared__ float sm[2][32];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, c = lane & 31;
+  const int sh = blockIdx.y;
+  const int s = sh / H, h = sh % H;
+  const int qtile = gridDim.x - 1 - blockIdx.x;          // heavy (late) tiles first
+  const int blk = LAZY ? (wave >> 1) : wave;
+  const int role = LAZY ? (wave & 1) : 0;                 // 0 = current, 1 = previous loop
+  const int r = qtile * ROWS + blk * 32 + c;
+  const bool vrow = r < a.n_rows;
+  const int tok = vrow ? row_token(a, s, r) : -1;
+
+  // queries: Q^T fragments (B operand), one row per lane column
+  bf16x8 qf[DC];
+  {
+    const uint16_t* q = static_cast<const uint16_t*>(role ? a.q_prev : a.q_cur);
+    const int64_t rows_q = a.q_compact ? a.n_rows : N;
+    const int64_t qr = a.q_compact ? r : tok;
+    const uint16_t* src = q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + 8 * hh;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      if (vrow) qf[dc] = *reinterpret_cast<const bf16x8*>(src + dc * 16);
+      else qf[dc] = bf16x8{};
+    }
+  }
+  const int64_t rows_o = a.o_compact ? a.n_rows : N;
+  const int64_t orow = a.o_compact ? r : tok;
+  float lse_prev = 0.0f;
+  if (LAZY && vrow) lse_prev = a.lse[(static_cast<int64_t>(s) * rows_o + orow) * H + h];
+
+  // key tiles needed by the last row of this workgroup
+  if (tid == 0) {
+    int rl = min(a.n_rows, (qtile + 1) * ROWS) - 1;
+    const int last_tok = row_token(a, s, rl);
+    const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
+    int lo = 0, hi = a.n_keys;
+    while (lo < hi) { const int mid = (lo + hi) >> 1; if (kx[mid] <= last_tok) lo = mid + 1; else hi = mid; }
+    s_last = lo;                                           // visible key slots of the last row
+  }
+  __syncthreads();
+  const int n_tiles = (s_last + KT - 1) / KT;
+  // first row token of this wave's block (rows ascending)
+  const int blk_first = min(a.n_rows - 1, qtile * ROWS + blk * 32);
+  const int tok_first = row_token(a, s, blk_first);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;                  // current-loop online softmax (lane half)
+  float mass = 0.0f;                                      // previous-loop mass (lane half)
+
+  const uint16_t* kbase[NR];
+  const uint16_t* vbase[NR];
+  kbase[0] = a.kc + static_cast<int64_t>(sh) * a.n_keys_pad * D;
+  vbase[0] = a.vtc + static_cast<int64_t>(sh) * D * a.n_keys_pad;
+  if (LAZY) {
+    kbase[NR - 1] = a.kp + static_cast<int64_t>(sh) * a.n_keys_pad * D;
+    vbase[NR - 1] = a.vtp + static_cast<int64_t>(sh) * D * a.n_keys_pad;
+  }
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NR; ++w) {
+      for (int i = tid; i < KT * D / 8; i += 256) {        // K tile: KT rows of D
+        const int row = i / (D / 8), col = (i % (D / 8)) * 8;
+        *reinterpret_cast<uint4*>(&sk[w][row * KS + col]) =
+            *reinterpret_cast<const uint4*>(kbase[w] + static_cast<int64_t>(tile * KT + row) * D + col);
+      }
+      for (int i = tid; i < D * KT / 8; i += 256) {        // V^T tile: D rows of KT
+        const int row = i / (KT / 8), col = (i % (KT / 8)) * 8;
+        *reinterpret_cast<uint4*>(&sv[w][row * VS + col]) =
+            *reinterpret_cast<const uint4*>(vbase[w] + static_cast<int64_t>(row) * a.n_keys_pad + tile * KT + col);
+      }
+    }
+    if (tid < KT) skidx[tid] = a.kidx[static_cast<int64_t>(sh) * a.n_keys_pad + tile * KT + tid];
+    __syncthreads();
+    if (tok_first < 0 || skidx[0] > row_token(a, s, min(a.n_rows - 1, qtile * ROWS + blk * 32 + 31))) {
+      // every key of this tile is past every row of the block: nothing to add
+      continue;
+    }
+    const uint16_t* K = sk[role];
+    const uint16_t* V = sv[role];
+    f32x16 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&K[(kb * 32 + c) * KS + dc * 16 + 8 * hh]);
+        st[kb] = mfma32(ka, qf[dc], st[kb]);
+      }
+    }
+    const bool need_mask = !vrow || skidx[KT - 1] > tok_first;
+    float pv[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = st[kb][i] * a.scale;
+        if (need_mask) {
+          const int key = skidx[kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)];
+          if (!vrow || key > tok) x = -INFINITY;
+        }
+        pv[kb * 16 + i] = x;
+      }
+    if (role == 0) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) tmax = fmaxf(tmax, pv[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      float alpha = 1.0f, psum = 0.0f;
+      if (m_new == -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) pv[i] = 0.0f;
+      } else {
+        alpha = __expf(m_run - m_new);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) { pv[i] = __expf(pv[i] - m_new); psum += pv[i]; }
+        m_run = m_new;
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) { pv[i] = __expf(pv[i] - lse_prev); mass += pv[i]; }
+    }
+    // O^T += V^T P^T over four 16-key chunks
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      f16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[i] = static_cast<_Float16>(pv[cc * 8 + i]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f16x8 va = *reinterpret_cast<const f16x8*>(&V[(db * 32 + c) * VS + cc * 16 + 8 * hh]);
+        acc[db] = mfma32h(va, pb, acc[db]);
+      }
+    }
+  }
+
+  // ---- epilogue
+  float* lse_ptr = a.lse + (static_cast<int64_t>(s) * rows_o + orow) * H + h;
+  float* o_ptr = a.o + ((static_cast<int64_t>(s) * rows_o + orow) * H + h) * D;
+  float* st_ptr = a.stat + (static_cast<int64_t>(sh) * a.n_rows + r) * 4;
+  if (!LAZY) {
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (vrow && l_tot > 0.0f) {
+      const float inv = 1.0f / l_tot;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int dim = db * 32 + 8 * q4 + 4 * hh;
+          *reinterpret_cast<float4*>(o_ptr + dim) =
+              make_float4(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv, acc[db][4 * q4 + 2] * inv,
+                          acc[db][4 * q4 + 3] * inv);
+        }
+      if (hh == 0) {
+        const float l = m_run + __logf(l_tot);
+        *lse_ptr = l;
+        *reinterpret_cast<float4*>(st_ptr) = make_float4(l, l, 1.0f, __int_as_float(tok));
+      }
+    }
+    return;
+  }
+  // lazy: the previous-loop wave hands its mass and contribution to its partner
+  __syncthreads();
+  float* sa = reinterpret_cast<float*>(&sk[0][0]);        // [blk][DB][16][64] floats
+  if (role == 1) {
+    const float m_tot = mass + __shfl_xor(mass, 32, 64);
+    if (hh == 0) sm[blk][c] = m_tot;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sa[((blk * DB + db) * 16 + i) * 64 + lane] = acc[db][i];
+  }
+  __syncthreads();
+  if (role == 0 && vrow) {
+    const float z = l_run + __shfl_xor(l_run, 32, 64);
+    const float m = sm[blk][c];
+    const bool valid = z > 0.0f && m > 0.0f;
+    if (valid) {
+      const float f = m / z;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int dim = db * 32 + 8 * q4 + 4 * hh;
+          float4 op = *reinterpret_cast<const float4*>(o_ptr + dim);
+          const float* av = &sa[((blk * DB + db) * 16 + 4 * q4) * 64 + lane];
+          op.x = fmaf(f, acc[db][4 * q4 + 0], op.x - av[0]);
+          op.y = fmaf(f, acc[db][4 * q4 + 1], op.y - av[64]);
+          op.z = fmaf(f, acc[db][4 * q4 + 2], op.z - av[128]);
+          op.w = fmaf(f, acc[db][4 * q4 + 3], op.w - av[192]);
+          *reinterpret_cast<float4*>(o_ptr + dim) = op;
+        }
+    }
+    if (hh == 0) {
+      const float lnew = valid ? m_run + __logf(z) - __logf(m) : lse_prev;
+      if (valid) *lse_ptr = lnew;
+      *reinterpret_cast<float4*>(st_ptr) = make_float4(lse_prev, lnew, valid ? 1.0f : 0.0f, __int_as_float(tok));
+    }
+  }
+}
+
+// --------------------------------------------------------------------------- colmass
+template <int D, bool LAZY>
+__global__ __launch_bounds__(256) void k_mfma_colmass(int32_t H, int32_t N, MfmaArgs a) {
+  constexpr int QT = 64;
+  constexpr int DC = D / 16;
+  constexpr int QS = D + 8;
+  constexpr int NR = LAZY ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t sq[NR][QT * QS];
+  __shared__ float4 sst[QT];
+  __shared__ int s_start;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, c = lane & 31;
+  const int sh = blockIdx.y;
+  const int s = sh / H, h = sh % H;
+  const int t0 = blockIdx.x * 128 + wave * 32;
+  const int t = t0 + c;
+  const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
+  const int kj = kx[t];                                    // INT_MAX for padding
+
+  bf16x8 kf[NR][DC];
+#pragma unroll
+  for (int w = 0; w < NR; ++w) {
+    const uint16_t* kb = (w ? a.kp : a.kc) + (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * hh;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) kf[w][dc] = *reinterpret_cast<const bf16x8*>(kb + dc * 16);
+  }
+  if (tid == 0) {                                          // first row that sees the block's first key
+    const int kfirst = kx[blockIdx.x * 128];
+    int lo = 0, hi = a.n_rows;
+    while (lo < hi) { const int mid = (lo + hi) >> 1; if (row_token(a, s, mid) < kfirst) lo = mid + 1; else hi = mid; }
+    s_start = lo;
+  }
+  __syncthreads();
+  const int r_begin = (s_start / QT) * QT;
+  float acc = 0.0f;
+  const int64_t rows_q = a.q_compact ? a.n_rows : N;
+  for (int q0 = r_begin; q0 < a.n_rows; q0 += QT) {
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NR; ++w) {
+      const uint16_t* q = static_cast<const uint16_t*>(w ? a.q_prev : a.q_cur);
+      for (int i = tid; i < QT * D / 8; i += 256) {
+        const int row = i / (D / 8), col = (i % (D / 8)) * 8;
+        const int r = q0 + row;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < a.n_rows) {
+          const int64_t qr = a.q_compact ? r : row_token(a, s, r);
+          v = *reinterpret_cast<const uint4*>(q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + col);
+        }
+        *reinterpret_cast<uint4*>(&sq[w][row * QS + col]) = v;
+      }
+    }
+    if (tid < QT) {
+      const int r = q0 + tid;
+      sst[tid] = r < a.n_rows ? *reinterpret_cast<const float4*>(a.stat + (static_cast<int64_t>(sh) * a.n_rows + r) * 4)
+                              : make_float4(0.f, 0.f, 0.f, __int_as_float(-1));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 sc = f32x16{}, sp = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[0][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
+        sc = mfma32(qa, kf[0][dc], sc);
+        if (LAZY) {
+          const bf16x8 qpa = *reinterpret_cast<const bf16x8*>(&sq[NR - 1][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
+          sp = mfma32(qpa, kf[NR - 1][dc], sp);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 st = sst[qb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)];
+        if (st.z != 0.0f && kj <= __float_as_int(st.w)) {
+          float v = __expf(sc[i] * a.scale - st.y);
+          if (LAZY) v -= __expf(sp[i] * a.scale - st.x);
+          acc += v;
+        }
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 32, 64);
+  if (hh == 0 && t < a.n_keys) {
+    float* dst = a.colmass + static_cast<int64_t>(sh) * N + kj;
+    if (LAZY) *dst += acc; else *dst = acc;
+  }
+}
+
+// --------------------------------------------------------------------------- launch
+template <int D>
+static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st) {
+  const bool lazy = x.mode == FL_ATTEND_LAZY;
+  MfmaArgs a{};
+  a.act = x.active_idx;
+  a.n_rows = x.n_active;
+  a.q_cur = x.q_cur; a.q_prev = x.q_prev;
+  a.q_compact = x.q_layout == FL_ROWS_COMPACT; a.o_compact = x.o_layout == FL_ROWS_COMPACT;
+  a.o = x.o; a.lse = x.lse; a.colmass = x.colmass;
+  a.key_idx = lazy ? x.key_idx : nullptr;
+  a.n_keys = static_cast<int32_t>(p.keys);
+  a.n_keys_pad = static_cast<int32_t>((p.keys + 127) / 128 * 128);
+  a.version = x.version;
+  a.scale = 1.0f / sqrtf(static_cast<float>(D));
+  uint8_t* ws = static_cast<uint8_t*>(x.workspace);
+  const uint64_t sh = static_cast<uint64_t>(kv.n_seq) * kv.H;
+  const uint64_t kbytes = sh * a.n_keys_pad * D * 2;
+  a.kc = reinterpret_cast<uint16_t*>(ws + p.off_gather);
+  a.vtc = reinterpret_cast<uint16_t*>(ws + p.off_gather + kbytes);
+  a.kp = reinterpret_cast<uint16_t*>(ws + p.off_gather + 2 * kbytes);
+  a.vtp = reinterpret_cast<uint16_t*>(ws + p.off_gather + 3 * kbytes);
+  a.kidx = reinterpret_cast<int32_t*>(ws + p.off_gather + (lazy ? 4 : 2) * kbytes);
+  a.stat = reinterpret_cast<float*>(ws + p.off_stat);
+
+  dim3 gg(a.n_keys_pad / 64, static_cast<unsigned>(sh));
+  {
+    TimedLaunch t(st, lazy ? "gather_lazy" : "gather_full");
+    if (kv.dtype == FL_BF16) {
+      if (lazy) hipLaunchKernelGGL((k_gather<FL_BF16, D, true>), gg, dim3(256), 0, st, kv, a);
+      else hipLaunchKernelGGL((k_gather<FL_BF16, D, false>), gg, dim3(256), 0, st, kv, a);
+    } else {
+      if (lazy) hipLaunchKernelGGL((k_gather<FL_F32, D, true>), gg, dim3(256), 0, st, kv, a);
+      else hipLaunchKernelGGL((k_gather<FL_F32, D, false>), gg, dim3(256), 0, st, kv, a);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows_per = lazy ? 64 : 128;
+  dim3 gf((a.n_rows + rows_per - 1) / rows_per, static_cast<unsigned>(sh));
+  {
+    TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
+    if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, true>), gf, dim3(256), 0, st, kv.H, kv.N, a);
+    else hipLaunchKernelGGL((k_mfma_fwd<D, false>), gf, dim3(256), 0, st, kv.H, kv.N, a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  dim3 gc(a.n_keys_pad / 128, static_cast<unsigned>(sh));
+  {
+    TimedLaunch t(st, lazy ? "mfma_colmass_lazy" : "mfma_colmass_full");
+    if (lazy) hipLaunchKernelGGL((k_mfma_colmass<D, true>), gc, dim3(256), 0, st, kv.H, kv.N, a);
+    else hipLaunchKernelGGL((k_mfma_colmass<D, false>), gc, dim3(256), 0, st, kv.H, kv.N, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st) {
+  switch (kv.d) {
+    case 64: return launch_d<64>(x, kv, p, st);
+    case 96: return launch_d<96>(x, kv, p, st);
+    default: return launch_d<128>(x, kv, p, st);
+  }
+}
+
+}  // namespace fl

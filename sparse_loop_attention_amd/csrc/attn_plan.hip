@@ -1,10 +1,17 @@
 // Workspace planning and dispatch of an attend call to the per-row path or the
 // tiled MFMA path.
+//
+// The tiled bf16 MFMA path serves bf16 stores with at least kMfmaMinRows
+// active rows (prefill loops); the per-row path serves float32 stores and
+// calls with few rows per head (decode), where a 32-row MFMA tile would idle.
 #include "fl_launch.hpp"
 
 namespace fl {
 
 hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);
+hipError_t launch_mfma(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);
+
+constexpr int kMfmaMinRows = 64;
 
 static uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
@@ -12,15 +19,27 @@ AttendPlan plan_attend(const fl_attend_args& a) {
   AttendPlan p{};
   const fl_kv_desc& d = *a.kv;
   const bool lazy = a.mode == FL_ATTEND_LAZY;
-  p.mfma = false;
+  const uint64_t sh = static_cast<uint64_t>(d.n_seq) * d.n_heads;
+  const uint64_t D = static_cast<uint64_t>(d.head_dim);
   p.rows = a.n_active;
   p.keys = lazy ? a.n_keys : d.n_tokens;
-  p.splits = static_cast<int>((p.keys + 63) / 64);
-  const uint64_t sh = static_cast<uint64_t>(d.n_seq) * d.n_heads;
+  p.mfma = d.base_dtype == FL_BF16 && a.n_active >= kMfmaMinRows;
   const uint64_t rows = static_cast<uint64_t>(p.rows);
   uint64_t off = 0;
+  if (p.mfma) {
+    const uint64_t kpad = (static_cast<uint64_t>(p.keys) + 127) / 128 * 128;
+    p.splits = 0;
+    p.off_stat = off;
+    off = align256(off + sh * rows * 16);
+    p.off_gather = off;
+    off = align256(off + (lazy ? 4 : 2) * sh * kpad * D * 2 + sh * kpad * 4);
+    p.off_part = p.off_logit = off;
+    p.off_total = off;
+    return p;
+  }
+  p.splits = static_cast<int>((p.keys + 63) / 64);
   p.off_part = off;
-  off = align256(off + sh * rows * p.splits * (4 + 2 * static_cast<uint64_t>(d.head_dim)) * 4);
+  off = align256(off + sh * rows * p.splits * (4 + 2 * D) * 4);
   p.off_logit = off;
   off = align256(off + 2 * sh * rows * static_cast<uint64_t>(p.keys) * 4);
   p.off_stat = off;
@@ -31,7 +50,7 @@ AttendPlan plan_attend(const fl_attend_args& a) {
 }
 
 hipError_t launch_attend(const fl_attend_args& a, const KvView& kv, const AttendPlan& p, hipStream_t st) {
-  return launch_rows(a, kv, p, st);
+  return p.mfma ? launch_mfma(a, kv, p, st) : launch_rows(a, kv, p, st);
 }
 
 }  // namespace fl

@@ -94,6 +94,12 @@ __global__ __launch_bounds__(64) void k_rows_partial(KvView kv, RowArgs a) {
     if (live) {
       recon8<DT>(kv, 0, s, row_kv, j, a.version, p, kc, LAZY ? kp : nullptr);
       recon8<DT>(kv, 1, s, row_kv, j, a.version, p, vc, LAZY ? vp : nullptr);
+      to_working8<DT>(kc);
+      to_working8<DT>(vc);
+      if (LAZY) {
+        to_working8<DT>(kp);
+        to_working8<DT>(vp);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         dc = fmaf(qc[e], kc[e], dc);

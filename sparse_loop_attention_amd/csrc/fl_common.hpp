@@ -19,6 +19,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
 }
+// Value of f rounded to the nearest bfloat16 (ties to even), as float32.
+__device__ __forceinline__ float round_bf16(float f) {
+  return __uint_as_float(static_cast<uint32_t>(f32_to_bf16(f)) << 16);
+}
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
   _Float16 v = __builtin_bit_cast(_Float16, h);
   return static_cast<float>(v);
@@ -94,6 +98,17 @@ __device__ __forceinline__ void add_delta8(const KvView& kv, int which, int l, i
   for (int e = 0; e < 8; ++e) {
     const int c = static_cast<int>(static_cast<int32_t>(codes << (28 - 4 * e)) >> 28);  // sign-extend nibble e
     x[e] = x[e] + static_cast<float>(c) * s;
+  }
+}
+
+// Attention consumes the reconstruction in the store's working dtype: a
+// bf16 store's float32 reconstruction is rounded to bf16 (the int4 chain
+// itself stays float32).
+template <int DT>
+__device__ __forceinline__ void to_working8(float x[8]) {
+  if constexpr (DT == FL_BF16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = round_bf16(x[e]);
   }
 }
 

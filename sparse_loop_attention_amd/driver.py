@@ -192,7 +192,7 @@ class DecodeRun:
         slot_base = 0 if l == 1 else self.ctx[l].shape[1]
         abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False)
         if l >= 2:
-            abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
+            abi.select_keys(self.colmass, wl.n_keys, self.keys)
         abi.attend(self._args(l, self.workspace))
 
     def run(self, record: bool = False) -> List[LoopRecord]:

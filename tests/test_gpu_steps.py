@@ -183,7 +183,9 @@ def _setup_attend(rng, n, H, d, dtype, sets, nS=None):
 
 
 @pytest.mark.parametrize("dtype,d,n", [(torch.float32, 64, 256), (torch.bfloat16, 128, 300),
-                                       (torch.bfloat16, 96, 200), (torch.float32, 128, 129)])
+                                       (torch.bfloat16, 96, 200), (torch.float32, 128, 129),
+                                       (torch.bfloat16, 64, 1000), (torch.bfloat16, 128, 1333),
+                                       (torch.bfloat16, 96, 777), (torch.bfloat16, 128, 63)])
 def test_attend_full(dtype, d, n):
     rng = np.random.default_rng(n)
     H = 2
@@ -199,7 +201,9 @@ def test_attend_full(dtype, d, n):
         a = abi.attend_args(kv, abi.FL_ATTEND_FULL, version, to_dev(q[None], dtype), None, None, n, None, o, lse, c, ws)
         abi.attend(a)
         torch.cuda.synchronize()
-        o_r, lse_r, c_r = oracle.full_attention(q, st.reconstruct("k", version), st.reconstruct("v", version),
+        wd = "bf16" if dtype == torch.bfloat16 else "fp32"
+        o_r, lse_r, c_r = oracle.full_attention(q, oracle.to_working_dtype(st.reconstruct("k", version), wd),
+                                                oracle.to_working_dtype(st.reconstruct("v", version), wd),
                                                 np.arange(n))
         for got, want in ((o[0], o_r), (lse[0], lse_r), (c[0], c_r)):
             ok, err, rms = rel_err_ok(got.cpu().numpy(), want)
@@ -207,7 +211,9 @@ def test_attend_full(dtype, d, n):
 
 
 @pytest.mark.parametrize("dtype,d,n,na,ns", [(torch.float32, 64, 256, 64, 26), (torch.bfloat16, 128, 512, 103, 52),
-                                             (torch.bfloat16, 96, 300, 300, 300), (torch.bfloat16, 128, 700, 1, 70)])
+                                             (torch.bfloat16, 96, 300, 300, 300), (torch.bfloat16, 128, 700, 1, 70),
+                                             (torch.bfloat16, 128, 2000, 600, 200), (torch.bfloat16, 64, 1500, 1500, 150),
+                                             (torch.bfloat16, 96, 900, 65, 900), (torch.bfloat16, 128, 3000, 64, 1)])
 def test_attend_lazy(dtype, d, n, na, ns):
     rng = np.random.default_rng(n + na)
     H = 3
@@ -216,7 +222,9 @@ def test_attend_lazy(dtype, d, n, na, ns):
     st, kv, rnd = _setup_attend(rng, n, H, d, dtype, sets)
     q0 = rnd(rng.standard_normal((n, H, d)).astype(np.float32))
     q1 = rnd(q0 + 0.3 * rng.standard_normal((n, H, d)).astype(np.float32))
-    o0, lse0, c0 = oracle.full_attention(q0, st.reconstruct("k", 1), st.reconstruct("v", 1), np.arange(n))
+    wd = "bf16" if dtype == torch.bfloat16 else "fp32"
+    rec = lambda w, l: oracle.to_working_dtype(st.reconstruct(w, l), wd)
+    o0, lse0, c0 = oracle.full_attention(q0, rec("k", 1), rec("v", 1), np.arange(n))
     keys = oracle.select_keys(c0, ns)
     o = torch.from_numpy(o0.astype(np.float32)[None]).to(DEV)
     lse = torch.from_numpy(lse0.astype(np.float32)[None]).to(DEV)
@@ -231,8 +239,7 @@ def test_attend_lazy(dtype, d, n, na, ns):
     abi.attend(a)
     torch.cuda.synchronize()
     o_r, lse_r, c_r, m, upd = oracle.lazy_attention(
-        q1[act], q0[act], st.reconstruct("k", 1), st.reconstruct("v", 1), st.reconstruct("k", 2),
-        st.reconstruct("v", 2), o0[act], lse0[act], c0, act, keys)
+        q1[act], q0[act], rec("k", 1), rec("v", 1), rec("k", 2), rec("v", 2), o0[act], lse0[act], c0, act, keys)
     got_o = o[0].cpu().numpy()
     ok, err, rms = rel_err_ok(got_o[act], o_r)
     assert ok, ("o", err, rms)

@@ -165,3 +165,19 @@ def test_chain_delta_is_against_previous_reconstruction():
     assert np.array_equal(recs["k"].codes, c) and np.array_equal(recs["k"].scales, s)
     err3 = np.abs(st.reconstruct("k", 3) - k3).max()
     assert err3 <= np.abs(k3 - rec2).max() / 7 / 2 * 1.01 + 1e-7
+
+
+def test_working_dtype_rounding_matches_torch_bfloat16():
+    """Reading R9: attention operands are the reconstruction rounded to bf16;
+    pinned to torch's float32 -> bfloat16 conversion (nearest-even)."""
+    import torch
+    from oracle import to_working_dtype
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(200000) * 10.0 ** rng.uniform(-30, 30, 200000)).astype(np.float32)
+    # exact bf16 half-way cases: low 16 bits == 0x8000, both parities of the kept bit
+    mid = (rng.integers(0, 2 ** 31, 2000, dtype=np.uint32) & np.uint32(0x7F7F0000)) | np.uint32(0x8000)
+    x = np.concatenate([x, mid.view(np.float32), np.array([0.0, -0.0, 1.0, -3.5], np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = to_working_dtype(x, "bf16")
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert to_working_dtype(x, "fp32") is not None and np.array_equal(to_working_dtype(x, "fp32"), x)
