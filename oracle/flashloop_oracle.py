@@ -44,10 +44,11 @@ Readings of points the page leaves open (all listed in the design doc):
      bfloat16 (nearest-even) for bf16 workloads, as the version-1 base already
      is; queries are used as given.  The int4 chain itself (R7, R8) stays in
      float32.
-Parity unpinned: the page prints no worked example of the mass-corrected
-formula (R4), so its exact form is pinned only by invariants (full attention
-when all keys are selected, fixed point when nothing changed, mass
-preservation) and by brute force; see tests/test_oracle_attention.py.
+The page prints no worked example of the mass-corrected formula (R4); it is
+pinned by invariants that follow from the mathematics (full attention when
+every key is selected, the dense loop when every row and key is, a fixed point
+when nothing changed, mass preservation, single-key closed forms) and by a
+loop-level evaluation; see tests/test_oracle_attention.py.
 """
 from __future__ import annotations
 
