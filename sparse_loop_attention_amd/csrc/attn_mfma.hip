@@ -37,6 +37,7 @@ namespace fl {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16-byte chunk (promotes to registers)
 
 struct MfmaArgs {
   // rows
@@ -141,19 +142,37 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a) {
 }
 
 // --------------------------------------------------------------------------- fwd
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Tile geometry: K (KT x D, bf16) and V^T (D x KT, fp16) of one role, 16-byte
+// chunks striped over the 256 threads; global loads go to registers first so
+// that they overlap the MFMA work on the other LDS buffer.
+template <int D, int KT, int NT>
+struct TileIO {
+  static constexpr int KCH = KT * D / 8;   // 16-byte chunks of a K tile (KT x D bf16)
+  static constexpr int VCH = D * KT / 8;   // 16-byte chunks of a V^T tile (D x KT fp16)
+  static constexpr int PER = (KCH + VCH) / NT;
+  static constexpr int KS = D + 8;         // padded LDS row strides
+  static constexpr int VS = KT + 8;
+};
+
 template <int D, bool LAZY>
-__global__ __launch_bounds__(256) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
+__global__ __launch_bounds__(LAZY ? 512 : 256, LAZY ? 1 : 2) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
   constexpr int KT = 64;
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
-  constexpr int KS = D + 8;
-  constexpr int VS = KT + 8;
   constexpr int NR = LAZY ? 2 : 1;
-  constexpr int ROWS = LAZY ? 64 : 128;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[NR][KT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[NR][D * VS];
-  __shared__ int skidx[KT];
-  __shared__ float sm[2][32];
+  constexpr int NT = LAZY ? 512 : 256;                    // threads: 4 row blocks (x2 roles in a lazy loop)
+  constexpr int ROWS = 128;
+  using IO = TileIO<D, KT, NT>;
+  constexpr int KS = IO::KS, VS = IO::VS;
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][NR][KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][NR][D * VS];
+  __shared__ int skidx[2][KT];
+  __shared__ float sm[4][32];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -163,11 +182,15 @@ __global__ __launch_bounds__(256) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs
   const int qtile = gridDim.x - 1 - blockIdx.x;          // heavy (late) tiles first
   const int blk = LAZY ? (wave >> 1) : wave;
   const int role = LAZY ? (wave & 1) : 0;                 // 0 = current, 1 = previous loop
-  const int r = qtile * ROWS + blk * 32 + c;
+  const int r0 = qtile * ROWS + blk * 32;                 // first row of this wave's block
+  const int r = r0 + c;
   const bool vrow = r < a.n_rows;
   const int tok = vrow ? row_token(a, s, r) : -1;
+  const bool blk_full = r0 + 31 < a.n_rows;               // all 32 rows of the block exist
+  const int tok_first = row_token(a, s, min(r0, a.n_rows - 1));
+  const int tok_last = row_token(a, s, min(r0 + 31, a.n_rows - 1));
+  const float c1 = a.scale * kLog2e;                      // logits in log2 units
 
-  // queries: Q^T fragments (B operand), one row per lane column
   bf16x8 qf[DC];
   {
     const uint16_t* q = static_cast<const uint16_t*>(role ? a.q_prev : a.q_cur);
@@ -175,37 +198,21 @@ __global__ __launch_bounds__(256) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs
     const int64_t qr = a.q_compact ? r : tok;
     const uint16_t* src = q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + 8 * hh;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      if (vrow) qf[dc] = *reinterpret_cast<const bf16x8*>(src + dc * 16);
-      else qf[dc] = bf16x8{};
-    }
+    for (int dc = 0; dc < DC; ++dc) qf[dc] = vrow ? *reinterpret_cast<const bf16x8*>(src + dc * 16) : bf16x8{};
   }
   const int64_t rows_o = a.o_compact ? a.n_rows : N;
   const int64_t orow = a.o_compact ? r : tok;
   float lse_prev = 0.0f;
   if (LAZY && vrow) lse_prev = a.lse[(static_cast<int64_t>(s) * rows_o + orow) * H + h];
+  const float b_prev = lse_prev * kLog2e;
 
-  // key tiles needed by the last row of this workgroup
-  if (tid == 0) {
-    int rl = min(a.n_rows, (qtile + 1) * ROWS) - 1;
-    const int last_tok = row_token(a, s, rl);
-    const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
+  const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
+  if (tid == 0) {                                        // key slots visible to the workgroup's last row
+    const int last_tok = row_token(a, s, min(a.n_rows, (qtile + 1) * ROWS) - 1);
     int lo = 0, hi = a.n_keys;
     while (lo < hi) { const int mid = (lo + hi) >> 1; if (kx[mid] <= last_tok) lo = mid + 1; else hi = mid; }
-    s_last = lo;                                           // visible key slots of the last row
+    s_last = lo;
   }
-  __syncthreads();
-  const int n_tiles = (s_last + KT - 1) / KT;
-  // first row token of this wave's block (rows ascending)
-  const int blk_first = min(a.n_rows - 1, qtile * ROWS + blk * 32);
-  const int tok_first = row_token(a, s, blk_first);
-
-  f32x16 acc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;                  // current-loop online softmax (lane half)
-  float mass = 0.0f;                                      // previous-loop mass (lane half)
-
   const uint16_t* kbase[NR];
   const uint16_t* vbase[NR];
   kbase[0] = a.kc + static_cast<int64_t>(sh) * a.n_keys_pad * D;
@@ -214,91 +221,123 @@ __global__ __launch_bounds__(256) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs
     kbase[NR - 1] = a.kp + static_cast<int64_t>(sh) * a.n_keys_pad * D;
     vbase[NR - 1] = a.vtp + static_cast<int64_t>(sh) * D * a.n_keys_pad;
   }
+  __syncthreads();
+  const int n_tiles = (s_last + KT - 1) / KT;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;                  // current loop, log2 units, lane half
+  float mass = 0.0f;                                      // previous loop, lane half
+
+  u32x4 pre[NR][IO::PER];
+  int pre_k = INT_MAX;
+#define FL_FWD_GLOAD(TILE)                                                              \
+  {                                                                                     \
+    _Pragma("unroll") for (int w = 0; w < NR; ++w)                                      \
+      _Pragma("unroll") for (int i = 0; i < IO::PER; ++i) {                             \
+        const int q = tid + NT * i;                                                     \
+        if (q < IO::KCH) {                                                              \
+          const int row = q / (D / 8), col = (q % (D / 8)) * 8;                         \
+          pre[w][i] = *reinterpret_cast<const u32x4*>(kbase[w] + static_cast<int64_t>((TILE) * KT + row) * D + col); \
+        } else {                                                                        \
+          const int qv = q - IO::KCH;                                                   \
+          const int row = qv / (KT / 8), col = (qv % (KT / 8)) * 8;                     \
+          pre[w][i] = *reinterpret_cast<const u32x4*>(vbase[w] + static_cast<int64_t>(row) * a.n_keys_pad + (TILE) * KT + col); \
+        }                                                                               \
+      }                                                                                 \
+    if (tid < KT) pre_k = kx[(TILE) * KT + tid];                                        \
+  }
+#define FL_FWD_SSTORE(BUF)                                                              \
+  {                                                                                     \
+    _Pragma("unroll") for (int w = 0; w < NR; ++w)                                      \
+      _Pragma("unroll") for (int i = 0; i < IO::PER; ++i) {                             \
+        const int q = tid + NT * i;                                                     \
+        if (q < IO::KCH) {                                                              \
+          const int row = q / (D / 8), col = (q % (D / 8)) * 8;                         \
+          *reinterpret_cast<u32x4*>(&sk[BUF][w][row * KS + col]) = pre[w][i];           \
+        } else {                                                                        \
+          const int qv = q - IO::KCH;                                                   \
+          const int row = qv / (KT / 8), col = (qv % (KT / 8)) * 8;                     \
+          *reinterpret_cast<u32x4*>(&sv[BUF][w][row * VS + col]) = pre[w][i];           \
+        }                                                                               \
+      }                                                                                 \
+    if (tid < KT) skidx[BUF][tid] = pre_k;                                              \
+  }
+  if (n_tiles > 0) {
+    FL_FWD_GLOAD(0)
+    FL_FWD_SSTORE(0)
+  }
+  __syncthreads();
 
   for (int tile = 0; tile < n_tiles; ++tile) {
-    __syncthreads();
+    const int buf = tile & 1;
+    if (tile + 1 < n_tiles) FL_FWD_GLOAD(tile + 1)
+    const int* kk = skidx[buf];
+    if (kk[0] <= tok_last) {                              // some key of the tile is visible to the block
+      const uint16_t* K = sk[buf][role];
+      const uint16_t* V = sv[buf][role];
+      f32x16 st[2];
 #pragma unroll
-    for (int w = 0; w < NR; ++w) {
-      for (int i = tid; i < KT * D / 8; i += 256) {        // K tile: KT rows of D
-        const int row = i / (D / 8), col = (i % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(&sk[w][row * KS + col]) =
-            *reinterpret_cast<const uint4*>(kbase[w] + static_cast<int64_t>(tile * KT + row) * D + col);
-      }
-      for (int i = tid; i < D * KT / 8; i += 256) {        // V^T tile: D rows of KT
-        const int row = i / (KT / 8), col = (i % (KT / 8)) * 8;
-        *reinterpret_cast<uint4*>(&sv[w][row * VS + col]) =
-            *reinterpret_cast<const uint4*>(vbase[w] + static_cast<int64_t>(row) * a.n_keys_pad + tile * KT + col);
-      }
-    }
-    if (tid < KT) skidx[tid] = a.kidx[static_cast<int64_t>(sh) * a.n_keys_pad + tile * KT + tid];
-    __syncthreads();
-    if (tok_first < 0 || skidx[0] > row_token(a, s, min(a.n_rows - 1, qtile * ROWS + blk * 32 + 31))) {
-      // every key of this tile is past every row of the block: nothing to add
-      continue;
-    }
-    const uint16_t* K = sk[role];
-    const uint16_t* V = sv[role];
-    f32x16 st[2];
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&K[(kb * 32 + c) * KS + dc * 16 + 8 * hh]);
-        st[kb] = mfma32(ka, qf[dc], st[kb]);
-      }
-    }
-    const bool need_mask = !vrow || skidx[KT - 1] > tok_first;
-    float pv[32];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = st[kb][i] * a.scale;
-        if (need_mask) {
-          const int key = skidx[kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)];
-          if (!vrow || key > tok) x = -INFINITY;
+        for (int dc = 0; dc < DC; ++dc) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&K[(kb * 32 + c) * KS + dc * 16 + 8 * hh]);
+          st[kb] = mfma32(ka, qf[dc], st[kb]);
         }
-        pv[kb * 16 + i] = x;
       }
-    if (role == 0) {
-      float tmax = -INFINITY;
+      const bool need_mask = !blk_full || kk[KT - 1] > tok_first;
+      float pv[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) tmax = fmaxf(tmax, pv[i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      float alpha = 1.0f, psum = 0.0f;
-      if (m_new == -INFINITY) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 32; ++i) pv[i] = 0.0f;
-      } else {
-        alpha = __expf(m_run - m_new);
+        for (int i = 0; i < 16; ++i) {
+          float x = st[kb][i] * c1;
+          if (need_mask && kk[kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] > tok) x = -INFINITY;
+          pv[kb * 16 + i] = x;
+        }
+      if (role == 0) {
+        float tmax = pv[0];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) { pv[i] = __expf(pv[i] - m_new); psum += pv[i]; }
+        for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, pv[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;   // fully masked so far: p = 0
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) { pv[i] = ex2(pv[i] - m_use); psum += pv[i]; }
+        if (__ballot(m_new != m_run)) {                   // the running max moved for some row
+          const float alpha = ex2(m_run - m_use);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        }
         m_run = m_new;
+        l_run += psum;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) { pv[i] = ex2(pv[i] - b_prev); mass += pv[i]; }
       }
-      l_run = l_run * alpha + psum;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int cc = 0; cc < 4; ++cc) {
+        f16x8 pb;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-    } else {
+        for (int i = 0; i < 8; ++i) pb[i] = static_cast<_Float16>(pv[cc * 8 + i]);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) { pv[i] = __expf(pv[i] - lse_prev); mass += pv[i]; }
-    }
-    // O^T += V^T P^T over four 16-key chunks
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      f16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = static_cast<_Float16>(pv[cc * 8 + i]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f16x8 va = *reinterpret_cast<const f16x8*>(&V[(db * 32 + c) * VS + cc * 16 + 8 * hh]);
-        acc[db] = mfma32h(va, pb, acc[db]);
+        for (int db = 0; db < DB; ++db) {
+          const f16x8 va = *reinterpret_cast<const f16x8*>(&V[(db * 32 + c) * VS + cc * 16 + 8 * hh]);
+          acc[db] = mfma32h(va, pb, acc[db]);
+        }
       }
     }
+    if (tile + 1 < n_tiles) FL_FWD_SSTORE(buf ^ 1)
+    __syncthreads();
   }
+#undef FL_FWD_GLOAD
+#undef FL_FWD_SSTORE
 
   // ---- epilogue
   float* lse_ptr = a.lse + (static_cast<int64_t>(s) * rows_o + orow) * H + h;
@@ -318,16 +357,15 @@ __global__ __launch_bounds__(256) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs
                           acc[db][4 * q4 + 3] * inv);
         }
       if (hh == 0) {
-        const float l = m_run + __logf(l_tot);
-        *lse_ptr = l;
-        *reinterpret_cast<float4*>(st_ptr) = make_float4(l, l, 1.0f, __int_as_float(tok));
+        const float b = m_run + __log2f(l_tot);           // lse in log2 units
+        *lse_ptr = b * kLn2;
+        *reinterpret_cast<float4*>(st_ptr) = make_float4(b, b, 1.0f, __int_as_float(tok));
       }
     }
     return;
   }
   // lazy: the previous-loop wave hands its mass and contribution to its partner
-  __syncthreads();
-  float* sa = reinterpret_cast<float*>(&sk[0][0]);        // [blk][DB][16][64] floats
+  float* sa = reinterpret_cast<float*>(&sk[0][0][0]);     // [blk][DB][16][64] floats
   if (role == 1) {
     const float m_tot = mass + __shfl_xor(mass, 32, 64);
     if (hh == 0) sm[blk][c] = m_tot;
@@ -358,22 +396,29 @@ __global__ __launch_bounds__(256) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs
         }
     }
     if (hh == 0) {
-      const float lnew = valid ? m_run + __logf(z) - __logf(m) : lse_prev;
-      if (valid) *lse_ptr = lnew;
-      *reinterpret_cast<float4*>(st_ptr) = make_float4(lse_prev, lnew, valid ? 1.0f : 0.0f, __int_as_float(tok));
+      // new lse in log2 units: M + log2 Z - log2 m
+      const float b = valid ? m_run + __log2f(z) - __log2f(m) : b_prev;
+      if (valid) *lse_ptr = b * kLn2;
+      *reinterpret_cast<float4*>(st_ptr) =
+          make_float4(valid ? b_prev : INFINITY, valid ? b : INFINITY, valid ? 1.0f : 0.0f, __int_as_float(tok));
     }
   }
 }
 
 // --------------------------------------------------------------------------- colmass
+// stat rows hold (b_prev, b_cur, valid, token) with b = lse * log2(e); rows
+// that did not update carry b = +inf so that their probabilities vanish.
 template <int D, bool LAZY>
-__global__ __launch_bounds__(256) void k_mfma_colmass(int32_t H, int32_t N, MfmaArgs a) {
+__global__ __launch_bounds__(256, 2) void k_mfma_colmass(int32_t H, int32_t N, MfmaArgs a) {
   constexpr int QT = 64;
   constexpr int DC = D / 16;
   constexpr int QS = D + 8;
   constexpr int NR = LAZY ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t sq[NR][QT * QS];
-  __shared__ float4 sst[QT];
+  constexpr int QCH = QT * D / 8;                          // 16-B chunks of one Q tile
+  constexpr int PER = QCH / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][NR][QT * QS];
+  __shared__ __attribute__((aligned(16))) float sb[2][2][QT];   // [buf][prev|cur][row]
+  __shared__ int stok[2][QT];
   __shared__ int s_start;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -384,6 +429,8 @@ __global__ __launch_bounds__(256) void k_mfma_colmass(int32_t H, int32_t N, Mfma
   const int t = t0 + c;
   const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
   const int kj = kx[t];                                    // INT_MAX for padding
+  const int kmax = kx[min(t0 + 31, a.n_keys - 1)];         // largest real key of this wave
+  const float c1 = a.scale * kLog2e;
 
   bf16x8 kf[NR][DC];
 #pragma unroll
@@ -400,52 +447,93 @@ __global__ __launch_bounds__(256) void k_mfma_colmass(int32_t H, int32_t N, Mfma
   }
   __syncthreads();
   const int r_begin = (s_start / QT) * QT;
-  float acc = 0.0f;
+  const int n_tiles = (a.n_rows - r_begin + QT - 1) / QT;
   const int64_t rows_q = a.q_compact ? a.n_rows : N;
-  for (int q0 = r_begin; q0 < a.n_rows; q0 += QT) {
-    __syncthreads();
+
+  u32x4 pre[NR][PER];
+  float pre_b0 = INFINITY, pre_b1 = INFINITY;
+  int pre_tok = -1;
+  auto gload = [&](int q0) {
 #pragma unroll
     for (int w = 0; w < NR; ++w) {
       const uint16_t* q = static_cast<const uint16_t*>(w ? a.q_prev : a.q_cur);
-      for (int i = tid; i < QT * D / 8; i += 256) {
-        const int row = i / (D / 8), col = (i % (D / 8)) * 8;
-        const int r = q0 + row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < a.n_rows) {
-          const int64_t qr = a.q_compact ? r : row_token(a, s, r);
-          v = *reinterpret_cast<const uint4*>(q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + col);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int ch = tid + 256 * i;
+        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+        const int rr = q0 + row;
+        pre[w][i] = u32x4{0, 0, 0, 0};
+        if (rr < a.n_rows) {
+          const int64_t qr = a.q_compact ? rr : row_token(a, s, rr);
+          pre[w][i] = *reinterpret_cast<const u32x4*>(q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + col);
         }
-        *reinterpret_cast<uint4*>(&sq[w][row * QS + col]) = v;
       }
     }
     if (tid < QT) {
-      const int r = q0 + tid;
-      sst[tid] = r < a.n_rows ? *reinterpret_cast<const float4*>(a.stat + (static_cast<int64_t>(sh) * a.n_rows + r) * 4)
-                              : make_float4(0.f, 0.f, 0.f, __int_as_float(-1));
+      const int rr = q0 + tid;
+      pre_b0 = pre_b1 = INFINITY;
+      pre_tok = -1;
+      if (rr < a.n_rows) {
+        const float4 st = *reinterpret_cast<const float4*>(a.stat + (static_cast<int64_t>(sh) * a.n_rows + rr) * 4);
+        pre_b0 = st.x; pre_b1 = st.y; pre_tok = __float_as_int(st.w);
+      }
     }
-    __syncthreads();
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int w = 0; w < NR; ++w)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int ch = tid + 256 * i;
+        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(&sq[buf][w][row * QS + col]) = pre[w][i];
+      }
+    if (tid < QT) { sb[buf][0][tid] = pre_b0; sb[buf][1][tid] = pre_b1; stok[buf][tid] = pre_tok; }
+  };
+  if (n_tiles > 0) {
+    gload(r_begin);
+    sstore(0);
+  }
+  __syncthreads();
+  float acc = 0.0f;
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    const int q0 = r_begin + it * QT;
+    if (it + 1 < n_tiles) gload(q0 + QT);
+    // rows of this tile that every key of the wave precedes need no mask
+    const bool need_mask = stok[buf][0] < kmax || q0 + QT > a.n_rows;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 sc = f32x16{}, sp = f32x16{};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[0][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[buf][0][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
         sc = mfma32(qa, kf[0][dc], sc);
         if (LAZY) {
-          const bf16x8 qpa = *reinterpret_cast<const bf16x8*>(&sq[NR - 1][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
+          const bf16x8 qpa = *reinterpret_cast<const bf16x8*>(&sq[buf][NR - 1][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
           sp = mfma32(qpa, kf[NR - 1][dc], sp);
         }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float4 st = sst[qb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)];
-        if (st.z != 0.0f && kj <= __float_as_int(st.w)) {
-          float v = __expf(sc[i] * a.scale - st.y);
-          if (LAZY) v -= __expf(sp[i] * a.scale - st.x);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int row0 = qb * 32 + 8 * q4 + 4 * hh;
+        const float4 bc = *reinterpret_cast<const float4*>(&sb[buf][1][row0]);
+        float4 bp = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (LAZY) bp = *reinterpret_cast<const float4*>(&sb[buf][0][row0]);
+        const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+        const float bpv[4] = {bp.x, bp.y, bp.z, bp.w};
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int i = 4 * q4 + k4;
+          float v = ex2(sc[i] * c1 - bcv[k4]);
+          if (LAZY) v -= ex2(sp[i] * c1 - bpv[k4]);
+          if (need_mask && kj > stok[buf][row0 + k4]) v = 0.0f;
           acc += v;
         }
       }
     }
+    if (it + 1 < n_tiles) sstore(buf ^ 1);
+    __syncthreads();
   }
   acc += __shfl_xor(acc, 32, 64);
   if (hh == 0 && t < a.n_keys) {
@@ -492,11 +580,10 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows_per = lazy ? 64 : 128;
-  dim3 gf((a.n_rows + rows_per - 1) / rows_per, static_cast<unsigned>(sh));
+  dim3 gf((a.n_rows + 127) / 128, static_cast<unsigned>(sh));
   {
     TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
-    if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, true>), gf, dim3(256), 0, st, kv.H, kv.N, a);
+    if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, true>), gf, dim3(512), 0, st, kv.H, kv.N, a);
     else hipLaunchKernelGGL((k_mfma_fwd<D, false>), gf, dim3(256), 0, st, kv.H, kv.N, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
