@@ -62,6 +62,7 @@ struct MfmaArgs {
   uint16_t* vtp;
   int32_t* kidx;            // [sh][n_keys_pad], INT_MAX for padding
   float* stat;              // [sh][n_rows][4] = lse_prev, lse_new, valid, token
+  int32_t n_sh;             // n_seq * H
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -76,6 +77,27 @@ __device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
 __device__ __forceinline__ uint16_t v_operand_bits(float v) {
   const float b = fminf(fmaxf(round_bf16(v), -65504.0f), 65504.0f);
   return f32_to_half_bits(b);
+}
+
+// Workgroup -> (head row sh, tile) map.  Workgroups are handed to the 8 XCDs
+// round-robin by linear id, and each XCD has its own L2; with at least 8
+// (sequence, head) rows, every XCD gets whole heads (sh = xcd + 8k), so the
+// gathered K/V tiles a head's query tiles share stay in one L2.  Tiles of a
+// head run heavy (late, causal) first.  Returns false for padding workgroups.
+__device__ __forceinline__ bool map_block(int n_sh, int n_tiles, int& sh, int& tile) {
+  const int b = blockIdx.x;
+  if (n_sh >= 8) {
+    const int xcd = b & 7, local = b >> 3;
+    sh = xcd + 8 * (local / n_tiles);
+    tile = n_tiles - 1 - local % n_tiles;
+    return sh < n_sh;
+  }
+  sh = b / n_tiles;
+  tile = n_tiles - 1 - b % n_tiles;
+  return sh < n_sh;
+}
+__host__ __device__ inline int mapped_grid(int n_sh, int n_tiles) {
+  return n_sh >= 8 ? 8 * ((n_sh + 7) / 8) * n_tiles : n_sh * n_tiles;
 }
 
 __device__ __forceinline__ int row_token(const MfmaArgs& a, int s, int r) {
@@ -177,9 +199,9 @@ __global__ __launch_bounds__(LAZY ? 512 : 256, LAZY ? 1 : 2) void k_mfma_fwd(int
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
-  const int sh = blockIdx.y;
+  int sh, qtile;
+  if (!map_block(a.n_sh, (a.n_rows + ROWS - 1) / ROWS, sh, qtile)) return;
   const int s = sh / H, h = sh % H;
-  const int qtile = gridDim.x - 1 - blockIdx.x;          // heavy (late) tiles first
   const int blk = LAZY ? (wave >> 1) : wave;
   const int role = LAZY ? (wave & 1) : 0;                 // 0 = current, 1 = previous loop
   const int r0 = qtile * ROWS + blk * 32;                 // first row of this wave's block
@@ -423,9 +445,11 @@ __global__ __launch_bounds__(256, 2) void k_mfma_colmass(int32_t H, int32_t N, M
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
-  const int sh = blockIdx.y;
+  int sh, kblk;
+  if (!map_block(a.n_sh, a.n_keys_pad / 128, sh, kblk)) return;
+  kblk = a.n_keys_pad / 128 - 1 - kblk;                   // early keys see the most rows: start them first
   const int s = sh / H, h = sh % H;
-  const int t0 = blockIdx.x * 128 + wave * 32;
+  const int t0 = kblk * 128 + wave * 32;
   const int t = t0 + c;
   const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
   const int kj = kx[t];                                    // INT_MAX for padding
@@ -440,7 +464,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_colmass(int32_t H, int32_t N, M
     for (int dc = 0; dc < DC; ++dc) kf[w][dc] = *reinterpret_cast<const bf16x8*>(kb + dc * 16);
   }
   if (tid == 0) {                                          // first row that sees the block's first key
-    const int kfirst = kx[blockIdx.x * 128];
+    const int kfirst = kx[kblk * 128];
     int lo = 0, hi = a.n_rows;
     while (lo < hi) { const int mid = (lo + hi) >> 1; if (row_token(a, s, mid) < kfirst) lo = mid + 1; else hi = mid; }
     s_start = lo;
@@ -580,14 +604,15 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 gf((a.n_rows + 127) / 128, static_cast<unsigned>(sh));
+  a.n_sh = static_cast<int32_t>(sh);
+  dim3 gf(mapped_grid(a.n_sh, (a.n_rows + 127) / 128));
   {
     TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
     if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, true>), gf, dim3(512), 0, st, kv.H, kv.N, a);
     else hipLaunchKernelGGL((k_mfma_fwd<D, false>), gf, dim3(256), 0, st, kv.H, kv.N, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dim3 gc(a.n_keys_pad / 128, static_cast<unsigned>(sh));
+  dim3 gc(mapped_grid(a.n_sh, a.n_keys_pad / 128));
   {
     TimedLaunch t(st, lazy ? "mfma_colmass_lazy" : "mfma_colmass_full");
     if (lazy) hipLaunchKernelGGL((k_mfma_colmass<D, true>), gc, dim3(256), 0, st, kv.H, kv.N, a);
