@@ -52,7 +52,7 @@ struct MfmaArgs {
   // keys
   const int32_t* key_idx;   // LAZY: [sh][n_keys]; FULL: null (all N keys)
   int32_t n_keys;           // key slots per head
-  int32_t n_keys_pad;       // multiple of 64
+  int32_t n_keys_pad;       // multiple of 256
   int32_t version;
   float scale;
   // workspace
@@ -182,13 +182,13 @@ struct TileIO {
 };
 
 template <int D, bool LAZY>
-__global__ __launch_bounds__(LAZY ? 512 : 256, LAZY ? 1 : 2) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
+__global__ __launch_bounds__(512, 1) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
   constexpr int KT = 64;
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
   constexpr int NR = LAZY ? 2 : 1;
-  constexpr int NT = LAZY ? 512 : 256;                    // threads: 4 row blocks (x2 roles in a lazy loop)
-  constexpr int ROWS = 128;
+  constexpr int NT = 512;                                 // 8 waves: 8 row blocks, or 4 x (current, previous)
+  constexpr int ROWS = LAZY ? 128 : 256;
   using IO = TileIO<D, KT, NT>;
   constexpr int KS = IO::KS, VS = IO::VS;
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][NR][KT * KS];
@@ -310,12 +310,12 @@ __global__ __launch_bounds__(LAZY ? 512 : 256, LAZY ? 1 : 2) void k_mfma_fwd(int
         }
       }
       const bool need_mask = !blk_full || kk[KT - 1] > tok_first;
-      float pv[32];
+      float pv[32];                                       // raw logits q.k
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float x = st[kb][i] * c1;
+          float x = st[kb][i];
           if (need_mask && kk[kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] > tok) x = -INFINITY;
           pv[kb * 16 + i] = x;
         }
@@ -324,11 +324,11 @@ __global__ __launch_bounds__(LAZY ? 512 : 256, LAZY ? 1 : 2) void k_mfma_fwd(int
 #pragma unroll
         for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, pv[i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
+        const float m_new = fmaxf(m_run, tmax * c1);      // running max in log2 units (c1 > 0)
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;   // fully masked so far: p = 0
         float psum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) { pv[i] = ex2(pv[i] - m_use); psum += pv[i]; }
+        for (int i = 0; i < 32; ++i) { pv[i] = ex2(fmaf(pv[i], c1, -m_use)); psum += pv[i]; }
         if (__ballot(m_new != m_run)) {                   // the running max moved for some row
           const float alpha = ex2(m_run - m_use);
           l_run *= alpha;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(LAZY ? 512 : 256, LAZY ? 1 : 2) void k_mfma_fwd(int
         l_run += psum;
       } else {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) { pv[i] = ex2(pv[i] - b_prev); mass += pv[i]; }
+        for (int i = 0; i < 32; ++i) { pv[i] = ex2(fmaf(pv[i], c1, -b_prev)); mass += pv[i]; }
       }
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
@@ -431,13 +431,15 @@ __global__ __launch_bounds__(LAZY ? 512 : 256, LAZY ? 1 : 2) void k_mfma_fwd(int
 // stat rows hold (b_prev, b_cur, valid, token) with b = lse * log2(e); rows
 // that did not update carry b = +inf so that their probabilities vanish.
 template <int D, bool LAZY>
-__global__ __launch_bounds__(256, 2) void k_mfma_colmass(int32_t H, int32_t N, MfmaArgs a) {
+__global__ __launch_bounds__(512, 1) void k_mfma_colmass(int32_t H, int32_t N, MfmaArgs a) {
   constexpr int QT = 64;
   constexpr int DC = D / 16;
   constexpr int QS = D + 8;
   constexpr int NR = LAZY ? 2 : 1;
+  constexpr int NT = 512;                                  // 8 waves x 32 keys
+  constexpr int KB = 256;                                  // key slots per workgroup
   constexpr int QCH = QT * D / 8;                          // 16-B chunks of one Q tile
-  constexpr int PER = QCH / 256;
+  constexpr int PER = (QCH + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) uint16_t sq[2][NR][QT * QS];
   __shared__ __attribute__((aligned(16))) float sb[2][2][QT];   // [buf][prev|cur][row]
   __shared__ int stok[2][QT];
@@ -446,10 +448,10 @@ __global__ __launch_bounds__(256, 2) void k_mfma_colmass(int32_t H, int32_t N, M
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
   int sh, kblk;
-  if (!map_block(a.n_sh, a.n_keys_pad / 128, sh, kblk)) return;
-  kblk = a.n_keys_pad / 128 - 1 - kblk;                   // early keys see the most rows: start them first
+  if (!map_block(a.n_sh, a.n_keys_pad / KB, sh, kblk)) return;
+  kblk = a.n_keys_pad / KB - 1 - kblk;                    // early keys see the most rows: start them first
   const int s = sh / H, h = sh % H;
-  const int t0 = kblk * 128 + wave * 32;
+  const int t0 = kblk * KB + wave * 32;
   const int t = t0 + c;
   const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
   const int kj = kx[t];                                    // INT_MAX for padding
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_colmass(int32_t H, int32_t N, M
     for (int dc = 0; dc < DC; ++dc) kf[w][dc] = *reinterpret_cast<const bf16x8*>(kb + dc * 16);
   }
   if (tid == 0) {                                          // first row that sees the block's first key
-    const int kfirst = kx[kblk * 128];
+    const int kfirst = kx[kblk * KB];
     int lo = 0, hi = a.n_rows;
     while (lo < hi) { const int mid = (lo + hi) >> 1; if (row_token(a, s, mid) < kfirst) lo = mid + 1; else hi = mid; }
     s_start = lo;
@@ -483,11 +485,11 @@ __global__ __launch_bounds__(256, 2) void k_mfma_colmass(int32_t H, int32_t N, M
       const uint16_t* q = static_cast<const uint16_t*>(w ? a.q_prev : a.q_cur);
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int ch = tid + 256 * i;
+        const int ch = tid + NT * i;
         const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
         const int rr = q0 + row;
         pre[w][i] = u32x4{0, 0, 0, 0};
-        if (rr < a.n_rows) {
+        if (ch < QCH && rr < a.n_rows) {
           const int64_t qr = a.q_compact ? rr : row_token(a, s, rr);
           pre[w][i] = *reinterpret_cast<const u32x4*>(q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + col);
         }
@@ -508,9 +510,9 @@ __global__ __launch_bounds__(256, 2) void k_mfma_colmass(int32_t H, int32_t N, M
     for (int w = 0; w < NR; ++w)
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int ch = tid + 256 * i;
+        const int ch = tid + NT * i;
         const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        *reinterpret_cast<u32x4*>(&sq[buf][w][row * QS + col]) = pre[w][i];
+        if (ch < QCH) *reinterpret_cast<u32x4*>(&sq[buf][w][row * QS + col]) = pre[w][i];
       }
     if (tid < QT) { sb[buf][0][tid] = pre_b0; sb[buf][1][tid] = pre_b1; stok[buf][tid] = pre_tok; }
   };
@@ -578,7 +580,7 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   a.o = x.o; a.lse = x.lse; a.colmass = x.colmass;
   a.key_idx = lazy ? x.key_idx : nullptr;
   a.n_keys = static_cast<int32_t>(p.keys);
-  a.n_keys_pad = static_cast<int32_t>((p.keys + 127) / 128 * 128);
+  a.n_keys_pad = static_cast<int32_t>((p.keys + 255) / 256 * 256);
   a.version = x.version;
   a.scale = 1.0f / sqrtf(static_cast<float>(D));
   uint8_t* ws = static_cast<uint8_t*>(x.workspace);
@@ -605,18 +607,19 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.n_sh = static_cast<int32_t>(sh);
-  dim3 gf(mapped_grid(a.n_sh, (a.n_rows + 127) / 128));
+  const int rows_per = lazy ? 128 : 256;
+  dim3 gf(mapped_grid(a.n_sh, (a.n_rows + rows_per - 1) / rows_per));
   {
     TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
     if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, true>), gf, dim3(512), 0, st, kv.H, kv.N, a);
-    else hipLaunchKernelGGL((k_mfma_fwd<D, false>), gf, dim3(256), 0, st, kv.H, kv.N, a);
+    else hipLaunchKernelGGL((k_mfma_fwd<D, false>), gf, dim3(512), 0, st, kv.H, kv.N, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dim3 gc(mapped_grid(a.n_sh, a.n_keys_pad / 128));
+  dim3 gc(mapped_grid(a.n_sh, a.n_keys_pad / 256));
   {
     TimedLaunch t(st, lazy ? "mfma_colmass_lazy" : "mfma_colmass_full");
-    if (lazy) hipLaunchKernelGGL((k_mfma_colmass<D, true>), gc, dim3(256), 0, st, kv.H, kv.N, a);
-    else hipLaunchKernelGGL((k_mfma_colmass<D, false>), gc, dim3(256), 0, st, kv.H, kv.N, a);
+    if (lazy) hipLaunchKernelGGL((k_mfma_colmass<D, true>), gc, dim3(512), 0, st, kv.H, kv.N, a);
+    else hipLaunchKernelGGL((k_mfma_colmass<D, false>), gc, dim3(512), 0, st, kv.H, kv.N, a);
   }
   return hipGetLastError();
 }

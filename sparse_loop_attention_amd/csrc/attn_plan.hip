@@ -27,7 +27,7 @@ AttendPlan plan_attend(const fl_attend_args& a) {
   const uint64_t rows = static_cast<uint64_t>(p.rows);
   uint64_t off = 0;
   if (p.mfma) {
-    const uint64_t kpad = (static_cast<uint64_t>(p.keys) + 127) / 128 * 128;
+    const uint64_t kpad = (static_cast<uint64_t>(p.keys) + 255) / 256 * 256;
     p.splits = 0;
     p.off_stat = off;
     off = align256(off + sh * rows * 16);
