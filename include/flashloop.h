@@ -76,17 +76,25 @@ typedef struct {
 } fl_kv_desc;
 
 /* Byte offsets inside the arena (every array 256-byte aligned):
- *   base_k, base_v        [n_seq][H][N][d]          base_dtype
- *   slot_map[l]           [n_seq][N]                int32: record slot of token j in layer l, or -1
- *   codes_k[l], codes_v[l][n_seq][H][cap_l][d/2]    uint8: two int4 codes per byte, low nibble = even element
- *   scales_k[l],scales_v[l][n_seq][H][cap_l][d/32]  binary16 bits: one scale per group of 32
- * The reconstruction of token j at version v is
- *   float(base[j]) + sum_{l=2..v, slot_map[l][j] >= 0} code * float(scale), added in float32 in increasing l. */
+ *   base_k, base_v  [n_seq][H][N][d]               base_dtype
+ *   slot_table      [n_seq][N][slot_pitch]         int32: entry l-2 = record slot of token j in
+ *                                                  layer l, or -1 (slot_pitch = n_versions - 1
+ *                                                  rounded up to 4; no table when n_versions = 1)
+ *   codes[l]        [n_seq][cap_l][H][2][d/2]      uint8: K then V codes of one head row, two int4
+ *                                                  codes per byte, low nibble = even element
+ *   scales[l]       [n_seq][cap_l][H][2][d/32]     binary16 bits: one scale per group of 32
+ * A token's slots of every layer sit together (one 16-byte read resolves up
+ * to four layers), and records are token-major: the K and V codes of one
+ * (token, head) fill one d-byte run (a 128-byte line at d = 128) and the
+ * scales of all heads of a token are adjacent, so a sparse set of keys reads
+ * whole lines.  The reconstruction of token j at version v is
+ *   float(base[j]) + sum_{l=2..v, slot(l, j) >= 0} code * float(scale), added in float32 in increasing l. */
 typedef struct {
   uint64_t base_k, base_v;
-  uint64_t slot_map[FL_MAX_VERSIONS + 1];
-  uint64_t codes_k[FL_MAX_VERSIONS + 1], codes_v[FL_MAX_VERSIONS + 1];
-  uint64_t scales_k[FL_MAX_VERSIONS + 1], scales_v[FL_MAX_VERSIONS + 1];
+  uint64_t slot_table;
+  uint64_t slot_pitch;
+  uint64_t codes[FL_MAX_VERSIONS + 1];
+  uint64_t scales[FL_MAX_VERSIONS + 1];
   uint64_t total_bytes;
 } fl_kv_layout;
 
@@ -104,8 +112,8 @@ uint64_t flashloop_kv_arena_bytes(const fl_kv_desc* desc);
 /* token j, head h and X in {K, V}: delta = X_new - X^(l-1) in float32, per   */
 /* group of 32: s = f16_rne(min(absmax/7, 65504)), code = clamp(rint(delta/s),*/
 /* -7, 7) (0 when s == 0); records go to slots slot_base + r (r = position in */
-/* active_idx) and slot_map[l][j] is set to that slot.  With reset_map != 0   */
-/* every other slot_map[l] entry of the sequence is set to -1; with 0 they    */
+/* active_idx) and slot(l, j) is set to that slot.  With reset_map != 0     */
+/* every other token's slot(l, .) of the sequence is set to -1; with 0 they   */
 /* are left as they are (to add rows to a layer written by an earlier call).  */
 /* Inactive tokens get no entry.                                              */
 /* ------------------------------------------------------------------------ */

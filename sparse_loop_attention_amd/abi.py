@@ -35,9 +35,8 @@ class fl_kv_desc(C.Structure):
 
 class fl_kv_layout(C.Structure):
     _fields_ = [("base_k", C.c_uint64), ("base_v", C.c_uint64),
-                ("slot_map", C.c_uint64 * (MAX_VERSIONS + 1)),
-                ("codes_k", C.c_uint64 * (MAX_VERSIONS + 1)), ("codes_v", C.c_uint64 * (MAX_VERSIONS + 1)),
-                ("scales_k", C.c_uint64 * (MAX_VERSIONS + 1)), ("scales_v", C.c_uint64 * (MAX_VERSIONS + 1)),
+                ("slot_table", C.c_uint64), ("slot_pitch", C.c_uint64),
+                ("codes", C.c_uint64 * (MAX_VERSIONS + 1)), ("scales", C.c_uint64 * (MAX_VERSIONS + 1)),
                 ("total_bytes", C.c_uint64)]
 
 
@@ -152,15 +151,16 @@ class KVStore:
             t = self.arena[off:off + n * es].view(self.dtype)
             return t.view(S, H, N, D)
         cap = d.layer_cap[layer]
-        if name == "slot_map":
-            off = lay.slot_map[layer]
-            return self.arena[off:off + S * N * 4].view(torch.int32).view(S, N)
-        if name in ("codes_k", "codes_v"):
-            off = getattr(lay, name)[layer]
-            return self.arena[off:off + S * H * cap * D // 2].view(S, H, cap, D // 2)
-        if name in ("scales_k", "scales_v"):
-            off = getattr(lay, name)[layer]
-            return self.arena[off:off + S * H * cap * (D // 32) * 2].view(torch.int16).view(S, H, cap, D // 32)
+        if name == "slot_map":                    # [S, N]: slot of each token in `layer`
+            off, sp = lay.slot_table, lay.slot_pitch
+            return self.arena[off:off + S * N * sp * 4].view(torch.int32).view(S, N, sp)[:, :, layer - 2]
+        if name == "codes":                       # [S, cap, H, 2 (K, V), d/2]
+            off = lay.codes[layer]
+            return self.arena[off:off + S * cap * H * D].view(S, cap, H, 2, D // 2)
+        if name == "scales":                      # [S, cap, H, 2 (K, V), d/32] binary16 bits
+            off = lay.scales[layer]
+            n = S * cap * H * 2 * (D // 32)
+            return self.arena[off:off + 2 * n].view(torch.int16).view(S, cap, H, 2, D // 32)
         raise KeyError(name)
 
 

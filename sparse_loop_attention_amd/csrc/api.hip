@@ -59,13 +59,12 @@ void layout_of(const fl_kv_desc* d, fl_kv_layout* o) {
   uint64_t off = 0;
   o->base_k = off; off = align256(off + S * H * N * D * es);
   o->base_v = off; off = align256(off + S * H * N * D * es);
+  o->slot_pitch = d->n_versions > 1 ? (static_cast<uint64_t>(d->n_versions - 1) + 3) / 4 * 4 : 0;
+  o->slot_table = off; off = align256(off + S * N * o->slot_pitch * 4);
   for (int l = 2; l <= d->n_versions; ++l) {
     const uint64_t cap = d->layer_cap[l];
-    o->slot_map[l] = off; off = align256(off + S * N * 4);
-    o->codes_k[l] = off; off = align256(off + S * H * cap * (D / 2));
-    o->codes_v[l] = off; off = align256(off + S * H * cap * (D / 2));
-    o->scales_k[l] = off; off = align256(off + S * H * cap * (D / 32) * 2);
-    o->scales_v[l] = off; off = align256(off + S * H * cap * (D / 32) * 2);
+    o->codes[l] = off; off = align256(off + S * cap * H * 2 * (D / 2));
+    o->scales[l] = off; off = align256(off + S * cap * H * 2 * (D / 32) * 2);
   }
   o->total_bytes = off;
 }
@@ -91,11 +90,12 @@ KvView make_view(const fl_kv_desc& d, const fl_kv_layout& lay) {
   v.n_seq = d.n_seq; v.H = d.n_heads; v.d = d.head_dim; v.N = d.n_tokens; v.T = d.n_versions;
   v.dtype = d.base_dtype;
   v.base[0] = lay.base_k; v.base[1] = lay.base_v;
+  v.slot_table = lay.slot_table;
+  v.slot_pitch = static_cast<int32_t>(lay.slot_pitch);
   for (int l = 2; l <= d.n_versions; ++l) {
     v.cap[l] = d.layer_cap[l];
-    v.slot_map[l] = lay.slot_map[l];
-    v.codes[0][l] = lay.codes_k[l]; v.codes[1][l] = lay.codes_v[l];
-    v.scales[0][l] = lay.scales_k[l]; v.scales[1][l] = lay.scales_v[l];
+    v.codes[l] = lay.codes[l];
+    v.scales[l] = lay.scales[l];
   }
   return v;
 }

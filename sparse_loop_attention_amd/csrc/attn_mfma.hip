@@ -120,7 +120,6 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a) {
   const int s = sh / kv.H, h = sh % kv.H;
   const int g = threadIdx.x >> 4, p = threadIdx.x & 15;
   const bool live = 8 * p < D;
-  const int64_t row_kv = static_cast<int64_t>(s) * kv.H + h;
 #pragma unroll 1
   for (int kk = 0; kk < 4; ++kk) {
     const int local = g * 4 + kk;
@@ -130,11 +129,11 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a) {
     float x[8] = {}, xp[8] = {};
     const int64_t krow = (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * p;
     if (live) {
-      if (j >= 0) recon8<DT>(kv, 0, s, row_kv, j, a.version, p, x, LAZY ? xp : nullptr);
+      if (j >= 0) recon8<DT>(kv, 0, s, h, j, a.version, p, x, LAZY ? xp : nullptr);
       store8<FL_BF16>(a.kc, krow, x);
       if (LAZY) store8<FL_BF16>(a.kp, krow, xp);
       float y[8] = {}, yp[8] = {};
-      if (j >= 0) recon8<DT>(kv, 1, s, row_kv, j, a.version, p, y, LAZY ? yp : nullptr);
+      if (j >= 0) recon8<DT>(kv, 1, s, h, j, a.version, p, y, LAZY ? yp : nullptr);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         sv[0][local][8 * p + e] = v_operand_bits(y[e]);

@@ -37,7 +37,7 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     p.off_total = off;
     return p;
   }
-  p.splits = static_cast<int>((p.keys + 63) / 64);
+  p.splits = static_cast<int>((p.keys + 63) / 64);      // keys per split (one wave) in the per-row path
   p.off_part = off;
   off = align256(off + sh * rows * p.splits * (4 + 2 * D) * 4);
   p.off_logit = off;

@@ -21,7 +21,7 @@
 
 namespace fl {
 
-constexpr int kKeysPerSplit = 64;
+constexpr int kKeysPerSplit = 64;     // one wave per split
 
 struct RowArgs {
   const void* q_cur;
@@ -54,6 +54,7 @@ __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int v) {
 
 template <int DT, bool LAZY>
 __global__ __launch_bounds__(64) void k_rows_partial(KvView kv, RowArgs a) {
+  constexpr int kU = LAZY ? 2 : 4;                        // keys per 16-lane group and step
   const int split = blockIdx.x, r = blockIdx.y, sh = blockIdx.z;
   const int H = kv.H, d = kv.d;
   const int s = sh / H, h = sh % H;
@@ -85,44 +86,92 @@ __global__ __launch_bounds__(64) void k_rows_partial(KvView kv, RowArgs a) {
   float acc[8] = {}, accp[8] = {};
   float* lg_cur = a.logit + srow * a.key_slots;
   float* lg_prev = a.logit + (static_cast<int64_t>(kv.n_seq) * H * rows_total + srow) * a.key_slots;
-  const int64_t row_kv = static_cast<int64_t>(s) * H + h;
 
-  for (int t = t_begin + g; t < t_end; t += 4) {
-    const int j = LAZY ? sel[t] : t;
-    float kc[8] = {}, kp[8] = {}, vc[8] = {}, vp[8] = {};
-    float dc = 0.0f, dp = 0.0f;
-    if (live) {
-      recon8<DT>(kv, 0, s, row_kv, j, a.version, p, kc, LAZY ? kp : nullptr);
-      recon8<DT>(kv, 1, s, row_kv, j, a.version, p, vc, LAZY ? vp : nullptr);
-      to_working8<DT>(kc);
-      to_working8<DT>(vc);
+  // stage the split's key positions and their first four layer slots in LDS:
+  // one round of loads for the whole split, so each step below only issues
+  // the (independent) base and record loads of its keys
+  __shared__ int s_j[kKeysPerSplit];
+  __shared__ i32x4 s_sl[kKeysPerSplit];
+  {
+    const int t = t_begin + lane;
+    int jj = 0;
+    i32x4 sl = i32x4{-1, -1, -1, -1};
+    if (t < t_end) {
+      jj = LAZY ? sel[t] : t;
+      if (a.version >= 2) sl = *reinterpret_cast<const i32x4*>(kv.slot_row(s, jj));
+    }
+    s_j[lane] = jj;
+    s_sl[lane] = sl;
+  }
+  __syncthreads();
+
+  // group g takes keys t0 .. t0+U-1 of every block of 4U keys
+  for (int t0 = t_begin + g * kU; t0 < t_end; t0 += 4 * kU) {
+    int j[kU];
+    bool ok[kU];
+    i32x4 pre[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int t = t0 + u;
+      ok[u] = live && t < t_end;
+      const int lt = min(t - t_begin, kKeysPerSplit - 1);
+      j[u] = s_j[lt];
+      pre[u] = s_sl[lt];
+    }
+    float kc[kU][8], vc[kU][8], kp[kU][8], vp[kU][8];
+    recon_kv<DT, kU, LAZY>(kv, s, h, j, ok, a.version, p, kc, vc, kp, vp, pre);
+    float sc[kU], sp[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      to_working8<DT>(kc[u]);
+      to_working8<DT>(vc[u]);
+      float dc = 0.0f, dp = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dc = fmaf(qc[e], kc[u][e], dc);
+      sc[u] = group_sum<16>(dc) * a.scale;
       if (LAZY) {
-        to_working8<DT>(kp);
-        to_working8<DT>(vp);
-      }
+        to_working8<DT>(kp[u]);
+        to_working8<DT>(vp[u]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dc = fmaf(qc[e], kc[e], dc);
-        if (LAZY) dp = fmaf(qp[e], kp[e], dp);
+        for (int e = 0; e < 8; ++e) dp = fmaf(qp[e], kp[u][e], dp);
+        sp[u] = group_sum<16>(dp) * a.scale;
       }
     }
-    const float sc = group_sum<16>(dc) * a.scale;
-    if (p == 0) lg_cur[t] = sc;
-    const float Mn = fmaxf(M, sc);
+    // ok[] differs only in lanes with 8p >= d; the logits come from the group sum
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool in = t0 + u < t_end;
+      if (in) {
+        tmax = fmaxf(tmax, sc[u]);
+        if (p == 0) {
+          lg_cur[t0 + u] = sc[u];
+          if (LAZY) lg_prev[t0 + u] = sp[u];
+        }
+      }
+    }
+    if (tmax == -INFINITY) continue;
+    const float Mn = fmaxf(M, tmax);
     const float corr = __expf(M - Mn);
-    const float w = __expf(sc - Mn);
-    Z = Z * corr + w;
+    Z *= corr;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * corr + w * vc[e];
-    M = Mn;
-    if (LAZY) {
-      const float sp = group_sum<16>(dp) * a.scale;
-      if (p == 0) lg_prev[t] = sp;
-      const float pp = __expf(sp - lse_prev);
-      m += pp;
+    for (int e = 0; e < 8; ++e) acc[e] *= corr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) accp[e] = fmaf(pp, vp[e], accp[e]);
+    for (int u = 0; u < kU; ++u) {
+      if (t0 + u < t_end) {
+        const float w = __expf(sc[u] - Mn);
+        Z += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, vc[u][e], acc[e]);
+        if (LAZY) {
+          const float pp = __expf(sp[u] - lse_prev);
+          m += pp;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) accp[e] = fmaf(pp, vp[u][e], accp[e]);
+        }
+      }
     }
+    M = Mn;
   }
   // merge the four 16-lane groups (they hold the same dims, different keys)
 #pragma unroll

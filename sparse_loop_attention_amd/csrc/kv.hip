@@ -11,8 +11,9 @@
 
 namespace fl {
 
-// slot_map[l][s][j] = slot_base + r if active_idx[s][r] == j, else -1 (reset) / untouched.
-__global__ __launch_bounds__(256) void k_slot_map(int32_t* __restrict__ slots, int32_t N,
+// slot(l, s, j) = slot_base + r if active_idx[s][r] == j, else -1 (reset) / untouched;
+// `slots` points at column l-2 of the slot table, rows `pitch` apart.
+__global__ __launch_bounds__(256) void k_slot_map(int32_t* __restrict__ slots, int32_t pitch, int32_t N,
                                                   const int32_t* __restrict__ act, int32_t n_act,
                                                   int32_t slot_base, int32_t reset) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -24,7 +25,7 @@ __global__ __launch_bounds__(256) void k_slot_map(int32_t* __restrict__ slots, i
     const int mid = (lo + hi) >> 1;
     if (a[mid] < j) lo = mid + 1; else hi = mid;
   }
-  int32_t* dst = slots + static_cast<int64_t>(s) * N + j;
+  int32_t* dst = slots + (static_cast<int64_t>(s) * N + j) * pitch;
   if (lo < n_act && a[lo] == j) *dst = slot_base + lo;
   else if (reset) *dst = -1;
 }
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) void k_commit(KvView kv, uint8_t* __restrict__
   float prev[8], delta[8];
   float amax = 0.0f;
   if (live) {
-    recon8<DT>(kv, which, s, row, j, l - 1, p, prev, nullptr);
+    recon8<DT>(kv, which, s, h, j, l - 1, p, prev, nullptr);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       delta[e] = x[e] - prev[e];
@@ -82,10 +83,10 @@ __global__ __launch_bounds__(256) void k_commit(KvView kv, uint8_t* __restrict__
     if (sc != 0.0f) c = static_cast<int>(fminf(fmaxf(__builtin_rintf(delta[e] / sc), -7.0f), 7.0f));
     packed |= (static_cast<uint32_t>(c) & 0xFu) << (4 * e);
   }
-  const int64_t rec = row * kv.cap[l] + slot_base + r;
-  *reinterpret_cast<uint32_t*>(arena_w + kv.codes[which][l] + rec * (d / 2) + 4 * p) = packed;
+  const int64_t rec = kv.record(l, s, slot_base + r, h, which);
+  *reinterpret_cast<uint32_t*>(arena_w + kv.codes[l] + rec * (d / 2) + 4 * p) = packed;
   if ((p & 3) == 0)
-    *reinterpret_cast<uint16_t*>(arena_w + kv.scales[which][l] + (rec * (d / 32) + (p >> 2)) * 2) = sbits;
+    *reinterpret_cast<uint16_t*>(arena_w + kv.scales[l] + (rec * (d / 32) + (p >> 2)) * 2) = sbits;
 }
 
 hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t st) {
@@ -95,8 +96,8 @@ hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t 
     dim3 g((kv.N + 255) / 256, kv.n_seq);
     TimedLaunch t(st, "slot_map");
     hipLaunchKernelGGL(k_slot_map, g, dim3(256), 0, st,
-                       reinterpret_cast<int32_t*>(arena + kv.slot_map[a.version]), kv.N, a.active_idx,
-                       a.n_active, a.slot_base, a.reset_map);
+                       reinterpret_cast<int32_t*>(arena + kv.slot_table) + (a.version - 2), kv.slot_pitch, kv.N,
+                       a.active_idx, a.n_active, a.slot_base, a.reset_map);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -51,9 +51,11 @@ def test_arena_layout_bytes(L, name):
     need = 2 * S * H * N * D * es
     for l, cap in zip(range(2, wl.n_loops + 1), wl.layer_caps()):
         need += S * N * 4 + 2 * S * H * cap * (D // 2 + 2 * (D // 32))
-        for arr in (lay.slot_map, lay.codes_k, lay.codes_v, lay.scales_k, lay.scales_v):
+        for arr in (lay.codes, lay.scales):
             assert arr[l] % 256 == 0
-    assert need <= lay.total_bytes <= need + 256 * (2 + 5 * wl.n_loops)
+    assert lay.slot_table % 256 == 0 and lay.slot_pitch == ((wl.n_loops - 1 + 3) // 4) * 4
+    need += S * N * 4 * (lay.slot_pitch - (wl.n_loops - 1))
+    assert need <= lay.total_bytes <= need + 256 * (3 + 2 * wl.n_loops)
     assert abi.kv_arena_bytes(d) == lay.total_bytes
 
 
@@ -63,7 +65,7 @@ def test_compression_ratio_single_layer(L):
     wl = configs.SINGLE_LAYER
     lay = abi.kv_layout(_desc(wl))
     naive = wl.n_loops * 2 * wl.n_heads * wl.n_tokens * wl.head_dim * 2
-    slot_maps = (wl.n_loops - 1) * wl.n_tokens * 4
+    slot_maps = lay.slot_pitch * wl.n_tokens * 4
     assert naive / (lay.total_bytes - slot_maps) == pytest.approx(2.87, abs=0.01)
 
 

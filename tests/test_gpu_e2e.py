@@ -60,12 +60,12 @@ def test_prefill_loops_match_oracle(wl):
             kv = run.kv
             arena_now = kv.arena.clone()
             kv.arena.copy_(g.arena)
-            for w in ("k", "v"):
+            for wi, w in enumerate(("k", "v")):
                 rr = r.store.layers[l][w][0]
-                codes = kv.view(f"codes_{w}", l).cpu().numpy()[0][:, :len(rr.idx)]
-                scales = kv.view(f"scales_{w}", l).cpu().numpy()[0][:, :len(rr.idx)]
-                assert np.array_equal(codes, oracle.pack_int4(rr.codes).transpose(1, 0, 2)), f"loop {l} {w} codes"
-                assert np.array_equal(scales.view(np.uint16), rr.scales.view(np.uint16).transpose(1, 0, 2))
+                codes = kv.view("codes", l).cpu().numpy()[0][:len(rr.idx), :, wi]
+                scales = kv.view("scales", l).cpu().numpy()[0][:len(rr.idx), :, wi]
+                assert np.array_equal(codes, oracle.pack_int4(rr.codes)), f"loop {l} {w} codes"
+                assert np.array_equal(scales.view(np.uint16), rr.scales.view(np.uint16))
             kv.arena.copy_(arena_now)
         _check_o(g.o.cpu().numpy(), r.o, f"loop {l} o")
         _check_o(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")

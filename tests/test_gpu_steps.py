@@ -142,12 +142,12 @@ def test_commit_codes_bit_exact(dtype, d):
         want_slots = np.full(n, -1)
         want_slots[sets[l]] = np.arange(len(sets[l]))
         assert np.array_equal(slots, want_slots)
-        for w in ("k", "v"):
+        for wi, w in enumerate(("k", "v")):
             rec = st.layers[l][w][0]
-            codes = kv.view(f"codes_{w}", l).cpu().numpy()[0]        # [H, cap, d/2]
-            scales = kv.view(f"scales_{w}", l).cpu().numpy()[0]      # [H, cap, d/32]
-            assert np.array_equal(codes, oracle.pack_int4(rec.codes).transpose(1, 0, 2)), (l, w)
-            assert np.array_equal(scales.view(np.uint16), rec.scales.view(np.uint16).transpose(1, 0, 2)), (l, w)
+            codes = kv.view("codes", l).cpu().numpy()[0][:, :, wi]    # [cap, H, d/2]
+            scales = kv.view("scales", l).cpu().numpy()[0][:, :, wi]  # [cap, H, d/32]
+            assert np.array_equal(codes, oracle.pack_int4(rec.codes)), (l, w)
+            assert np.array_equal(scales.view(np.uint16), rec.scales.view(np.uint16)), (l, w)
 
 
 def test_commit_appends_to_layer_without_reset():
