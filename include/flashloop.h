@@ -180,6 +180,13 @@ fl_status flashloop_select(const fl_select_args* args, void* stream);
 /*   m_i == 0 keep o and lse and add nothing to colmass.                     */
 /* o, lse and colmass are updated in place; rows that are not active are not */
 /* read or written.  Any key tensor entry not described above is untouched.  */
+/* Fused commit (LAZY, fuse_commit != 0; paragraph 4: the KV update and      */
+/* compression are fused with the compute): the call also does what          */
+/* flashloop_kv_commit(version, active_idx, k_new, v_new, commit_slot_base,  */
+/* commit_reset) would do, inside its first kernel; keys that are active in  */
+/* this loop derive version `version` from k_new/v_new with the commit's own */
+/* float32 arithmetic instead of reading the records being written, so the   */
+/* store and every output equal commit-then-attend bit for bit.              */
 /* ------------------------------------------------------------------------ */
 typedef struct {
   int32_t mode;                 /* fl_attend_mode */
@@ -198,6 +205,13 @@ typedef struct {
   float* colmass;               /* [n_seq][H][N] float32 */
   void* workspace;              /* device, >= flashloop_attend_workspace_bytes(args) */
   uint64_t workspace_bytes;
+  /* fused commit (LAZY only) */
+  int32_t fuse_commit;
+  const void* k_new;            /* [n_seq][R][H][d] base_dtype, R per kv_layout */
+  const void* v_new;
+  int32_t kv_layout;            /* fl_row_layout of k_new / v_new */
+  int32_t commit_slot_base;     /* slot_base + n_active <= layer_cap[version] */
+  int32_t commit_reset;         /* reset_map of the commit */
 } fl_attend_args;
 
 uint64_t  flashloop_attend_workspace_bytes(const fl_attend_args* args);

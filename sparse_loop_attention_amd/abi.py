@@ -58,7 +58,9 @@ class fl_attend_args(C.Structure):
                 ("q_cur", C.c_void_p), ("q_prev", C.c_void_p), ("q_layout", C.c_int32),
                 ("active_idx", C.c_void_p), ("n_active", C.c_int32), ("key_idx", C.c_void_p),
                 ("n_keys", C.c_int32), ("o", C.c_void_p), ("lse", C.c_void_p), ("o_layout", C.c_int32),
-                ("colmass", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64)]
+                ("colmass", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64),
+                ("fuse_commit", C.c_int32), ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("kv_layout", C.c_int32),
+                ("commit_slot_base", C.c_int32), ("commit_reset", C.c_int32)]
 
 
 class FlashLoopError(RuntimeError):
@@ -213,7 +215,10 @@ def select_keys(key_scores: torch.Tensor, k: int, out_idx: torch.Tensor, stream=
 
 # --------------------------------------------------------------------------- attend
 def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx, n_active: int,
-                key_idx, o, lse, colmass, workspace=None, q_compact=False, o_compact=False) -> fl_attend_args:
+                key_idx, o, lse, colmass, workspace=None, q_compact=False, o_compact=False,
+                commit=None) -> fl_attend_args:
+    """`commit` = dict(k_new=, v_new=, compact=False, slot_base=0, reset=True) fuses the
+    KV commit of this loop into the call (LAZY only)."""
     a = fl_attend_args()
     a.mode, a.kv, a.version = mode, C.pointer(kv.desc), version
     a.q_cur, a.q_prev = _ptr(q_cur), _ptr(q_prev)
@@ -225,6 +230,12 @@ def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx,
     a.o_layout = FL_ROWS_COMPACT if o_compact else FL_ROWS_BY_TOKEN
     if workspace is not None:
         a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    if commit is not None:
+        a.fuse_commit = 1
+        a.k_new, a.v_new = _ptr(commit["k_new"]), _ptr(commit["v_new"])
+        a.kv_layout = FL_ROWS_COMPACT if commit.get("compact", False) else FL_ROWS_BY_TOKEN
+        a.commit_slot_base = commit.get("slot_base", 0)
+        a.commit_reset = int(commit.get("reset", True))
     return a
 
 

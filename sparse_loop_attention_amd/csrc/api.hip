@@ -132,7 +132,14 @@ fl_status flashloop_kv_commit(const fl_commit_args* a, void* stream) {
   if (a->version < 1 || a->version > d.n_versions)
     return fail(FL_ERR_ARG, "commit: version %d outside 1..%d", a->version, d.n_versions);
   if (a->n_active < 0 || a->n_active > d.n_tokens) return fail(FL_ERR_ARG, "commit: n_active out of range");
-  if (a->n_active == 0) return ok();
+  if (a->n_active == 0) {
+    // no active token: no record; a reset still clears the layer's slots
+    if (a->version == 1 || !a->reset_map) return ok();
+    fl::KvView kv = fl::make_view(d, lay);
+    hipError_t e = fl::launch_commit(*a, kv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "commit launch");
+    return ok();
+  }
   if (!a->active_idx || !a->k_new || !a->v_new) return fail(FL_ERR_ARG, "commit: NULL index or K/V pointer");
   if (!aligned(a->k_new, 16) || !aligned(a->v_new, 16) || !aligned(a->active_idx, 4))
     return fail(FL_ERR_ARG, "commit: K/V must be 16-byte aligned");
@@ -198,6 +205,16 @@ static fl_status check_attend(const fl_attend_args* a, fl_kv_layout* lay) {
   if (!aligned(a->o, 16)) return fail(FL_ERR_ARG, "attend: o must be 16-byte aligned");
   if (a->q_layout != FL_ROWS_BY_TOKEN && a->q_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: q_layout");
   if (a->o_layout != FL_ROWS_BY_TOKEN && a->o_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: o_layout");
+  if (a->fuse_commit) {
+    if (!lazy) return fail(FL_ERR_ARG, "attend: fuse_commit needs LAZY mode");
+    if (!a->k_new || !a->v_new || !aligned(a->k_new, 16) || !aligned(a->v_new, 16))
+      return fail(FL_ERR_ARG, "attend: fused commit needs 16-byte aligned k_new and v_new");
+    if (a->kv_layout != FL_ROWS_BY_TOKEN && a->kv_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: kv_layout");
+    if (a->commit_slot_base < 0 ||
+        static_cast<int64_t>(a->commit_slot_base) + a->n_active > d.layer_cap[a->version])
+      return fail(FL_ERR_ARG, "attend: commit slots %d..%d exceed layer_cap[%d] = %d", a->commit_slot_base,
+                  a->commit_slot_base + a->n_active, a->version, d.layer_cap[a->version]);
+  }
   return FL_OK;
 }
 
@@ -212,7 +229,16 @@ fl_status flashloop_attend(const fl_attend_args* a, void* stream) {
   fl_kv_layout lay;
   fl_status st = check_attend(a, &lay);
   if (st != FL_OK) return st;
-  if (a->n_active == 0) return ok();               // LAZY with no active rows: nothing changes
+  if (a->n_active == 0) {                          // LAZY with no active rows: nothing changes
+    if (a->fuse_commit && a->commit_reset) {        // ... except that the layer's slots are cleared
+      fl_commit_args c{};
+      c.kv = a->kv; c.version = a->version; c.n_active = 0; c.reset_map = 1;
+      fl::KvView kv = fl::make_view(*a->kv, lay);
+      hipError_t e = fl::launch_commit(c, kv, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "attend launch");
+    }
+    return ok();
+  }
   const fl::AttendPlan p = fl::plan_attend(*a);
   if (p.off_total > 0 && (!a->workspace || a->workspace_bytes < p.off_total || !aligned(a->workspace, 256)))
     return fail(FL_ERR_WORKSPACE, "attend: workspace needs %llu bytes (256-byte aligned), got %llu",

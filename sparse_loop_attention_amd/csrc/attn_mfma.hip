@@ -29,6 +29,7 @@
 #include <climits>
 
 #include "fl_common.hpp"
+#include "fl_commit.hpp"
 #include "fl_launch.hpp"
 #include "fl_timing.hpp"
 
@@ -113,13 +114,50 @@ __device__ __forceinline__ int vt_pos(int k16) {
 }
 
 // --------------------------------------------------------------------------- gather
-template <int DT, int D, bool LAZY>
-__global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a) {
+// Grid (1-D): n_sh * n_tiles gather blocks (64 key slots each), then, when the
+// commit is fused, the commit blocks (16 head rows each) and the slot-table
+// blocks (256 tokens each).  The gather never reads what the fused commit
+// writes (layer `version`): an active key's version is derived from k_new/v_new.
+template <int DT, int D, bool LAZY, bool FUSE>
+__global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArgs cm) {
   __shared__ uint16_t sv[2][64][D + 2];
-  const int sh = blockIdx.y, tile = blockIdx.x;
-  const int s = sh / kv.H, h = sh % kv.H;
+  const int n_tiles = a.n_keys_pad / 64;
+  int b = blockIdx.x;
   const int g = threadIdx.x >> 4, p = threadIdx.x & 15;
+  if (FUSE && b >= a.n_sh * n_tiles) {
+    b -= a.n_sh * n_tiles;
+    const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2;
+    const int n_cb = static_cast<int>((items + 15) / 16);
+    if (b < n_cb) {                                       // records of the active rows
+      const int64_t item = static_cast<int64_t>(b) * 16 + g;
+      if (item >= items) return;
+      const int which = static_cast<int>(item & 1);
+      const int h = static_cast<int>((item >> 1) % kv.H);
+      const int64_t sr = (item >> 1) / kv.H;
+      const int r = static_cast<int>(sr % a.n_rows), s = static_cast<int>(sr / a.n_rows);
+      const int j = a.act[static_cast<int64_t>(s) * a.n_rows + r];
+      const int64_t src_rows = cm.src_compact ? a.n_rows : kv.N;
+      const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? r : j)) * kv.H + h) * D;
+      commit_row<DT>(kv, cm.arena, a.version, s, j, h, which, cm.slot_base + r, which ? cm.v_new : cm.k_new,
+                     src_elem, p);
+      return;
+    }
+    b -= n_cb;                                            // slot table column of layer `version`
+    const int per_seq = (kv.N + 255) / 256;
+    const int s = b / per_seq;
+    const int j = (b % per_seq) * 256 + threadIdx.x;
+    if (s >= kv.n_seq || j >= kv.N) return;
+    const int ra = find_active(a.act + static_cast<int64_t>(s) * a.n_rows, a.n_rows, j);
+    int32_t* dst = reinterpret_cast<int32_t*>(cm.arena + kv.slot_table) +
+                   (static_cast<int64_t>(s) * kv.N + j) * kv.slot_pitch + (a.version - 2);
+    if (ra >= 0) *dst = cm.slot_base + ra;
+    else if (cm.reset) *dst = -1;
+    return;
+  }
+  const int sh = b / n_tiles, tile = b % n_tiles;
+  const int s = sh / kv.H, h = sh % kv.H;
   const bool live = 8 * p < D;
+  const int32_t* act_s = FUSE ? a.act + static_cast<int64_t>(s) * a.n_rows : nullptr;
 #pragma unroll 1
   for (int kk = 0; kk < 4; ++kk) {
     const int local = g * 4 + kk;
@@ -129,11 +167,37 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a) {
     float x[8] = {}, xp[8] = {};
     const int64_t krow = (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * p;
     if (live) {
-      if (j >= 0) recon8<DT>(kv, 0, s, h, j, a.version, p, x, LAZY ? xp : nullptr);
+      float y[8] = {}, yp[8] = {};
+      if (FUSE) {
+        // versions v-1 from the chain, version v from this loop's new rows
+        if (j >= 0) {
+          // a reset commit clears layer v for the tokens it does not write; otherwise
+          // layer v may hold earlier commits' records (an active key's own entry is
+          // overridden below)
+          const int vw = cm.reset ? a.version - 1 : a.version;
+          recon8<DT>(kv, 0, s, h, j, vw, p, x, cm.reset ? nullptr : xp);
+          recon8<DT>(kv, 1, s, h, j, vw, p, y, cm.reset ? nullptr : yp);
+          if (cm.reset) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { xp[e] = x[e]; yp[e] = y[e]; }
+          }
+        }
+        const int ra = j >= 0 ? find_active(act_s, a.n_rows, j) : -1;
+        if (ra >= 0) {
+          const int64_t src_rows = cm.src_compact ? a.n_rows : kv.N;
+          const int64_t src = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? ra : j)) * kv.H + h) * D + 8 * p;
+          float kn[8], vn[8];
+          load8<DT>(cm.k_new, src, kn);
+          load8<DT>(cm.v_new, src, vn);
+          advance8(kn, xp, true, x);
+          advance8(vn, yp, true, y);
+        }
+      } else {
+        if (j >= 0) recon8<DT>(kv, 0, s, h, j, a.version, p, x, LAZY ? xp : nullptr);
+        if (j >= 0) recon8<DT>(kv, 1, s, h, j, a.version, p, y, LAZY ? yp : nullptr);
+      }
       store8<FL_BF16>(a.kc, krow, x);
       if (LAZY) store8<FL_BF16>(a.kp, krow, xp);
-      float y[8] = {}, yp[8] = {};
-      if (j >= 0) recon8<DT>(kv, 1, s, h, j, a.version, p, y, LAZY ? yp : nullptr);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         sv[0][local][8 * p + e] = v_operand_bits(y[e]);
@@ -592,20 +656,35 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   a.kidx = reinterpret_cast<int32_t*>(ws + p.off_gather + (lazy ? 4 : 2) * kbytes);
   a.stat = reinterpret_cast<float*>(ws + p.off_stat);
 
-  dim3 gg(a.n_keys_pad / 64, static_cast<unsigned>(sh));
+  a.n_sh = static_cast<int32_t>(sh);
+  const bool fuse = lazy && x.fuse_commit;
+  CommitArgs cm{};
+  int64_t gblocks = static_cast<int64_t>(sh) * (a.n_keys_pad / 64);
+  if (fuse) {
+    cm.arena = static_cast<uint8_t*>(x.kv->arena);
+    cm.k_new = x.k_new; cm.v_new = x.v_new;
+    cm.src_compact = x.kv_layout == FL_ROWS_COMPACT;
+    cm.slot_base = x.commit_slot_base; cm.reset = x.commit_reset;
+    const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2;
+    gblocks += (items + 15) / 16 + static_cast<int64_t>(kv.n_seq) * ((kv.N + 255) / 256);
+  }
+  dim3 gg(static_cast<unsigned>(gblocks));
   {
-    TimedLaunch t(st, lazy ? "gather_lazy" : "gather_full");
+    TimedLaunch t(st, fuse ? "gather_commit_lazy" : lazy ? "gather_lazy" : "gather_full");
+#define FL_GATHER(DTV, LZ, FU) hipLaunchKernelGGL((k_gather<DTV, D, LZ, FU>), gg, dim3(256), 0, st, kv, a, cm)
     if (kv.dtype == FL_BF16) {
-      if (lazy) hipLaunchKernelGGL((k_gather<FL_BF16, D, true>), gg, dim3(256), 0, st, kv, a);
-      else hipLaunchKernelGGL((k_gather<FL_BF16, D, false>), gg, dim3(256), 0, st, kv, a);
+      if (fuse) FL_GATHER(FL_BF16, true, true);
+      else if (lazy) FL_GATHER(FL_BF16, true, false);
+      else FL_GATHER(FL_BF16, false, false);
     } else {
-      if (lazy) hipLaunchKernelGGL((k_gather<FL_F32, D, true>), gg, dim3(256), 0, st, kv, a);
-      else hipLaunchKernelGGL((k_gather<FL_F32, D, false>), gg, dim3(256), 0, st, kv, a);
+      if (fuse) FL_GATHER(FL_F32, true, true);
+      else if (lazy) FL_GATHER(FL_F32, true, false);
+      else FL_GATHER(FL_F32, false, false);
     }
+#undef FL_GATHER
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.n_sh = static_cast<int32_t>(sh);
   const int rows_per = lazy ? 128 : 256;
   dim3 gf(mapped_grid(a.n_sh, (a.n_rows + rows_per - 1) / rows_per));
   {

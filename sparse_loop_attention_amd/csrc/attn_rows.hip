@@ -16,6 +16,7 @@
 //   colmass  - one lane per key slot sums the row probabilities in fixed
 //              row order (deterministic, no atomics).
 #include "fl_common.hpp"
+#include "fl_commit.hpp"
 #include "fl_launch.hpp"
 #include "fl_timing.hpp"
 
@@ -52,8 +53,12 @@ __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int v) {
   return lo;
 }
 
-template <int DT, bool LAZY>
-__global__ __launch_bounds__(64) void k_rows_partial(KvView kv, RowArgs a) {
+// With FUSE (lazy only) the call also commits this loop's records: versions
+// v-1 come from the chain, an active key's version v from k_new/v_new, and
+// one extra wave per (row, head) (split index == a.splits) writes that row's
+// K and V records (and, for head 0, the row's share of the slot-table column).
+template <int DT, bool LAZY, bool FUSE>
+__global__ __launch_bounds__(64) void k_rows_partial(KvView kv, RowArgs a, CommitArgs cm) {
   constexpr int kU = LAZY ? 2 : 4;                        // keys per 16-lane group and step
   const int split = blockIdx.x, r = blockIdx.y, sh = blockIdx.z;
   const int H = kv.H, d = kv.d;
@@ -87,20 +92,45 @@ __global__ __launch_bounds__(64) void k_rows_partial(KvView kv, RowArgs a) {
   float* lg_cur = a.logit + srow * a.key_slots;
   float* lg_prev = a.logit + (static_cast<int64_t>(kv.n_seq) * H * rows_total + srow) * a.key_slots;
 
+  const int32_t* act_s = a.act ? a.act + static_cast<int64_t>(s) * a.n_act : nullptr;
+  if (FUSE && split == a.splits) {
+    // this row's records of layer `version` (groups 0, 1: K, V)
+    if (g < 2) {
+      const int64_t src_rows = cm.src_compact ? a.n_act : kv.N;
+      const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? r : i)) * H + h) * d;
+      commit_row<DT>(kv, cm.arena, a.version, s, i, h, g, cm.slot_base + r, g ? cm.v_new : cm.k_new, src_elem, p);
+    }
+    if (h == 0) {
+      // slot-table entries of the tokens after the previous active row, up to this row
+      // (the last row also covers the tail of the sequence)
+      const int lo = r > 0 ? act_s[r - 1] + 1 : 0;
+      const int hi = r + 1 < a.n_act ? i : kv.N - 1;
+      int32_t* col = reinterpret_cast<int32_t*>(cm.arena + kv.slot_table) + (a.version - 2);
+      for (int jj = lo + lane; jj <= hi; jj += 64) {
+        int32_t* dst = col + (static_cast<int64_t>(s) * kv.N + jj) * kv.slot_pitch;
+        if (jj == i) *dst = cm.slot_base + r;
+        else if (cm.reset) *dst = -1;
+      }
+    }
+    return;
+  }
   // stage the split's key positions and their first four layer slots in LDS:
   // one round of loads for the whole split, so each step below only issues
   // the (independent) base and record loads of its keys
   __shared__ int s_j[kKeysPerSplit];
+  __shared__ int s_ra[kKeysPerSplit];                     // fused commit: position in the active list, or -1
   __shared__ i32x4 s_sl[kKeysPerSplit];
   {
     const int t = t_begin + lane;
-    int jj = 0;
+    int jj = 0, ra = -1;
     i32x4 sl = i32x4{-1, -1, -1, -1};
     if (t < t_end) {
       jj = LAZY ? sel[t] : t;
       if (a.version >= 2) sl = *reinterpret_cast<const i32x4*>(kv.slot_row(s, jj));
+      if (FUSE) ra = find_active(act_s, a.n_act, jj);
     }
     s_j[lane] = jj;
+    s_ra[lane] = ra;
     s_sl[lane] = sl;
   }
   __syncthreads();
@@ -119,7 +149,37 @@ __global__ __launch_bounds__(64) void k_rows_partial(KvView kv, RowArgs a) {
       pre[u] = s_sl[lt];
     }
     float kc[kU][8], vc[kU][8], kp[kU][8], vp[kU][8];
-    recon_kv<DT, kU, LAZY>(kv, s, h, j, ok, a.version, p, kc, vc, kp, vp, pre);
+    if (FUSE) {
+      // A reset commit clears layer v for every token it does not write: walk to v-1.
+      // Otherwise layer v may hold earlier commits' records: walk to v (an active
+      // key's own layer-v entry, possibly being written now, is then overridden).
+      if (cm.reset) {
+        recon_kv<DT, kU, false>(kv, s, h, j, ok, a.version - 1, p, kp, vp, kc, vc, pre);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { kc[u][e] = kp[u][e]; vc[u][e] = vp[u][e]; }
+      } else {
+        recon_kv<DT, kU, true>(kv, s, h, j, ok, a.version, p, kc, vc, kp, vp, pre);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int ra = (t0 + u < t_end) ? s_ra[t0 + u - t_begin] : -1;
+        if (ra >= 0) {                                    // uniform over the 16-lane group
+          float kn[8] = {}, vn[8] = {};
+          if (live) {
+            const int64_t src_rows = cm.src_compact ? a.n_act : kv.N;
+            const int64_t src = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? ra : j[u])) * H + h) * d + 8 * p;
+            load8<DT>(cm.k_new, src, kn);
+            load8<DT>(cm.v_new, src, vn);
+          }
+          advance8(kn, kp[u], live, kc[u]);
+          advance8(vn, vp[u], live, vc[u]);
+        }
+      }
+    } else {
+      recon_kv<DT, kU, LAZY>(kv, s, h, j, ok, a.version, p, kc, vc, kp, vp, pre);
+    }
     float sc[kU], sp[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -307,16 +367,28 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
   a.stat = reinterpret_cast<float*>(ws + p.off_stat);
   const bool lazy = x.mode == FL_ATTEND_LAZY;
   const int sh = kv.n_seq * kv.H;
-  dim3 g1(p.splits, x.n_active, sh);
-  {
-  TimedLaunch t(st, lazy ? "rows_partial_lazy" : "rows_partial_full");
-  if (kv.dtype == FL_BF16) {
-    if (lazy) hipLaunchKernelGGL((k_rows_partial<FL_BF16, true>), g1, dim3(64), 0, st, kv, a);
-    else hipLaunchKernelGGL((k_rows_partial<FL_BF16, false>), g1, dim3(64), 0, st, kv, a);
-  } else {
-    if (lazy) hipLaunchKernelGGL((k_rows_partial<FL_F32, true>), g1, dim3(64), 0, st, kv, a);
-    else hipLaunchKernelGGL((k_rows_partial<FL_F32, false>), g1, dim3(64), 0, st, kv, a);
+  const bool fuse = lazy && x.fuse_commit;
+  dim3 g1(p.splits + (fuse ? 1 : 0), x.n_active, sh);
+  CommitArgs cm{};
+  if (fuse) {
+    cm.arena = static_cast<uint8_t*>(x.kv->arena);
+    cm.k_new = x.k_new; cm.v_new = x.v_new;
+    cm.src_compact = x.kv_layout == FL_ROWS_COMPACT;
+    cm.slot_base = x.commit_slot_base; cm.reset = x.commit_reset;
   }
+  {
+    TimedLaunch t(st, fuse ? "rows_partial_commit_lazy" : lazy ? "rows_partial_lazy" : "rows_partial_full");
+#define FL_ROWS(DTV, LZ, FU) hipLaunchKernelGGL((k_rows_partial<DTV, LZ, FU>), g1, dim3(64), 0, st, kv, a, cm)
+    if (kv.dtype == FL_BF16) {
+      if (fuse) FL_ROWS(FL_BF16, true, true);
+      else if (lazy) FL_ROWS(FL_BF16, true, false);
+      else FL_ROWS(FL_BF16, false, false);
+    } else {
+      if (fuse) FL_ROWS(FL_F32, true, true);
+      else if (lazy) FL_ROWS(FL_F32, true, false);
+      else FL_ROWS(FL_F32, false, false);
+    }
+#undef FL_ROWS
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

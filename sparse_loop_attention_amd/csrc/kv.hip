@@ -6,6 +6,7 @@
 // active token writes a 4-bit difference from its previous state, an inactive
 // token writes nothing.
 #include "fl_common.hpp"
+#include "fl_commit.hpp"
 #include "fl_launch.hpp"
 #include "fl_timing.hpp"
 
@@ -30,9 +31,7 @@ __global__ __launch_bounds__(256) void k_slot_map(int32_t* __restrict__ slots, i
   else if (reset) *dst = -1;
 }
 
-// One 16-lane group per (sequence, active row, head, K|V) row; lane p owns the
-// 8 elements [8p, 8p+8) of the head row (lanes with 8p >= d idle).  A group of
-// 32 elements is 4 consecutive lanes.
+// One 16-lane group per (sequence, active row, head, K|V) row.
 template <int DT>
 __global__ __launch_bounds__(256) void k_commit(KvView kv, uint8_t* __restrict__ arena_w, int32_t l,
                                                 const int32_t* __restrict__ act, int32_t n_act,
@@ -40,7 +39,7 @@ __global__ __launch_bounds__(256) void k_commit(KvView kv, uint8_t* __restrict__
                                                 const void* __restrict__ v_new, int32_t src_compact) {
   const int64_t item = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int p = threadIdx.x & 15;
-  const int H = kv.H, d = kv.d;
+  const int H = kv.H;
   const int64_t total = static_cast<int64_t>(kv.n_seq) * n_act * H * 2;
   if (item >= total) return;                                    // uniform per 16-lane group
   const int which = static_cast<int>(item & 1);
@@ -51,48 +50,13 @@ __global__ __launch_bounds__(256) void k_commit(KvView kv, uint8_t* __restrict__
   const int j = act[static_cast<int64_t>(s) * n_act + r];
   const int64_t src_rows = src_compact ? n_act : kv.N;
   const int64_t src_row = src_compact ? r : j;
-  const void* src = which ? v_new : k_new;
-  const int64_t row = static_cast<int64_t>(s) * H + h;
-  const bool live = 8 * p < d;
-
-  float x[8];
-  if (live) load8<DT>(src, ((static_cast<int64_t>(s) * src_rows + src_row) * H + h) * d + 8 * p, x);
-  if (l == 1) {
-    if (live) store8<DT>(arena_w + kv.base[which], (row * kv.N + j) * d + 8 * p, x);
-    return;
-  }
-  float prev[8], delta[8];
-  float amax = 0.0f;
-  if (live) {
-    recon8<DT>(kv, which, s, h, j, l - 1, p, prev, nullptr);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      delta[e] = x[e] - prev[e];
-      amax = fmaxf(amax, fabsf(delta[e]));
-    }
-  }
-  amax = group_max<4>(amax);                                    // the 4 lanes of a group of 32
-  const float q = fminf(amax / 7.0f, 65504.0f);                 // correctly rounded division
-  const uint16_t sbits = f32_to_half_bits(q);
-  const float sc = half_bits_to_f32(sbits);
-  if (!live) return;
-  uint32_t packed = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    int c = 0;
-    if (sc != 0.0f) c = static_cast<int>(fminf(fmaxf(__builtin_rintf(delta[e] / sc), -7.0f), 7.0f));
-    packed |= (static_cast<uint32_t>(c) & 0xFu) << (4 * e);
-  }
-  const int64_t rec = kv.record(l, s, slot_base + r, h, which);
-  *reinterpret_cast<uint32_t*>(arena_w + kv.codes[l] + rec * (d / 2) + 4 * p) = packed;
-  if ((p & 3) == 0)
-    *reinterpret_cast<uint16_t*>(arena_w + kv.scales[l] + (rec * (d / 32) + (p >> 2)) * 2) = sbits;
+  const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + src_row) * H + h) * kv.d;
+  commit_row<DT>(kv, arena_w, l, s, j, h, which, slot_base + r, which ? v_new : k_new, src_elem, p);
 }
 
 hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t st) {
-  if (a.n_active == 0) return hipSuccess;
   uint8_t* arena = static_cast<uint8_t*>(a.kv->arena);
-  if (a.version >= 2) {
+  if (a.version >= 2 && (a.n_active > 0 || a.reset_map)) {
     dim3 g((kv.N + 255) / 256, kv.n_seq);
     TimedLaunch t(st, "slot_map");
     hipLaunchKernelGGL(k_slot_map, g, dim3(256), 0, st,
@@ -101,6 +65,7 @@ hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (a.n_active == 0) return hipSuccess;
   const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_active * kv.H * 2;
   dim3 grid(static_cast<unsigned>((items + 15) / 16)), block(256);
   const int compact = a.src_layout == FL_ROWS_COMPACT;

@@ -60,9 +60,9 @@ class LoopRecord:
 class PrefillRun:
     """GPU state of one prefill workload (n_seq = 1) and its loop sequence."""
 
-    def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], device="cuda"):
+    def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], device="cuda", fuse: bool = True):
         assert wl.n_seq == 1 and not wl.decode
-        self.wl, self.inp, self.dev = wl, inputs, device
+        self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
         n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
         dt = torch_dtype(wl)
         self.kv = abi.KVStore(1, H, d, n, wl.n_loops, dt, wl.layer_caps(), device)
@@ -95,9 +95,10 @@ class PrefillRun:
             return abi.attend_args(self.kv, abi.FL_ATTEND_FULL, l, self.inp[l]["q"], None, None, wl.n_tokens,
                                    None, self.o, self.lse, self.colmass, self.workspace)
         na = wl.n_active(l)
+        commit = dict(k_new=self.inp[l]["k"], v_new=self.inp[l]["v"]) if self.fuse else None
         return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, self.q_cur_rows[:na], self.q_prev_rows[:na],
                                self.act[l], na, self.keys_l[l], self.o, self.lse, self.colmass, self.workspace,
-                               q_compact=True)
+                               q_compact=True, commit=commit)
 
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
@@ -120,7 +121,8 @@ class PrefillRun:
         torch.index_select(self.q_eff, 0, idx, out=self.q_prev_rows[:na])
         torch.index_select(x["q"][0], 0, idx, out=self.q_cur_rows[:na])
         self.q_eff.index_copy_(0, idx, self.q_cur_rows[:na])
-        abi.kv_commit(self.kv, l, act, x["k"], x["v"])
+        if not self.fuse:
+            abi.kv_commit(self.kv, l, act, x["k"], x["v"])
         abi.attend(self._attend_args(l))
         return act
 
@@ -151,9 +153,9 @@ class DecodeRun:
     """Decode workload: n_seq sequences, one new query per sequence and loop."""
 
     def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], ctx_sets: Dict[int, List[np.ndarray]],
-                 device="cuda"):
+                 device="cuda", fuse: bool = True):
         assert wl.decode
-        self.wl, self.inp, self.dev = wl, inputs, device
+        self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
         S, n, H, d = wl.n_seq, wl.n_tokens, wl.n_heads, wl.head_dim
         dt = torch_dtype(wl)
         self.kv = abi.KVStore(S, H, d, n, wl.n_loops, dt, wl.layer_caps(), device)
@@ -179,8 +181,12 @@ class DecodeRun:
         if l == 1:
             return abi.attend_args(self.kv, abi.FL_ATTEND_FULL, 1, x["q"], None, self.last, 1, None,
                                    self.o, self.lse, self.colmass, ws, q_compact=True, o_compact=True)
+        commit = None
+        if self.fuse:
+            commit = dict(k_new=x["k"], v_new=x["v"], slot_base=self.ctx[l].shape[1], reset=False)
         return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, x["q"], self.inp[l - 1]["q"], self.last, 1,
-                               self.keys, self.o, self.lse, self.colmass, ws, q_compact=True, o_compact=True)
+                               self.keys, self.o, self.lse, self.colmass, ws, q_compact=True, o_compact=True,
+                               commit=commit)
 
     def build_context(self) -> None:
         for l in range(1, self.wl.n_loops + 1):
@@ -190,7 +196,8 @@ class DecodeRun:
     def loop(self, l: int) -> None:
         wl, x = self.wl, self.inp[l]
         slot_base = 0 if l == 1 else self.ctx[l].shape[1]
-        abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False)
+        if l == 1 or not self.fuse:
+            abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False)
         if l >= 2:
             abi.select_keys(self.colmass, wl.n_keys, self.keys)
         abi.attend(self._args(l, self.workspace))

@@ -93,3 +93,55 @@ def test_decode_loops_match_oracle(n_seq, n):
             _check_o(g.o.cpu().numpy()[s], r["o"], f"seq {s} loop {l} o")
             _check_o(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
             _check_o(g.colmass.cpu().numpy()[s], r["colmass"], f"seq {s} loop {l} colmass")
+
+
+def _arena_parts(kv, wl):
+    """Everything of the arena that the store defines (records up to each layer's use)."""
+    out = {"base_k": kv.view("base_k").cpu(), "base_v": kv.view("base_v").cpu()}
+    for l in range(2, wl.n_loops + 1):
+        out[f"slots{l}"] = kv.view("slot_map", l).cpu()
+        out[f"codes{l}"] = kv.view("codes", l).cpu()
+        out[f"scales{l}"] = kv.view("scales", l).cpu()
+    return out
+
+
+@pytest.mark.parametrize("wl", [configs.TINY, configs.scaled(configs.SINGLE_LAYER, 512, n_heads=4),
+                                configs.scaled(configs.DEEP, 320, n_heads=3)],
+                         ids=["tiny", "single_layer_512", "deep_320"])
+def test_fused_commit_equals_commit_then_attend(wl):
+    """The commit fused into the attention call writes the same store and gives
+    the same outputs, bit for bit, as a separate commit followed by attend."""
+    inputs = driver.upload_loops(wl, SyntheticLoops(wl), DEV)
+    res = []
+    for fuse in (False, True):
+        run = driver.PrefillRun(wl, inputs, DEV, fuse=fuse)
+        run.kv.arena.zero_()
+        recs = run.run(record=True)
+        torch.cuda.synchronize()
+        res.append((recs, _arena_parts(run.kv, wl)))
+    (ra, aa), (rb, ab) = res
+    for k in aa:
+        assert torch.equal(aa[k], ab[k]), k
+    for l in range(wl.n_loops):
+        assert torch.equal(ra[l].o, rb[l].o) and torch.equal(ra[l].lse, rb[l].lse)
+        assert torch.equal(ra[l].colmass, rb[l].colmass)
+
+
+def test_fused_commit_decode_equals_unfused():
+    wl = configs.scaled(configs.DECODE, 700, n_seq=3, n_heads=2)
+    syn = SyntheticLoops(wl)
+    ctx_sets = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)}
+    inputs = driver.upload_loops(wl, syn, DEV)
+    res = []
+    for fuse in (False, True):
+        run = driver.DecodeRun(wl, inputs, ctx_sets, DEV, fuse=fuse)
+        run.kv.arena.zero_()
+        run.build_context()
+        recs = run.run(record=True)
+        torch.cuda.synchronize()
+        res.append((recs, _arena_parts(run.kv, wl)))
+    (ra, aa), (rb, ab) = res
+    for k in aa:
+        assert torch.equal(aa[k], ab[k]), k
+    for l in range(wl.n_loops):
+        assert torch.equal(ra[l].o, rb[l].o) and torch.equal(ra[l].colmass, rb[l].colmass)
