@@ -61,7 +61,7 @@ import numpy as np
 __all__ = [
     "to_working_dtype", "token_scores", "topk_ascending", "select_keys", "f16_rne", "quantize_groups",
     "dequantize_groups", "pack_int4", "unpack_int4", "KVStore", "full_attention",
-    "lazy_attention", "LoopState", "run_prefill", "run_decode_seq",
+    "lazy_attention", "LoopState", "run_prefill", "run_prefill_chain", "run_decode_seq",
 ]
 
 F32 = np.float32
@@ -414,6 +414,40 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
         if keep:
             history.append(_copy_state(st))
     return (st, history) if keep else st
+
+
+def run_prefill_chain(wl, loops, upto: Optional[int] = None, seq: int = 0):
+    """Token selection and KV commits of loops 1..upto, without attention.
+
+    Neither step depends on attention ([FL/savings] par. 1 and 3: tokens are
+    ranked by their own hidden-state change, and active tokens write their
+    K/V difference), so the active sets and the whole base+delta store of a
+    large workload are computed here from the inputs alone.  Returns
+    (store, active: {loop: rows}, inputs_by_loop: {loop: dict(q, k, v)} of the
+    queries/keys/values the loops consumed, h_eff after the last loop).
+    """
+    n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
+    T = wl.n_loops if upto is None else upto
+    store = KVStore(n, H, d, wl.group)
+    h_eff = h_prev_eff = None
+    active = {}
+    for l, x in loops:
+        if l > T:
+            break
+        if l == 0:
+            h_eff = x["h"][seq].copy()
+            continue
+        if l <= wl.n_full:
+            rows = np.arange(n, dtype=np.int32)
+            h_prev_eff, h_eff = h_eff, x["h"][seq].copy()
+        else:
+            u = token_scores(h_eff, h_prev_eff)
+            rows = topk_ascending(u, wl.n_active(l))
+            h_prev_eff = h_eff.copy()
+            h_eff[rows] = x["h"][seq][rows]
+        store.commit(l, rows, x["k"][seq][rows], x["v"][seq][rows])
+        active[l] = rows
+    return store, active, h_eff
 
 
 def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], loops_data):

@@ -86,7 +86,8 @@ class PrefillRun:
         self.workspace = None
         ws = 0
         for l in range(1, wl.n_loops + 1):
-            ws = max(ws, abi.attend_workspace_bytes(self._attend_args(l)))
+            if l in self.inp:                      # loops whose inputs were drawn
+                ws = max(ws, abi.attend_workspace_bytes(self._attend_args(l)))
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
 
     def _attend_args(self, l: int):

@@ -85,3 +85,16 @@ def test_single_layer_scaled_nesting_and_carry():
     np.testing.assert_allclose(st.colmass.sum(1), wl.n_tokens, rtol=1e-10)
     # token scores at loop 4 are the change made by loop 3
     np.testing.assert_array_equal(u4, token_scores(hist[2].h, hist[1].h))
+
+
+def test_chain_driver_matches_full_driver():
+    """The attention-free chain driver reproduces the full driver's token sets and store."""
+    from oracle import run_prefill_chain
+    wl = configs.scaled(configs.SINGLE_LAYER, 256, n_heads=2)
+    st, hist = _run(wl)
+    store, active, _ = run_prefill_chain(wl, iter(SyntheticLoops(wl)))
+    for l in range(wl.n_full + 1, wl.n_loops + 1):
+        assert np.array_equal(active[l], hist[l - 1].records[l]["rows"])
+    for l in range(1, wl.n_loops + 1):
+        for w in ("k", "v"):
+            assert np.array_equal(store.reconstruct(w, l), st.store.reconstruct(w, l))
