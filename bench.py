@@ -59,12 +59,13 @@ def work_model(wl, run):
          "select_bytes": 0, "commit_bytes": 0, "kv_bytes": 0, "lazy_rows": 0, "rows": 0}
     if wl.decode:
         S = wl.n_seq
+        w["decode_full_bytes"] = w["decode_lazy_bytes"] = 0
         for l in range(1, wl.n_loops + 1):
             w["rows"] += S
             if l == 1:
                 p = S * H * N
                 w["attn_full_flops"] += 4 * d * p
-                w["kv_bytes"] += S * H * N * d * es * 2
+                w["decode_full_bytes"] += S * H * N * d * es * 2
             else:
                 keys = run.keys.cpu().numpy()
                 p = S * H * wl.n_keys
@@ -76,7 +77,8 @@ def work_model(wl, run):
                     for lp in range(2, l + 1):
                         present = set(run.ctx[lp][s].cpu().numpy().tolist()) | {N - 1}
                         layers_present += sum(int(j in present) for j in keys[s, 0])
-                w["kv_bytes"] += 2 * H * (S * wl.n_keys * d * es + layers_present * rec)
+                w["decode_lazy_bytes"] += 2 * H * (S * wl.n_keys * d * es + layers_present * rec)
+        w["kv_bytes"] = w["decode_full_bytes"] + w["decode_lazy_bytes"]
         return w
     for l in range(1, wl.n_loops + 1):
         if l <= wl.n_full:
@@ -112,16 +114,37 @@ KERNEL_WORK = {
     "mfma_colmass_lazy": ("colmass_lazy_flops", "TFLOP/s", "mfma"),
     "delta_norm": ("select_bytes", "GB/s", "hbm"),
     "commit_delta": ("commit_bytes", "GB/s", "hbm"),
-    "decode_partial": ("kv_bytes", "GB/s", "hbm"),
 }
+# the decode workload's per-row kernels stream the stored context: HBM-bound
+KERNEL_WORK_DECODE = dict(KERNEL_WORK, **{
+    "rows_partial_full": ("decode_full_bytes", "GB/s", "hbm"),
+    "rows_partial_commit_lazy": ("decode_lazy_bytes", "GB/s", "hbm"),
+    "rows_partial_lazy": ("decode_lazy_bytes", "GB/s", "hbm"),
+})
 
 
-def roofline(timings, work, steps):
+def measured_traffic(timer, workload):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary of
+    this kernel and workload; null when there is none or the library sources
+    changed since the counters were taken."""
+    from sparse_loop_attention_amd import profiling
+    now = profiling.source_hash()
+    for rec in profiling.load_traffic_records(os.path.join(ROOT, "profiles")):
+        if rec["timer"] == timer and rec["workload"] == workload:
+            if rec["source_hash"] != now:
+                return {"traffic": None, "traffic_note": f"{rec['file']} is stale (sources changed)"}
+            return {"traffic": rec["traffic_bytes"], "traffic_unit": "bytes per launch",
+                    "traffic_source": rec["file"]}
+    return {}
+
+
+def roofline(timings, work, steps, decode=False, workload=""):
+    table = KERNEL_WORK_DECODE if decode else KERNEL_WORK
     name, (ms, launches) = max(timings.items(), key=lambda kv: kv[1][0])
     avg_ms = ms / max(launches, 1)
     entry = {"kernel": name, "launches_per_step": launches / steps, "avg_launch_ms": avg_ms}
-    if name in KERNEL_WORK:
-        key, unit, bound = KERNEL_WORK[name]
+    if name in table:
+        key, unit, bound = table[name]
         per_step = work[key]
         secs = ms / 1e3 / steps
         if unit == "GB/s":
@@ -132,6 +155,7 @@ def roofline(timings, work, steps):
             peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else FP32_VECTOR_PEAK_TFLOPS
         entry.update({"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                       "frac": achieved / peak, "traffic": None})
+        entry.update(measured_traffic(name, workload))
     else:
         entry.update({"bound": None, "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None})
     return entry
@@ -139,40 +163,65 @@ def roofline(timings, work, steps):
 
 # --------------------------------------------------------------------------- CPU oracle
 def cpu_baseline(wl, target_s):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    Decode: the T loops of one sequence over its built context (the context
+    build is outside the timed work, as on the GPU).  Prefill: whole steps;
+    when one step of all heads would take well over the target, whole steps
+    of the same workload with fewer heads (same N, schedule and key count),
+    scaled by the head fraction (every part of a step is per head or
+    proportional to the hidden width).
+    """
+    import copy
     from threadpoolctl import threadpool_info
     import oracle
+    from sparse_loop_attention_amd import configs
     from sparse_loop_attention_amd.synth import SyntheticLoops
     cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     if wl.decode:
         syn = SyntheticLoops(wl, seqs=(0,))
         data = {l: {k: v.copy() for k, v in x.items()} for l, x in syn}
         ctx = {l: syn.context_active_sets(l)[0] for l in range(2, wl.n_loops + 1)}
-        t0 = time.perf_counter()
-        n = 0
-        while True:
-            oracle.run_decode_seq(wl, syn, 0, ctx, data)
+        store = oracle.build_decode_context(wl, 0, ctx, data)
+        n, busy = 0, 0.0
+        while busy < target_s:
+            st = copy.deepcopy(store)
+            t0 = time.perf_counter()
+            oracle.run_decode_loops(wl, st, 0, data)
+            busy += time.perf_counter() - t0
             n += 1
-            if time.perf_counter() - t0 >= target_s:
-                break
-        dt = time.perf_counter() - t0
-        rows = n * wl.n_loops
-        return {"value": rows / dt, "unit": "active-token loop-steps/s", "cores": cores, "kind": "oracle",
-                "sample": f"{n} run(s) of all {wl.n_loops} decode loops of 1 of {wl.n_seq} sequences "
-                          f"(context build included), {dt:.1f} s"}
-    data = [(l, {k: v.copy() for k, v in x.items()}) for l, x in SyntheticLoops(wl)]
+            print(f"[bench] oracle decode run {n}: {busy:.1f} s", file=sys.stderr, flush=True)
+        return {"value": n * wl.n_loops / busy, "unit": "active-token loop-steps/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"{n} run(s) of the {wl.n_loops} decode loops of 1 of {wl.n_seq} sequences "
+                          f"over its built context, {busy:.1f} s"}
+
+    def steps_of(w, budget):
+        data = [(l, {k: v.copy() for k, v in x.items()}) for l, x in SyntheticLoops(w)]
+        n, busy = 0, 0.0
+        while True:
+            t0 = time.perf_counter()
+            oracle.run_prefill(w, iter(data))
+            busy += time.perf_counter() - t0
+            n += 1
+            print(f"[bench] oracle step {n} ({w.n_heads} heads): {busy:.1f} s", file=sys.stderr, flush=True)
+            if busy >= budget:
+                return n, busy
+
+    H = wl.n_heads
     rows_per_step = sum(wl.n_active(l) for l in range(1, wl.n_loops + 1))
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        oracle.run_prefill(wl, iter(data))
-        n += 1
-        if time.perf_counter() - t0 >= target_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": n * rows_per_step / dt, "unit": "active-token loop-steps/s", "cores": cores,
-            "kind": "oracle", "sample": f"{n} whole step(s) of the workload ({wl.n_loops} loops), {dt:.1f} s"}
+    probe = configs.scaled(wl, wl.n_tokens, n_heads=1)
+    n1, t1 = steps_of(probe, 0.0)
+    hs = H if t1 * H <= 1.5 * target_s else max(1, min(H, int(target_s // t1)))
+    if hs == 1 and t1 >= 0.5 * target_s:
+        n, dt = n1, t1
+    else:
+        n, dt = steps_of(wl if hs == H else configs.scaled(wl, wl.n_tokens, n_heads=hs), target_s)
+    what = "all heads" if hs == H else f"{hs} of its {H} heads, scaled by {hs}/{H}"
+    return {"value": n * rows_per_step / dt * hs / H, "unit": "active-token loop-steps/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n} whole step(s) of the workload ({wl.n_loops} loops, N = {wl.n_tokens}) with {what}, "
+                      f"{dt:.1f} s"}
 
 
 # --------------------------------------------------------------------------- main
@@ -238,7 +287,7 @@ def main():
         "kv_GBps": work["kv_bytes"] / (elapsed / args.steps) / 1e9,
         "lazy_active_token_steps_per_s": (work["lazy_rows"] / (lazy_ms / 1e3)) if lazy_ms > 0 else None,
         "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in sorted(timings.items())},
-        "roofline": roofline(timings, work, args.steps),
+        "roofline": roofline(timings, work, args.steps, wl.decode, wl.name),
     }
     if args.cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

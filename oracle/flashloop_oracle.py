@@ -61,7 +61,8 @@ import numpy as np
 __all__ = [
     "to_working_dtype", "token_scores", "topk_ascending", "select_keys", "f16_rne", "quantize_groups",
     "dequantize_groups", "pack_int4", "unpack_int4", "KVStore", "full_attention",
-    "lazy_attention", "LoopState", "run_prefill", "run_prefill_chain", "run_decode_seq",
+    "lazy_attention", "LoopState", "run_prefill", "run_prefill_chain", "build_decode_context",
+    "run_decode_loops", "run_decode_seq",
 ]
 
 F32 = np.float32
@@ -312,7 +313,7 @@ def lazy_attention(q_cur, q_prev, k_prev, v_prev, k_cur, v_cur, o_prev, lse_prev
             mask = sel[None, :] <= rr[:, None]
             # previous loop's probabilities on the selected keys
             sp = (q_prev[r0:r1, h, :].astype(F64) @ kp.T) * scale
-            pp = np.where(mask, np.exp(sp - lse_prev[r0:r1, h].astype(F64)[:, None]), 0.0)
+            pp = np.exp(np.where(mask, sp - lse_prev[r0:r1, h].astype(F64)[:, None], -np.inf))
             m = pp.sum(axis=1)
             a = pp @ vp
             # current softmax restricted to the selected keys
@@ -450,26 +451,30 @@ def run_prefill_chain(wl, loops, upto: Optional[int] = None, seq: int = 0):
     return store, active, h_eff
 
 
-def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], loops_data):
-    """Decode workload, one sequence (O-6).
-
-    The stored context (positions 0..N-2) is committed first: the base from
-    loop 1 and one delta layer per later loop for the positions in
-    ``ctx_sets[l]``.  Then the new token at position N-1 runs T loops: loop 1
-    attends in full over version 1, loops l >= 2 select keys from that row's
-    column mass, commit the token's own delta and run mass-corrected
-    attention over version l.  ``loops_data[l]`` holds dict(q [S,1,H,d],
-    k [S,N,H,d], v [S,N,H,d]).  Returns a list of per-loop dicts.
-    """
+def build_decode_context(wl, seq_index: int, ctx_sets: Dict[int, np.ndarray], loops_data) -> KVStore:
+    """The stored context of one decode sequence (positions 0..N-2): the base
+    from loop 1 and one delta layer per later loop for the positions in
+    ``ctx_sets[l]`` (O-6's fixed context)."""
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
     si = seq_index
     store = KVStore(n, H, d, wl.group)
     ctx = np.arange(n - 1)
-    last = np.array([n - 1])
     for l in range(1, wl.n_loops + 1):
         x = loops_data[l]
         sel = ctx if l == 1 else np.asarray(ctx_sets[l], np.int64)
         store.commit(l, sel, x["k"][si][sel], x["v"][si][sel])
+    return store
+
+
+def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data):
+    """The T decode loops of the new token at position N-1 over a built
+    context: loop 1 attends in full over version 1, loops l >= 2 select keys
+    from that row's column mass, commit the token's own delta and run
+    mass-corrected attention over version l.  Returns a list of per-loop
+    dicts."""
+    n = wl.n_tokens
+    si = seq_index
+    last = np.array([n - 1])
     out = []
     o = lse = colmass = None
     q_prev = None
@@ -492,4 +497,12 @@ def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], 
                                                      last, keys)
             out.append(dict(o=o.copy(), lse=lse.copy(), colmass=colmass.copy(), keys=keys, mass=m))
         q_prev = q.copy()
-    return out, store
+    return out
+
+
+def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], loops_data):
+    """Decode workload, one sequence (O-6): the stored context, then the T
+    loops of the new token.  ``loops_data[l]`` holds dict(q [S,1,H,d],
+    k [S,N,H,d], v [S,N,H,d]).  Returns (per-loop dicts, store)."""
+    store = build_decode_context(wl, seq_index, ctx_sets, loops_data)
+    return run_decode_loops(wl, store, seq_index, loops_data), store

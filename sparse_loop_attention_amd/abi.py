@@ -12,7 +12,9 @@ from typing import Optional, Sequence
 
 import torch  # noqa: F401  (loads the HIP runtime that the library binds to)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashloop.so")
+# FLASHLOOP_LIBRARY selects another build of the same library (e.g. a kernel variant)
+LIB_PATH = os.environ.get("FLASHLOOP_LIBRARY",
+                          os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashloop.so"))
 MAX_VERSIONS = 32
 
 FL_OK, FL_ERR_ARG, FL_ERR_UNSUPPORTED, FL_ERR_WORKSPACE, FL_ERR_HIP = range(5)

@@ -64,6 +64,9 @@ struct MfmaArgs {
   int32_t* kidx;            // [sh][n_keys_pad], INT_MAX for padding
   float* stat;              // [sh][n_rows][4] = lse_prev, lse_new, valid, token
   int32_t n_sh;             // n_seq * H
+  // column mass: rows split into col_chunks ranges of col_rows rows
+  int32_t col_chunks, col_rows;
+  float* col_part;          // [col_chunks][sh][n_keys_pad] partial sums (col_chunks > 1)
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -232,32 +235,232 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Tile geometry: K (KT x D, bf16) and V^T (D x KT, fp16) of one role, 16-byte
-// chunks striped over the 256 threads; global loads go to registers first so
-// that they overlap the MFMA work on the other LDS buffer.
-template <int D, int KT, int NT>
-struct TileIO {
-  static constexpr int KCH = KT * D / 8;   // 16-byte chunks of a K tile (KT x D bf16)
-  static constexpr int VCH = D * KT / 8;   // 16-byte chunks of a V^T tile (D x KT fp16)
-  static constexpr int PER = (KCH + VCH) / NT;
-  static constexpr int KS = D + 8;         // padded LDS row strides
-  static constexpr int VS = KT + 8;
+// x combined with the value of lane l ^ 32 (the other key half of the same
+// query), without a trip through LDS
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// One wave owns 32 query rows (one per lane pair: lane c and c+32 hold the
+// two key halves of query c).  A workgroup of NW waves streams the key tiles
+// of one role through LDS; per tile the wave computes S^T = K Q^T (bf16
+// MFMA), the probabilities, and O^T += V^T P^T (fp16 MFMA).  The three steps
+// are software-pipelined: while the softmax of tile t runs on the VALU, the
+// matrix cores work on the QK product of tile t+1 and the PV product of tile
+// t-1, which are independent of it.
+//
+// SOFTMAX role: online softmax over the visible keys (base-2 logits); the
+// reference maximum is only moved when a new logit exceeds it by more than
+// 2^8 (P stays far inside the fp16 range), so the O rescale is rare.
+// FIXED role: probabilities against a fixed normaliser b_fix (the previous
+// loop's lse), summed into the mass.
+template <int D, int NW, int KT_>
+struct FwdTiles {
+  static constexpr int KT = KT_;                          // keys per tile: 32 or 64
+  static constexpr int NT = 64 * NW;
+  static constexpr int KS = D + 8, VS = KT + 8;          // padded LDS row strides
+  static constexpr int KCH = KT * D / 8, VCH = D * KT / 8;
+  static constexpr int KPER = (KCH + NT - 1) / NT, VPER = (VCH + NT - 1) / NT;
 };
 
-template <int D, bool LAZY>
-__global__ __launch_bounds__(512, 1) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
-  constexpr int KT = 64;
-  constexpr int DC = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int NR = LAZY ? 2 : 1;
-  constexpr int NT = 512;                                 // 8 waves: 8 row blocks, or 4 x (current, previous)
-  constexpr int ROWS = LAZY ? 128 : 256;
-  using IO = TileIO<D, KT, NT>;
-  constexpr int KS = IO::KS, VS = IO::VS;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][NR][KT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][NR][D * VS];
-  __shared__ int skidx[2][KT];
-  __shared__ float sm[4][32];
+template <int D, int NW, int KT_, bool FIXED>
+__device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const uint16_t* kbase, const uint16_t* vbase,
+                                         const int32_t* kx, uint16_t (*sk)[KT_ * FwdTiles<D, NW, KT_>::KS],
+                                         uint16_t (*sv)[D * FwdTiles<D, NW, KT_>::VS], int (*skx)[KT_],
+                                         const bf16x8 (&qf)[D / 16], int tok, int tok_first, int tok_last, bool blk_full,
+                                         float c1, float b_fix, f32x16 (&acc)[D / 32], float& ref, float& lsum) {
+  using T = FwdTiles<D, NW, KT_>;
+  constexpr int KT = T::KT, NT = T::NT, KS = T::KS, VS = T::VS;
+  constexpr int DC = D / 16, DB = D / 32;
+  constexpr int NKB = KT / 32, NCC = KT / 16;             // 32-key logit blocks, 16-key PV chunks
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int hh = lane >> 5, c = lane & 31;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  ref = -INFINITY;
+  lsum = 0.0f;
+
+  u32x4 pk[T::KPER], pv[T::VPER];
+  int pkx = INT_MAX;
+  auto gload_k = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < T::KPER; ++i) {
+      const int q = min(tid + NT * i, T::KCH - 1);           // a partial last round repeats the last chunk
+      pk[i] = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(tile * KT + q / (D / 8)) * D +
+                                              (q % (D / 8)) * 8);
+    }
+    pkx = kx[tile * KT + (tid & (KT - 1))];               // every wave reads the tile's positions
+  };
+  auto gload_v = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < T::VPER; ++i) {
+      const int q = min(tid + NT * i, T::VCH - 1);
+      pv[i] = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(q / (KT / 8)) * a.n_keys_pad +
+                                              tile * KT + (q % (KT / 8)) * 8);
+    }
+  };
+  auto sstore_k = [&](int buf, int tile) {
+#pragma unroll
+    for (int i = 0; i < T::KPER; ++i) {
+      const int q = min(tid + NT * i, T::KCH - 1);
+      *reinterpret_cast<u32x4*>(&sk[buf][(q / (D / 8)) * KS + (q % (D / 8)) * 8]) = pk[i];
+    }
+    skx[tile & 3][tid & (KT - 1)] = pkx;                   // identical values from every wave: no branch
+  };
+  auto sstore_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < T::VPER; ++i) {
+      const int q = min(tid + NT * i, T::VCH - 1);
+      *reinterpret_cast<u32x4*>(&sv[buf][(q / (KT / 8)) * VS + (q % (KT / 8)) * 8]) = pv[i];
+    }
+  };
+  auto qk = [&](int buf, f32x16 (&S)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      S[kb] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sk[buf][(kb * 32 + c) * KS + dc * 16 + 8 * hh]);
+        S[kb] = mfma32(ka, qf[dc], S[kb]);
+      }
+    }
+  };
+  auto pv_acc = [&](int buf, const f16x8 (&P)[NCC]) {
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f16x8 va = *reinterpret_cast<const f16x8*>(&sv[buf][(db * 32 + c) * VS + cc * 16 + 8 * hh]);
+        acc[db] = mfma32h(va, P[cc], acc[db]);
+      }
+  };
+  // keys of tile `tile` after this lane's row get logit -inf (wave-uniform test)
+  auto mask = [&](int tile, f32x16 (&S)[NKB]) {
+    const int* kk = skx[tile & 3];
+    if (!blk_full || kk[KT - 1] > tok_first) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const i32x4 kv = *reinterpret_cast<const i32x4*>(&kk[kb * 32 + 8 * q4 + 4 * hh]);
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4)
+            if (kv[k4] > tok) S[kb][4 * q4 + k4] = -INFINITY;
+        }
+    }
+  };
+  // probabilities from masked logits, branch-free; returns (wave-uniform)
+  // whether O must be rescaled by alpha before this tile's PV product
+  auto softmax = [&](f32x16 (&S)[NKB], f16x8 (&P)[NCC], float& alpha) -> bool {
+    bool resc = false;
+    float sub;
+    if (FIXED) {
+      sub = b_fix;
+    } else {
+      float mx[4 * NKB];                                    // tree: independent partial maxima
+#pragma unroll
+      for (int j = 0; j < 4 * NKB; ++j) mx[j] = fmaxf(fmaxf(S[j >> 2][(j & 3) * 4], S[j >> 2][(j & 3) * 4 + 1]),
+                                                      fmaxf(S[j >> 2][(j & 3) * 4 + 2], S[j >> 2][(j & 3) * 4 + 3]));
+      if (NKB == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], mx[j + 4]);
+      }
+      float tmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      tmax = max_xor32(tmax) * c1;
+      resc = __ballot(tmax > ref + 8.0f) != 0;            // some row's maximum moved far: exact rescale
+      const float nref = resc ? fmaxf(ref, tmax) : ref;
+      alpha = (ref == -INFINITY) ? 0.0f : ex2(ref - nref);
+      lsum *= alpha;
+      ref = nref;
+      sub = (ref == -INFINITY) ? 0.0f : ref;
+    }
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) P[cc][i] = static_cast<_Float16>(ex2(fmaf(S[cc >> 1][(cc & 1) * 8 + i], c1, -sub)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {1.0f16, 1.0f16};
+    float ps = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps = __builtin_amdgcn_fdot2(h2{P[cc][2 * i], P[cc][2 * i + 1]}, one, ps, false);
+    lsum += ps;
+    return resc;
+  };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+  };
+
+  if (n_tiles == 0) return;
+  // prologue: K tiles 0 and 1 in LDS, logits of tile 0
+  gload_k(0);
+  sstore_k(0, 0);
+  if (n_tiles > 1) { gload_k(1); sstore_k(1, 1); }
+  __syncthreads();
+  f32x16 S0[NKB], S1[NKB];
+  f16x8 P[NCC];
+  qk(0, S0);
+  __syncthreads();
+
+  // iteration t: QK(t+1) into Sn, PV(t-1) with P, softmax(t) of Sc into P;
+  // K(t+2) and V(t) are loaded for the next iterations.  Tiles past the end
+  // are computed on whatever the buffers hold and never used.
+  bool resc_prev = false;
+  float alpha_prev = 1.0f;
+  auto step = [&](int t, f32x16 (&Sc)[NKB], f32x16 (&Sn)[NKB], bool first) {
+    gload_k(min(t + 2, n_tiles - 1));
+    gload_v(t);
+    if (resc_prev) rescale(alpha_prev);
+    mask(t, Sc);
+    qk((t + 1) & 1, Sn);
+    if (!first) pv_acc((t + 1) & 1, P);
+    float alpha = 1.0f;
+    const bool resc = softmax(Sc, P, alpha);
+    // interleave: operand reads run 4 ahead; every MFMA is followed by
+    // independent softmax work for the VALU
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NKB * DC + NCC * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+    }
+    // P of this tile is complete here (keeps its conversion from sinking
+    // into the next iteration, away from the MFMAs it should overlap)
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) asm volatile("" ::"v"(P[cc]));
+    sstore_k(t & 1, t + 2);
+    sstore_v(t & 1);
+    __syncthreads();
+    resc_prev = resc;
+    alpha_prev = alpha;
+  };
+  step(0, S0, S1, true);
+  int t = 1;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, S1, S0, false);
+    step(t + 1, S0, S1, false);
+  }
+  if (t < n_tiles) step(t, S1, S0, false);
+  if (resc_prev) rescale(alpha_prev);                      // PV of the last tile
+  pv_acc((n_tiles - 1) & 1, P);
+}
+
+template <int D, int NW, int KT_, bool LAZY>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2))) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
+  using T = FwdTiles<D, NW, KT_>;
+  constexpr int KT = T::KT;
+  constexpr int DC = D / 16, DB = D / 32;
+  constexpr int ROWS = 32 * NW;
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][KT * T::KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * T::VS];
+  __shared__ __attribute__((aligned(16))) int skx[4][KT];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -265,171 +468,47 @@ __global__ __launch_bounds__(512, 1) void k_mfma_fwd(int32_t H, int32_t N, MfmaA
   int sh, qtile;
   if (!map_block(a.n_sh, (a.n_rows + ROWS - 1) / ROWS, sh, qtile)) return;
   const int s = sh / H, h = sh % H;
-  const int blk = LAZY ? (wave >> 1) : wave;
-  const int role = LAZY ? (wave & 1) : 0;                 // 0 = current, 1 = previous loop
-  const int r0 = qtile * ROWS + blk * 32;                 // first row of this wave's block
+  const int r0 = qtile * ROWS + wave * 32;                // first row of this wave
   const int r = r0 + c;
   const bool vrow = r < a.n_rows;
-  const int tok = vrow ? row_token(a, s, r) : -1;
-  const bool blk_full = r0 + 31 < a.n_rows;               // all 32 rows of the block exist
+  const int tok = vrow ? row_token(a, s, r) : -1;         // -1: every key is masked
+  const bool blk_full = r0 + 31 < a.n_rows;
   const int tok_first = row_token(a, s, min(r0, a.n_rows - 1));
   const int tok_last = row_token(a, s, min(r0 + 31, a.n_rows - 1));
   const float c1 = a.scale * kLog2e;                      // logits in log2 units
 
-  bf16x8 qf[DC];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(role ? a.q_prev : a.q_cur);
-    const int64_t rows_q = a.q_compact ? a.n_rows : N;
-    const int64_t qr = a.q_compact ? r : tok;
-    const uint16_t* src = q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + 8 * hh;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qf[dc] = vrow ? *reinterpret_cast<const bf16x8*>(src + dc * 16) : bf16x8{};
-  }
-  const int64_t rows_o = a.o_compact ? a.n_rows : N;
-  const int64_t orow = a.o_compact ? r : tok;
-  float lse_prev = 0.0f;
-  if (LAZY && vrow) lse_prev = a.lse[(static_cast<int64_t>(s) * rows_o + orow) * H + h];
-  const float b_prev = lse_prev * kLog2e;
-
   const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
-  if (tid == 0) {                                        // key slots visible to the workgroup's last row
+  if (tid == 0) {                                          // key slots visible to the workgroup's last row
     const int last_tok = row_token(a, s, min(a.n_rows, (qtile + 1) * ROWS) - 1);
     int lo = 0, hi = a.n_keys;
     while (lo < hi) { const int mid = (lo + hi) >> 1; if (kx[mid] <= last_tok) lo = mid + 1; else hi = mid; }
     s_last = lo;
   }
-  const uint16_t* kbase[NR];
-  const uint16_t* vbase[NR];
-  kbase[0] = a.kc + static_cast<int64_t>(sh) * a.n_keys_pad * D;
-  vbase[0] = a.vtc + static_cast<int64_t>(sh) * D * a.n_keys_pad;
-  if (LAZY) {
-    kbase[NR - 1] = a.kp + static_cast<int64_t>(sh) * a.n_keys_pad * D;
-    vbase[NR - 1] = a.vtp + static_cast<int64_t>(sh) * D * a.n_keys_pad;
-  }
   __syncthreads();
   const int n_tiles = (s_last + KT - 1) / KT;
 
-  f32x16 acc[DB];
+  const int64_t rows_q = a.q_compact ? a.n_rows : N;
+  const int64_t qr = a.q_compact ? r : tok;
+  auto load_q = [&](const void* src, bf16x8 (&qf)[DC]) {
+    const uint16_t* p = static_cast<const uint16_t*>(src) + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + 8 * hh;
 #pragma unroll
-  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;                  // current loop, log2 units, lane half
-  float mass = 0.0f;                                      // previous loop, lane half
-
-  u32x4 pre[NR][IO::PER];
-  int pre_k = INT_MAX;
-#define FL_FWD_GLOAD(TILE)                                                              \
-  {                                                                                     \
-    _Pragma("unroll") for (int w = 0; w < NR; ++w)                                      \
-      _Pragma("unroll") for (int i = 0; i < IO::PER; ++i) {                             \
-        const int q = tid + NT * i;                                                     \
-        if (q < IO::KCH) {                                                              \
-          const int row = q / (D / 8), col = (q % (D / 8)) * 8;                         \
-          pre[w][i] = *reinterpret_cast<const u32x4*>(kbase[w] + static_cast<int64_t>((TILE) * KT + row) * D + col); \
-        } else {                                                                        \
-          const int qv = q - IO::KCH;                                                   \
-          const int row = qv / (KT / 8), col = (qv % (KT / 8)) * 8;                     \
-          pre[w][i] = *reinterpret_cast<const u32x4*>(vbase[w] + static_cast<int64_t>(row) * a.n_keys_pad + (TILE) * KT + col); \
-        }                                                                               \
-      }                                                                                 \
-    if (tid < KT) pre_k = kx[(TILE) * KT + tid];                                        \
-  }
-#define FL_FWD_SSTORE(BUF)                                                              \
-  {                                                                                     \
-    _Pragma("unroll") for (int w = 0; w < NR; ++w)                                      \
-      _Pragma("unroll") for (int i = 0; i < IO::PER; ++i) {                             \
-        const int q = tid + NT * i;                                                     \
-        if (q < IO::KCH) {                                                              \
-          const int row = q / (D / 8), col = (q % (D / 8)) * 8;                         \
-          *reinterpret_cast<u32x4*>(&sk[BUF][w][row * KS + col]) = pre[w][i];           \
-        } else {                                                                        \
-          const int qv = q - IO::KCH;                                                   \
-          const int row = qv / (KT / 8), col = (qv % (KT / 8)) * 8;                     \
-          *reinterpret_cast<u32x4*>(&sv[BUF][w][row * VS + col]) = pre[w][i];           \
-        }                                                                               \
-      }                                                                                 \
-    if (tid < KT) skidx[BUF][tid] = pre_k;                                              \
-  }
-  if (n_tiles > 0) {
-    FL_FWD_GLOAD(0)
-    FL_FWD_SSTORE(0)
-  }
-  __syncthreads();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) FL_FWD_GLOAD(tile + 1)
-    const int* kk = skidx[buf];
-    if (kk[0] <= tok_last) {                              // some key of the tile is visible to the block
-      const uint16_t* K = sk[buf][role];
-      const uint16_t* V = sv[buf][role];
-      f32x16 st[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&K[(kb * 32 + c) * KS + dc * 16 + 8 * hh]);
-          st[kb] = mfma32(ka, qf[dc], st[kb]);
-        }
-      }
-      const bool need_mask = !blk_full || kk[KT - 1] > tok_first;
-      float pv[32];                                       // raw logits q.k
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = st[kb][i];
-          if (need_mask && kk[kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] > tok) x = -INFINITY;
-          pv[kb * 16 + i] = x;
-        }
-      if (role == 0) {
-        float tmax = pv[0];
-#pragma unroll
-        for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, pv[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax * c1);      // running max in log2 units (c1 > 0)
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;   // fully masked so far: p = 0
-        float psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) { pv[i] = ex2(fmaf(pv[i], c1, -m_use)); psum += pv[i]; }
-        if (__ballot(m_new != m_run)) {                   // the running max moved for some row
-          const float alpha = ex2(m_run - m_use);
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-        }
-        m_run = m_new;
-        l_run += psum;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) { pv[i] = ex2(fmaf(pv[i], c1, -b_prev)); mass += pv[i]; }
-      }
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        f16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = static_cast<_Float16>(pv[cc * 8 + i]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const f16x8 va = *reinterpret_cast<const f16x8*>(&V[(db * 32 + c) * VS + cc * 16 + 8 * hh]);
-          acc[db] = mfma32h(va, pb, acc[db]);
-        }
-      }
-    }
-    if (tile + 1 < n_tiles) FL_FWD_SSTORE(buf ^ 1)
-    __syncthreads();
-  }
-#undef FL_FWD_GLOAD
-#undef FL_FWD_SSTORE
-
-  // ---- epilogue
+    for (int dc = 0; dc < DC; ++dc) qf[dc] = vrow ? *reinterpret_cast<const bf16x8*>(p + dc * 16) : bf16x8{};
+  };
+  const int64_t rows_o = a.o_compact ? a.n_rows : N;
+  const int64_t orow = a.o_compact ? r : tok;
   float* lse_ptr = a.lse + (static_cast<int64_t>(s) * rows_o + orow) * H + h;
   float* o_ptr = a.o + ((static_cast<int64_t>(s) * rows_o + orow) * H + h) * D;
   float* st_ptr = a.stat + (static_cast<int64_t>(sh) * a.n_rows + r) * 4;
+  const int64_t kofs = static_cast<int64_t>(sh) * a.n_keys_pad * D;
+
+  bf16x8 qf[DC];
+  f32x16 acc[DB];
+  float ref, lsum;
   if (!LAZY) {
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    load_q(a.q_cur, qf);
+    fwd_pass<D, NW, KT_, false>(a, n_tiles, a.kc + kofs, a.vtc + kofs, kx, sk, sv, skx, qf, tok, tok_first, tok_last,
+                           blk_full, c1, 0.0f, acc, ref, lsum);
+    const float l_tot = lsum + __shfl_xor(lsum, 32, 64);
     if (vrow && l_tot > 0.0f) {
       const float inv = 1.0f / l_tot;
 #pragma unroll
@@ -442,77 +521,283 @@ __global__ __launch_bounds__(512, 1) void k_mfma_fwd(int32_t H, int32_t N, MfmaA
                           acc[db][4 * q4 + 3] * inv);
         }
       if (hh == 0) {
-        const float b = m_run + __log2f(l_tot);           // lse in log2 units
+        const float b = ref + __log2f(l_tot);              // lse in log2 units
         *lse_ptr = b * kLn2;
         *reinterpret_cast<float4*>(st_ptr) = make_float4(b, b, 1.0f, __int_as_float(tok));
       }
     }
     return;
   }
-  // lazy: the previous-loop wave hands its mass and contribution to its partner
-  float* sa = reinterpret_cast<float*>(&sk[0][0][0]);     // [blk][DB][16][64] floats
-  if (role == 1) {
-    const float m_tot = mass + __shfl_xor(mass, 32, 64);
-    if (hh == 0) sm[blk][c] = m_tot;
+  // lazy: pass 1 over the previous loop's keys with the fixed normaliser
+  // lse_prev gives the mass m and contribution a; o_prev - a is written back
+  // at once, and pass 2 (current loop, online softmax) adds m * otilde.
+  const float b_prev = vrow ? a.lse[(static_cast<int64_t>(s) * rows_o + orow) * H + h] * kLog2e : 0.0f;
+  load_q(a.q_prev, qf);
+  fwd_pass<D, NW, KT_, true>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok, tok_first, tok_last,
+                        blk_full, c1, b_prev, acc, ref, lsum);
+  const float m = lsum + __shfl_xor(lsum, 32, 64);
+  const bool valid = vrow && m > 0.0f;
+  if (valid) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sa[((blk * DB + db) * 16 + i) * 64 + lane] = acc[db][i];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dim = db * 32 + 8 * q4 + 4 * hh;
+        float4 op = *reinterpret_cast<const float4*>(o_ptr + dim);
+        op.x -= acc[db][4 * q4 + 0];
+        op.y -= acc[db][4 * q4 + 1];
+        op.z -= acc[db][4 * q4 + 2];
+        op.w -= acc[db][4 * q4 + 3];
+        *reinterpret_cast<float4*>(o_ptr + dim) = op;
+      }
   }
-  __syncthreads();
-  if (role == 0 && vrow) {
-    const float z = l_run + __shfl_xor(l_run, 32, 64);
-    const float m = sm[blk][c];
-    const bool valid = z > 0.0f && m > 0.0f;
-    if (valid) {
-      const float f = m / z;
+  __syncthreads();                                         // pass 2 reuses the tile buffers
+  load_q(a.q_cur, qf);
+  fwd_pass<D, NW, KT_, false>(a, n_tiles, a.kc + kofs, a.vtc + kofs, kx, sk, sv, skx, qf, tok, tok_first, tok_last,
+                         blk_full, c1, 0.0f, acc, ref, lsum);
+  const float z = lsum + __shfl_xor(lsum, 32, 64);
+  if (valid) {
+    const float f = z > 0.0f ? m / z : 0.0f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int dim = db * 32 + 8 * q4 + 4 * hh;
-          float4 op = *reinterpret_cast<const float4*>(o_ptr + dim);
-          const float* av = &sa[((blk * DB + db) * 16 + 4 * q4) * 64 + lane];
-          op.x = fmaf(f, acc[db][4 * q4 + 0], op.x - av[0]);
-          op.y = fmaf(f, acc[db][4 * q4 + 1], op.y - av[64]);
-          op.z = fmaf(f, acc[db][4 * q4 + 2], op.z - av[128]);
-          op.w = fmaf(f, acc[db][4 * q4 + 3], op.w - av[192]);
-          *reinterpret_cast<float4*>(o_ptr + dim) = op;
-        }
-    }
-    if (hh == 0) {
-      // new lse in log2 units: M + log2 Z - log2 m
-      const float b = valid ? m_run + __log2f(z) - __log2f(m) : b_prev;
-      if (valid) *lse_ptr = b * kLn2;
-      *reinterpret_cast<float4*>(st_ptr) =
-          make_float4(valid ? b_prev : INFINITY, valid ? b : INFINITY, valid ? 1.0f : 0.0f, __int_as_float(tok));
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dim = db * 32 + 8 * q4 + 4 * hh;
+        float4 op = *reinterpret_cast<const float4*>(o_ptr + dim);
+        op.x = fmaf(f, acc[db][4 * q4 + 0], op.x);
+        op.y = fmaf(f, acc[db][4 * q4 + 1], op.y);
+        op.z = fmaf(f, acc[db][4 * q4 + 2], op.z);
+        op.w = fmaf(f, acc[db][4 * q4 + 3], op.w);
+        *reinterpret_cast<float4*>(o_ptr + dim) = op;
+      }
+  }
+  if (vrow && hh == 0) {
+    // new lse in log2 units: M + log2 Z - log2 m
+    const float b = valid ? ref + __log2f(z) - __log2f(m) : b_prev;
+    if (valid) *lse_ptr = b * kLn2;
+    *reinterpret_cast<float4*>(st_ptr) =
+        make_float4(valid ? b_prev : INFINITY, valid ? b : INFINITY, valid ? 1.0f : 0.0f, __int_as_float(tok));
   }
 }
 
 // --------------------------------------------------------------------------- colmass
-// stat rows hold (b_prev, b_cur, valid, token) with b = lse * log2(e); rows
-// that did not update carry b = +inf so that their probabilities vanish.
+// Key-major: a wave owns 32 key slots (K^ rows in registers, keys in lanes so
+// that column sums are lane-local) and streams tiles of 64 query rows through
+// LDS; S = Q K^T on the MFMA, p = 2^(s*c1 - b) with the row's final base-2
+// normaliser b, summed per key in a fixed order.  Software-pipelined like the
+// forward pass: the QK product of row tile t+1 runs on the matrix cores while
+// the VALU exponentiates tile t.  A lazy loop makes two passes: the previous
+// loop's probabilities (b_prev, q_prev, K^ of version v-1) are subtracted, the
+// current ones added.  The rows can be split over several workgroups, whose
+// per-key partial sums a second kernel adds in a fixed order.
+//
+// stat rows hold (b_prev, b_cur, valid, token); rows that did not update
+// carry b = +inf so that their probabilities vanish.
+template <int D>
+struct ColTiles {
+  static constexpr int QT = 64;
+  static constexpr int NT = 512;
+  static constexpr int QS = D + 8;
+  static constexpr int QCH = QT * D / 8;
+  static constexpr int QPER = (QCH + NT - 1) / NT;
+};
+
+template <int D, bool SUB>
+__device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H, int N, int r_begin, int r_end,
+                                         const void* qsrc, const uint16_t* krow, int bsel, int kj, int kmax,
+                                         uint16_t (*sq)[ColTiles<D>::QT * ColTiles<D>::QS], float (*sb)[64],
+                                         int (*stok)[64], float c1, float& acc) {
+  using T = ColTiles<D>;
+  constexpr int QT = T::QT, NT = T::NT, QS = T::QS;
+  constexpr int DC = D / 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int hh = lane >> 5, c = lane & 31;
+  const int n_tiles = (r_end - r_begin + QT - 1) / QT;
+  if (n_tiles <= 0) return;
+  bf16x8 kf[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) kf[dc] = *reinterpret_cast<const bf16x8*>(krow + dc * 16);
+  const int64_t rows_q = a.q_compact ? a.n_rows : N;
+
+  u32x4 pq[T::QPER];
+  float pb = INFINITY;
+  int ptok = -1;
+  // branch-free: rows past the range are read clamped and then neutralised
+  auto gload = [&](int tile) {
+    const int q0 = r_begin + tile * QT;
+#pragma unroll
+    for (int i = 0; i < T::QPER; ++i) {
+      const int ch = min(tid + NT * i, T::QCH - 1);         // a partial last round repeats the last chunk
+      const int rr = q0 + ch / (D / 8);
+      const int rc = min(rr, r_end - 1);
+      const int64_t qr = a.q_compact ? rc : row_token(a, s, rc);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(qsrc) +
+                                                      ((static_cast<int64_t>(s) * rows_q + qr) * H + (sh % H)) * D +
+                                                      (ch % (D / 8)) * 8);
+      pq[i] = rr < r_end ? v : u32x4{0, 0, 0, 0};
+    }
+    const int rr = q0 + (tid & 63);                         // every wave reads the tile's row statistics
+    const float4 st =
+        *reinterpret_cast<const float4*>(a.stat + (static_cast<int64_t>(sh) * a.n_rows + min(rr, r_end - 1)) * 4);
+    pb = rr < r_end ? (bsel ? st.y : st.x) : INFINITY;
+    ptok = rr < r_end ? __float_as_int(st.w) : -1;
+  };
+  auto sstore = [&](int buf, int tile) {
+#pragma unroll
+    for (int i = 0; i < T::QPER; ++i) {
+      const int ch = min(tid + NT * i, T::QCH - 1);
+      *reinterpret_cast<u32x4*>(&sq[buf][(ch / (D / 8)) * QS + (ch % (D / 8)) * 8]) = pq[i];
+    }
+    sb[tile & 3][tid & 63] = pb;                            // identical values from every wave
+    stok[tile & 3][tid & 63] = ptok;
+  };
+  auto qk = [&](int buf, f32x16 (&S)[2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      S[qb] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[buf][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
+        S[qb] = mfma32(qa, kf[dc], S[qb]);
+      }
+    }
+  };
+  // pairs (row, key) with the key after the row get logit -inf (wave-uniform test)
+  auto mask = [&](int tile, f32x16 (&S)[2]) {
+    const int slot = tile & 3;
+    if (stok[slot][0] < kmax) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const i32x4 t4 = *reinterpret_cast<const i32x4*>(&stok[slot][qb * 32 + 8 * q4 + 4 * hh]);
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4)
+            if (kj > t4[k4]) S[qb][4 * q4 + k4] = -INFINITY;
+        }
+    }
+  };
+  auto expsum = [&](int tile, const f32x16 (&S)[2]) {
+    const int slot = tile & 3;
+    float part = 0.0f;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 b4 = *reinterpret_cast<const float4*>(&sb[slot][qb * 32 + 8 * q4 + 4 * hh]);
+        part += ex2(fmaf(S[qb][4 * q4 + 0], c1, -b4.x));
+        part += ex2(fmaf(S[qb][4 * q4 + 1], c1, -b4.y));
+        part += ex2(fmaf(S[qb][4 * q4 + 2], c1, -b4.z));
+        part += ex2(fmaf(S[qb][4 * q4 + 3], c1, -b4.w));
+      }
+    acc += SUB ? -part : part;
+  };
+
+  gload(0);
+  sstore(0, 0);
+  if (n_tiles > 1) { gload(1); sstore(1, 1); }
+  __syncthreads();
+  f32x16 S0[2], S1[2];
+  qk(0, S0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    gload(min(t + 2, n_tiles - 1));
+    mask(t, S0);
+    qk((t + 1) & 1, S1);
+    expsum(t, S0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    }
+    asm volatile("" ::"v"(acc));
+    sstore(t & 1, t + 2);
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) S0[qb] = S1[qb];
+  }
+  __syncthreads();                                           // the buffers are reused by the next pass
+}
+
 template <int D, bool LAZY>
-__global__ __launch_bounds__(512, 1) void k_mfma_colmass(int32_t H, int32_t N, MfmaArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(4))) void k_mfma_colmass(int32_t H, int32_t N, MfmaArgs a) {
+  using T = ColTiles<D>;
+  constexpr int QT = T::QT;
+  constexpr int KB = 256;                                    // key slots per workgroup (8 waves x 32)
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][QT * T::QS];
+  __shared__ __attribute__((aligned(16))) float sb[4][64];
+  __shared__ __attribute__((aligned(16))) int stok[4][64];
+  __shared__ int s_start;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, c = lane & 31;
+  const int n_kblk = a.n_keys_pad / KB;
+  int sh, item;
+  if (!map_block(a.n_sh, n_kblk * a.col_chunks, sh, item)) return;
+  const int chunk = item % a.col_chunks;
+  const int kblk = n_kblk - 1 - item / a.col_chunks;        // early keys see the most rows: start them first
+  const int s = sh / H;
+  const int t0 = kblk * KB + wave * 32;
+  const int t = t0 + c;
+  const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
+  const int kj = kx[t];                                      // INT_MAX for padding
+  const int kmax = kx[min(t0 + 31, a.n_keys - 1)];           // largest real key of this wave
+  const float c1 = a.scale * kLog2e;
+  if (tid == 0) {                                            // first row that sees the block's first key
+    const int kfirst = kx[kblk * KB];
+    int lo = 0, hi = a.n_rows;
+    while (lo < hi) { const int mid = (lo + hi) >> 1; if (row_token(a, s, mid) < kfirst) lo = mid + 1; else hi = mid; }
+    s_start = lo;
+  }
+  __syncthreads();
+  const int c_lo = chunk * a.col_rows;
+  const int r_end = min(a.n_rows, c_lo + a.col_rows);
+  const int r_begin = max(c_lo, (s_start / QT) * QT);
+  const int64_t kofs = (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * hh;
+  float acc = 0.0f;
+  if (LAZY) {
+    col_pass<D, true>(a, s, sh, H, N, r_begin, r_end, a.q_prev, a.kp + kofs, 0, kj, kmax, sq, sb, stok, c1, acc);
+    col_pass<D, false>(a, s, sh, H, N, r_begin, r_end, a.q_cur, a.kc + kofs, 1, kj, kmax, sq, sb, stok, c1, acc);
+  } else {
+    col_pass<D, false>(a, s, sh, H, N, r_begin, r_end, a.q_cur, a.kc + kofs, 1, kj, kmax, sq, sb, stok, c1, acc);
+  }
+  acc += __shfl_xor(acc, 32, 64);
+  if (hh != 0) return;
+  if (a.col_chunks > 1) {
+    a.col_part[(static_cast<int64_t>(chunk) * a.n_sh + sh) * a.n_keys_pad + t] = acc;
+  } else if (t < a.n_keys) {
+    float* dst = a.colmass + static_cast<int64_t>(sh) * N + kj;
+    if (LAZY) *dst += acc; else *dst = acc;
+  }
+}
+
+// Full loops: the same key-major layout in a plain double-buffered loop (no
+// second pass, small register footprint: four waves per SIMD hide the
+// exponentials behind the other waves' MFMAs).
+template <int D>
+__global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t N, MfmaArgs a) {
   constexpr int QT = 64;
   constexpr int DC = D / 16;
   constexpr int QS = D + 8;
-  constexpr int NR = LAZY ? 2 : 1;
   constexpr int NT = 512;                                  // 8 waves x 32 keys
   constexpr int KB = 256;                                  // key slots per workgroup
   constexpr int QCH = QT * D / 8;                          // 16-B chunks of one Q tile
   constexpr int PER = (QCH + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t sq[2][NR][QT * QS];
-  __shared__ __attribute__((aligned(16))) float sb[2][2][QT];   // [buf][prev|cur][row]
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][QT * QS];
+  __shared__ __attribute__((aligned(16))) float sb[2][QT];
   __shared__ int stok[2][QT];
   __shared__ int s_start;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
-  int sh, kblk;
-  if (!map_block(a.n_sh, a.n_keys_pad / KB, sh, kblk)) return;
-  kblk = a.n_keys_pad / KB - 1 - kblk;                    // early keys see the most rows: start them first
+  const int n_kblk = a.n_keys_pad / KB;
+  int sh, item;
+  if (!map_block(a.n_sh, n_kblk * a.col_chunks, sh, item)) return;
+  const int chunk = item % a.col_chunks;
+  const int kblk = n_kblk - 1 - item / a.col_chunks;      // early keys see the most rows: start them first
   const int s = sh / H, h = sh % H;
   const int t0 = kblk * KB + wave * 32;
   const int t = t0 + c;
@@ -521,12 +806,11 @@ __global__ __launch_bounds__(512, 1) void k_mfma_colmass(int32_t H, int32_t N, M
   const int kmax = kx[min(t0 + 31, a.n_keys - 1)];         // largest real key of this wave
   const float c1 = a.scale * kLog2e;
 
-  bf16x8 kf[NR][DC];
+  bf16x8 kf[DC];
+  {
+    const uint16_t* kb = a.kc + (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * hh;
 #pragma unroll
-  for (int w = 0; w < NR; ++w) {
-    const uint16_t* kb = (w ? a.kp : a.kc) + (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * hh;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) kf[w][dc] = *reinterpret_cast<const bf16x8*>(kb + dc * 16);
+    for (int dc = 0; dc < DC; ++dc) kf[dc] = *reinterpret_cast<const bf16x8*>(kb + dc * 16);
   }
   if (tid == 0) {                                          // first row that sees the block's first key
     const int kfirst = kx[kblk * KB];
@@ -535,49 +819,46 @@ __global__ __launch_bounds__(512, 1) void k_mfma_colmass(int32_t H, int32_t N, M
     s_start = lo;
   }
   __syncthreads();
-  const int r_begin = (s_start / QT) * QT;
-  const int n_tiles = (a.n_rows - r_begin + QT - 1) / QT;
+  const int c_lo = chunk * a.col_rows;
+  const int r_end = min(a.n_rows, c_lo + a.col_rows);
+  const int r_begin = max(c_lo, (s_start / QT) * QT);
+  const int n_tiles = r_end > r_begin ? (r_end - r_begin + QT - 1) / QT : 0;
   const int64_t rows_q = a.q_compact ? a.n_rows : N;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q_cur);
 
-  u32x4 pre[NR][PER];
-  float pre_b0 = INFINITY, pre_b1 = INFINITY;
+  u32x4 pre[PER];
+  float pre_b = INFINITY;
   int pre_tok = -1;
   auto gload = [&](int q0) {
 #pragma unroll
-    for (int w = 0; w < NR; ++w) {
-      const uint16_t* q = static_cast<const uint16_t*>(w ? a.q_prev : a.q_cur);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int ch = tid + NT * i;
-        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        const int rr = q0 + row;
-        pre[w][i] = u32x4{0, 0, 0, 0};
-        if (ch < QCH && rr < a.n_rows) {
-          const int64_t qr = a.q_compact ? rr : row_token(a, s, rr);
-          pre[w][i] = *reinterpret_cast<const u32x4*>(q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D + col);
-        }
+    for (int i = 0; i < PER; ++i) {
+      const int ch = tid + NT * i;
+      const int rr = q0 + ch / (D / 8);
+      pre[i] = u32x4{0, 0, 0, 0};
+      if (ch < QCH && rr < r_end) {
+        const int64_t qr = a.q_compact ? rr : row_token(a, s, rr);
+        pre[i] = *reinterpret_cast<const u32x4*>(q + ((static_cast<int64_t>(s) * rows_q + qr) * H + h) * D +
+                                                 (ch % (D / 8)) * 8);
       }
     }
     if (tid < QT) {
       const int rr = q0 + tid;
-      pre_b0 = pre_b1 = INFINITY;
+      pre_b = INFINITY;
       pre_tok = -1;
-      if (rr < a.n_rows) {
+      if (rr < r_end) {
         const float4 st = *reinterpret_cast<const float4*>(a.stat + (static_cast<int64_t>(sh) * a.n_rows + rr) * 4);
-        pre_b0 = st.x; pre_b1 = st.y; pre_tok = __float_as_int(st.w);
+        pre_b = st.y;
+        pre_tok = __float_as_int(st.w);
       }
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int w = 0; w < NR; ++w)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int ch = tid + NT * i;
-        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        if (ch < QCH) *reinterpret_cast<u32x4*>(&sq[buf][w][row * QS + col]) = pre[w][i];
-      }
-    if (tid < QT) { sb[buf][0][tid] = pre_b0; sb[buf][1][tid] = pre_b1; stok[buf][tid] = pre_tok; }
+    for (int i = 0; i < PER; ++i) {
+      const int ch = tid + NT * i;
+      if (ch < QCH) *reinterpret_cast<u32x4*>(&sq[buf][(ch / (D / 8)) * QS + (ch % (D / 8)) * 8]) = pre[i];
+    }
+    if (tid < QT) { sb[buf][tid] = pre_b; stok[buf][tid] = pre_tok; }
   };
   if (n_tiles > 0) {
     gload(r_begin);
@@ -590,32 +871,23 @@ __global__ __launch_bounds__(512, 1) void k_mfma_colmass(int32_t H, int32_t N, M
     const int q0 = r_begin + it * QT;
     if (it + 1 < n_tiles) gload(q0 + QT);
     // rows of this tile that every key of the wave precedes need no mask
-    const bool need_mask = stok[buf][0] < kmax || q0 + QT > a.n_rows;
+    const bool need_mask = stok[buf][0] < kmax || q0 + QT > r_end;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 sc = f32x16{}, sp = f32x16{};
+      f32x16 sc = f32x16{};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[buf][0][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
-        sc = mfma32(qa, kf[0][dc], sc);
-        if (LAZY) {
-          const bf16x8 qpa = *reinterpret_cast<const bf16x8*>(&sq[buf][NR - 1][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
-          sp = mfma32(qpa, kf[NR - 1][dc], sp);
-        }
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[buf][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
+        sc = mfma32(qa, kf[dc], sc);
       }
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int row0 = qb * 32 + 8 * q4 + 4 * hh;
-        const float4 bc = *reinterpret_cast<const float4*>(&sb[buf][1][row0]);
-        float4 bp = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (LAZY) bp = *reinterpret_cast<const float4*>(&sb[buf][0][row0]);
+        const float4 bc = *reinterpret_cast<const float4*>(&sb[buf][row0]);
         const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
-        const float bpv[4] = {bp.x, bp.y, bp.z, bp.w};
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
-          const int i = 4 * q4 + k4;
-          float v = ex2(sc[i] * c1 - bcv[k4]);
-          if (LAZY) v -= ex2(sp[i] * c1 - bpv[k4]);
+          float v = ex2(sc[4 * q4 + k4] * c1 - bcv[k4]);
           if (need_mask && kj > stok[buf][row0 + k4]) v = 0.0f;
           acc += v;
         }
@@ -625,10 +897,22 @@ __global__ __launch_bounds__(512, 1) void k_mfma_colmass(int32_t H, int32_t N, M
     __syncthreads();
   }
   acc += __shfl_xor(acc, 32, 64);
-  if (hh == 0 && t < a.n_keys) {
-    float* dst = a.colmass + static_cast<int64_t>(sh) * N + kj;
-    if (LAZY) *dst += acc; else *dst = acc;
-  }
+  if (hh != 0) return;
+  if (a.col_chunks > 1) a.col_part[(static_cast<int64_t>(chunk) * a.n_sh + sh) * a.n_keys_pad + t] = acc;
+  else if (t < a.n_keys) a.colmass[static_cast<int64_t>(sh) * N + kj] = acc;
+}
+
+// Sums the per-chunk partial column masses in chunk order.
+template <bool LAZY>
+__global__ __launch_bounds__(256) void k_colmass_reduce(int32_t N, MfmaArgs a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(a.n_sh) * a.n_keys_pad) return;
+  const int sh = static_cast<int>(i / a.n_keys_pad), t = static_cast<int>(i % a.n_keys_pad);
+  if (t >= a.n_keys) return;
+  float acc = 0.0f;
+  for (int ch = 0; ch < a.col_chunks; ++ch) acc += a.col_part[(static_cast<int64_t>(ch) * a.n_sh) * a.n_keys_pad + i];
+  float* dst = a.colmass + static_cast<int64_t>(sh) * N + a.kidx[i];
+  if (LAZY) *dst += acc; else *dst = acc;
 }
 
 // --------------------------------------------------------------------------- launch
@@ -685,19 +969,38 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows_per = lazy ? 128 : 256;
+  // 256-row workgroups with 64-key tiles when they fill the chip, else
+  // 128-row workgroups with 32-key tiles (more, lighter workgroups)
+  const bool big = static_cast<int64_t>(a.n_sh) * ((a.n_rows + 255) / 256) >= 512;
+  const int rows_per = big ? 256 : 128;
   dim3 gf(mapped_grid(a.n_sh, (a.n_rows + rows_per - 1) / rows_per));
   {
     TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
-    if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, true>), gf, dim3(512), 0, st, kv.H, kv.N, a);
-    else hipLaunchKernelGGL((k_mfma_fwd<D, false>), gf, dim3(512), 0, st, kv.H, kv.N, a);
+    if (big) {
+      if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, 8, 64, true>), gf, dim3(512), 0, st, kv.H, kv.N, a);
+      else hipLaunchKernelGGL((k_mfma_fwd<D, 8, 64, false>), gf, dim3(512), 0, st, kv.H, kv.N, a);
+    } else {
+      if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, 4, 32, true>), gf, dim3(256), 0, st, kv.H, kv.N, a);
+      else hipLaunchKernelGGL((k_mfma_fwd<D, 4, 32, false>), gf, dim3(256), 0, st, kv.H, kv.N, a);
+    }
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dim3 gc(mapped_grid(a.n_sh, a.n_keys_pad / 256));
+  a.col_chunks = p.col_chunks;
+  a.col_rows = p.col_rows;
+  a.col_part = reinterpret_cast<float*>(ws + p.off_part);
+  dim3 gc(mapped_grid(a.n_sh, a.n_keys_pad / 256 * a.col_chunks));
   {
     TimedLaunch t(st, lazy ? "mfma_colmass_lazy" : "mfma_colmass_full");
     if (lazy) hipLaunchKernelGGL((k_mfma_colmass<D, true>), gc, dim3(512), 0, st, kv.H, kv.N, a);
-    else hipLaunchKernelGGL((k_mfma_colmass<D, false>), gc, dim3(512), 0, st, kv.H, kv.N, a);
+    else hipLaunchKernelGGL((k_colmass_full_rows<D>), gc, dim3(512), 0, st, kv.H, kv.N, a);
+  }
+  if (a.col_chunks > 1) {
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t n = static_cast<int64_t>(a.n_sh) * a.n_keys_pad;
+    dim3 gr(static_cast<unsigned>((n + 255) / 256));
+    TimedLaunch t(st, "colmass_reduce");
+    if (lazy) hipLaunchKernelGGL((k_colmass_reduce<true>), gr, dim3(256), 0, st, kv.N, a);
+    else hipLaunchKernelGGL((k_colmass_reduce<false>), gr, dim3(256), 0, st, kv.N, a);
   }
   return hipGetLastError();
 }

@@ -4,6 +4,8 @@
 // The tiled bf16 MFMA path serves bf16 stores with at least kMfmaMinRows
 // active rows (prefill loops); the per-row path serves float32 stores and
 // calls with few rows per head (decode), where a 32-row MFMA tile would idle.
+#include <algorithm>
+
 #include "fl_launch.hpp"
 
 namespace fl {
@@ -33,7 +35,18 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     off = align256(off + sh * rows * 16);
     p.off_gather = off;
     off = align256(off + (lazy ? 4 : 2) * sh * kpad * D * 2 + sh * kpad * 4);
-    p.off_part = p.off_logit = off;
+    // enough column-mass workgroups to fill the chip: split the rows when
+    // the key blocks alone are few
+    const uint64_t kblk_wgs = sh * (kpad / 256);
+    const uint64_t row_tiles = (rows + 63) / 64;
+    uint64_t chunks = kblk_wgs >= 1024 ? 1 : (1024 + kblk_wgs - 1) / kblk_wgs;
+    chunks = std::max<uint64_t>(1, std::min(chunks, row_tiles));
+    p.col_rows = static_cast<int>((row_tiles + chunks - 1) / chunks * 64);
+    p.col_chunks = static_cast<int>((rows + p.col_rows - 1) / p.col_rows);
+    if (p.col_chunks < 1) p.col_chunks = 1;
+    p.off_part = off;
+    if (p.col_chunks > 1) off = align256(off + static_cast<uint64_t>(p.col_chunks) * sh * kpad * 4);
+    p.off_logit = off;
     p.off_total = off;
     return p;
   }

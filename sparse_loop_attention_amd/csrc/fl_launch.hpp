@@ -18,6 +18,8 @@ struct AttendPlan {
   int64_t rows;         // active rows per sequence
   int64_t keys;         // key slots per (sequence, head): n_keys (LAZY) or N (FULL)
   int splits;           // per-row path: key splits
+  int col_chunks;       // MFMA path: row ranges of the column-mass pass
+  int col_rows;         // rows per range (a multiple of 64)
   // byte offsets in the workspace
   uint64_t off_part, off_logit, off_stat, off_gather, off_total;
 };

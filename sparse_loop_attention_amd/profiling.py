@@ -1,0 +1,162 @@
+"""Profiler helpers: a copy kernel of known size for counter calibration, and
+text summaries of rocprofv3 output (kernel statistics, HBM traffic).
+
+    python -m sparse_loop_attention_amd.profiling copy [--gib 1] [--reps 3]
+        one torch copy of a known size per rep, to calibrate FETCH_SIZE and
+        WRITE_SIZE against bytes actually moved;
+    python -m sparse_loop_attention_amd.profiling stats STATS_CSV --title T --command C
+        markdown table of a `rocprofv3 --kernel-trace --stats` summary;
+    python -m sparse_loop_attention_amd.profiling traffic --fetch DIR --write DIR
+            --cal-fetch DIR --cal-write DIR --kernel SUBSTR --timer NAME
+            --workload NAME --command C [--cal-bytes B]
+        per-dispatch HBM bytes of one kernel from two `--pmc` runs, each
+        counter scaled by what it reads for the copy kernel; the result
+        carries a hash of the library sources so that a reader can tell
+        whether the kernel changed since the counters were taken.
+
+Traffic summaries are markdown files under profiles/ holding one line
+`traffic-record: {json}` that bench.py reads.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+
+def source_hash() -> str:
+    """Hash of everything the kernels are built from."""
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [os.path.join(ROOT, "include", "flashloop.h"),
+                                                                 os.path.join(PKG, "build.py")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic_records(profiles_dir: str):
+    """Every `traffic-record:` line of the markdown files under profiles/."""
+    out = []
+    for f in sorted(glob.glob(os.path.join(profiles_dir, "*.md"))):
+        with open(f) as fh:
+            for line in fh:
+                if line.startswith("traffic-record:"):
+                    rec = json.loads(line[len("traffic-record:"):])
+                    rec["file"] = os.path.relpath(f, ROOT)
+                    out.append(rec)
+    return out
+
+
+def _counter_csv(d: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(hits) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {len(hits)}")
+    return hits[0]
+
+
+def per_dispatch(d: str, counter: str, kernel_substr: str):
+    """Values of `counter` per dispatch of kernels whose name contains kernel_substr."""
+    vals = collections.defaultdict(float)
+    names = {}
+    with open(_counter_csv(d)) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter or kernel_substr not in r["Kernel_Name"]:
+                continue
+            k = int(r["Dispatch_Id"])
+            vals[k] += float(r["Counter_Value"])
+            names[k] = r["Kernel_Name"]
+    return [vals[k] for k in sorted(vals)], sorted(set(names.values()))
+
+
+def cmd_copy(a):
+    import torch
+    n = int(a.gib * (1 << 30)) // 4
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    x.fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(a.reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(f"copied {a.reps} x {n * 4} bytes", flush=True)
+
+
+def cmd_stats(a):
+    with open(a.stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    out = [f"# {a.title}", "", "Command (from the repository root, one MI355X):", "", "```", a.command, "```", "",
+           "| kernel | calls | total ms | avg us | % |", "|---|---|---|---|---|"]
+    for r in rows[:a.top]:
+        name = r["Name"]
+        if len(name) > 96:
+            name = name[:93] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {int(r['TotalDurationNs']) / 1e6:.3f} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    print("\n".join(out))
+
+
+def cmd_traffic(a):
+    fetch, names = per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    write, _ = per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    cal_f, _ = per_dispatch(a.cal_fetch, "FETCH_SIZE", a.cal_kernel)
+    cal_w, _ = per_dispatch(a.cal_write, "WRITE_SIZE", a.cal_kernel)
+    if not (fetch and write and cal_f and cal_w):
+        raise SystemExit("missing dispatches")
+    kib = 1024.0
+    # bytes moved per KiB the counter reports, from the copy of known size
+    f_factor = a.cal_bytes / (sum(cal_f) / len(cal_f) * kib)
+    w_factor = a.cal_bytes / (sum(cal_w) / len(cal_w) * kib)
+    f_avg = sum(fetch) / len(fetch)
+    w_avg = sum(write) / len(write)
+    traffic = f_avg * kib * f_factor + w_avg * kib * w_factor
+    rec = {"timer": a.timer, "workload": a.workload, "kernel": names[0] if names else a.kernel,
+           "dispatches": len(fetch), "fetch_kib": f_avg, "write_kib": w_avg,
+           "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "traffic_bytes": traffic, "source_hash": source_hash()}
+    out = [f"# HBM traffic of `{a.timer}` on the {a.workload} workload", "",
+           "Commands (from the repository root, one MI355X; each counter in a run of its own):", "", "```",
+           a.command, "```", "",
+           f"* kernel: `{rec['kernel'][:120]}`, {len(fetch)} dispatch(es) averaged",
+           f"* FETCH_SIZE {f_avg:.0f} KiB/dispatch x {f_factor:.3f} (copy calibration) = "
+           f"{f_avg * kib * f_factor / 1e6:.1f} MB",
+           f"* WRITE_SIZE {w_avg:.0f} KiB/dispatch x {w_factor:.3f} (copy calibration) = "
+           f"{w_avg * kib * w_factor / 1e6:.1f} MB",
+           f"* copy calibration: {a.cal_bytes} bytes read and written per dispatch; FETCH_SIZE reads "
+           f"{sum(cal_f) / len(cal_f):.0f} KiB, WRITE_SIZE {sum(cal_w) / len(cal_w):.0f} KiB",
+           f"* sources hash {rec['source_hash']} (the record is stale once the library sources change)",
+           "", "traffic-record: " + json.dumps(rec)]
+    print("\n".join(out))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--gib", type=float, default=1.0)
+    c.add_argument("--reps", type=int, default=3)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--top", type=int, default=16)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "cal_fetch", "cal_write", "kernel", "timer", "workload", "command"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--cal-kernel", default="copyBuffer")
+    t.add_argument("--cal-bytes", type=float, default=float(1 << 30))
+    a = ap.parse_args(argv)
+    {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()

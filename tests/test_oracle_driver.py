@@ -98,3 +98,31 @@ def test_chain_driver_matches_full_driver():
     for l in range(1, wl.n_loops + 1):
         for w in ("k", "v"):
             assert np.array_equal(store.reconstruct(w, l), st.store.reconstruct(w, l))
+
+
+def test_decode_with_every_key_equals_full_attention_each_loop():
+    """I1 applied loop after loop: when every key is selected, each lazy decode
+    loop keeps mass 1 and reproduces full attention of the new token over its
+    own version of the store."""
+    import dataclasses
+    from oracle import build_decode_context, run_decode_loops, to_working_dtype
+    wl = dataclasses.replace(configs.scaled(configs.DECODE, 96, n_seq=2, n_heads=2), n_keys=96)
+    syn = SyntheticLoops(wl)
+    ctx = {l: syn.context_active_sets(l)[1] for l in range(2, wl.n_loops + 1)}
+    data = {l: {k: v.copy() for k, v in x.items()} for l, x in SyntheticLoops(wl)}
+    store = build_decode_context(wl, 1, ctx, data)
+    out = run_decode_loops(wl, store, 1, data)
+    last = np.array([wl.n_tokens - 1])
+    for l in range(1, wl.n_loops + 1):
+        kh = to_working_dtype(store.reconstruct("k", l), wl.dtype)
+        vh = to_working_dtype(store.reconstruct("v", l), wl.dtype)
+        o, lse, c = full_attention(data[l]["q"][1], kh, vh, last)
+        np.testing.assert_allclose(out[l - 1]["o"], o, rtol=1e-9, atol=1e-9)
+        np.testing.assert_allclose(out[l - 1]["lse"], lse, rtol=1e-9, atol=1e-9)
+        np.testing.assert_allclose(out[l - 1]["colmass"], c, rtol=1e-9, atol=1e-12)
+        if l >= 2:
+            np.testing.assert_allclose(out[l - 1]["mass"], 1.0, rtol=1e-9)
+    # the token's own record sits in every layer, the context's only where it was active
+    for l in range(2, wl.n_loops + 1):
+        idx = np.concatenate([r.idx for r in store.layers[l]["k"]])
+        assert np.array_equal(np.sort(idx), np.union1d(ctx[l], last))
