@@ -106,8 +106,9 @@ def work_model(wl, run):
 
 KERNEL_WORK = {
     # kernel name -> (work key, unit, bound)
-    "rows_partial_full": ("attn_full_flops", "TFLOP/s", "alu"),
-    "rows_partial_lazy": ("attn_lazy_flops", "TFLOP/s", "alu"),
+    "rows_attend_full": ("attn_full_flops", "TFLOP/s", "alu"),
+    "rows_attend_lazy": ("attn_lazy_flops", "TFLOP/s", "alu"),
+    "rows_attend_commit_lazy": ("attn_lazy_flops", "TFLOP/s", "alu"),
     "mfma_fwd_full": ("attn_full_flops", "TFLOP/s", "mfma"),
     "mfma_fwd_lazy": ("attn_lazy_flops", "TFLOP/s", "mfma"),
     "mfma_colmass_full": ("colmass_full_flops", "TFLOP/s", "mfma"),
@@ -117,9 +118,9 @@ KERNEL_WORK = {
 }
 # the decode workload's per-row kernels stream the stored context: HBM-bound
 KERNEL_WORK_DECODE = dict(KERNEL_WORK, **{
-    "rows_partial_full": ("decode_full_bytes", "GB/s", "hbm"),
-    "rows_partial_commit_lazy": ("decode_lazy_bytes", "GB/s", "hbm"),
-    "rows_partial_lazy": ("decode_lazy_bytes", "GB/s", "hbm"),
+    "rows_attend_full": ("decode_full_bytes", "GB/s", "hbm"),
+    "rows_attend_commit_lazy": ("decode_lazy_bytes", "GB/s", "hbm"),
+    "rows_attend_lazy": ("decode_lazy_bytes", "GB/s", "hbm"),
 })
 
 
@@ -271,7 +272,7 @@ def main():
     value = work["rows"] * args.steps / elapsed
     lazy_ms = sum(ms for name, (ms, _) in timings.items()
                   if name.endswith("_lazy") or name in ("delta_norm", "topk", "commit_delta", "slot_map",
-                                                        "rows_combine", "rows_colmass")) / args.steps
+                                                        "rows_colmass", "colmass_reduce")) / args.steps
     out = {
         "metric": "active-token loop-steps/sec + KV GB/s; % of HBM / bf16-MFMA roofline",
         "value": value,

@@ -50,10 +50,9 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     p.off_total = off;
     return p;
   }
-  p.splits = static_cast<int>((p.keys + 63) / 64);      // keys per split (one wave) in the per-row path
+  p.splits = 0;
   p.off_part = off;
-  off = align256(off + sh * rows * p.splits * (4 + 2 * D) * 4);
-  p.off_logit = off;
+  p.off_logit = off;                                     // per-row path: logits of every row for the column pass
   off = align256(off + 2 * sh * rows * static_cast<uint64_t>(p.keys) * 4);
   p.off_stat = off;
   off = align256(off + sh * rows * 16);

@@ -17,7 +17,7 @@ struct AttendPlan {
   bool mfma;            // tiled bf16 MFMA path (else the per-row path)
   int64_t rows;         // active rows per sequence
   int64_t keys;         // key slots per (sequence, head): n_keys (LAZY) or N (FULL)
-  int splits;           // per-row path: key splits
+  int splits;           // unused (0)
   int col_chunks;       // MFMA path: row ranges of the column-mass pass
   int col_rows;         // rows per range (a multiple of 64)
   // byte offsets in the workspace
