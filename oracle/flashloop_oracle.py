@@ -44,6 +44,17 @@ Readings of points the page leaves open (all listed in the design doc):
      bfloat16 (nearest-even) for bf16 workloads, as the version-1 base already
      is; queries are used as given.  The int4 chain itself (R7, R8) stays in
      float32.
+Variants (off by default):
+  V1 formula="mixture", the other grammatical reading of keeping the group's
+     mass:  o_i = m_i * otilde_i + (1 - m_i) * o_prev_i  (no previous-loop
+     contribution a_i is needed).  The page gives no statistics for it; lse
+     and the column mass are updated exactly as under R4 (the selected
+     group's part of the row: lse = M + log Z - log m, c_j += p_ij - p'_ij on
+     the selected keys), so only the output formula differs.
+  V2 freeze_keys=True: the keys chosen for the first lazy loop are reused by
+     every later lazy loop ([FL/late] par. 4 calls the group that carries the
+     change small and stable) instead of being re-chosen from each loop's
+     column mass.
 The page prints no worked example of the mass-corrected formula (R4); it is
 pinned by invariants that follow from the mathematics (full attention when
 every key is selected, the dense loop when every row and key is, a fixed point
@@ -277,7 +288,7 @@ def full_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray
 
 
 def lazy_attention(q_cur, q_prev, k_prev, v_prev, k_cur, v_cur, o_prev, lse_prev, colmass_prev,
-                   rows: np.ndarray, keys: np.ndarray, chunk: int = 1024):
+                   rows: np.ndarray, keys: np.ndarray, chunk: int = 1024, formula: str = "column"):
     """Mass-corrected attention on the selected keys (O-5, readings R4-R6), float64.
 
     [FL/savings] par. 2: keys are selected from the previous loop's
@@ -288,10 +299,13 @@ def lazy_attention(q_cur, q_prev, k_prev, v_prev, k_cur, v_cur, o_prev, lse_prev
 
     q_cur, q_prev, o_prev: [n_rows, H, d] for the active rows ``rows``;
     lse_prev [n_rows, H]; k_*, v_* [N, H, d] reconstructions at versions l-1
-    and l; colmass_prev [H, N]; keys [H, nS] ascending.
+    and l; colmass_prev [H, N]; keys [H, nS] ascending.  formula "column"
+    is R4, "mixture" the variant V1 (module docstring).
     Returns (o [n_rows,H,d], lse [n_rows,H], colmass [H,N], m [n_rows,H],
     updated [n_rows,H] bool).
     """
+    if formula not in ("column", "mixture"):
+        raise ValueError(f"unknown formula {formula!r}")
     rows = np.asarray(rows, np.int64)
     n_rows, n_heads, d = q_cur.shape
     scale = 1.0 / math.sqrt(d)
@@ -325,7 +339,11 @@ def lazy_attention(q_cur, q_prev, k_prev, v_prev, k_cur, v_cur, o_prev, lse_prev
             ok = any_key & (m > 0)
             zs = np.where(ok, z, 1.0)
             otil = (e @ vc) / zs[:, None]
-            o_new = m[:, None] * otil + (o_prev[r0:r1, h, :].astype(F64) - a)
+            op = o_prev[r0:r1, h, :].astype(F64)
+            if formula == "column":
+                o_new = m[:, None] * otil + (op - a)
+            else:
+                o_new = m[:, None] * otil + (1.0 - m)[:, None] * op
             lse_new = mx + np.log(zs) - np.log(np.where(ok, m, 1.0))
             p = (m / zs)[:, None] * e
             o[r0:r1, h, :] = np.where(ok[:, None], o_new, o[r0:r1, h, :])
@@ -358,15 +376,17 @@ def _copy_state(st: LoopState) -> LoopState:
     return copy.deepcopy(st)
 
 
-def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: int = 0):
+def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: int = 0,
+                formula: str = "column", freeze_keys: bool = False):
     """Run loops 1..T of a prefill workload on one sequence.
 
     ``loops`` yields (l, dict(h, q, k, v)) with l = 0..T, arrays shaped
     [S, N, ...] (sequence ``seq`` is used); values are already in the
     working dtype.  Early loops run in full; later loops select tokens and
     keys, commit deltas of the active tokens and run mass-corrected attention
-    ([FL/savings] par. 1-3).  Returns the final LoopState (and, with
-    keep=True, the list of states after every loop).
+    ([FL/savings] par. 1-3).  ``formula`` and ``freeze_keys`` select the
+    variants V1 and V2 (module docstring).  Returns the final LoopState (and,
+    with keep=True, the list of states after every loop).
     """
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
     T = wl.n_loops if upto is None else upto
@@ -375,6 +395,7 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
     o = lse = colmass = None
     history = []
     st = None
+    frozen = None
     for l, x in loops:
         if l > T:
             break
@@ -394,7 +415,9 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
         else:
             u = token_scores(h_eff, h_prev_eff)
             rows = topk_ascending(u, wl.n_active(l))
-            keys = select_keys(colmass, wl.n_keys)
+            keys = frozen if frozen is not None else select_keys(colmass, wl.n_keys)
+            if freeze_keys:
+                frozen = keys
             # the shared block recomputes only the active rows; others carry
             h_prev_eff = h_eff.copy()
             h_eff[rows] = x["h"][seq][rows]
@@ -407,7 +430,7 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
             v_hat = to_working_dtype(store.reconstruct("v", l), wl.dtype)
             o_r, lse_r, colmass, m, upd = lazy_attention(
                 q_eff[rows], q_prev_rows, k_prev_hat, v_prev_hat, k_hat, v_hat,
-                o[rows], lse[rows], colmass, rows, keys)
+                o[rows], lse[rows], colmass, rows, keys, formula=formula)
             o[rows] = o_r
             lse[rows] = lse_r
             rec.update(rows=rows, keys=keys, scores=u, mass=m, updated=upd, records=recs)
@@ -466,18 +489,20 @@ def build_decode_context(wl, seq_index: int, ctx_sets: Dict[int, np.ndarray], lo
     return store
 
 
-def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data):
+def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data, formula: str = "column",
+                     freeze_keys: bool = False):
     """The T decode loops of the new token at position N-1 over a built
     context: loop 1 attends in full over version 1, loops l >= 2 select keys
     from that row's column mass, commit the token's own delta and run
-    mass-corrected attention over version l.  Returns a list of per-loop
-    dicts."""
+    mass-corrected attention over version l (variants V1, V2 as in
+    run_prefill).  Returns a list of per-loop dicts."""
     n = wl.n_tokens
     si = seq_index
     last = np.array([n - 1])
     out = []
     o = lse = colmass = None
     q_prev = None
+    frozen = None
     for l in range(1, wl.n_loops + 1):
         x = loops_data[l]
         q = x["q"][si]                       # [1, H, d]
@@ -488,21 +513,24 @@ def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data):
             o, lse, colmass = full_attention(q, kh, vh, last)
             out.append(dict(o=o.copy(), lse=lse.copy(), colmass=colmass.copy()))
         else:
-            keys = select_keys(colmass, wl.n_keys)
+            keys = frozen if frozen is not None else select_keys(colmass, wl.n_keys)
+            if freeze_keys:
+                frozen = keys
             kp = to_working_dtype(store.reconstruct("k", l - 1), wl.dtype)
             vp = to_working_dtype(store.reconstruct("v", l - 1), wl.dtype)
             kc = to_working_dtype(store.reconstruct("k", l), wl.dtype)
             vc = to_working_dtype(store.reconstruct("v", l), wl.dtype)
             o, lse, colmass, m, upd = lazy_attention(q, q_prev, kp, vp, kc, vc, o, lse, colmass,
-                                                     last, keys)
+                                                     last, keys, formula=formula)
             out.append(dict(o=o.copy(), lse=lse.copy(), colmass=colmass.copy(), keys=keys, mass=m))
         q_prev = q.copy()
     return out
 
 
-def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], loops_data):
+def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], loops_data,
+                   formula: str = "column", freeze_keys: bool = False):
     """Decode workload, one sequence (O-6): the stored context, then the T
     loops of the new token.  ``loops_data[l]`` holds dict(q [S,1,H,d],
     k [S,N,H,d], v [S,N,H,d]).  Returns (per-loop dicts, store)."""
     store = build_decode_context(wl, seq_index, ctx_sets, loops_data)
-    return run_decode_loops(wl, store, seq_index, loops_data), store
+    return run_decode_loops(wl, store, seq_index, loops_data, formula, freeze_keys), store
