@@ -39,6 +39,9 @@ def parse():
                     help="tiny | single_layer | long_prefill | decode | deep")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the host oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--quality", action="store_true",
+                    help="instead of timing: error of every lazy loop against the dense loop, for the output "
+                         "formulas and key policies")
     return ap.parse_args()
 
 
@@ -225,6 +228,50 @@ def cpu_baseline(wl, target_s):
                       f"{dt:.1f} s"}
 
 
+# --------------------------------------------------------------------------- quality
+def quality(wl):
+    """Lazy loops against the dense loop they stand in for.
+
+    After each lazy loop l the dense reference is full causal attention of
+    every row (the effective queries) over the store's version l, computed by
+    the library's full mode; the error is ||o - o_dense|| / ||o_dense|| over
+    all rows and over the loop's active rows, for each output formula and key
+    policy.
+    """
+    import torch
+    from sparse_loop_attention_amd import abi, driver
+    from sparse_loop_attention_amd.synth import SyntheticLoops
+    inputs = driver.upload_loops(wl, SyntheticLoops(wl), "cuda")
+    n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
+    o_ref = torch.empty(n, H, d, dtype=torch.float32, device="cuda")
+    lse_ref = torch.empty(n, H, dtype=torch.float32, device="cuda")
+    c_ref = torch.empty(H, n, dtype=torch.float32, device="cuda")
+    out = {}
+    for formula in ("column", "mixture"):
+        for freeze in (False, True):
+            run = driver.PrefillRun(wl, inputs, "cuda", formula=formula, freeze_keys=freeze)
+            rows = []
+            for l in range(1, wl.n_loops + 1):
+                if l <= wl.n_full:
+                    run.full_loop(l)
+                    cand = None
+                    continue
+                act = run.lazy_loop(l, cand)
+                cand = act
+                abi.attend(abi.attend_args(run.kv, abi.FL_ATTEND_FULL, l, run.q_eff, None, None, n, None,
+                                           o_ref, lse_ref, c_ref, run.workspace))
+                torch.cuda.synchronize()
+                diff = (run.o - o_ref).double()
+                ref = o_ref.double()
+                idx = act.long()
+                rows.append({"loop": l,
+                             "rel_err_all": float(diff.norm() / ref.norm()),
+                             "rel_err_active": float(diff[idx].norm() / ref[idx].norm())})
+            out[f"{formula}{'+frozen' if freeze else ''}"] = rows
+            print(f"[bench] quality {formula} frozen={freeze} done", file=sys.stderr, flush=True)
+    return out
+
+
 # --------------------------------------------------------------------------- main
 def main():
     args = parse()
@@ -241,6 +288,12 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     abi.lib()
     wl = configs.WORKLOADS[args.workload]
+    if args.quality:
+        if wl.decode:
+            raise SystemExit("--quality covers the prefill workloads")
+        print(json.dumps({"workload": wl.name, "metric": "relative L2 error of o against the dense loop",
+                          "data": "synthetic", "variants": quality(wl)}), flush=True)
+        return
     print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
     syn = SyntheticLoops(wl)
     if wl.decode:

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLASHLOOP_ABI_VERSION 1
+#define FLASHLOOP_ABI_VERSION 2
 #define FL_MAX_VERSIONS 32          /* versions 1..FL_MAX_VERSIONS */
 
 typedef enum {
@@ -56,6 +56,10 @@ typedef enum {
 typedef enum { FL_F32 = 0, FL_BF16 = 1 } fl_dtype;
 typedef enum { FL_SEL_TOKENS = 0, FL_SEL_KEYS = 1 } fl_select_mode;
 typedef enum { FL_ATTEND_FULL = 0, FL_ATTEND_LAZY = 1 } fl_attend_mode;
+typedef enum {
+  FL_FORMULA_COLUMN = 0,        /* o <- m*otilde + (o - a): the selected columns are updated */
+  FL_FORMULA_MIXTURE = 1        /* o <- m*otilde + (1 - m)*o */
+} fl_formula;
 typedef enum { FL_ROWS_BY_TOKEN = 0, FL_ROWS_COMPACT = 1 } fl_row_layout;
 
 /* ------------------------------------------------------------------------ */
@@ -178,6 +182,9 @@ fl_status flashloop_select(const fl_select_args* args, void* stream);
 /*   lse_i <- M + log Z - log m_i; colmass[h][j] += sum_i (p_ij - p'_ij) for   */
 /*   selected j, with p_ij = exp(s_ij - lse_i(new)).  Rows with empty S_i or */
 /*   m_i == 0 keep o and lse and add nothing to colmass.                     */
+/* formula FL_FORMULA_MIXTURE (LAZY only) replaces the output update by the  */
+/* other reading of the group keeping its mass, o_i <- m_i*otilde_i +        */
+/* (1 - m_i)*o_i (a_i is not needed); lse and colmass are updated as above.  */
 /* o, lse and colmass are updated in place; rows that are not active are not */
 /* read or written.  Any key tensor entry not described above is untouched.  */
 /* Fused commit (LAZY, fuse_commit != 0; paragraph 4: the KV update and      */
@@ -212,6 +219,7 @@ typedef struct {
   int32_t kv_layout;            /* fl_row_layout of k_new / v_new */
   int32_t commit_slot_base;     /* slot_base + n_active <= layer_cap[version] */
   int32_t commit_reset;         /* reset_map of the commit */
+  int32_t formula;              /* fl_formula (LAZY); FULL requires FL_FORMULA_COLUMN */
 } fl_attend_args;
 
 uint64_t  flashloop_attend_workspace_bytes(const fl_attend_args* args);

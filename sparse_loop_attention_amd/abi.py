@@ -19,6 +19,8 @@ MAX_VERSIONS = 32
 
 FL_OK, FL_ERR_ARG, FL_ERR_UNSUPPORTED, FL_ERR_WORKSPACE, FL_ERR_HIP = range(5)
 FL_F32, FL_BF16 = 0, 1
+FL_FORMULA_COLUMN, FL_FORMULA_MIXTURE = 0, 1
+FORMULAS = {"column": FL_FORMULA_COLUMN, "mixture": FL_FORMULA_MIXTURE}
 FL_SEL_TOKENS, FL_SEL_KEYS = 0, 1
 FL_ATTEND_FULL, FL_ATTEND_LAZY = 0, 1
 FL_ROWS_BY_TOKEN, FL_ROWS_COMPACT = 0, 1
@@ -62,7 +64,7 @@ class fl_attend_args(C.Structure):
                 ("n_keys", C.c_int32), ("o", C.c_void_p), ("lse", C.c_void_p), ("o_layout", C.c_int32),
                 ("colmass", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64),
                 ("fuse_commit", C.c_int32), ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("kv_layout", C.c_int32),
-                ("commit_slot_base", C.c_int32), ("commit_reset", C.c_int32)]
+                ("commit_slot_base", C.c_int32), ("commit_reset", C.c_int32), ("formula", C.c_int32)]
 
 
 class FlashLoopError(RuntimeError):
@@ -218,9 +220,10 @@ def select_keys(key_scores: torch.Tensor, k: int, out_idx: torch.Tensor, stream=
 # --------------------------------------------------------------------------- attend
 def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx, n_active: int,
                 key_idx, o, lse, colmass, workspace=None, q_compact=False, o_compact=False,
-                commit=None) -> fl_attend_args:
+                commit=None, formula: str = "column") -> fl_attend_args:
     """`commit` = dict(k_new=, v_new=, compact=False, slot_base=0, reset=True) fuses the
-    KV commit of this loop into the call (LAZY only)."""
+    KV commit of this loop into the call (LAZY only); `formula` is "column" or
+    "mixture" (LAZY only)."""
     a = fl_attend_args()
     a.mode, a.kv, a.version = mode, C.pointer(kv.desc), version
     a.q_cur, a.q_prev = _ptr(q_cur), _ptr(q_prev)
@@ -238,6 +241,7 @@ def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx,
         a.kv_layout = FL_ROWS_COMPACT if commit.get("compact", False) else FL_ROWS_BY_TOKEN
         a.commit_slot_base = commit.get("slot_base", 0)
         a.commit_reset = int(commit.get("reset", True))
+    a.formula = FORMULAS[formula]
     return a
 
 

@@ -205,6 +205,8 @@ static fl_status check_attend(const fl_attend_args* a, fl_kv_layout* lay) {
   if (!aligned(a->o, 16)) return fail(FL_ERR_ARG, "attend: o must be 16-byte aligned");
   if (a->q_layout != FL_ROWS_BY_TOKEN && a->q_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: q_layout");
   if (a->o_layout != FL_ROWS_BY_TOKEN && a->o_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: o_layout");
+  if (a->formula != FL_FORMULA_COLUMN && !(lazy && a->formula == FL_FORMULA_MIXTURE))
+    return fail(FL_ERR_ARG, "attend: formula %d (FULL needs FL_FORMULA_COLUMN)", a->formula);
   if (a->fuse_commit) {
     if (!lazy) return fail(FL_ERR_ARG, "attend: fuse_commit needs LAZY mode");
     if (!a->k_new || !a->v_new || !aligned(a->k_new, 16) || !aligned(a->v_new, 16))

@@ -264,7 +264,8 @@ struct FwdTiles {
   static constexpr int KPER = (KCH + NT - 1) / NT, VPER = (VCH + NT - 1) / NT;
 };
 
-template <int D, int NW, int KT_, bool FIXED>
+// NOPV: the pass needs only the probability mass (no V tiles, no PV product).
+template <int D, int NW, int KT_, bool FIXED, bool NOPV = false>
 __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const uint16_t* kbase, const uint16_t* vbase,
                                          const int32_t* kx, uint16_t (*sk)[KT_ * FwdTiles<D, NW, KT_>::KS],
                                          uint16_t (*sv)[D * FwdTiles<D, NW, KT_>::VS], int (*skx)[KT_],
@@ -414,11 +415,11 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
   float alpha_prev = 1.0f;
   auto step = [&](int t, f32x16 (&Sc)[NKB], f32x16 (&Sn)[NKB], bool first) {
     gload_k(min(t + 2, n_tiles - 1));
-    gload_v(t);
+    if (!NOPV) gload_v(t);
     if (resc_prev) rescale(alpha_prev);
     mask(t, Sc);
     qk((t + 1) & 1, Sn);
-    if (!first) pv_acc((t + 1) & 1, P);
+    if (!NOPV && !first) pv_acc((t + 1) & 1, P);
     float alpha = 1.0f;
     const bool resc = softmax(Sc, P, alpha);
     // interleave: operand reads run 4 ahead; every MFMA is followed by
@@ -426,7 +427,7 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
 #pragma unroll
     for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-    for (int i = 0; i < NKB * DC + NCC * DB; ++i) {
+    for (int i = 0; i < NKB * DC + (NOPV ? 0 : NCC * DB); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
@@ -436,7 +437,7 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) asm volatile("" ::"v"(P[cc]));
     sstore_k(t & 1, t + 2);
-    sstore_v(t & 1);
+    if (!NOPV) sstore_v(t & 1);
     __syncthreads();
     resc_prev = resc;
     alpha_prev = alpha;
@@ -448,11 +449,14 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     step(t + 1, S0, S1, false);
   }
   if (t < n_tiles) step(t, S1, S0, false);
+  if (NOPV) return;
   if (resc_prev) rescale(alpha_prev);                      // PV of the last tile
   pv_acc((n_tiles - 1) & 1, P);
 }
 
-template <int D, int NW, int KT_, bool LAZY>
+// MIX (lazy only): the mixture formula o = m*otilde + (1-m)*o_prev; the
+// previous-loop pass then needs only the mass.
+template <int D, int NW, int KT_, bool LAZY, bool MIX = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2))) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
   using T = FwdTiles<D, NW, KT_>;
   constexpr int KT = T::KT;
@@ -533,11 +537,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   // at once, and pass 2 (current loop, online softmax) adds m * otilde.
   const float b_prev = vrow ? a.lse[(static_cast<int64_t>(s) * rows_o + orow) * H + h] * kLog2e : 0.0f;
   load_q(a.q_prev, qf);
-  fwd_pass<D, NW, KT_, true>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok, tok_first, tok_last,
-                        blk_full, c1, b_prev, acc, ref, lsum);
+  fwd_pass<D, NW, KT_, true, MIX>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok, tok_first,
+                                  tok_last, blk_full, c1, b_prev, acc, ref, lsum);
   const float m = lsum + __shfl_xor(lsum, 32, 64);
   const bool valid = vrow && m > 0.0f;
-  if (valid) {
+  if (valid && MIX) {
+    const float keep = 1.0f - m;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dim = db * 32 + 8 * q4 + 4 * hh;
+        float4 op = *reinterpret_cast<const float4*>(o_ptr + dim);
+        op.x *= keep; op.y *= keep; op.z *= keep; op.w *= keep;
+        *reinterpret_cast<float4*>(o_ptr + dim) = op;
+      }
+  } else if (valid) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -976,13 +991,16 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   dim3 gf(mapped_grid(a.n_sh, (a.n_rows + rows_per - 1) / rows_per));
   {
     TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
-    if (big) {
-      if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, 8, 64, true>), gf, dim3(512), 0, st, kv.H, kv.N, a);
-      else hipLaunchKernelGGL((k_mfma_fwd<D, 8, 64, false>), gf, dim3(512), 0, st, kv.H, kv.N, a);
-    } else {
-      if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, 4, 32, true>), gf, dim3(256), 0, st, kv.H, kv.N, a);
-      else hipLaunchKernelGGL((k_mfma_fwd<D, 4, 32, false>), gf, dim3(256), 0, st, kv.H, kv.N, a);
-    }
+    const bool mix = lazy && x.formula == FL_FORMULA_MIXTURE;
+#define FL_FWD(NWV, KTV, THREADS)                                                                           \
+  do {                                                                                                       \
+    if (mix) hipLaunchKernelGGL((k_mfma_fwd<D, NWV, KTV, true, true>), gf, dim3(THREADS), 0, st, kv.H, kv.N, a); \
+    else if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, NWV, KTV, true>), gf, dim3(THREADS), 0, st, kv.H, kv.N, a); \
+    else hipLaunchKernelGGL((k_mfma_fwd<D, NWV, KTV, false>), gf, dim3(THREADS), 0, st, kv.H, kv.N, a);          \
+  } while (0)
+    if (big) FL_FWD(8, 64, 512);
+    else FL_FWD(4, 32, 256);
+#undef FL_FWD
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.col_chunks = p.col_chunks;

@@ -36,6 +36,7 @@ struct RowArgs {
   int32_t version;
   float scale;              // 1/sqrt(d)
   int64_t key_slots;        // logit row length (n_keys or N)
+  int32_t mixture;          // LAZY: o = m*otilde + (1-m)*o_prev instead of m*otilde + o_prev - a
   float* logit;             // [2][sh][rows][key_slots]
   float* stat;              // [sh][rows][4] = lse_prev, lse_new, valid, -
 };
@@ -76,7 +77,6 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a
   __shared__ i32x4 s_sl[kRowWaves][64];
   __shared__ float s_mzm[kRowWaves][3];
   __shared__ float s_acc[kRowWaves][2][128];
-  __shared__ float s_fin[4];
 
   if (FUSE && wave == 0) {
     // this row's records of layer `version` (groups 0, 1: K, V)
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a
       av += s_acc[w][1][tid];
     }
     if (!LAZY) o_row[tid] = ov / Zt;
-    else if (valid) o_row[tid] = fmaf(mt / Zt, ov, o_row[tid] - av);
+    else if (valid) o_row[tid] = fmaf(mt / Zt, ov, a.mixture ? (1.0f - mt) * o_row[tid] : o_row[tid] - av);
   }
   const float lnew = LAZY ? (valid ? Mt + __logf(Zt) - __logf(mt) : lse_prev) : Mt + __logf(Zt);
   if (tid == 0) {
@@ -353,6 +353,7 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
   a.version = x.version;
   a.scale = 1.0f / sqrtf(static_cast<float>(kv.d));
   a.key_slots = p.keys;
+  a.mixture = x.formula == FL_FORMULA_MIXTURE;
   uint8_t* ws = static_cast<uint8_t*>(x.workspace);
   a.logit = reinterpret_cast<float*>(ws + p.off_logit);
   a.stat = reinterpret_cast<float*>(ws + p.off_stat);

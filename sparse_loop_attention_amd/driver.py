@@ -60,9 +60,13 @@ class LoopRecord:
 class PrefillRun:
     """GPU state of one prefill workload (n_seq = 1) and its loop sequence."""
 
-    def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], device="cuda", fuse: bool = True):
+    def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], device="cuda", fuse: bool = True,
+                 formula: str = "column", freeze_keys: bool = False):
+        """formula "column" (default) or "mixture"; freeze_keys reuses the first
+        lazy loop's key group in every later lazy loop."""
         assert wl.n_seq == 1 and not wl.decode
         self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
+        self.formula, self.freeze_keys = formula, freeze_keys
         n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
         dt = torch_dtype(wl)
         self.kv = abi.KVStore(1, H, d, n, wl.n_loops, dt, wl.layer_caps(), device)
@@ -99,7 +103,7 @@ class PrefillRun:
         commit = dict(k_new=self.inp[l]["k"], v_new=self.inp[l]["v"]) if self.fuse else None
         return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, self.q_cur_rows[:na], self.q_prev_rows[:na],
                                self.act[l], na, self.keys_l[l], self.o, self.lse, self.colmass, self.workspace,
-                               q_compact=True, commit=commit)
+                               q_compact=True, commit=commit, formula=self.formula)
 
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
@@ -114,7 +118,11 @@ class PrefillRun:
         wl, x = self.wl, self.inp[l]
         act, na = self.act[l], wl.n_active(l)
         abi.select_tokens(self.h_eff, self.h_prev, na, self.scores, act, cand)
-        abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
+        first = wl.n_full + 1
+        if self.freeze_keys and l > first:
+            self.keys_l[l].copy_(self.keys_l[first])
+        else:
+            abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
         # model stand-in: the shared block recomputes the active rows only
         idx = act.long()
         self.h_prev.index_copy_(0, idx, self.h_eff.index_select(0, idx))
@@ -154,9 +162,10 @@ class DecodeRun:
     """Decode workload: n_seq sequences, one new query per sequence and loop."""
 
     def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], ctx_sets: Dict[int, List[np.ndarray]],
-                 device="cuda", fuse: bool = True):
+                 device="cuda", fuse: bool = True, formula: str = "column", freeze_keys: bool = False):
         assert wl.decode
         self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
+        self.formula, self.freeze_keys = formula, freeze_keys
         S, n, H, d = wl.n_seq, wl.n_tokens, wl.n_heads, wl.head_dim
         dt = torch_dtype(wl)
         self.kv = abi.KVStore(S, H, d, n, wl.n_loops, dt, wl.layer_caps(), device)
@@ -187,7 +196,7 @@ class DecodeRun:
             commit = dict(k_new=x["k"], v_new=x["v"], slot_base=self.ctx[l].shape[1], reset=False)
         return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, x["q"], self.inp[l - 1]["q"], self.last, 1,
                                self.keys, self.o, self.lse, self.colmass, ws, q_compact=True, o_compact=True,
-                               commit=commit)
+                               commit=commit, formula=self.formula)
 
     def build_context(self) -> None:
         for l in range(1, self.wl.n_loops + 1):
@@ -199,7 +208,7 @@ class DecodeRun:
         slot_base = 0 if l == 1 else self.ctx[l].shape[1]
         if l == 1 or not self.fuse:
             abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False)
-        if l >= 2:
+        if l >= 2 and not (self.freeze_keys and l > 2):
             abi.select_keys(self.colmass, wl.n_keys, self.keys)
         abi.attend(self._args(l, self.workspace))
 

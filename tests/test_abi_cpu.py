@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(abi.EXPORTS)
-    assert abi.abi_version() == 1
+    assert abi.abi_version() == 2
 
 
 def _desc(wl):
@@ -143,3 +143,21 @@ def test_attend_validation(L):
     assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_WORKSPACE
     a.mode, a.version, a.active_idx, a.n_active = abi.FL_ATTEND_FULL, 1, None, 10
     assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG          # NULL rows need n_active == N
+
+
+def test_attend_formula_validation(L):
+    d = _desc(configs.TINY)
+    d.arena, d.arena_bytes = 256, abi.kv_arena_bytes(d)
+    a = abi.fl_attend_args()
+    a.kv = C.pointer(d)
+    a.mode, a.version, a.n_active = abi.FL_ATTEND_LAZY, 2, 0
+    a.q_cur = a.q_prev = a.o = a.lse = a.colmass = 256
+    a.key_idx, a.n_keys = 256, 26
+    a.formula = abi.FL_FORMULA_MIXTURE
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_OK              # LAZY accepts the mixture
+    a.formula = 7
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG
+    assert b"formula" in L.flashloop_last_error()
+    a.mode, a.version, a.active_idx, a.n_active = abi.FL_ATTEND_FULL, 1, None, 256
+    a.formula = abi.FL_FORMULA_MIXTURE
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG          # FULL: column only

@@ -145,3 +145,47 @@ def test_fused_commit_decode_equals_unfused():
         assert torch.equal(aa[k], ab[k]), k
     for l in range(wl.n_loops):
         assert torch.equal(ra[l].o, rb[l].o) and torch.equal(ra[l].colmass, rb[l].colmass)
+
+
+@pytest.mark.parametrize("formula,freeze", [("mixture", False), ("column", True), ("mixture", True)])
+@pytest.mark.parametrize("wl", [configs.TINY, configs.scaled(configs.SINGLE_LAYER, 512, n_heads=4),
+                                configs.scaled(configs.DEEP, 320, n_heads=3)],
+                         ids=["tiny", "single_layer_512", "deep_320"])
+def test_prefill_variants_match_oracle(wl, formula, freeze):
+    """The mixture formula and frozen key groups against the oracle's variants."""
+    inputs = driver.upload_loops(wl, SyntheticLoops(wl), DEV)
+    run = driver.PrefillRun(wl, inputs, DEV, formula=formula, freeze_keys=freeze)
+    recs = run.run(record=True)
+    torch.cuda.synchronize()
+    _, hist = oracle.run_prefill(wl, iter(SyntheticLoops(wl)), keep=True, formula=formula, freeze_keys=freeze)
+    for l in range(1, wl.n_loops + 1):
+        g, r = recs[l - 1], hist[l - 1]
+        if l > wl.n_full:
+            assert np.array_equal(g.rows.cpu().numpy(), r.records[l]["rows"]), f"loop {l}: token sets differ"
+            assert np.array_equal(g.keys.cpu().numpy(), r.records[l]["keys"]), f"loop {l}: key sets differ"
+        _check_o(g.o.cpu().numpy(), r.o, f"loop {l} o")
+        _check_o(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")
+        _check_o(g.colmass.cpu().numpy(), r.colmass, f"loop {l} colmass")
+
+
+@pytest.mark.parametrize("formula,freeze", [("mixture", False), ("column", True)])
+def test_decode_variants_match_oracle(formula, freeze):
+    wl = configs.scaled(configs.DECODE, 600, n_seq=2, n_heads=2)
+    syn = SyntheticLoops(wl)
+    ctx_sets = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)}
+    inputs = driver.upload_loops(wl, syn, DEV)
+    run = driver.DecodeRun(wl, inputs, ctx_sets, DEV, formula=formula, freeze_keys=freeze)
+    run.build_context()
+    recs = run.run(record=True)
+    torch.cuda.synchronize()
+    data = {l: {k: v.copy() for k, v in x.items()} for l, x in SyntheticLoops(wl)}
+    for s in range(wl.n_seq):
+        ref, _ = oracle.run_decode_seq(wl, None, s, {l: ctx_sets[l][s] for l in ctx_sets}, data,
+                                       formula=formula, freeze_keys=freeze)
+        for l in range(1, wl.n_loops + 1):
+            g, r = recs[l - 1], ref[l - 1]
+            if l >= 2:
+                assert np.array_equal(g.keys.cpu().numpy()[s], r["keys"]), f"seq {s} loop {l} keys"
+            _check_o(g.o.cpu().numpy()[s], r["o"], f"seq {s} loop {l} o")
+            _check_o(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
+            _check_o(g.colmass.cpu().numpy()[s], r["colmass"], f"seq {s} loop {l} colmass")
