@@ -112,6 +112,7 @@ KERNEL_WORK = {
     "rows_attend_full": ("attn_full_flops", "TFLOP/s", "alu"),
     "rows_attend_lazy": ("attn_lazy_flops", "TFLOP/s", "alu"),
     "rows_attend_commit_lazy": ("attn_lazy_flops", "TFLOP/s", "alu"),
+    "rows_colmass": ("colmass_full_flops", "TFLOP/s", "alu"),
     "mfma_fwd_full": ("attn_full_flops", "TFLOP/s", "mfma"),
     "mfma_fwd_lazy": ("attn_lazy_flops", "TFLOP/s", "mfma"),
     "mfma_colmass_full": ("colmass_full_flops", "TFLOP/s", "mfma"),

@@ -6,26 +6,27 @@
 // the chosen group's previous probability mass) and paragraph 4 (the selected
 // data is gathered into dense buffers so that sparsity turns into speed).
 //
-// Three launches per call:
+// Launches per call:
 //   gather   - walks the base+delta chain of every key slot (all N keys in a
 //              full loop, the selected keys in a lazy loop) once, and writes
 //              dense tiles: K^ rows [sh][slot][d] in bf16 and V^ transposed
 //              [sh][d][slot] as fp16 holding the bf16-rounded values (keys
 //              permuted inside each 16-key chunk so that an MFMA operand is
 //              one 16-byte LDS read), plus the key positions; a lazy loop
-//              gathers versions v-1 and v;
-//   fwd      - one workgroup per 128 (full) or 64 (lazy) query rows of one
-//              head.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 keeps every query
-//              in one lane, so the row softmax needs a single cross-half
-//              exchange; P^T feeds the PV product straight from the
-//              accumulators.  In a lazy loop waves pair up: one computes the
-//              current softmax over the selected keys, its partner the
-//              previous loop's probabilities with the fixed normaliser lse_prev
-//              (mass m and contribution a); they combine through LDS into
-//              o = m*otilde + o_prev - a;
-//   colmass  - key-major: one workgroup per 128 key slots, streaming the
-//              query tiles, S = Q K^T with keys in lanes so that the column
-//              sums are lane-local; fixed order, no atomics.
+//              gathers versions v-1 and v, and with a fused commit extra
+//              blocks write this loop's records;
+//   fwd      - one workgroup per 256 (or, for small calls, 128) query rows of
+//              one head.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 keeps every
+//              query in one lane pair, so the row softmax needs a single
+//              cross-half exchange; P^T feeds the PV product straight from
+//              the accumulators.  A lazy loop makes two passes: the previous
+//              loop's probabilities with the fixed normaliser lse_prev (mass
+//              m and contribution a, o <- o_prev - a), then the current
+//              softmax over the selected keys (o <- o + m * otilde);
+//   colmass  - key-major: one workgroup per 256 key slots (and a row range),
+//              streaming the query tiles, S = Q K^T with keys in lanes so that
+//              the column sums are lane-local; fixed order, no atomics (row
+//              ranges are added by a small reduction kernel).
 #include <climits>
 
 #include "fl_common.hpp"

@@ -308,14 +308,18 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a
   }
 }
 
+// 64 key slots per workgroup, the rows split over its 4 waves (wave w takes
+// rows lo+w, lo+w+4, ...); the 4 partial sums are added in wave order.
 template <bool LAZY>
-__global__ __launch_bounds__(64) void k_rows_colmass(int32_t n_seq, int32_t H, int32_t N, RowArgs a) {
+__global__ __launch_bounds__(256) void k_rows_colmass(int32_t n_seq, int32_t H, int32_t N, RowArgs a) {
+  __shared__ float s_part[4][64];
   const int sh = blockIdx.y;
-  const int t = blockIdx.x * 64 + threadIdx.x;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 64 + lane;
   const int s = sh / H;
   const int64_t slots = LAZY ? a.n_keys : N;
-  if (t >= slots) return;
-  const int j = LAZY ? a.keys[static_cast<int64_t>(sh) * a.n_keys + t] : t;
+  const bool live = t < slots;
+  const int j = !live ? 0 : LAZY ? a.keys[static_cast<int64_t>(sh) * a.n_keys + t] : t;
   const int32_t* act = a.act ? a.act + static_cast<int64_t>(s) * a.n_act : nullptr;
   const float* lg_cur = a.logit + static_cast<int64_t>(sh) * a.n_act * a.key_slots;
   const float* lg_prev = a.logit + (static_cast<int64_t>(n_seq) * H + sh) * a.n_act * a.key_slots;
@@ -331,14 +335,20 @@ __global__ __launch_bounds__(64) void k_rows_colmass(int32_t n_seq, int32_t H, i
     }
   }
   float acc = 0.0f;
-  for (int r = lo; r < a.n_act; ++r) {
-    const float* sr = st + r * 4;
-    if (sr[2] == 0.0f) continue;
-    const int64_t at = static_cast<int64_t>(r) * a.key_slots + t;
-    float v = __expf(lg_cur[at] - sr[1]);
-    if (LAZY) v -= __expf(lg_prev[at] - sr[0]);
-    acc += v;
+  if (live) {
+    for (int r = lo + w; r < a.n_act; r += 4) {
+      const float4 sr = *reinterpret_cast<const float4*>(st + r * 4);
+      if (sr.z == 0.0f) continue;
+      const int64_t at = static_cast<int64_t>(r) * a.key_slots + t;
+      float v = __expf(lg_cur[at] - sr.y);
+      if (LAZY) v -= __expf(lg_prev[at] - sr.x);
+      acc += v;
+    }
   }
+  s_part[w][lane] = acc;
+  __syncthreads();
+  if (w != 0 || !live) return;
+  acc = ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
   float* c = a.colmass + static_cast<int64_t>(sh) * N + j;
   if (LAZY) *c += acc; else *c = acc;
 }
@@ -395,8 +405,8 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
   if (e != hipSuccess || col) return e;
   dim3 g3(static_cast<unsigned>((p.keys + 63) / 64), sh);
   TimedLaunch t(st, "rows_colmass");
-  if (lazy) hipLaunchKernelGGL(k_rows_colmass<true>, g3, dim3(64), 0, st, kv.n_seq, kv.H, kv.N, a);
-  else hipLaunchKernelGGL(k_rows_colmass<false>, g3, dim3(64), 0, st, kv.n_seq, kv.H, kv.N, a);
+  if (lazy) hipLaunchKernelGGL(k_rows_colmass<true>, g3, dim3(256), 0, st, kv.n_seq, kv.H, kv.N, a);
+  else hipLaunchKernelGGL(k_rows_colmass<false>, g3, dim3(256), 0, st, kv.n_seq, kv.H, kv.N, a);
   return hipGetLastError();
 }
 
