@@ -260,20 +260,29 @@ template <int D, int NW, int KT_>
 struct FwdTiles {
   static constexpr int KT = KT_;                          // keys per tile: 32 or 64
   static constexpr int NT = 64 * NW;
-  static constexpr int KS = D + 8, VS = KT + 8;          // padded LDS row strides
+  static constexpr int KS = D + 8, VS = KT + 8;          // padded LDS row strides (staged through registers)
   static constexpr int KCH = KT * D / 8, VCH = D * KT / 8;
   static constexpr int KPER = (KCH + NT - 1) / NT, VPER = (VCH + NT - 1) / NT;
+  // Tiles are staged through registers: the loads of iteration t are stored
+  // to LDS at its end, so they overlap its MFMA work; padded rows keep the
+  // MFMA operand reads free of bank conflicts.
+  static constexpr int RK = D / 8, RV = KT / 8;          // data chunks per K row, per V^T row
+  static constexpr int KBUF = KT * KS, VBUF = D * VS;    // buffer elements
+  __device__ static __forceinline__ int k_off(int row, int lc) { return row * KS + (lc << 3); }
+  __device__ static __forceinline__ int v_off(int row, int lc) { return row * VS + (lc << 3); }
 };
+
 
 // NOPV: the pass needs only the probability mass (no V tiles, no PV product).
 template <int D, int NW, int KT_, bool FIXED, bool NOPV = false>
 __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const uint16_t* kbase, const uint16_t* vbase,
-                                         const int32_t* kx, uint16_t (*sk)[KT_ * FwdTiles<D, NW, KT_>::KS],
-                                         uint16_t (*sv)[D * FwdTiles<D, NW, KT_>::VS], int (*skx)[KT_],
+                                         const int32_t* kx, uint16_t (*sk)[FwdTiles<D, NW, KT_>::KBUF],
+                                         uint16_t (*sv)[FwdTiles<D, NW, KT_>::VBUF], int (*skx)[KT_],
                                          const bf16x8 (&qf)[D / 16], int tok, int tok_first, int tok_last, bool blk_full,
                                          float c1, float b_fix, f32x16 (&acc)[D / 32], float& ref, float& lsum) {
   using T = FwdTiles<D, NW, KT_>;
   constexpr int KT = T::KT, NT = T::NT, KS = T::KS, VS = T::VS;
+  (void)NT;
   constexpr int DC = D / 16, DB = D / 32;
   constexpr int NKB = KT / 32, NCC = KT / 16;             // 32-key logit blocks, 16-key PV chunks
   const int tid = threadIdx.x, lane = tid & 63;
@@ -283,47 +292,49 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
   ref = -INFINITY;
   lsum = 0.0f;
 
-  u32x4 pk[T::KPER], pv[T::VPER];
   int pkx = INT_MAX;
-  auto gload_k = [&](int tile) {
+  constexpr int KPER = (KT * D / 8 + NT - 1) / NT, VPER = (D * KT / 8 + NT - 1) / NT;
+  u32x4 pk[KPER], pv[VPER];
+  int kbuf_pending = 0, vbuf_pending = 0;             // LDS buffers the staged tiles go to
+  auto load_k = [&](int buf, int tile) {
 #pragma unroll
-    for (int i = 0; i < T::KPER; ++i) {
-      const int q = min(tid + NT * i, T::KCH - 1);           // a partial last round repeats the last chunk
-      pk[i] = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(tile * KT + q / (D / 8)) * D +
-                                              (q % (D / 8)) * 8);
+    for (int i = 0; i < KPER; ++i) {
+      const int q = min(tid + NT * i, KT * D / 8 - 1);
+      pk[i] = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(tile * KT + q / (D / 8)) * D + (q % (D / 8)) * 8);
     }
-    pkx = kx[tile * KT + (tid & (KT - 1))];               // every wave reads the tile's positions
+    kbuf_pending = buf;
+    pkx = kx[tile * KT + (tid & (KT - 1))];
   };
-  auto gload_v = [&](int tile) {
+  auto load_v = [&](int buf, int tile) {
 #pragma unroll
-    for (int i = 0; i < T::VPER; ++i) {
-      const int q = min(tid + NT * i, T::VCH - 1);
-      pv[i] = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(q / (KT / 8)) * a.n_keys_pad +
-                                              tile * KT + (q % (KT / 8)) * 8);
+    for (int i = 0; i < VPER; ++i) {
+      const int q = min(tid + NT * i, D * KT / 8 - 1);
+      pv[i] = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(q / (KT / 8)) * a.n_keys_pad + tile * KT + (q % (KT / 8)) * 8);
     }
+    vbuf_pending = buf;
   };
-  auto sstore_k = [&](int buf, int tile) {
+  auto flush_k = [&]() {
 #pragma unroll
-    for (int i = 0; i < T::KPER; ++i) {
-      const int q = min(tid + NT * i, T::KCH - 1);
-      *reinterpret_cast<u32x4*>(&sk[buf][(q / (D / 8)) * KS + (q % (D / 8)) * 8]) = pk[i];
-    }
-    skx[tile & 3][tid & (KT - 1)] = pkx;                   // identical values from every wave: no branch
-  };
-  auto sstore_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < T::VPER; ++i) {
-      const int q = min(tid + NT * i, T::VCH - 1);
-      *reinterpret_cast<u32x4*>(&sv[buf][(q / (KT / 8)) * VS + (q % (KT / 8)) * 8]) = pv[i];
+    for (int i = 0; i < KPER; ++i) {
+      const int q = min(tid + NT * i, KT * D / 8 - 1);
+      *reinterpret_cast<u32x4*>(&sk[kbuf_pending][(q / (D / 8)) * KS + (q % (D / 8)) * 8]) = pk[i];
     }
   };
+  auto flush_v = [&]() {
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int q = min(tid + NT * i, D * KT / 8 - 1);
+      *reinterpret_cast<u32x4*>(&sv[vbuf_pending][(q / (KT / 8)) * VS + (q % (KT / 8)) * 8]) = pv[i];
+    }
+  };
+  auto store_kx = [&](int tile) { skx[tile & 3][tid & (KT - 1)] = pkx; };   // identical values from every wave
   auto qk = [&](int buf, f32x16 (&S)[NKB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       S[kb] = f32x16{};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sk[buf][(kb * 32 + c) * KS + dc * 16 + 8 * hh]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sk[buf][T::k_off(kb * 32 + c, 2 * dc + hh)]);
         S[kb] = mfma32(ka, qf[dc], S[kb]);
       }
     }
@@ -333,7 +344,7 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     for (int cc = 0; cc < NCC; ++cc)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const f16x8 va = *reinterpret_cast<const f16x8*>(&sv[buf][(db * 32 + c) * VS + cc * 16 + 8 * hh]);
+        const f16x8 va = *reinterpret_cast<const f16x8*>(&sv[buf][T::v_off(db * 32 + c, 2 * cc + hh)]);
         acc[db] = mfma32h(va, P[cc], acc[db]);
       }
   };
@@ -352,45 +363,6 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
         }
     }
   };
-  // probabilities from masked logits, branch-free; returns (wave-uniform)
-  // whether O must be rescaled by alpha before this tile's PV product
-  auto softmax = [&](f32x16 (&S)[NKB], f16x8 (&P)[NCC], float& alpha) -> bool {
-    bool resc = false;
-    float sub;
-    if (FIXED) {
-      sub = b_fix;
-    } else {
-      float mx[4 * NKB];                                    // tree: independent partial maxima
-#pragma unroll
-      for (int j = 0; j < 4 * NKB; ++j) mx[j] = fmaxf(fmaxf(S[j >> 2][(j & 3) * 4], S[j >> 2][(j & 3) * 4 + 1]),
-                                                      fmaxf(S[j >> 2][(j & 3) * 4 + 2], S[j >> 2][(j & 3) * 4 + 3]));
-      if (NKB == 2) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], mx[j + 4]);
-      }
-      float tmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-      tmax = max_xor32(tmax) * c1;
-      resc = __ballot(tmax > ref + 8.0f) != 0;            // some row's maximum moved far: exact rescale
-      const float nref = resc ? fmaxf(ref, tmax) : ref;
-      alpha = (ref == -INFINITY) ? 0.0f : ex2(ref - nref);
-      lsum *= alpha;
-      ref = nref;
-      sub = (ref == -INFINITY) ? 0.0f : ref;
-    }
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) P[cc][i] = static_cast<_Float16>(ex2(fmaf(S[cc >> 1][(cc & 1) * 8 + i], c1, -sub)));
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 one = {1.0f16, 1.0f16};
-    float ps = 0.0f;
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ps = __builtin_amdgcn_fdot2(h2{P[cc][2 * i], P[cc][2 * i + 1]}, one, ps, false);
-    lsum += ps;
-    return resc;
-  };
   auto rescale = [&](float alpha) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -400,9 +372,14 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
 
   if (n_tiles == 0) return;
   // prologue: K tiles 0 and 1 in LDS, logits of tile 0
-  gload_k(0);
-  sstore_k(0, 0);
-  if (n_tiles > 1) { gload_k(1); sstore_k(1, 1); }
+  load_k(0, 0);
+  flush_k();
+  store_kx(0);
+  if (n_tiles > 1) {
+    load_k(1, 1);
+    flush_k();
+    store_kx(1);
+  }
   __syncthreads();
   f32x16 S0[NKB], S1[NKB];
   f16x8 P[NCC];
@@ -414,34 +391,127 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
   // are computed on whatever the buffers hold and never used.
   bool resc_prev = false;
   float alpha_prev = 1.0f;
+  // The softmax of a tile as a list of small pieces, in dependency order:
+  // partial maxima, the reduction and the reference update (SOFTMAX role
+  // only), then the exponentials two values at a time (written back into S).
+  // The step below issues one piece batch after every MFMA, in source order,
+  // so that the scheduler keeps matrix and vector work interleaved.
+  constexpr int kMaxPieces = FIXED ? 0 : 4 * NKB;
+  constexpr int kExpBase = FIXED ? 0 : 4 * NKB + 5;
+  constexpr int kPieces = kExpBase + 8 * NKB;             // 16 values per 32-key block, two per piece
+  float mx[4 * NKB];
+  float tmax = 0.0f, nref = 0.0f, sub = FIXED ? b_fix : 0.0f, alpha_cur = 1.0f;
+  bool resc_cur = false;
+  auto piece = [&](f32x16 (&S)[NKB], int q) {
+    if (!FIXED && q < kMaxPieces) {
+      const int j = q;
+      mx[j] = fmaxf(fmaxf(S[j >> 2][(j & 3) * 4], S[j >> 2][(j & 3) * 4 + 1]),
+                    fmaxf(S[j >> 2][(j & 3) * 4 + 2], S[j >> 2][(j & 3) * 4 + 3]));
+    } else if (!FIXED && q == kMaxPieces) {
+      if (NKB == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], mx[j + 4]);
+      }
+      tmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+    } else if (!FIXED && q == kMaxPieces + 1) {
+      tmax = max_xor32(tmax) * c1;
+    } else if (!FIXED && q == kMaxPieces + 2) {
+      resc_cur = __ballot(tmax > ref + 8.0f) != 0;         // some row's maximum moved far: exact rescale
+      nref = resc_cur ? fmaxf(ref, tmax) : ref;
+    } else if (!FIXED && q == kMaxPieces + 3) {
+      alpha_cur = (ref == -INFINITY) ? 0.0f : ex2(ref - nref);
+      lsum *= alpha_cur;
+    } else if (!FIXED && q == kMaxPieces + 4) {
+      ref = nref;
+      sub = (ref == -INFINITY) ? 0.0f : ref;
+    } else {
+      const int e = 2 * (q - kExpBase);                   // values e, e+1 (of 16 * NKB)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) S[(e + k) >> 4][(e + k) & 15] = ex2(fmaf(S[(e + k) >> 4][(e + k) & 15], c1, -sub));
+    }
+  };
+  // P chunk cc (keys 16cc .. 16cc+15) from the exponentials, and its row sum
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  auto convert = [&](f32x16 (&S)[NKB], int cc) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) P[cc][i] = static_cast<_Float16>(S[cc >> 1][(cc & 1) * 8 + i]);
+    const h2 one = {1.0f16, 1.0f16};
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ps = __builtin_amdgcn_fdot2(h2{P[cc][2 * i], P[cc][2 * i + 1]}, one, ps, false);
+    lsum += ps;
+  };
+
+  // iteration t: QK(t+1) into Sn, PV(t-1) with P, softmax(t) of Sc into P;
+  // K(t+2) and V(t) are loaded for the next iterations.  Tiles past the end
+  // are computed on whatever the buffers hold and never used.
   auto step = [&](int t, f32x16 (&Sc)[NKB], f32x16 (&Sn)[NKB], bool first) {
-    gload_k(min(t + 2, n_tiles - 1));
-    if (!NOPV) gload_v(t);
+    load_k(t & 1, min(t + 2, n_tiles - 1));
+    if (!NOPV) load_v(t & 1, t);
     if (resc_prev) rescale(alpha_prev);
     mask(t, Sc);
-    qk((t + 1) & 1, Sn);
-    if (!NOPV && !first) pv_acc((t + 1) & 1, P);
-    float alpha = 1.0f;
-    const bool resc = softmax(Sc, P, alpha);
-    // interleave: operand reads run 4 ahead; every MFMA is followed by
-    // independent softmax work for the VALU
+    resc_cur = false;
+    alpha_cur = 1.0f;
+    const bool pv = !NOPV && !first;
+    constexpr int NQK = NKB * DC, NPV = NOPV ? 0 : NCC * DB;
+    const uint16_t* K = sk[(t + 1) & 1];
+    const uint16_t* V = sv[(t + 1) & 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int kb = 0; kb < NKB; ++kb) Sn[kb] = f32x16{};
+    int done = 0;
+    // MFMA operands (K fragments, then V^T fragments) in a 3-entry register
+    // ring, read two products ahead of their use
+    const int n_mfma = pv ? NQK + NPV : NQK;
+    auto fetch = [&](int m) -> u32x4 {
+      if (m < NQK) {
+        const int kb = m / DC, dc = m % DC;
+        return *reinterpret_cast<const u32x4*>(&K[T::k_off(kb * 32 + c, 2 * dc + hh)]);
+      }
+      const int j = m - NQK, cc = j / DB, db = j % DB;
+      return *reinterpret_cast<const u32x4*>(&V[T::v_off(db * 32 + c, 2 * cc + hh)]);
+    };
+    u32x4 ring[3];
+    ring[0] = fetch(0);
+    if (n_mfma > 1) ring[1] = fetch(1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int i = 0; i < NKB * DC + (NOPV ? 0 : NCC * DB); ++i) {
+    for (int m = 0; m < NQK + NPV; ++m) {
+      if (m >= n_mfma) break;
+      if (m + 2 < n_mfma) ring[(m + 2) % 3] = fetch(m + 2);
+      if (m < NQK) {
+        const int kb = m / DC, dc = m % DC;
+        Sn[kb] = mfma32(__builtin_bit_cast(bf16x8, ring[m % 3]), qf[dc], Sn[kb]);
+      } else {
+        const int j = m - NQK, cc = j / DB, db = j % DB;
+        acc[db] = mfma32h(__builtin_bit_cast(f16x8, ring[m % 3]), P[cc], acc[db]);
+      }
+      const int slots = pv ? NQK + NPV : NQK;
+      const int target = min(kPieces, (m + 1) * kPieces / slots);
+      for (; done < target; ++done) piece(Sc, done);
+      if (pv && m >= NQK && (m - NQK) % DB == DB - 1) {  // the last PV product that reads P[cc]
+        const int cc = (m - NQK) / DB;
+        for (; done < kExpBase + 4 * (cc + 1); ++done) piece(Sc, done);
+        convert(Sc, cc);
+      }
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    }
+    for (; done < kPieces; ++done) piece(Sc, done);
+    if (!pv) {
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) convert(Sc, cc);
     }
     // P of this tile is complete here (keeps its conversion from sinking
     // into the next iteration, away from the MFMAs it should overlap)
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) asm volatile("" ::"v"(P[cc]));
-    sstore_k(t & 1, t + 2);
-    if (!NOPV) sstore_v(t & 1);
+    flush_k();
+    if (!NOPV) flush_v();
+    store_kx(t + 2);
     __syncthreads();
-    resc_prev = resc;
-    alpha_prev = alpha;
+    resc_prev = resc_cur;
+    alpha_prev = alpha_cur;
   };
   step(0, S0, S1, true);
   int t = 1;
@@ -463,8 +533,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   constexpr int KT = T::KT;
   constexpr int DC = D / 16, DB = D / 32;
   constexpr int ROWS = 32 * NW;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][KT * T::KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * T::VS];
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][T::KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][T::VBUF];
   __shared__ __attribute__((aligned(16))) int skx[4][KT];
   __shared__ int s_last;
 
@@ -985,9 +1055,10 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 256-row workgroups with 64-key tiles when they fill the chip, else
-  // 128-row workgroups with 32-key tiles (more, lighter workgroups)
-  const bool big = static_cast<int64_t>(a.n_sh) * ((a.n_rows + 255) / 256) >= 512;
+  // 256-row workgroups with 64-key tiles for full loops and for lazy loops
+  // that fill the chip, else 128-row workgroups with 32-key tiles (more,
+  // lighter workgroups)
+  const bool big = !lazy || static_cast<int64_t>(a.n_sh) * ((a.n_rows + 255) / 256) >= 512;
   const int rows_per = big ? 256 : 128;
   dim3 gf(mapped_grid(a.n_sh, (a.n_rows + rows_per - 1) / rows_per));
   {
