@@ -37,6 +37,10 @@ Readings of points the page leaves open (all listed in the design doc):
      consecutive elements of a head row, s = f16_rne(min(absmax/7, 65504)),
      code = rint(delta/s) clamped to [-7, 7] (0 when s == 0), low nibble =
      even element; delta is taken against the previous reconstruction.
+     The workload's delta_bits (2 or 4) and group (32 or 64) generalise it:
+     codes -q..q with q = 2^(bits-1) - 1, s from absmax/q; 2-bit codes sit
+     four to a byte, lowest bits first (variant V3, lower-bit deltas and
+     larger groups, [FL/savings] par. 3).
   R8 loop 1 stores the base (working dtype); every later loop, full or lazy,
      appends one delta layer holding records of that loop's active tokens.
   R9 all attention reads the reconstructed K^, V^ of every key, in the
@@ -71,7 +75,7 @@ import numpy as np
 
 __all__ = [
     "to_working_dtype", "token_scores", "topk_ascending", "select_keys", "f16_rne", "quantize_groups",
-    "dequantize_groups", "pack_int4", "unpack_int4", "KVStore", "full_attention",
+    "dequantize_groups", "pack_int4", "unpack_int4", "pack_codes", "unpack_codes", "KVStore", "full_attention",
     "lazy_attention", "LoopState", "run_prefill", "run_prefill_chain", "build_decode_context",
     "run_decode_loops", "run_decode_seq",
 ]
@@ -138,22 +142,26 @@ def f16_rne(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=F32).astype(np.float16)
 
 
-def quantize_groups(delta: np.ndarray, group: int = 32):
+def quantize_groups(delta: np.ndarray, group: int = 32, bits: int = 4):
     """float32 delta [..., d] -> (codes int8 [..., d], scales float16 [..., d/group]).
 
-    Reading R7; all arithmetic in float32 (correctly rounded division, rint
-    half-to-even), so the codes are a pure function of the float32 delta.
+    Reading R7 with q = 2^(bits-1) - 1 (7 for the default 4-bit codes, 1 for
+    2-bit codes): s = f16_rne(min(absmax/q, 65504)), code = clamp(rint(delta/s),
+    -q, q), 0 when s == 0.  All arithmetic in float32 (correctly rounded
+    division, rint half-to-even), so the codes are a pure function of the
+    float32 delta.
     """
     delta = np.asarray(delta, dtype=F32)
+    qmax = (1 << (bits - 1)) - 1
     d = delta.shape[-1]
     g = delta.reshape(delta.shape[:-1] + (d // group, group))
     absmax = np.max(np.abs(g), axis=-1)
-    q = np.minimum(absmax / F32(7.0), F32(65504.0))
+    q = np.minimum(absmax / F32(qmax), F32(65504.0))
     scales = f16_rne(q)
     sf = scales.astype(F32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(sf == 0, F32(0), g / np.where(sf == 0, F32(1), sf))
-    codes = np.clip(np.rint(ratio), -7, 7).astype(np.int8)
+    codes = np.clip(np.rint(ratio), -qmax, qmax).astype(np.int8)
     return codes.reshape(delta.shape), scales
 
 
@@ -181,6 +189,30 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def pack_codes(codes: np.ndarray, bits: int = 4) -> np.ndarray:
+    """bits-wide two's-complement fields, element e of each byte's run at bit
+    bits*(e mod (8/bits)) (lowest bits = first element) -> uint8 [..., d*bits/8]."""
+    if bits == 4:
+        return pack_int4(codes)
+    per = 8 // bits
+    c = (codes.astype(np.int16) & ((1 << bits) - 1)).astype(np.uint8)
+    out = np.zeros(codes.shape[:-1] + (codes.shape[-1] // per,), np.uint8)
+    for e in range(per):
+        out |= (c[..., e::per] << (bits * e)).astype(np.uint8)
+    return out
+
+
+def unpack_codes(packed: np.ndarray, bits: int = 4) -> np.ndarray:
+    if bits == 4:
+        return unpack_int4(packed)
+    per = 8 // bits
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * per,), np.int8)
+    for e in range(per):
+        f = ((packed >> (bits * e)) & ((1 << bits) - 1)).astype(np.int16)
+        out[..., e::per] = np.where(f >= (1 << (bits - 1)), f - (1 << bits), f)
+    return out
+
+
 @dataclass
 class _Records:
     idx: np.ndarray        # [n] token positions
@@ -196,8 +228,8 @@ class KVStore:
     their previous state, inactive tokens write no entry.
     """
 
-    def __init__(self, n_tokens: int, n_heads: int, head_dim: int, group: int = 32):
-        self.n, self.h, self.d, self.group = n_tokens, n_heads, head_dim, group
+    def __init__(self, n_tokens: int, n_heads: int, head_dim: int, group: int = 32, bits: int = 4):
+        self.n, self.h, self.d, self.group, self.bits = n_tokens, n_heads, head_dim, group, bits
         self.base = {"k": np.zeros((n_tokens, n_heads, head_dim), F32),
                      "v": np.zeros((n_tokens, n_heads, head_dim), F32)}
         self.layers: Dict[int, Dict[str, List[_Records]]] = {}
@@ -233,7 +265,7 @@ class KVStore:
                 continue
             prev = self.reconstruct(which, version - 1, idx)
             delta = new - prev                      # float32 subtraction
-            codes, scales = quantize_groups(delta, self.group)
+            codes, scales = quantize_groups(delta, self.group, self.bits)
             rec = _Records(idx.copy(), codes, scales)
             self.layers.setdefault(version, {"k": [], "v": []})[which].append(rec)
             out[which] = rec
@@ -390,7 +422,7 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
     """
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
     T = wl.n_loops if upto is None else upto
-    store = KVStore(n, H, d, wl.group)
+    store = KVStore(n, H, d, wl.group, wl.delta_bits)
     h_eff = h_prev_eff = q_eff = None
     o = lse = colmass = None
     history = []
@@ -452,7 +484,7 @@ def run_prefill_chain(wl, loops, upto: Optional[int] = None, seq: int = 0):
     """
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
     T = wl.n_loops if upto is None else upto
-    store = KVStore(n, H, d, wl.group)
+    store = KVStore(n, H, d, wl.group, wl.delta_bits)
     h_eff = h_prev_eff = None
     active = {}
     for l, x in loops:
@@ -480,7 +512,7 @@ def build_decode_context(wl, seq_index: int, ctx_sets: Dict[int, np.ndarray], lo
     ``ctx_sets[l]`` (O-6's fixed context)."""
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
     si = seq_index
-    store = KVStore(n, H, d, wl.group)
+    store = KVStore(n, H, d, wl.group, wl.delta_bits)
     ctx = np.arange(n - 1)
     for l in range(1, wl.n_loops + 1):
         x = loops_data[l]

@@ -34,7 +34,8 @@ class Workload:
     n_full: int             # F: loops 1..F run densely
     active: Tuple[int, ...]  # nA for lazy loops F+1..T
     n_keys: int             # nS: selected keys per (sequence, head)
-    group: int = 32         # int4 quantisation group
+    group: int = 32         # quantisation group of the delta codes (32 or 64)
+    delta_bits: int = 4     # bits per delta code (4, or 2)
     seed: int = 0
     n_heavy: int = 0        # planted heavy keys per sequence
     sigma_model: str = "lognormal"   # per-token change scale: "lognormal" | "pareto"

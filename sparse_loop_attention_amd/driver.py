@@ -107,10 +107,13 @@ class PrefillRun:
 
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
-        x = self.inp[l]
-        self.h_prev.copy_(self.inp[0]["h"][0] if l == 1 else self.h_eff)
-        self.h_eff.copy_(x["h"][0])
-        self.q_eff.copy_(x["q"][0])
+        x, wl = self.inp[l], self.wl
+        if l == wl.n_full and wl.n_loops > wl.n_full:
+            # the effective state the lazy loops start from (model stand-in:
+            # the block's outputs of the last full loop and the loop before)
+            self.h_prev.copy_(self.inp[l - 1]["h"][0])
+            self.h_eff.copy_(x["h"][0])
+            self.q_eff.copy_(x["q"][0])
         abi.kv_commit(self.kv, l, self.all_rows, x["k"], x["v"])
         abi.attend(self._attend_args(l))
 

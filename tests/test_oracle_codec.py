@@ -181,3 +181,82 @@ def test_working_dtype_rounding_matches_torch_bfloat16():
     got = to_working_dtype(x, "bf16")
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
     assert to_working_dtype(x, "fp32") is not None and np.array_equal(to_working_dtype(x, "fp32"), x)
+
+
+# ---------------------------------------------------------------- lower-bit deltas and larger groups
+@pytest.mark.parametrize("bits,group", [(2, 32), (2, 64), (4, 64)])
+def test_lattice_round_trip_other_formats(bits, group):
+    """delta = s * integers in [-q, q] with absmax = q*s (s a float16 value)
+    round-trips exactly, for q = 2^(bits-1) - 1."""
+    from oracle import quantize_groups, dequantize_groups
+    rng = np.random.default_rng(31)
+    q = (1 << (bits - 1)) - 1
+    n, d = 40, 128
+    s = np.float16(rng.uniform(0.01, 4.0, (n, d // group))).astype(np.float32)
+    ints = rng.integers(-q, q + 1, (n, d // group, group))
+    ints[..., 0] = q                                    # absmax = q*s in every group
+    delta = (ints * s[..., None]).astype(np.float32).reshape(n, d)
+    codes, scales = quantize_groups(delta, group, bits)
+    assert np.array_equal(scales.astype(np.float32), s)
+    assert np.array_equal(codes.reshape(n, d // group, group), ints)
+    assert np.array_equal(dequantize_groups(codes, scales, group), delta)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (2, 64), (4, 64)])
+def test_error_bound_and_symmetry_other_formats(bits, group):
+    """|delta - deq| <= s/2 + |absmax - q*s| per element, codes odd-symmetric,
+    a zero group gives s = 0 and zero codes."""
+    from oracle import quantize_groups, dequantize_groups
+    rng = np.random.default_rng(32)
+    q = (1 << (bits - 1)) - 1
+    delta = (rng.standard_normal((64, 128)) * np.exp(rng.standard_normal((64, 1)))).astype(np.float32)
+    delta[3, :group] = 0.0
+    codes, scales = quantize_groups(delta, group, bits)
+    assert codes.min() >= -q and codes.max() <= q
+    deq = dequantize_groups(codes, scales, group)
+    g = delta.reshape(64, -1, group)
+    s = scales.astype(np.float32)
+    bound = s / 2 + np.abs(np.abs(g).max(-1) - q * s)
+    err = np.abs(g - deq.reshape(64, -1, group)).max(-1)
+    assert np.all(err <= bound * (1 + 1e-6) + 1e-30)
+    neg, _ = quantize_groups(-delta, group, bits)
+    assert np.array_equal(neg, -codes)
+    assert scales[3, 0] == 0 and not codes[3, :group].any()
+
+
+def test_two_bit_packing():
+    """2-bit fields: lowest bits = first element; -1 is binary 11."""
+    from oracle import pack_codes, unpack_codes
+    codes = np.array([[1, -1, 0, 1, -1, -1, 0, 0]], np.int8)
+    packed = pack_codes(codes, 2)
+    # byte 0: e0=01, e1=11, e2=00, e3=01 -> 0b01_00_11_01; byte 1: 11, 11, 00, 00 -> 0b00_00_11_11
+    assert packed.tolist() == [[0b01001101, 0b00001111]]
+    assert np.array_equal(unpack_codes(packed, 2), codes)
+    rng = np.random.default_rng(33)
+    c = rng.integers(-1, 2, (5, 128)).astype(np.int8)
+    assert np.array_equal(unpack_codes(pack_codes(c, 2), 2), c)
+    c4 = rng.integers(-7, 8, (5, 128)).astype(np.int8)
+    assert np.array_equal(unpack_codes(pack_codes(c4, 4), 4), c4)
+
+
+def test_store_with_two_bit_layers_reconstructs_lattice_chain():
+    """A chain of lattice deltas reconstructs exactly at every version with
+    2-bit codes and 64-element groups too."""
+    from oracle import KVStore
+    rng = np.random.default_rng(34)
+    n, H, d = 16, 2, 128
+    st = KVStore(n, H, d, group=64, bits=2)
+    base = rng.standard_normal((n, H, d)).astype(np.float32)
+    st.commit(1, np.arange(n), base, base)
+    x = base.copy()
+    for l in (2, 3):
+        idx = np.sort(rng.choice(n, 6, replace=False))
+        s = np.float16(rng.uniform(0.05, 0.5, (6, H, d // 64))).astype(np.float32)
+        ints = rng.integers(-1, 2, (6, H, d // 64, 64))
+        ints[..., 0] = 1
+        step = (ints * s[..., None]).reshape(6, H, d).astype(np.float32)
+        new = (x[idx] + step).astype(np.float32)
+        # representable exactly: the delta against the reconstruction is the lattice step
+        st.commit(l, idx, new, new)
+        x[idx] = new
+        assert np.array_equal(st.reconstruct("k", l), x)
