@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLASHLOOP_ABI_VERSION 2
+#define FLASHLOOP_ABI_VERSION 3
 #define FL_MAX_VERSIONS 32          /* versions 1..FL_MAX_VERSIONS */
 
 typedef enum {
@@ -63,7 +63,7 @@ typedef enum {
 typedef enum { FL_ROWS_BY_TOKEN = 0, FL_ROWS_COMPACT = 1 } fl_row_layout;
 
 /* ------------------------------------------------------------------------ */
-/* KV store: a base (version 1) plus int4 delta layers 2..n_versions.        */
+/* KV store: a base (version 1) plus low-bit delta layers 2..n_versions.     */
 /* (section "FlashLoop combines three kinds of savings", paragraph 3)        */
 /* ------------------------------------------------------------------------ */
 typedef struct {
@@ -73,7 +73,9 @@ typedef struct {
   int32_t n_tokens;     /* N positions per sequence */
   int32_t n_versions;   /* T >= 1; delta layers 2..T */
   int32_t base_dtype;   /* fl_dtype of the base, and of every K/V/Q/h input */
-  int32_t group;        /* quantisation group; must be 32 */
+  int32_t group;        /* quantisation group: 32 or 64 consecutive elements of a head row;
+                           must divide head_dim (FL_ERR_UNSUPPORTED otherwise) */
+  int32_t delta_bits;   /* bits per delta code: 4 or 2 (0 means 4) */
   int32_t layer_cap[FL_MAX_VERSIONS + 1]; /* [l], l in 2..T: record slots per sequence in layer l */
   void* arena;          /* device memory of flashloop_kv_arena_bytes() bytes, caller-owned */
   uint64_t arena_bytes;
@@ -84,9 +86,11 @@ typedef struct {
  *   slot_table      [n_seq][N][slot_pitch]         int32: entry l-2 = record slot of token j in
  *                                                  layer l, or -1 (slot_pitch = n_versions - 1
  *                                                  rounded up to 4; no table when n_versions = 1)
- *   codes[l]        [n_seq][cap_l][H][2][d/2]      uint8: K then V codes of one head row, two int4
- *                                                  codes per byte, low nibble = even element
- *   scales[l]       [n_seq][cap_l][H][2][d/32]     binary16 bits: one scale per group of 32
+ *   codes[l]        [n_seq][cap_l][H][2][d*b/8]    uint8: K then V codes of one head row, b =
+ *                                                  delta_bits: two 4-bit codes per byte (low nibble
+ *                                                  = even element) or four 2-bit codes per byte
+ *                                                  (lowest bits = first element)
+ *   scales[l]       [n_seq][cap_l][H][2][d/group]  binary16 bits: one scale per group
  * A token's slots of every layer sit together (one 16-byte read resolves up
  * to four layers), and records are token-major: the K and V codes of one
  * (token, head) fill one d-byte run (a 128-byte line at d = 128) and the
@@ -114,8 +118,9 @@ uint64_t flashloop_kv_arena_bytes(const fl_kv_desc* desc);
 /* (section "FlashLoop combines three kinds of savings", paragraph 3)        */
 /* version 1: copies the rows into the base.  version l >= 2: for each active */
 /* token j, head h and X in {K, V}: delta = X_new - X^(l-1) in float32, per   */
-/* group of 32: s = f16_rne(min(absmax/7, 65504)), code = clamp(rint(delta/s),*/
-/* -7, 7) (0 when s == 0); records go to slots slot_base + r (r = position in */
+/* group: s = f16_rne(min(absmax/q, 65504)), code = clamp(rint(delta/s), -q,  */
+/* q) (0 when s == 0), q = 2^(delta_bits-1) - 1 (7 for 4-bit codes, 1 for     */
+/* 2-bit); records go to slots slot_base + r (r = position in                 */
 /* active_idx) and slot(l, j) is set to that slot.  With reset_map != 0     */
 /* every other token's slot(l, .) of the sequence is set to -1; with 0 they   */
 /* are left as they are (to add rows to a layer written by an earlier call).  */

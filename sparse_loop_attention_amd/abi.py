@@ -33,7 +33,7 @@ EXPORTS = ("flashloop_kv_layout", "flashloop_kv_arena_bytes", "flashloop_kv_comm
 class fl_kv_desc(C.Structure):
     _fields_ = [("n_seq", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("n_tokens", C.c_int32), ("n_versions", C.c_int32), ("base_dtype", C.c_int32),
-                ("group", C.c_int32), ("layer_cap", C.c_int32 * (MAX_VERSIONS + 1)),
+                ("group", C.c_int32), ("delta_bits", C.c_int32), ("layer_cap", C.c_int32 * (MAX_VERSIONS + 1)),
                 ("arena", C.c_void_p), ("arena_bytes", C.c_uint64)]
 
 
@@ -130,10 +130,11 @@ class KVStore:
     """A KV arena (torch uint8 tensor) and its descriptor."""
 
     def __init__(self, n_seq: int, n_heads: int, head_dim: int, n_tokens: int, n_versions: int,
-                 dtype: torch.dtype, layer_caps: Sequence[int], device="cuda", arena: Optional[torch.Tensor] = None):
+                 dtype: torch.dtype, layer_caps: Sequence[int], device="cuda", arena: Optional[torch.Tensor] = None,
+                 group: int = 32, delta_bits: int = 4):
         d = fl_kv_desc()
         d.n_seq, d.n_heads, d.head_dim, d.n_tokens = n_seq, n_heads, head_dim, n_tokens
-        d.n_versions, d.base_dtype, d.group = n_versions, dtype_code(dtype), 32
+        d.n_versions, d.base_dtype, d.group, d.delta_bits = n_versions, dtype_code(dtype), group, delta_bits
         for i, cap in enumerate(layer_caps):
             d.layer_cap[i + 2] = cap
         self.desc = d
@@ -160,13 +161,15 @@ class KVStore:
         if name == "slot_map":                    # [S, N]: slot of each token in `layer`
             off, sp = lay.slot_table, lay.slot_pitch
             return self.arena[off:off + S * N * sp * 4].view(torch.int32).view(S, N, sp)[:, :, layer - 2]
-        if name == "codes":                       # [S, cap, H, 2 (K, V), d/2]
+        b, g = (d.delta_bits or 4), d.group
+        if name == "codes":                       # [S, cap, H, 2 (K, V), d*bits/8]
             off = lay.codes[layer]
-            return self.arena[off:off + S * cap * H * D].view(S, cap, H, 2, D // 2)
-        if name == "scales":                      # [S, cap, H, 2 (K, V), d/32] binary16 bits
+            n = S * cap * H * 2 * (D * b // 8)
+            return self.arena[off:off + n].view(S, cap, H, 2, D * b // 8)
+        if name == "scales":                      # [S, cap, H, 2 (K, V), d/group] binary16 bits
             off = lay.scales[layer]
-            n = S * cap * H * 2 * (D // 32)
-            return self.arena[off:off + 2 * n].view(torch.int16).view(S, cap, H, 2, D // 32)
+            n = S * cap * H * 2 * (D // g)
+            return self.arena[off:off + 2 * n].view(torch.int16).view(S, cap, H, 2, D // g)
         raise KeyError(name)
 
 

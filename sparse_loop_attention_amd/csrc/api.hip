@@ -43,7 +43,11 @@ fl_status check_desc(const fl_kv_desc* d, bool need_arena) {
   if (d->n_versions < 1 || d->n_versions > FL_MAX_VERSIONS)
     return fail(FL_ERR_ARG, "kv: n_versions %d outside 1..%d", d->n_versions, FL_MAX_VERSIONS);
   if (d->base_dtype != FL_F32 && d->base_dtype != FL_BF16) return fail(FL_ERR_ARG, "kv: unknown base_dtype");
-  if (d->group != 32) return fail(FL_ERR_UNSUPPORTED, "kv: group must be 32");
+  if (d->group != 32 && d->group != 64) return fail(FL_ERR_UNSUPPORTED, "kv: group %d not in {32, 64}", d->group);
+  if (d->head_dim % d->group)
+    return fail(FL_ERR_UNSUPPORTED, "kv: group %d does not divide head_dim %d", d->group, d->head_dim);
+  if (d->delta_bits != 0 && d->delta_bits != 2 && d->delta_bits != 4)
+    return fail(FL_ERR_UNSUPPORTED, "kv: delta_bits %d not in {2, 4}", d->delta_bits);
   for (int l = 2; l <= d->n_versions; ++l)
     if (d->layer_cap[l] < 0 || d->layer_cap[l] > d->n_tokens)
       return fail(FL_ERR_ARG, "kv: layer_cap[%d] = %d outside 0..n_tokens", l, d->layer_cap[l]);
@@ -61,10 +65,11 @@ void layout_of(const fl_kv_desc* d, fl_kv_layout* o) {
   o->base_v = off; off = align256(off + S * H * N * D * es);
   o->slot_pitch = d->n_versions > 1 ? (static_cast<uint64_t>(d->n_versions - 1) + 3) / 4 * 4 : 0;
   o->slot_table = off; off = align256(off + S * N * o->slot_pitch * 4);
+  const uint64_t bits = d->delta_bits ? d->delta_bits : 4;
   for (int l = 2; l <= d->n_versions; ++l) {
     const uint64_t cap = d->layer_cap[l];
-    o->codes[l] = off; off = align256(off + S * cap * H * 2 * (D / 2));
-    o->scales[l] = off; off = align256(off + S * cap * H * 2 * (D / 32) * 2);
+    o->codes[l] = off; off = align256(off + S * cap * H * 2 * (D * bits / 8));
+    o->scales[l] = off; off = align256(off + S * cap * H * 2 * (D / d->group) * 2);
   }
   o->total_bytes = off;
 }
@@ -92,6 +97,8 @@ KvView make_view(const fl_kv_desc& d, const fl_kv_layout& lay) {
   v.base[0] = lay.base_k; v.base[1] = lay.base_v;
   v.slot_table = lay.slot_table;
   v.slot_pitch = static_cast<int32_t>(lay.slot_pitch);
+  v.bits = d.delta_bits ? d.delta_bits : 4;
+  v.gshift = d.group == 64 ? 3 : 2;
   for (int l = 2; l <= d.n_versions; ++l) {
     v.cap[l] = d.layer_cap[l];
     v.codes[l] = lay.codes[l];

@@ -193,8 +193,8 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
           float kn[8], vn[8];
           load8<DT>(cm.k_new, src, kn);
           load8<DT>(cm.v_new, src, vn);
-          advance8(kn, xp, true, x);
-          advance8(vn, yp, true, y);
+          advance8(kv, kn, xp, true, x);
+          advance8(kv, vn, yp, true, y);
         }
       } else {
         if (j >= 0) recon8<DT>(kv, 0, s, h, j, a.version, p, x, LAZY ? xp : nullptr);
@@ -430,15 +430,24 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
       for (int k = 0; k < 2; ++k) S[(e + k) >> 4][(e + k) & 15] = ex2(fmaf(S[(e + k) >> 4][(e + k) & 15], c1, -sub));
     }
   };
-  // P chunk cc (keys 16cc .. 16cc+15) from the exponentials, and its row sum
+  // P chunk cc (keys 16cc .. 16cc+15) from the exponentials, and its row
+  // sum: over the fp16 values the PV product uses (softmax: the output's
+  // weights are then normalised exactly), or in float32 for the fixed-
+  // normaliser mass, whose terms can all lie below fp16's range and which
+  // decides the row's validity and lse
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   auto convert = [&](f32x16 (&S)[NKB], int cc) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) P[cc][i] = static_cast<_Float16>(S[cc >> 1][(cc & 1) * 8 + i]);
-    const h2 one = {1.0f16, 1.0f16};
     float ps = 0.0f;
+    if (FIXED) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ps = __builtin_amdgcn_fdot2(h2{P[cc][2 * i], P[cc][2 * i + 1]}, one, ps, false);
+      for (int i = 0; i < 8; ++i) ps += S[cc >> 1][(cc & 1) * 8 + i];
+    } else {
+      const h2 one = {1.0f16, 1.0f16};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps = __builtin_amdgcn_fdot2(h2{P[cc][2 * i], P[cc][2 * i + 1]}, one, ps, false);
+    }
     lsum += ps;
   };
 

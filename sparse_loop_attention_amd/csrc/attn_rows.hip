@@ -180,8 +180,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a
               load8<DT>(cm.k_new, src, kn);
               load8<DT>(cm.v_new, src, vn);
             }
-            advance8(kn, kp[u], live, kc[u]);
-            advance8(vn, vp[u], live, vc[u]);
+            advance8(kv, kn, kp[u], live, kc[u]);
+            advance8(kv, vn, vp[u], live, vc[u]);
           }
         }
       } else {

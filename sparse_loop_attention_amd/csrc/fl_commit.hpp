@@ -1,54 +1,59 @@
-// Device pieces of the int4 delta commit, shared by the commit kernel and by
-// the kernels that fuse the commit into an attention call.
+// Device pieces of the low-bit delta commit, shared by the commit kernel and
+// by the kernels that fuse the commit into an attention call.
 //
 // Page "FlashLoop: Fast and Memory-Efficient Looped Transformers via Lazy
 // Updates", section "FlashLoop combines three kinds of savings", paragraph 3
 // (a 4-bit difference from the previous state, written for active tokens
 // only) and paragraph 4 (the KV update and compression are fused with the
-// compute).  Group format: 32 consecutive elements of a head row share one
-// binary16 scale s = f16_rne(min(absmax/7, 65504)); code = clamp(rint(d/s),
-// -7, 7), 0 when s == 0.  A 16-lane group covers a head row, lane p owning
-// elements [8p, 8p+8), so a group of 32 elements is one DPP quad.
+// compute).  Group format: 32 (or 64) consecutive elements of a head row
+// share one binary16 scale s = f16_rne(min(absmax/q, 65504)); code =
+// clamp(rint(d/s), -q, q), 0 when s == 0, with q = 2^(bits-1) - 1 (7 for
+// 4-bit codes, 1 for 2-bit).  A 16-lane group covers a head row, lane p
+// owning elements [8p, 8p+8), so a scale group is one DPP quad (or half-row).
 #pragma once
 #include "fl_common.hpp"
 
 namespace fl {
 
-// Quantises this lane's 8 deltas.  All four lanes of the quad must call it
-// (dead lanes pass live = false and contribute absmax 0).
-__device__ __forceinline__ void quantize8(const float delta[8], bool live, uint32_t& packed, uint16_t& sbits,
-                                          float& sc) {
+// Quantises this lane's 8 deltas into `bits`-wide fields of `packed`.  All
+// lanes of the scale group must call it (dead lanes pass live = false and
+// contribute absmax 0).
+__device__ __forceinline__ void quantize8(const KvView& kv, const float delta[8], bool live, uint32_t& packed,
+                                          uint16_t& sbits, float& sc) {
   float amax = 0.0f;
   if (live) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(delta[e]));
   }
-  amax = group_max<4>(amax);
-  const float q = fminf(amax / 7.0f, 65504.0f);              // correctly rounded division
+  amax = kv.gshift == 3 ? group_max<8>(amax) : group_max<4>(amax);
+  const float qmax = static_cast<float>((1 << (kv.bits - 1)) - 1);
+  const float q = fminf(amax / qmax, 65504.0f);              // correctly rounded division
   sbits = f32_to_half_bits(q);
   sc = half_bits_to_f32(sbits);
+  const uint32_t mask = (1u << kv.bits) - 1u;
   packed = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     int c = 0;
-    if (sc != 0.0f) c = static_cast<int>(fminf(fmaxf(__builtin_rintf(delta[e] / sc), -7.0f), 7.0f));
-    packed |= (static_cast<uint32_t>(c) & 0xFu) << (4 * e);
+    if (sc != 0.0f) c = static_cast<int>(fminf(fmaxf(__builtin_rintf(delta[e] / sc), -qmax), qmax));
+    packed |= (static_cast<uint32_t>(c) & mask) << (kv.bits * e);
   }
 }
 
 // Version l of a row whose version l-1 is x_prev: the new row's quantised
 // delta is added (exactly what a reader of the written record would add).
-__device__ __forceinline__ void advance8(const float x_new[8], const float x_prev[8], bool live, float x_out[8]) {
+__device__ __forceinline__ void advance8(const KvView& kv, const float x_new[8], const float x_prev[8], bool live,
+                                         float x_out[8]) {
   float delta[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) delta[e] = x_new[e] - x_prev[e];
   uint32_t packed;
   uint16_t sbits;
   float sc;
-  quantize8(delta, live, packed, sbits, sc);
+  quantize8(kv, delta, live, packed, sbits, sc);
 #pragma unroll
   for (int e = 0; e < 8; ++e) x_out[e] = x_prev[e];
-  add_codes8(packed, sc, x_out);
+  add_codes8(packed, kv.bits, sc, x_out);
 }
 
 // Position of token j in the ascending active list act[0..n), or -1.
@@ -82,12 +87,14 @@ __device__ __forceinline__ void commit_row(const KvView& kv, uint8_t* arena_w, i
   uint32_t packed;
   uint16_t sbits;
   float sc;
-  quantize8(delta, live, packed, sbits, sc);
+  quantize8(kv, delta, live, packed, sbits, sc);
   if (!live) return;
   const int64_t rec = kv.record(l, s, slot, h, which);
-  *reinterpret_cast<uint32_t*>(arena_w + kv.codes[l] + rec * (d / 2) + 4 * p) = packed;
-  if ((p & 3) == 0)
-    *reinterpret_cast<uint16_t*>(arena_w + kv.scales[l] + (rec * (d / 32) + (p >> 2)) * 2) = sbits;
+  uint8_t* cb = arena_w + kv.codes[l] + rec * (d * kv.bits / 8) + p * kv.bits;
+  if (kv.bits == 4) *reinterpret_cast<uint32_t*>(cb) = packed;
+  else *reinterpret_cast<uint16_t*>(cb) = static_cast<uint16_t>(packed);
+  if ((p & ((1 << kv.gshift) - 1)) == 0)
+    reinterpret_cast<uint16_t*>(arena_w + kv.scales[l])[kv.scale_index(rec, p)] = sbits;
 }
 
 // Everything a fused commit needs besides the store view.

@@ -78,8 +78,9 @@ __device__ __forceinline__ void store8(void* base, int64_t elem, const float in[
 
 // ---- device view of the KV arena ------------------------------------------
 // Records are token-major: record (s, slot, h, which) with which = 0 for K and
-// 1 for V has index ((s * cap + slot) * H + h) * 2 + which; its codes are d/2
-// bytes and its scales d/32 binary16 values.
+// 1 for V has index ((s * cap + slot) * H + h) * 2 + which; its codes are
+// d*bits/8 bytes (lane p of a 16-lane group owns the `bits` bytes of elements
+// [8p, 8p+8)) and its scales d/group binary16 values (one per 2^gshift lanes).
 struct KvView {
   const uint8_t* arena;
   int32_t n_seq, H, d, N, T, dtype;
@@ -89,6 +90,8 @@ struct KvView {
   int32_t slot_pitch;
   uint64_t codes[FL_MAX_VERSIONS + 1];
   uint64_t scales[FL_MAX_VERSIONS + 1];
+  int32_t bits;                                  // bits per delta code: 4 or 2
+  int32_t gshift;                                // log2(lanes per scale group): 2 (group 32) or 3 (64)
 
   // the slots of token j of sequence s in layers 2, 3, ... (entry l-2)
   __device__ __forceinline__ const int32_t* slot_row(int s, int j) const {
@@ -98,13 +101,26 @@ struct KvView {
   __device__ __forceinline__ int64_t record(int l, int s, int slot, int h, int which) const {
     return ((static_cast<int64_t>(s) * cap[l] + slot) * H + h) * 2 + which;
   }
+  // codes of lane p (8 elements) of record `rec` in layer l, right-aligned
+  __device__ __forceinline__ uint32_t load_codes(int l, int64_t rec, int p) const {
+    const uint8_t* b = arena + codes[l] + rec * (d * bits / 8) + p * bits;
+    return bits == 4 ? *reinterpret_cast<const uint32_t*>(b) : *reinterpret_cast<const uint16_t*>(b);
+  }
+  __device__ __forceinline__ int64_t scale_index(int64_t rec, int p) const {
+    return rec * (d >> (3 + gshift)) + (p >> gshift);
+  }
+  __device__ __forceinline__ uint16_t load_scale(int l, int64_t rec, int p) const {
+    return reinterpret_cast<const uint16_t*>(arena + scales[l])[scale_index(rec, p)];
+  }
 };
 
-// Adds nibble-coded deltas (8 codes in `codes`, scale `s`) to x[0..7].
-__device__ __forceinline__ void add_codes8(uint32_t codes, float s, float x[8]) {
+// Adds the deltas of 8 `bits`-wide two's-complement codes (element e in bits
+// [bits*e, bits*e + bits) of `codes`), scale `s`, to x[0..7].
+__device__ __forceinline__ void add_codes8(uint32_t codes, int bits, float s, float x[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int c = static_cast<int>(static_cast<int32_t>(codes << (28 - 4 * e)) >> 28);  // sign-extend nibble e
+    const int c = bits == 4 ? static_cast<int32_t>(codes << (28 - 4 * e)) >> 28      // sign-extend field e
+                            : static_cast<int32_t>(codes << (30 - 2 * e)) >> 30;
     x[e] = x[e] + static_cast<float>(c) * s;
   }
 }
@@ -113,12 +129,8 @@ __device__ __forceinline__ void add_codes8(uint32_t codes, float s, float x[8]) 
 // the 8 elements [8p, 8p+8) of x.
 __device__ __forceinline__ void add_delta8(const KvView& kv, int which, int l, int s, int h, int slot, int p,
                                            float x[8]) {
-  const int d = kv.d;
   const int64_t rec = kv.record(l, s, slot, h, which);
-  const uint32_t codes = *reinterpret_cast<const uint32_t*>(kv.arena + kv.codes[l] + rec * (d / 2) + 4 * p);
-  const uint16_t sbits =
-      *reinterpret_cast<const uint16_t*>(kv.arena + kv.scales[l] + (rec * (d / 32) + (p >> 2)) * 2);
-  add_codes8(codes, half_bits_to_f32(sbits), x);
+  add_codes8(kv.load_codes(l, rec, p), kv.bits, half_bits_to_f32(kv.load_scale(l, rec, p)), x);
 }
 
 // Attention consumes the reconstruction in the store's working dtype: a
@@ -200,12 +212,10 @@ __device__ __forceinline__ void recon_kv(const KvView& kv, int s, int h, const i
         if (slot[b][u] >= 0) {
           const int l = l0 + b;
           const int64_t rec = kv.record(l, s, slot[b][u], h, 0);
-          const uint8_t* cb = kv.arena + kv.codes[l] + rec * (d / 2) + 4 * p;
-          ck[b][u] = *reinterpret_cast<const uint32_t*>(cb);
-          cv[b][u] = *reinterpret_cast<const uint32_t*>(cb + d / 2);
-          const uint16_t* sb = reinterpret_cast<const uint16_t*>(kv.arena + kv.scales[l]) + rec * (d / 32) + (p >> 2);
-          sk[b][u] = sb[0];
-          sv[b][u] = sb[d / 32];
+          ck[b][u] = kv.load_codes(l, rec, p);
+          cv[b][u] = kv.load_codes(l, rec + 1, p);
+          sk[b][u] = kv.load_scale(l, rec, p);
+          sv[b][u] = kv.load_scale(l, rec + 1, p);
         }
       }
 #pragma unroll
@@ -219,8 +229,8 @@ __device__ __forceinline__ void recon_kv(const KvView& kv, int s, int h, const i
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (slot[b][u] >= 0) {
-          add_codes8(ck[b][u], half_bits_to_f32(sk[b][u]), k[u]);
-          add_codes8(cv[b][u], half_bits_to_f32(sv[b][u]), vv[u]);
+          add_codes8(ck[b][u], kv.bits, half_bits_to_f32(sk[b][u]), k[u]);
+          add_codes8(cv[b][u], kv.bits, half_bits_to_f32(sv[b][u]), vv[u]);
         }
       }
     }
@@ -252,13 +262,11 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {
-  static_assert(WIDTH == 16 || WIDTH == 4, "DPP reductions cover 4 or 16 lanes");
+  static_assert(WIDTH == 16 || WIDTH == 8 || WIDTH == 4, "DPP reductions cover 4, 8 or 16 lanes");
   v = fmaxf(v, dpp_mov<kDppQuadSwap1>(v));
   v = fmaxf(v, dpp_mov<kDppQuadSwap2>(v));
-  if constexpr (WIDTH == 16) {
-    v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
-    v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
-  }
+  if constexpr (WIDTH >= 8) v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
+  if constexpr (WIDTH == 16) v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
   return v;
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {

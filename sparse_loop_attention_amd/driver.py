@@ -69,7 +69,8 @@ class PrefillRun:
         self.formula, self.freeze_keys = formula, freeze_keys
         n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
         dt = torch_dtype(wl)
-        self.kv = abi.KVStore(1, H, d, n, wl.n_loops, dt, wl.layer_caps(), device)
+        self.kv = abi.KVStore(1, H, d, n, wl.n_loops, dt, wl.layer_caps(), device,
+                              group=wl.group, delta_bits=wl.delta_bits)
         # effective hidden state (carried rows keep their value) and, at the rows
         # of the last active set, its value one loop earlier
         self.h_eff = torch.empty(n, H * d, dtype=dt, device=device)
@@ -171,7 +172,8 @@ class DecodeRun:
         self.formula, self.freeze_keys = formula, freeze_keys
         S, n, H, d = wl.n_seq, wl.n_tokens, wl.n_heads, wl.head_dim
         dt = torch_dtype(wl)
-        self.kv = abi.KVStore(S, H, d, n, wl.n_loops, dt, wl.layer_caps(), device)
+        self.kv = abi.KVStore(S, H, d, n, wl.n_loops, dt, wl.layer_caps(), device,
+                              group=wl.group, delta_bits=wl.delta_bits)
         self.ctx = {}
         for l in range(1, wl.n_loops + 1):
             if l == 1:

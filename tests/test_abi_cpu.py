@@ -28,29 +28,38 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(abi.EXPORTS)
-    assert abi.abi_version() == 2
+    assert abi.abi_version() == 3
 
 
-def _desc(wl):
+def _desc(wl, group=32, bits=4):
     d = abi.fl_kv_desc()
     d.n_seq, d.n_heads, d.head_dim, d.n_tokens = wl.n_seq, wl.n_heads, wl.head_dim, wl.n_tokens
-    d.n_versions, d.base_dtype, d.group = wl.n_loops, abi.FL_BF16 if wl.dtype == "bf16" else abi.FL_F32, 32
+    d.n_versions, d.base_dtype, d.group = wl.n_loops, abi.FL_BF16 if wl.dtype == "bf16" else abi.FL_F32, group
+    d.delta_bits = bits
     for i, c in enumerate(wl.layer_caps()):
         d.layer_cap[i + 2] = c
     return d
 
 
-@pytest.mark.parametrize("name", list(configs.WORKLOADS))
-def test_arena_layout_bytes(L, name):
+# every workload with every store format whose group divides its head_dim
+# (the others are rejected: test_invalid_descriptors)
+LAYOUT_CASES = [pytest.param(name, (g, b), id=f"{name}-{b}b{g}")
+                for name, wl in configs.WORKLOADS.items()
+                for g, b in [(32, 4), (64, 4), (32, 2), (64, 2)] if wl.head_dim % g == 0]
+
+
+@pytest.mark.parametrize("name,fmt", LAYOUT_CASES)
+def test_arena_layout_bytes(L, name, fmt):
     wl = configs.WORKLOADS[name]
-    d = _desc(wl)
+    group, bits = fmt
+    d = _desc(wl, group, bits)
     lay = abi.kv_layout(d)
     S, H, N, D = wl.n_seq, wl.n_heads, wl.n_tokens, wl.head_dim
     es = 2 if wl.dtype == "bf16" else 4
     assert lay.base_v - lay.base_k >= S * H * N * D * es
     need = 2 * S * H * N * D * es
     for l, cap in zip(range(2, wl.n_loops + 1), wl.layer_caps()):
-        need += S * N * 4 + 2 * S * H * cap * (D // 2 + 2 * (D // 32))
+        need += S * N * 4 + 2 * S * H * cap * (D * bits // 8 + 2 * (D // group))
         for arr in (lay.codes, lay.scales):
             assert arr[l] % 256 == 0
     assert lay.slot_table % 256 == 0 and lay.slot_pitch == ((wl.n_loops - 1 + 3) // 4) * 4
@@ -77,6 +86,13 @@ def test_invalid_descriptors(L):
     d = _desc(configs.TINY)
     d.group = 16
     assert L.flashloop_kv_layout(C.byref(d), C.byref(abi.fl_kv_layout())) == abi.FL_ERR_UNSUPPORTED
+    d = _desc(configs.scaled(configs.DEEP, 320), group=64)                # head_dim 96
+    assert L.flashloop_kv_layout(C.byref(d), C.byref(abi.fl_kv_layout())) == abi.FL_ERR_UNSUPPORTED
+    assert b"divide" in L.flashloop_last_error()
+    d = _desc(configs.TINY)
+    d.delta_bits = 3
+    assert L.flashloop_kv_layout(C.byref(d), C.byref(abi.fl_kv_layout())) == abi.FL_ERR_UNSUPPORTED
+    assert b"delta_bits" in L.flashloop_last_error()
     d = _desc(configs.TINY)
     d.layer_cap[2] = 10 ** 6
     assert L.flashloop_kv_layout(C.byref(d), C.byref(abi.fl_kv_layout())) == abi.FL_ERR_ARG

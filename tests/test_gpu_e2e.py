@@ -189,3 +189,65 @@ def test_decode_variants_match_oracle(formula, freeze):
             _check_o(g.o.cpu().numpy()[s], r["o"], f"seq {s} loop {l} o")
             _check_o(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
             _check_o(g.colmass.cpu().numpy()[s], r["colmass"], f"seq {s} loop {l} colmass")
+
+
+FORMATS = [(2, 32), (4, 64), (2, 64)]
+FORMAT_WORKLOADS = [("single_layer_512", configs.scaled(configs.SINGLE_LAYER, 512, n_heads=4)),
+                    ("deep_320", configs.scaled(configs.DEEP, 320, n_heads=3)),
+                    ("tiny", configs.scaled(configs.TINY, 256))]
+# every format whose group divides the workload's head_dim (deep's 96 takes
+# only 32-element groups; the library rejects the others)
+FORMAT_CASES = [pytest.param(wl, b, g, id=f"{name}-{b}b{g}")
+                for name, wl in FORMAT_WORKLOADS for b, g in FORMATS if wl.head_dim % g == 0]
+
+
+@pytest.mark.parametrize("wl,bits,group", FORMAT_CASES)
+def test_prefill_delta_formats_match_oracle(wl, bits, group):
+    """2-bit codes and 64-element groups: every record bit-exact, outputs
+    within tolerance, against the oracle's store of the same format."""
+    import dataclasses
+    wl = dataclasses.replace(wl, delta_bits=bits, group=group)
+    inputs = driver.upload_loops(wl, SyntheticLoops(wl), DEV)
+    run = driver.PrefillRun(wl, inputs, DEV)
+    recs = run.run(record=True)
+    torch.cuda.synchronize()
+    st, hist = oracle.run_prefill(wl, iter(SyntheticLoops(wl)), keep=True)
+    for l in range(1, wl.n_loops + 1):
+        g, r = recs[l - 1], hist[l - 1]
+        if l > wl.n_full:
+            assert np.array_equal(g.rows.cpu().numpy(), r.records[l]["rows"]), f"loop {l}: token sets differ"
+            assert np.array_equal(g.keys.cpu().numpy(), r.records[l]["keys"]), f"loop {l}: key sets differ"
+        _check_o(g.o.cpu().numpy(), r.o, f"loop {l} o")
+        _check_o(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")
+        _check_o(g.colmass.cpu().numpy(), r.colmass, f"loop {l} colmass")
+    kv = run.kv
+    for l in range(2, wl.n_loops + 1):
+        for wi, w in enumerate(("k", "v")):
+            rr = st.store.layers[l][w][0]
+            codes = kv.view("codes", l).cpu().numpy()[0][:len(rr.idx), :, wi]
+            scales = kv.view("scales", l).cpu().numpy()[0][:len(rr.idx), :, wi]
+            assert np.array_equal(codes, oracle.pack_codes(rr.codes, bits)), f"layer {l} {w} codes"
+            assert np.array_equal(scales.view(np.uint16), rr.scales.view(np.uint16)), f"layer {l} {w} scales"
+
+
+@pytest.mark.parametrize("bits,group", FORMATS, ids=["2b32", "4b64", "2b64"])
+def test_decode_delta_formats_match_oracle(bits, group):
+    import dataclasses
+    wl = dataclasses.replace(configs.scaled(configs.DECODE, 600, n_seq=2, n_heads=2), delta_bits=bits, group=group)
+    syn = SyntheticLoops(wl)
+    ctx_sets = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)}
+    inputs = driver.upload_loops(wl, syn, DEV)
+    run = driver.DecodeRun(wl, inputs, ctx_sets, DEV)
+    run.build_context()
+    recs = run.run(record=True)
+    torch.cuda.synchronize()
+    data = {l: {k: v.copy() for k, v in x.items()} for l, x in SyntheticLoops(wl)}
+    for s in range(wl.n_seq):
+        ref, _ = oracle.run_decode_seq(wl, None, s, {l: ctx_sets[l][s] for l in ctx_sets}, data)
+        for l in range(1, wl.n_loops + 1):
+            g, r = recs[l - 1], ref[l - 1]
+            if l >= 2:
+                assert np.array_equal(g.keys.cpu().numpy()[s], r["keys"]), f"seq {s} loop {l} keys"
+            _check_o(g.o.cpu().numpy()[s], r["o"], f"seq {s} loop {l} o")
+            _check_o(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
+            _check_o(g.colmass.cpu().numpy()[s], r["colmass"], f"seq {s} loop {l} colmass")
