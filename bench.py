@@ -2,10 +2,12 @@
 """Benchmark of the FlashLoop loop step on one MI355X.
 
 One step = every loop of one workload, in order: the full early loops (commit
-the base or a dense int4 layer, full causal attention with column mass) and
-the lazy loops (token selection, key selection, int4 delta commit of the
+the base or a dense delta layer, full causal attention with column mass) and
+the lazy loops (token selection, key selection, delta commit of the
 active tokens, mass-corrected attention), i.e. every step of the hot path
-over one batch of synthetic input already resident in HBM.
+over one batch of synthetic input already resident in HBM.  Deltas are
+stored as 4-bit codes with one binary16 scale per 32 elements unless
+--delta-bits / --group ask for 2-bit codes or 64-element groups.
 
 Metric: active-token loop-steps per second = (sum over the step's loops of the
 rows that loop computes: N in a full loop, n_active in a lazy loop) / step
@@ -39,6 +41,10 @@ def parse():
                     help="tiny | single_layer | long_prefill | decode | deep")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the host oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--delta-bits", type=int, default=4, choices=(2, 4),
+                    help="bits per stored delta element of the lazy loops' KV versions")
+    ap.add_argument("--group", type=int, default=32, choices=(32, 64),
+                    help="delta elements sharing one binary16 scale (must divide head_dim)")
     ap.add_argument("--quality", action="store_true",
                     help="instead of timing: error of every lazy loop against the dense loop, for the output "
                          "formulas and key policies")
@@ -57,7 +63,7 @@ def work_model(wl, run):
     import numpy as np
     H, d, N = wl.n_heads, wl.head_dim, wl.n_tokens
     es = 2 if wl.dtype == "bf16" else 4
-    rec = d // 2 + 2 * (d // 32)                    # bytes of one int4 record (one head row)
+    rec = d * wl.delta_bits // 8 + 2 * (d // wl.group)   # bytes of one delta record (one head row)
     w = {"attn_full_flops": 0, "attn_lazy_flops": 0, "colmass_full_flops": 0, "colmass_lazy_flops": 0,
          "select_bytes": 0, "commit_bytes": 0, "kv_bytes": 0, "lazy_rows": 0, "rows": 0}
     if wl.decode:
@@ -289,13 +295,20 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     abi.lib()
     wl = configs.WORKLOADS[args.workload]
+    if wl.head_dim % args.group:
+        raise SystemExit(f"--group {args.group} does not divide head_dim {wl.head_dim}")
+    import dataclasses
+    wl = dataclasses.replace(wl, delta_bits=args.delta_bits, group=args.group)
     if args.quality:
         if wl.decode:
             raise SystemExit("--quality covers the prefill workloads")
-        print(json.dumps({"workload": wl.name, "metric": "relative L2 error of o against the dense loop",
+        print(json.dumps({"workload": wl.name, "delta_bits": wl.delta_bits, "group": wl.group,
+                          "metric": "relative L2 error of o against the dense loop",
                           "data": "synthetic", "variants": quality(wl)}), flush=True)
         return
-    print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    # traffic records name the workload, and the store format when it is not the default
+    label = wl.name if (wl.delta_bits, wl.group) == (4, 32) else f"{wl.name}-{wl.delta_bits}b{wl.group}"
+    print(f"[bench] workload {label}: generating inputs", file=sys.stderr, flush=True)
     syn = SyntheticLoops(wl)
     if wl.decode:
         ctx_sets = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)}
@@ -338,11 +351,12 @@ def main():
         "data": "synthetic (seeded; shapes and change/heavy-key structure of the pages' workloads)",
         "config": {"workload": wl.name, "n_seq": wl.n_seq, "heads": wl.n_heads, "head_dim": wl.head_dim,
                    "seq_len": wl.n_tokens, "loops": wl.n_loops, "full_loops": wl.n_full,
-                   "active": list(wl.active), "keys": wl.n_keys},
+                   "active": list(wl.active), "keys": wl.n_keys,
+                   "delta_bits": wl.delta_bits, "group": wl.group},
         "kv_GBps": work["kv_bytes"] / (elapsed / args.steps) / 1e9,
         "lazy_active_token_steps_per_s": (work["lazy_rows"] / (lazy_ms / 1e3)) if lazy_ms > 0 else None,
         "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in sorted(timings.items())},
-        "roofline": roofline(timings, work, args.steps, wl.decode, wl.name),
+        "roofline": roofline(timings, work, args.steps, wl.decode, label),
     }
     if args.cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -260,3 +260,32 @@ def test_store_with_two_bit_layers_reconstructs_lattice_chain():
         st.commit(l, idx, new, new)
         x[idx] = new
         assert np.array_equal(st.reconstruct("k", l), x)
+
+
+LOWBIT_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "lowbit_group_examples.json")
+
+
+def _lowbit_cases():
+    with open(LOWBIT_GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _lowbit_cases(), ids=lambda c: c["name"])
+def test_golden_lowbit_examples(case):
+    """Hand-derived 2-bit and 64-element-group cases: scales, codes, packed bytes."""
+    from oracle import pack_codes, unpack_codes
+    bits, group, n = case["bits"], case["group"], case["length"]
+    delta = np.zeros(n, np.float32)
+    for i, s in case["delta"].items():
+        delta[int(i)] = np.float32(s)
+    codes, scales = quantize_groups(delta[None], group, bits)
+    assert [int(b) for b in scales.view(np.uint16)[0]] == [int(b, 16) for b in case["scale_bits"]]
+    want = np.zeros(n, np.int8)
+    for i, c in case["codes"].items():
+        want[int(i)] = c
+    assert codes[0].tolist() == want.tolist()
+    packed = np.zeros(n * bits // 8, np.uint8)
+    for i, h in case["packed"].items():
+        packed[int(i)] = int(h, 16)
+    assert pack_codes(codes[0], bits).tolist() == packed.tolist()
+    assert unpack_codes(packed, bits).tolist() == want.tolist()
