@@ -15,8 +15,10 @@
 //              one 16-byte LDS read), plus the key positions; a lazy loop
 //              gathers versions v-1 and v, and with a fused commit extra
 //              blocks write this loop's records;
-//   fwd      - one workgroup per 256 (or, for small calls, 128) query rows of
-//              one head.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 keeps every
+//   fwd      - one workgroup per 256 (or, for small lazy calls, 128 or 64)
+//              query rows of one head; a full loop whose grid would leave CUs
+//              idle cuts the heavy row tiles' keys into parts, merged by the
+//              part that finishes last.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 keeps every
 //              query in one lane pair, so the row softmax needs a single
 //              cross-half exchange; P^T feeds the PV product straight from
 //              the accumulators.  A lazy loop makes two passes: the previous
@@ -68,6 +70,11 @@ struct MfmaArgs {
   // column mass: rows split into col_chunks ranges of col_rows rows
   int32_t col_chunks, col_rows;
   float* col_part;          // [col_chunks][sh][n_keys_pad] partial sums (col_chunks > 1)
+  // forward key split (full loops): the key tiles of row tile t are cut into
+  // ceil(tiles / fsplit_u) parts, one workgroup each (fsplit_u = 0: none)
+  int32_t fsplit_u, f_items, f_tiles;   // workgroups and row tiles per head
+  float4* fpart;            // [sh][f_items][D/8 + 1][512] partial acc, (max, sum)
+  int32_t* fcount;          // [sh][f_tiles] parts finished (zeroed by the gather launch)
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -128,6 +135,8 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
   const int n_tiles = a.n_keys_pad / 64;
   int b = blockIdx.x;
   const int g = threadIdx.x >> 4, p = threadIdx.x & 15;
+  if (a.fcount && b == 0)                                 // the forward pass's arrival counters
+    for (int i = threadIdx.x; i < a.n_sh * a.f_tiles; i += 256) a.fcount[i] = 0;
   if (FUSE && b >= a.n_sh * n_tiles) {
     b -= a.n_sh * n_tiles;
     const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2;
@@ -545,12 +554,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][T::KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][T::VBUF];
   __shared__ __attribute__((aligned(16))) int skx[4][KT];
-  __shared__ int s_last;
+  __shared__ int s_last, s_arrived;
+  constexpr int NT = 64 * NW;
+  // the key split serves full loops in the 256-row, 64-key-tile shape
+  constexpr bool kSplit = !LAZY && ROWS == 256 && KT == 64;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
-  int sh, qtile;
-  if (!map_block(a.n_sh, (a.n_rows + ROWS - 1) / ROWS, sh, qtile)) return;
+  int sh, qtile, item = 0, part = 0, parts = 1;
+  if (kSplit && a.fsplit_u > 0) {
+    // workgroups in launch order: row tiles heaviest first, the parts of a
+    // tile one after another
+    int rev;
+    if (!map_block(a.n_sh, a.f_items, sh, rev)) return;
+    item = a.f_items - 1 - rev;
+    int i = item;
+    for (qtile = a.f_tiles - 1;; --qtile) {
+      const int kt = (min(a.n_rows, ROWS * (qtile + 1)) + KT - 1) / KT;
+      parts = (kt + a.fsplit_u - 1) / a.fsplit_u;
+      if (i < parts || qtile == 0) break;
+      i -= parts;
+    }
+    part = i;
+  } else if (!map_block(a.n_sh, (a.n_rows + ROWS - 1) / ROWS, sh, qtile)) {
+    return;
+  }
   const int s = sh / H, h = sh % H;
   const int r0 = qtile * ROWS + wave * 32;                // first row of this wave
   const int r = r0 + c;
@@ -590,8 +618,65 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   float ref, lsum;
   if (!LAZY) {
     load_q(a.q_cur, qf);
-    fwd_pass<D, NW, KT_, false>(a, n_tiles, a.kc + kofs, a.vtc + kofs, kx, sk, sv, skx, qf, tok, tok_first, tok_last,
-                           blk_full, c1, 0.0f, acc, ref, lsum);
+    // a part covers key tiles [t_lo, t_hi) of the row tile
+    const int t_lo = part * n_tiles / parts, t_hi = (part + 1) * n_tiles / parts;
+    fwd_pass<D, NW, KT_, false>(a, t_hi - t_lo, a.kc + kofs + static_cast<int64_t>(t_lo) * KT * D,
+                                a.vtc + kofs + t_lo * KT, kx + t_lo * KT, sk, sv, skx, qf, tok, tok_first,
+                                tok_last, blk_full, c1, 0.0f, acc, ref, lsum);
+    if (kSplit && parts > 1) {
+      // every part stores its partial state (acc against its own reference
+      // max, the max, the lane's sum); the part that finishes last merges all
+      // of them in part order (the result does not depend on which one it is).
+      // All parts of a head run on one XCD (map_block), whose L2 every CU
+      // shares and every CU's vector L1 writes through to: a part's stores
+      // are in that L2 once acknowledged (s_waitcnt before the count), and
+      // the merging part reads them past its own L1 (device-scope loads).  No
+      // L2 writeback or invalidate is needed, which would evict the K/V
+      // tiles the other row tiles of the head are streaming.
+      constexpr int SLOT = (D / 8 + 1) * NT;
+      float4* mine = a.fpart + (static_cast<int64_t>(sh) * a.f_items + item) * SLOT;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          mine[(db * 4 + q4) * NT + tid] =
+              make_float4(acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]);
+      mine[(D / 8) * NT + tid] = make_float4(ref, lsum, 0.0f, 0.0f);
+      __builtin_amdgcn_s_waitcnt(0);                       // this lane's stores acknowledged
+      __syncthreads();
+      if (tid == 0)
+        s_arrived = __hip_atomic_fetch_add(a.fcount + static_cast<int64_t>(sh) * a.f_tiles + qtile, 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (s_arrived != parts - 1) return;
+      auto ld4 = [](const float4* q) {
+        const float* f = reinterpret_cast<const float*>(q);
+        return make_float4(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                           __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                           __hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                           __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      };
+      const float4* first = a.fpart + (static_cast<int64_t>(sh) * a.f_items + item - part) * SLOT;
+      for (int j = 0; j < parts; ++j) {
+        const float4* pj = first + static_cast<int64_t>(j) * SLOT;
+        const float4 st = ld4(pj + (D / 8) * NT + tid);
+        const float m = j == 0 ? st.x : fmaxf(ref, st.x);
+        const float w_run = (j == 0 || ref == -INFINITY) ? 0.0f : ex2(ref - m);
+        const float w_new = st.x == -INFINITY ? 0.0f : ex2(st.x - m);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v = ld4(pj + (db * 4 + q4) * NT + tid);
+            acc[db][4 * q4 + 0] = fmaf(w_new, v.x, w_run * acc[db][4 * q4 + 0]);
+            acc[db][4 * q4 + 1] = fmaf(w_new, v.y, w_run * acc[db][4 * q4 + 1]);
+            acc[db][4 * q4 + 2] = fmaf(w_new, v.z, w_run * acc[db][4 * q4 + 2]);
+            acc[db][4 * q4 + 3] = fmaf(w_new, v.w, w_run * acc[db][4 * q4 + 3]);
+          }
+        lsum = fmaf(w_new, st.y, w_run * lsum);
+        ref = m;
+      }
+    }
     const float l_tot = lsum + __shfl_xor(lsum, 32, 64);
     if (vrow && l_tot > 0.0f) {
       const float inv = 1.0f / l_tot;
@@ -1036,6 +1121,13 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   a.stat = reinterpret_cast<float*>(ws + p.off_stat);
 
   a.n_sh = static_cast<int32_t>(sh);
+  if (!lazy && p.fsplit_u > 0) {
+    a.fsplit_u = p.fsplit_u;
+    a.f_items = p.f_items;
+    a.f_tiles = p.f_tiles;
+    a.fpart = reinterpret_cast<float4*>(ws + p.off_fpart);
+    a.fcount = reinterpret_cast<int32_t*>(ws + p.off_fcount);
+  }
   const bool fuse = lazy && x.fuse_commit;
   CommitArgs cm{};
   int64_t gblocks = static_cast<int64_t>(sh) * (a.n_keys_pad / 64);
@@ -1065,11 +1157,14 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 256-row workgroups with 64-key tiles for full loops and for lazy loops
-  // that fill the chip, else 128-row workgroups with 32-key tiles (more,
-  // lighter workgroups)
-  const bool big = !lazy || static_cast<int64_t>(a.n_sh) * ((a.n_rows + 255) / 256) >= 512;
-  const int rows_per = big ? 256 : 128;
-  dim3 gf(mapped_grid(a.n_sh, (a.n_rows + rows_per - 1) / rows_per));
+  // that fill the chip, else 128-row workgroups with 32-key tiles, or 64-row
+  // ones for lazy grids too small even for those (more, lighter workgroups)
+  const int64_t wg256 = static_cast<int64_t>(a.n_sh) * ((a.n_rows + 255) / 256);
+  const int64_t wg128 = static_cast<int64_t>(a.n_sh) * ((a.n_rows + 127) / 128);
+  const int cfg = (!lazy || wg256 >= 512) ? 0 : wg128 >= 512 ? 1 : 2;
+  const int rows_per = cfg == 0 ? 256 : cfg == 1 ? 128 : 64;
+  if (a.fsplit_u > 0 && cfg != 0) return hipErrorInvalidConfiguration;   // the split assumes 256-row tiles
+  dim3 gf(mapped_grid(a.n_sh, a.fsplit_u > 0 ? a.f_items : (a.n_rows + rows_per - 1) / rows_per));
   {
     TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
     const bool mix = lazy && x.formula == FL_FORMULA_MIXTURE;
@@ -1079,8 +1174,9 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     else if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, NWV, KTV, true>), gf, dim3(THREADS), 0, st, kv.H, kv.N, a); \
     else hipLaunchKernelGGL((k_mfma_fwd<D, NWV, KTV, false>), gf, dim3(THREADS), 0, st, kv.H, kv.N, a);          \
   } while (0)
-    if (big) FL_FWD(8, 64, 512);
-    else FL_FWD(4, 32, 256);
+    if (cfg == 0) FL_FWD(8, 64, 512);
+    else if (cfg == 1) FL_FWD(4, 32, 256);
+    else FL_FWD(2, 32, 128);
 #undef FL_FWD
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -5,10 +5,94 @@
 // active rows (prefill loops); the per-row path serves float32 stores and
 // calls with few rows per head (decode), where a 32-row MFMA tile would idle.
 #include <algorithm>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <vector>
 
 #include "fl_launch.hpp"
 
 namespace fl {
+
+// Forward pass of a full loop (MFMA path): 256-row tiles, 64-key tiles, one
+// 8-wave workgroup per CU; MI355X has 8 XCDs of 32 CUs, and workgroup b of a
+// launch starts on XCD b % 8.
+constexpr int kFwdRows = 256, kFwdKeyTile = 64, kXcds = 8, kCusPerXcd = 32;
+
+static int64_t fwd_key_tiles(int64_t n_rows, int64_t t) {
+  return (std::min<int64_t>(n_rows, kFwdRows * (t + 1)) + kFwdKeyTile - 1) / kFwdKeyTile;
+}
+
+int fwd_split_items(int64_t n_rows, int u) {
+  const int64_t T = (n_rows + kFwdRows - 1) / kFwdRows;
+  int64_t n = 0;
+  for (int64_t t = 0; t < T; ++t) n += u > 0 ? (fwd_key_tiles(n_rows, t) + u - 1) / u : 1;
+  return static_cast<int>(n);
+}
+
+// Time, in key tiles, until the last forward workgroup ends, with the
+// workgroups started in launch order (the order k_mfma_fwd maps them in: row
+// tiles heaviest first, the parts of a split tile one after another, heads
+// xcd + 8g on XCD xcd), each XCD starting its next workgroup on the first CU
+// that frees.  A workgroup costs its key tiles plus a fixed overhead, one
+// tile more for a part (its partial result is written and merged).
+static double fwd_makespan(int64_t n_sh, int64_t n_rows, int u) {
+  const int64_t T = (n_rows + kFwdRows - 1) / kFwdRows;
+  std::vector<double> work;
+  for (int64_t t = T - 1; t >= 0; --t) {
+    const int64_t kt = fwd_key_tiles(n_rows, t);
+    const int64_t p = u > 0 ? (kt + u - 1) / u : 1;
+    for (int64_t j = 0; j < p; ++j) {
+      const int64_t tiles = (j + 1) * kt / p - j * kt / p;
+      work.push_back(static_cast<double>(tiles) + 2.0 + (p > 1 ? 1.0 : 0.0));
+    }
+  }
+  const int64_t n_items = static_cast<int64_t>(work.size());
+  const int64_t groups = (n_sh + kXcds - 1) / kXcds;
+  double end = 0.0;
+  for (int x = 0; x < kXcds; ++x) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+    for (int c = 0; c < kCusPerXcd; ++c) cu.push(0.0);
+    for (int64_t local = 0; local < groups * n_items; ++local) {
+      const int64_t sh = x + kXcds * (local / n_items);
+      if (sh >= n_sh) continue;
+      const double t0 = cu.top();
+      cu.pop();
+      const double t1 = t0 + work[local % n_items];
+      cu.push(t1);
+      end = std::max(end, t1);
+    }
+  }
+  return end;
+}
+
+int plan_fwd_split(int64_t n_sh, int64_t n_rows) {
+  const int64_t T = (n_rows + kFwdRows - 1) / kFwdRows;
+  // Only grids that leave CUs idle are split (parts of one head stay on one
+  // XCD: n_sh >= 8).  From one workgroup per CU up, the split measured no
+  // faster or slower: the chip's shared throughput, not the heaviest row
+  // tile, then sets the time (16 heads x 4096 rows: 130 -> 133 us; 32 x 2048:
+  // 74 -> 105 us), while 8 x 4096 went 124 -> 84 us.
+  if (n_sh < kXcds || T < 2 || n_sh * T >= kXcds * kCusPerXcd) return 0;
+  static std::mutex mu;
+  static std::map<std::pair<int64_t, int64_t>, int> memo;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(n_sh, n_rows);
+  const auto it = memo.find(key);
+  if (it != memo.end()) return it->second;
+  const int64_t kt_max = fwd_key_tiles(n_rows, T - 1);
+  int best = 0;
+  double best_t = fwd_makespan(n_sh, n_rows, 0);
+  for (int k = 2; k <= 8; ++k) {
+    const int u = static_cast<int>((kt_max + k - 1) / k);
+    if (u < 8) break;                                    // parts of at least 512 keys
+    const double t = fwd_makespan(n_sh, n_rows, u);
+    if (t < 0.9 * best_t) { best_t = t; best = u; }
+  }
+  memo[key] = best;
+  return best;
+}
 
 hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);
 hipError_t launch_mfma(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);
@@ -47,6 +131,18 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     p.off_part = off;
     if (p.col_chunks > 1) off = align256(off + static_cast<uint64_t>(p.col_chunks) * sh * kpad * 4);
     p.off_logit = off;
+    // forward key split of full loops: one partial (acc, max, sum of every
+    // lane of the 512-thread workgroup) per workgroup, one counter per row tile
+    p.fsplit_u = lazy ? 0 : plan_fwd_split(static_cast<int64_t>(sh), p.rows);
+    p.f_tiles = static_cast<int>((rows + 255) / 256);
+    p.f_items = p.fsplit_u > 0 ? fwd_split_items(p.rows, p.fsplit_u) : p.f_tiles;
+    p.off_fpart = off;
+    p.off_fcount = off;
+    if (p.fsplit_u > 0) {
+      off = align256(off + sh * p.f_items * (D / 8 + 1) * 512 * 16);   // D/8 float4 of acc + (max, sum)
+      p.off_fcount = off;
+      off = align256(off + sh * p.f_tiles * 4);
+    }
     p.off_total = off;
     return p;
   }

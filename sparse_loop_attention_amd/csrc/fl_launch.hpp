@@ -20,9 +20,18 @@ struct AttendPlan {
   int splits;           // unused (0)
   int col_chunks;       // MFMA path: row ranges of the column-mass pass
   int col_rows;         // rows per range (a multiple of 64)
+  // MFMA path, full loops: the key tiles of a 256-row tile are cut into parts
+  // of at most fsplit_u tiles, each a workgroup of its own (0 = no split);
+  // f_items workgroups per (sequence, head), f_tiles row tiles
+  int fsplit_u, f_items, f_tiles;
   // byte offsets in the workspace
-  uint64_t off_part, off_logit, off_stat, off_gather, off_total;
+  uint64_t off_part, off_logit, off_stat, off_gather, off_fpart, off_fcount, off_total;
 };
+// Forward key split of a full loop (0 = none) for n_sh (sequence, head) rows of
+// n_rows rows; the same answer at sizing and at launch.
+int plan_fwd_split(int64_t n_sh, int64_t n_rows);
+// Workgroups per (sequence, head) of the forward pass under key split u.
+int fwd_split_items(int64_t n_rows, int u);
 AttendPlan plan_attend(const fl_attend_args& a);
 hipError_t launch_attend(const fl_attend_args& a, const KvView& kv, const AttendPlan& p, hipStream_t st);
 

@@ -210,6 +210,37 @@ def test_attend_full(dtype, d, n):
             assert ok, (version, err, rms)
 
 
+@pytest.mark.parametrize("d,n,H", [(128, 2048, 8), (64, 1024, 16), (96, 1800, 8), (128, 2500, 12)])
+def test_attend_full_key_split(d, n, H):
+    """Full loops on grids of about one round (at least 8 heads, few row
+    tiles) cut the heavy row tiles' keys into parts merged by the last part
+    to finish: outputs within tolerance of the oracle, and identical from run
+    to run whichever part finishes last."""
+    rng = np.random.default_rng(1000 + n)
+    dtype = torch.bfloat16
+    st, kv, rnd = _setup_attend(rng, n, H, d, dtype, {})
+    q = rnd(rng.standard_normal((n, H, d)).astype(np.float32) * 1.5)
+    outs = []
+    for rep in range(3):
+        o = torch.zeros(1, n, H, d, device=DEV)
+        lse = torch.zeros(1, n, H, device=DEV)
+        c = torch.full((1, H, n), 7.0, device=DEV)
+        a = abi.attend_args(kv, abi.FL_ATTEND_FULL, 1, to_dev(q[None], dtype), None, None, n, None, o, lse, c)
+        ws = torch.full((abi.attend_workspace_bytes(a),), 0xA5, dtype=torch.uint8, device=DEV)
+        a = abi.attend_args(kv, abi.FL_ATTEND_FULL, 1, to_dev(q[None], dtype), None, None, n, None, o, lse, c, ws)
+        abi.attend(a)
+        torch.cuda.synchronize()
+        outs.append((o.cpu().numpy(), lse.cpu().numpy(), c.cpu().numpy()))
+    o_r, lse_r, c_r = oracle.full_attention(q, oracle.to_working_dtype(st.reconstruct("k", 1), "bf16"),
+                                            oracle.to_working_dtype(st.reconstruct("v", 1), "bf16"), np.arange(n))
+    for got, want in zip(outs[0], (o_r[None], lse_r[None], c_r[None])):
+        ok, err, rms = rel_err_ok(got, want)
+        assert ok, (err, rms)
+    for rep in (1, 2):
+        for x, y in zip(outs[0], outs[rep]):
+            assert np.array_equal(x, y)
+
+
 @pytest.mark.parametrize("dtype,d,n,na,ns", [(torch.float32, 64, 256, 64, 26), (torch.bfloat16, 128, 512, 103, 52),
                                              (torch.bfloat16, 96, 300, 300, 300), (torch.bfloat16, 128, 700, 1, 70),
                                              (torch.bfloat16, 128, 2000, 600, 200), (torch.bfloat16, 64, 1500, 1500, 150),
