@@ -30,6 +30,7 @@
 //              the column sums are lane-local; fixed order, no atomics (row
 //              ranges are added by a small reduction kernel).
 #include <climits>
+#include <type_traits>
 
 #include "fl_common.hpp"
 #include "fl_commit.hpp"
@@ -968,7 +969,7 @@ __global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t
   constexpr int PER = (QCH + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) uint16_t sq[2][QT * QS];
   __shared__ __attribute__((aligned(16))) float sb[2][QT];
-  __shared__ int stok[2][QT];
+  __shared__ __attribute__((aligned(16))) int stok[2][QT];
   __shared__ int s_start;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1050,29 +1051,40 @@ __global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t
     const int buf = it & 1;
     const int q0 = r_begin + it * QT;
     if (it + 1 < n_tiles) gload(q0 + QT);
-    // rows of this tile that every key of the wave precedes need no mask
-    const bool need_mask = stok[buf][0] < kmax || q0 + QT > r_end;
+    // the tile's products and exponentials; MASKED: the key after the row
+    // contributes nothing (rows past the range carry b = +inf, so their
+    // exponentials are 0 either way)
+    auto tile = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 sc = f32x16{};
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 sc = f32x16{};
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[buf][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
-        sc = mfma32(qa, kf[dc], sc);
-      }
+        for (int dc = 0; dc < DC; ++dc) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[buf][(qb * 32 + c) * QS + dc * 16 + 8 * hh]);
+          sc = mfma32(qa, kf[dc], sc);
+        }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int row0 = qb * 32 + 8 * q4 + 4 * hh;
-        const float4 bc = *reinterpret_cast<const float4*>(&sb[buf][row0]);
-        const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int row0 = qb * 32 + 8 * q4 + 4 * hh;
+          const float4 bc = *reinterpret_cast<const float4*>(&sb[buf][row0]);
+          const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+          int tkv[4] = {};
+          if (MASKED) {
+            const int4 tk = *reinterpret_cast<const int4*>(&stok[buf][row0]);
+            tkv[0] = tk.x; tkv[1] = tk.y; tkv[2] = tk.z; tkv[3] = tk.w;
+          }
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          float v = ex2(sc[4 * q4 + k4] * c1 - bcv[k4]);
-          if (need_mask && kj > stok[buf][row0 + k4]) v = 0.0f;
-          acc += v;
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const float v = ex2(fmaf(sc[4 * q4 + k4], c1, -bcv[k4]));
+            acc += (MASKED && kj > tkv[k4]) ? 0.0f : v;
+          }
         }
       }
-    }
+    };
+    // wave-uniform: some row of the tile precedes the wave's last key
+    if (__builtin_amdgcn_readfirstlane(stok[buf][0] < kmax ? 1 : 0)) tile(std::true_type{});
+    else tile(std::false_type{});
     if (it + 1 < n_tiles) sstore(buf ^ 1);
     __syncthreads();
   }
