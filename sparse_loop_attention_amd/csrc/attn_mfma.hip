@@ -246,6 +246,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max that propagates NaN (IEEE maximum): v_maximum3_f32 on gfx950, with no
+// canonicalising copy of each MFMA result first (which fmaxf needs)
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // x combined with the value of lane l ^ 32 (the other key half of the same
 // query), without a trip through LDS
 __device__ __forceinline__ float max_xor32(float x) {
@@ -415,14 +419,14 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
   auto piece = [&](f32x16 (&S)[NKB], int q) {
     if (!FIXED && q < kMaxPieces) {
       const int j = q;
-      mx[j] = fmaxf(fmaxf(S[j >> 2][(j & 3) * 4], S[j >> 2][(j & 3) * 4 + 1]),
-                    fmaxf(S[j >> 2][(j & 3) * 4 + 2], S[j >> 2][(j & 3) * 4 + 3]));
+      mx[j] = vmax(vmax(S[j >> 2][(j & 3) * 4], S[j >> 2][(j & 3) * 4 + 1]),
+                   vmax(S[j >> 2][(j & 3) * 4 + 2], S[j >> 2][(j & 3) * 4 + 3]));
     } else if (!FIXED && q == kMaxPieces) {
       if (NKB == 2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], mx[j + 4]);
+        for (int j = 0; j < 4; ++j) mx[j] = vmax(mx[j], mx[j + 4]);
       }
-      tmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      tmax = vmax(vmax(mx[0], mx[1]), vmax(mx[2], mx[3]));
     } else if (!FIXED && q == kMaxPieces + 1) {
       tmax = max_xor32(tmax) * c1;
     } else if (!FIXED && q == kMaxPieces + 2) {
