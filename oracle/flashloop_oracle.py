@@ -59,6 +59,18 @@ Variants (off by default):
      every later lazy loop ([FL/late] par. 4 calls the group that carries the
      change small and stable) instead of being re-chosen from each loop's
      column mass.
+  E1 exit_threshold=tau: early exit per sequence.  The page on looped
+     Transformers ("深度解析循环Transformer架构：隐式推理如何重塑大模型算力效率",
+     section 四 "开发者实践", item 1 "计算图的动态控制": dynamic loop depth)
+     stops iterating once the change of the state between two loops falls
+     below a threshold; it fixes neither the measure nor when it is taken.
+     Reading: before each lazy loop l the sequence's change is the largest
+     token score of R1, max_i ||h_eff^(l-1)_i - h_eff^(l-2)_i||^2 (float64;
+     a decode sequence has the new token's row only); if it is < tau the
+     sequence runs no further loops and keeps the outputs and store of loop
+     l-1.  (The page's sketch also discards the state of the loop that made
+     the small change; here that loop's outputs, already computed and within
+     tau of the previous ones, are kept.)  Full loops always run.
 The page prints no worked example of the mass-corrected formula (R4); it is
 pinned by invariants that follow from the mathematics (full attention when
 every key is selected, the dense loop when every row and key is, a fixed point
@@ -401,6 +413,7 @@ class LoopState:
     colmass: np.ndarray            # [H, N] float64
     store: KVStore
     records: Dict[int, dict] = field(default_factory=dict)   # loop -> details
+    exited_at: Optional[int] = None                          # E1: the loop that was not run
 
 
 def _copy_state(st: LoopState) -> LoopState:
@@ -409,7 +422,7 @@ def _copy_state(st: LoopState) -> LoopState:
 
 
 def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: int = 0,
-                formula: str = "column", freeze_keys: bool = False):
+                formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None):
     """Run loops 1..T of a prefill workload on one sequence.
 
     ``loops`` yields (l, dict(h, q, k, v)) with l = 0..T, arrays shaped
@@ -417,8 +430,9 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
     working dtype.  Early loops run in full; later loops select tokens and
     keys, commit deltas of the active tokens and run mass-corrected attention
     ([FL/savings] par. 1-3).  ``formula`` and ``freeze_keys`` select the
-    variants V1 and V2 (module docstring).  Returns the final LoopState (and,
-    with keep=True, the list of states after every loop).
+    variants V1 and V2, ``exit_threshold`` the early exit E1 (module
+    docstring).  Returns the final LoopState (and, with keep=True, the list
+    of states after every loop that ran).
     """
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
     T = wl.n_loops if upto is None else upto
@@ -446,6 +460,9 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
             rec.update(rows=rows)
         else:
             u = token_scores(h_eff, h_prev_eff)
+            if exit_threshold is not None and float(np.max(u)) < exit_threshold:
+                st.exited_at = l                   # E1: loops l.. are not run
+                break
             rows = topk_ascending(u, wl.n_active(l))
             keys = frozen if frozen is not None else select_keys(colmass, wl.n_keys)
             if freeze_keys:
@@ -522,12 +539,14 @@ def build_decode_context(wl, seq_index: int, ctx_sets: Dict[int, np.ndarray], lo
 
 
 def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data, formula: str = "column",
-                     freeze_keys: bool = False):
+                     freeze_keys: bool = False, exit_threshold: Optional[float] = None):
     """The T decode loops of the new token at position N-1 over a built
     context: loop 1 attends in full over version 1, loops l >= 2 select keys
     from that row's column mass, commit the token's own delta and run
-    mass-corrected attention over version l (variants V1, V2 as in
-    run_prefill).  Returns a list of per-loop dicts."""
+    mass-corrected attention over version l (variants V1, V2 and the early
+    exit E1 as in run_prefill; E1 reads the new token's hidden state,
+    ``loops_data[l]["h"]`` for l = 0..T).  Returns a list of per-loop dicts,
+    one per loop that ran."""
     n = wl.n_tokens
     si = seq_index
     last = np.array([n - 1])
@@ -538,6 +557,10 @@ def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data, formula: st
     for l in range(1, wl.n_loops + 1):
         x = loops_data[l]
         q = x["q"][si]                       # [1, H, d]
+        if l >= 2 and exit_threshold is not None:
+            u = token_scores(loops_data[l - 1]["h"][si], loops_data[l - 2]["h"][si])
+            if float(np.max(u)) < exit_threshold:
+                break                              # E1: loops l.. are not run
         store.commit(l, last, x["k"][si][last], x["v"][si][last])
         if l == 1:
             kh = to_working_dtype(store.reconstruct("k", 1), wl.dtype)
@@ -560,9 +583,10 @@ def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data, formula: st
 
 
 def run_decode_seq(wl, inputs, seq_index: int, ctx_sets: Dict[int, np.ndarray], loops_data,
-                   formula: str = "column", freeze_keys: bool = False):
+                   formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None):
     """Decode workload, one sequence (O-6): the stored context, then the T
-    loops of the new token.  ``loops_data[l]`` holds dict(q [S,1,H,d],
-    k [S,N,H,d], v [S,N,H,d]).  Returns (per-loop dicts, store)."""
+    loops of the new token.  ``loops_data[l]`` holds dict(h [S,1,H*d],
+    q [S,1,H,d], k [S,N,H,d], v [S,N,H,d]) (l = 0: h only).  Returns
+    (per-loop dicts, store)."""
     store = build_decode_context(wl, seq_index, ctx_sets, loops_data)
-    return run_decode_loops(wl, store, seq_index, loops_data, formula, freeze_keys), store
+    return run_decode_loops(wl, store, seq_index, loops_data, formula, freeze_keys, exit_threshold), store

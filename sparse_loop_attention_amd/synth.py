@@ -24,7 +24,8 @@ independently and in parallel):
   fp32) after each loop, and returned as float32 arrays holding those values.
 
 Shapes: h [n_seq, N, H*d]; q, k, v [n_seq, N, H, d].  Decode workloads carry
-one new query per sequence (q has N = 1) and no h.
+the new token's rows only for h and q (N = 1: its hidden state, which the
+early-exit test reads, and its query).
 """
 from __future__ import annotations
 
@@ -79,8 +80,8 @@ class SyntheticLoops:
         self.uvec = np.stack([self._uvec(s) for s in self.seqs])              # [S, H, d]
         self._state: Dict[str, np.ndarray] = {}
         self._next = 0
-        nq = 1 if wl.decode else n
-        self.shapes = {"h": (n, h * d), "q": (nq, h, d), "k": (n, h, d), "v": (n, h, d)}
+        nq = 1 if wl.decode else n        # decode: the new token's rows only
+        self.shapes = {"h": (nq, h * d), "q": (nq, h, d), "k": (n, h, d), "v": (n, h, d)}
 
     # -- per-sequence constants ------------------------------------------------
     def _sigma(self, s: int) -> np.ndarray:
@@ -143,7 +144,7 @@ class SyntheticLoops:
     def _step(self, si: int, loop: int, name: str, prev: np.ndarray) -> np.ndarray:
         eps = self._draw(si, loop, name)
         sig = self.sigma[si]
-        if name == "q" and self.wl.decode:
+        if name in ("q", "h") and self.wl.decode:
             sig = sig[-1:]
         scale = (sig * np.float32(0.7 ** (loop - 1))).astype(np.float32)
         shape = (-1,) + (1,) * (eps.ndim - 1)
@@ -151,8 +152,8 @@ class SyntheticLoops:
 
     def names(self, loop: int):
         if loop == 0:
-            return () if self.wl.decode else ("h",)
-        return ("q", "k", "v") if self.wl.decode else ("h", "q", "k", "v")
+            return ("h",)
+        return ("h", "q", "k", "v")
 
     def loop(self, l: int) -> Dict[str, np.ndarray]:
         if l != self._next:
@@ -181,8 +182,5 @@ class SyntheticLoops:
         return {name: self._state[name] for name in self.names(l)}
 
     def __iter__(self) -> Iterator[Tuple[int, Dict[str, np.ndarray]]]:
-        start = 1 if self.wl.decode else 0
-        if start == 1:
-            self._next = 1
-        for l in range(start, self.wl.n_loops + 1):
+        for l in range(0, self.wl.n_loops + 1):
             yield l, self.loop(l)
