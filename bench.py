@@ -46,6 +46,9 @@ def parse():
                     help="bits per stored delta element of the lazy loops' KV versions")
     ap.add_argument("--group", type=int, default=32, choices=(32, 64),
                     help="delta elements sharing one binary16 scale (must divide head_dim)")
+    ap.add_argument("--exit-threshold", type=float, default=None,
+                    help="instead of the benchmark line: step time with early exit at this threshold against "
+                         "the full loop count, and the loops each sequence ran")
     ap.add_argument("--quality", action="store_true",
                     help="instead of timing: error of every lazy loop against the dense loop, for the output "
                          "formulas and key policies")
@@ -280,6 +283,44 @@ def quality(wl):
     return out
 
 
+# --------------------------------------------------------------------------- early exit
+def exit_report(wl, tau, steps, warmup):
+    """Step time with early exit at threshold tau against the same step without
+    it, and the number of loops each sequence ran."""
+    import torch
+    from sparse_loop_attention_amd import driver
+    from sparse_loop_attention_amd.synth import SyntheticLoops
+    syn = SyntheticLoops(wl)
+    inputs = driver.upload_loops(wl, syn, "cuda")
+    ctx = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)} if wl.decode else None
+
+    def make(thr):
+        if wl.decode:
+            r = driver.DecodeRun(wl, inputs, ctx, "cuda", exit_threshold=thr)
+            r.build_context()
+            return r
+        return driver.PrefillRun(wl, inputs, "cuda", exit_threshold=thr)
+
+    out = {"workload": wl.name, "threshold": tau, "loops": wl.n_loops, "data": "synthetic"}
+    for name, thr in (("no_exit", None), ("exit", tau)):
+        run = make(thr)
+        for _ in range(warmup):
+            run.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run.run()
+        torch.cuda.synchronize()
+        out[f"ms_per_step_{name}"] = (time.perf_counter() - t0) / steps * 1e3
+        if thr is not None:
+            recs = run.run(record=True)
+            torch.cuda.synchronize()
+            flags = torch.stack([r.exited for r in recs]).cpu().numpy()      # [loop, seq]
+            out["loops_run_per_sequence"] = [int((flags[:, s] == 0).sum()) for s in range(flags.shape[1])]
+        print(f"[bench] exit report: {name} done", file=sys.stderr, flush=True)
+    return out
+
+
 # --------------------------------------------------------------------------- main
 def main():
     args = parse()
@@ -300,6 +341,9 @@ def main():
         raise SystemExit(f"--group {args.group} does not divide head_dim {wl.head_dim}")
     import dataclasses
     wl = dataclasses.replace(wl, delta_bits=args.delta_bits, group=args.group)
+    if args.exit_threshold is not None:
+        print(json.dumps(exit_report(wl, args.exit_threshold, args.steps, args.warmup)), flush=True)
+        return
     if args.quality:
         if wl.decode:
             raise SystemExit("--quality covers the prefill workloads")

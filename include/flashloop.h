@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLASHLOOP_ABI_VERSION 3
+#define FLASHLOOP_ABI_VERSION 4
 #define FL_MAX_VERSIONS 32          /* versions 1..FL_MAX_VERSIONS */
 
 typedef enum {
@@ -136,6 +136,8 @@ typedef struct {
   const void* k_new;            /* [n_seq][R][H][d] base_dtype, R = N (rows by token) or n_active */
   const void* v_new;
   int32_t src_layout;           /* fl_row_layout of k_new / v_new */
+  const int32_t* exit_flags;    /* optional [n_seq] device: sequences with a nonzero flag are
+                                   skipped (their store is left as it is); see flashloop_exit_check */
 } fl_commit_args;
 
 fl_status flashloop_kv_commit(const fl_commit_args* args, void* stream);
@@ -225,10 +227,42 @@ typedef struct {
   int32_t commit_slot_base;     /* slot_base + n_active <= layer_cap[version] */
   int32_t commit_reset;         /* reset_map of the commit */
   int32_t formula;              /* fl_formula (LAZY); FULL requires FL_FORMULA_COLUMN */
+  const int32_t* exit_flags;    /* optional [n_seq] device: sequences with a nonzero flag are
+                                   skipped (o, lse, colmass and store left as they are) */
 } fl_attend_args;
 
 uint64_t  flashloop_attend_workspace_bytes(const fl_attend_args* args);
 fl_status flashloop_attend(const fl_attend_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* flashloop_exit_check -- early exit per sequence.                           */
+/* (page "深度解析循环Transformer架构：隐式推理如何重塑大模型算力效率", on    */
+/* looped Transformers, section 四 "开发者实践", item 1 "计算图的动态控制":   */
+/* looping stops once the state's change between two loops falls below a     */
+/* threshold)  Before a lazy loop, a sequence's change is its largest token   */
+/* change: max over its n_rows rows of sum_k (h_cur[r,k] - h_prev[r,k])^2 in  */
+/* float64 (the token score of flashloop_select), or the max of precomputed   */
+/* scores.  When that maximum is < threshold, exit_flags[s] is set to 1; a    */
+/* set flag is never cleared, so later loops passing exit_flags to            */
+/* flashloop_attend / flashloop_kv_commit leave the sequence's outputs and    */
+/* store as they are, with no host round trip.  max_change[s] (optional)      */
+/* receives the maximum.  NaN changes are ignored.  One small launch, no      */
+/* workspace; flags and outputs are device memory owned by the caller.        */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const double* scores;         /* [n_seq][n_rows] changes (e.g. flashloop_select's scores), or NULL */
+  const void* h_cur;            /* used when scores == NULL: [n_seq][n_rows][hidden] h_dtype */
+  const void* h_prev;
+  int32_t h_dtype;
+  int32_t n_seq;                /* 1..65535 */
+  int32_t n_rows;               /* rows per sequence, 1..2^24 */
+  int32_t hidden;               /* multiple of 8 (hidden-state mode) */
+  double threshold;             /* exit when the largest change is < threshold */
+  int32_t* exit_flags;          /* [n_seq] in/out, required */
+  double* max_change;           /* [n_seq] out, optional */
+} fl_exit_args;
+
+fl_status flashloop_exit_check(const fl_exit_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Kernel timing (diagnostics, not part of the method).  While enabled, each  */

@@ -27,7 +27,7 @@ FL_ROWS_BY_TOKEN, FL_ROWS_COMPACT = 0, 1
 
 EXPORTS = ("flashloop_kv_layout", "flashloop_kv_arena_bytes", "flashloop_kv_commit", "flashloop_select",
            "flashloop_attend_workspace_bytes", "flashloop_attend", "flashloop_last_error",
-           "flashloop_abi_version", "flashloop_timing_enable", "flashloop_timing_read")
+           "flashloop_abi_version", "flashloop_timing_enable", "flashloop_timing_read", "flashloop_exit_check")
 
 
 class fl_kv_desc(C.Structure):
@@ -47,7 +47,8 @@ class fl_kv_layout(C.Structure):
 class fl_commit_args(C.Structure):
     _fields_ = [("kv", C.POINTER(fl_kv_desc)), ("version", C.c_int32), ("active_idx", C.c_void_p),
                 ("n_active", C.c_int32), ("slot_base", C.c_int32), ("reset_map", C.c_int32),
-                ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("src_layout", C.c_int32)]
+                ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("src_layout", C.c_int32),
+                ("exit_flags", C.c_void_p)]
 
 
 class fl_select_args(C.Structure):
@@ -64,7 +65,14 @@ class fl_attend_args(C.Structure):
                 ("n_keys", C.c_int32), ("o", C.c_void_p), ("lse", C.c_void_p), ("o_layout", C.c_int32),
                 ("colmass", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64),
                 ("fuse_commit", C.c_int32), ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("kv_layout", C.c_int32),
-                ("commit_slot_base", C.c_int32), ("commit_reset", C.c_int32), ("formula", C.c_int32)]
+                ("commit_slot_base", C.c_int32), ("commit_reset", C.c_int32), ("formula", C.c_int32),
+                ("exit_flags", C.c_void_p)]
+
+
+class fl_exit_args(C.Structure):
+    _fields_ = [("scores", C.c_void_p), ("h_cur", C.c_void_p), ("h_prev", C.c_void_p), ("h_dtype", C.c_int32),
+                ("n_seq", C.c_int32), ("n_rows", C.c_int32), ("hidden", C.c_int32), ("threshold", C.c_double),
+                ("exit_flags", C.c_void_p), ("max_change", C.c_void_p)]
 
 
 class FlashLoopError(RuntimeError):
@@ -96,7 +104,9 @@ def lib():
         L.flashloop_timing_enable.argtypes = [C.c_int32]
         L.flashloop_timing_read.argtypes = [C.c_char_p, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.c_int32]
         L.flashloop_timing_read.restype = C.c_int32
-        for f in ("flashloop_kv_layout", "flashloop_kv_commit", "flashloop_select", "flashloop_attend"):
+        L.flashloop_exit_check.argtypes = [C.POINTER(fl_exit_args), C.c_void_p]
+        for f in ("flashloop_kv_layout", "flashloop_kv_commit", "flashloop_select", "flashloop_attend",
+                  "flashloop_exit_check"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -184,7 +194,8 @@ def kv_arena_bytes(desc: fl_kv_desc) -> int:
 
 
 def kv_commit(kv: KVStore, version: int, active_idx: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-              slot_base: int = 0, reset_map: bool = True, compact: bool = False, stream=None) -> None:
+              slot_base: int = 0, reset_map: bool = True, compact: bool = False,
+              exit_flags: Optional[torch.Tensor] = None, stream=None) -> None:
     a = fl_commit_args()
     a.kv = C.pointer(kv.desc)
     a.version = version
@@ -193,6 +204,7 @@ def kv_commit(kv: KVStore, version: int, active_idx: torch.Tensor, k_new: torch.
     a.slot_base, a.reset_map = slot_base, int(reset_map)
     a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
     a.src_layout = FL_ROWS_COMPACT if compact else FL_ROWS_BY_TOKEN
+    a.exit_flags = _ptr(exit_flags)
     _check(lib().flashloop_kv_commit(C.byref(a), _stream(stream)))
 
 
@@ -223,10 +235,10 @@ def select_keys(key_scores: torch.Tensor, k: int, out_idx: torch.Tensor, stream=
 # --------------------------------------------------------------------------- attend
 def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx, n_active: int,
                 key_idx, o, lse, colmass, workspace=None, q_compact=False, o_compact=False,
-                commit=None, formula: str = "column") -> fl_attend_args:
+                commit=None, formula: str = "column", exit_flags=None) -> fl_attend_args:
     """`commit` = dict(k_new=, v_new=, compact=False, slot_base=0, reset=True) fuses the
     KV commit of this loop into the call (LAZY only); `formula` is "column" or
-    "mixture" (LAZY only)."""
+    "mixture" (LAZY only); `exit_flags` (int32 [n_seq]) skips exited sequences."""
     a = fl_attend_args()
     a.mode, a.kv, a.version = mode, C.pointer(kv.desc), version
     a.q_cur, a.q_prev = _ptr(q_cur), _ptr(q_prev)
@@ -245,6 +257,7 @@ def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx,
         a.commit_slot_base = commit.get("slot_base", 0)
         a.commit_reset = int(commit.get("reset", True))
     a.formula = FORMULAS[formula]
+    a.exit_flags = _ptr(exit_flags)
     return a
 
 
@@ -254,6 +267,26 @@ def attend_workspace_bytes(a: fl_attend_args) -> int:
 
 def attend(a: fl_attend_args, stream=None) -> None:
     _check(lib().flashloop_attend(C.byref(a), _stream(stream)))
+
+
+def exit_check(exit_flags: torch.Tensor, threshold: float, scores: Optional[torch.Tensor] = None,
+               h_cur: Optional[torch.Tensor] = None, h_prev: Optional[torch.Tensor] = None,
+               max_change: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Sets exit_flags[s] (int32 [n_seq], never cleared) where the sequence's
+    largest change is below `threshold`: from `scores` (float64 [n_seq, n_rows])
+    or from h_cur/h_prev ([n_seq, n_rows, hidden])."""
+    a = fl_exit_args()
+    a.n_seq = exit_flags.numel()
+    if scores is not None:
+        a.scores = _ptr(scores)
+        a.n_rows = scores.numel() // a.n_seq
+    else:
+        a.h_cur, a.h_prev, a.h_dtype = _ptr(h_cur), _ptr(h_prev), dtype_code(h_cur.dtype)
+        a.hidden = h_cur.shape[-1]
+        a.n_rows = h_cur.numel() // (a.n_seq * a.hidden)
+    a.threshold = float(threshold)
+    a.exit_flags, a.max_change = _ptr(exit_flags), _ptr(max_change)
+    _check(lib().flashloop_exit_check(C.byref(a), _stream(stream)))
 
 
 def timing_enable(on: bool) -> None:

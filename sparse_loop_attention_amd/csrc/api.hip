@@ -157,7 +157,9 @@ fl_status flashloop_kv_commit(const fl_commit_args* a, void* stream) {
       return fail(FL_ERR_ARG, "commit: slots %d..%d exceed layer_cap[%d] = %d", a->slot_base,
                   a->slot_base + a->n_active, a->version, d.layer_cap[a->version]);
   }
+  if (a->exit_flags && !aligned(a->exit_flags, 4)) return fail(FL_ERR_ARG, "commit: exit_flags must be 4-byte aligned");
   fl::KvView kv = fl::make_view(d, lay);
+  kv.exit_flags = a->exit_flags;
   hipError_t e = fl::launch_commit(*a, kv, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "commit launch");
   return ok();
@@ -214,6 +216,7 @@ static fl_status check_attend(const fl_attend_args* a, fl_kv_layout* lay) {
   if (a->o_layout != FL_ROWS_BY_TOKEN && a->o_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: o_layout");
   if (a->formula != FL_FORMULA_COLUMN && !(lazy && a->formula == FL_FORMULA_MIXTURE))
     return fail(FL_ERR_ARG, "attend: formula %d (FULL needs FL_FORMULA_COLUMN)", a->formula);
+  if (a->exit_flags && !aligned(a->exit_flags, 4)) return fail(FL_ERR_ARG, "attend: exit_flags must be 4-byte aligned");
   if (a->fuse_commit) {
     if (!lazy) return fail(FL_ERR_ARG, "attend: fuse_commit needs LAZY mode");
     if (!a->k_new || !a->v_new || !aligned(a->k_new, 16) || !aligned(a->v_new, 16))
@@ -242,7 +245,9 @@ fl_status flashloop_attend(const fl_attend_args* a, void* stream) {
     if (a->fuse_commit && a->commit_reset) {        // ... except that the layer's slots are cleared
       fl_commit_args c{};
       c.kv = a->kv; c.version = a->version; c.n_active = 0; c.reset_map = 1;
+      c.exit_flags = a->exit_flags;
       fl::KvView kv = fl::make_view(*a->kv, lay);
+      kv.exit_flags = a->exit_flags;
       hipError_t e = fl::launch_commit(c, kv, static_cast<hipStream_t>(stream));
       if (e != hipSuccess) return hip_fail(e, "attend launch");
     }
@@ -253,8 +258,28 @@ fl_status flashloop_attend(const fl_attend_args* a, void* stream) {
     return fail(FL_ERR_WORKSPACE, "attend: workspace needs %llu bytes (256-byte aligned), got %llu",
                 (unsigned long long)p.off_total, (unsigned long long)a->workspace_bytes);
   fl::KvView kv = fl::make_view(*a->kv, lay);
+  kv.exit_flags = a->exit_flags;
   hipError_t e = fl::launch_attend(*a, kv, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attend launch");
+  return ok();
+}
+
+fl_status flashloop_exit_check(const fl_exit_args* a, void* stream) {
+  if (!a) return fail(FL_ERR_ARG, "exit args are NULL");
+  if (!a->exit_flags || !aligned(a->exit_flags, 4)) return fail(FL_ERR_ARG, "exit: exit_flags NULL or misaligned");
+  if (a->n_seq < 1 || a->n_seq > 65535) return fail(FL_ERR_ARG, "exit: n_seq outside 1..65535");
+  if (a->n_rows < 1 || a->n_rows > (1 << 24)) return fail(FL_ERR_ARG, "exit: n_rows outside 1..2^24");
+  if (a->max_change && !aligned(a->max_change, 8)) return fail(FL_ERR_ARG, "exit: max_change must be 8-byte aligned");
+  if (a->scores) {
+    if (!aligned(a->scores, 8)) return fail(FL_ERR_ARG, "exit: scores must be 8-byte aligned");
+  } else {
+    if (!a->h_cur || !a->h_prev) return fail(FL_ERR_ARG, "exit: NULL scores and NULL h");
+    if (a->h_dtype != FL_F32 && a->h_dtype != FL_BF16) return fail(FL_ERR_ARG, "exit: unknown h_dtype");
+    if (a->hidden < 8 || a->hidden % 8) return fail(FL_ERR_UNSUPPORTED, "exit: hidden must be a multiple of 8");
+    if (!aligned(a->h_cur, 16) || !aligned(a->h_prev, 16)) return fail(FL_ERR_ARG, "exit: h must be 16-byte aligned");
+  }
+  hipError_t e = fl::launch_exit_check(*a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "exit launch");
   return ok();
 }
 

@@ -76,6 +76,10 @@ struct MfmaArgs {
   int32_t fsplit_u, f_items, f_tiles;   // workgroups and row tiles per head
   float4* fpart;            // [sh][f_items][D/8 + 1][512] partial acc, (max, sum)
   int32_t* fcount;          // [sh][f_tiles] parts finished (zeroed by the gather launch)
+  // early exit: sequences with a nonzero flag are skipped by every kernel
+  const int32_t* exit_flags;  // [n_seq] or null
+  int32_t heads;
+  __device__ __forceinline__ bool exited(int s) const { return exit_flags && exit_flags[s]; }
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -149,6 +153,7 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
       const int h = static_cast<int>((item >> 1) % kv.H);
       const int64_t sr = (item >> 1) / kv.H;
       const int r = static_cast<int>(sr % a.n_rows), s = static_cast<int>(sr / a.n_rows);
+      if (kv.exited(s)) return;                           // uniform per 16-lane group
       const int j = a.act[static_cast<int64_t>(s) * a.n_rows + r];
       const int64_t src_rows = cm.src_compact ? a.n_rows : kv.N;
       const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? r : j)) * kv.H + h) * D;
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
     const int per_seq = (kv.N + 255) / 256;
     const int s = b / per_seq;
     const int j = (b % per_seq) * 256 + threadIdx.x;
-    if (s >= kv.n_seq || j >= kv.N) return;
+    if (s >= kv.n_seq || j >= kv.N || kv.exited(s)) return;
     const int ra = find_active(a.act + static_cast<int64_t>(s) * a.n_rows, a.n_rows, j);
     int32_t* dst = reinterpret_cast<int32_t*>(cm.arena + kv.slot_table) +
                    (static_cast<int64_t>(s) * kv.N + j) * kv.slot_pitch + (a.version - 2);
@@ -170,6 +175,7 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
   }
   const int sh = b / n_tiles, tile = b % n_tiles;
   const int s = sh / kv.H, h = sh % kv.H;
+  if (kv.exited(s)) return;                               // uniform per workgroup
   const bool live = 8 * p < D;
   const int32_t* act_s = FUSE ? a.act + static_cast<int64_t>(s) * a.n_rows : nullptr;
 #pragma unroll 1
@@ -585,6 +591,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
     return;
   }
   const int s = sh / H, h = sh % H;
+  if (a.exited(s)) return;
   const int r0 = qtile * ROWS + wave * 32;                // first row of this wave
   const int r = r0 + c;
   const bool vrow = r < a.n_rows;
@@ -925,6 +932,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_
   const int chunk = item % a.col_chunks;
   const int kblk = n_kblk - 1 - item / a.col_chunks;        // early keys see the most rows: start them first
   const int s = sh / H;
+  if (a.exited(s)) return;
   const int t0 = kblk * KB + wave * 32;
   const int t = t0 + c;
   const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
@@ -984,6 +992,7 @@ __global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t
   const int chunk = item % a.col_chunks;
   const int kblk = n_kblk - 1 - item / a.col_chunks;      // early keys see the most rows: start them first
   const int s = sh / H, h = sh % H;
+  if (a.exited(s)) return;
   const int t0 = kblk * KB + wave * 32;
   const int t = t0 + c;
   const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
@@ -1104,7 +1113,7 @@ __global__ __launch_bounds__(256) void k_colmass_reduce(int32_t N, MfmaArgs a) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= static_cast<int64_t>(a.n_sh) * a.n_keys_pad) return;
   const int sh = static_cast<int>(i / a.n_keys_pad), t = static_cast<int>(i % a.n_keys_pad);
-  if (t >= a.n_keys) return;
+  if (t >= a.n_keys || a.exited(sh / a.heads)) return;
   float acc = 0.0f;
   for (int ch = 0; ch < a.col_chunks; ++ch) acc += a.col_part[(static_cast<int64_t>(ch) * a.n_sh) * a.n_keys_pad + i];
   float* dst = a.colmass + static_cast<int64_t>(sh) * N + a.kidx[i];
@@ -1137,6 +1146,8 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   a.stat = reinterpret_cast<float*>(ws + p.off_stat);
 
   a.n_sh = static_cast<int32_t>(sh);
+  a.heads = kv.H;
+  a.exit_flags = kv.exit_flags;
   if (!lazy && p.fsplit_u > 0) {
     a.fsplit_u = p.fsplit_u;
     a.f_items = p.f_items;

@@ -39,6 +39,7 @@ struct RowArgs {
   int32_t mixture;          // LAZY: o = m*otilde + (1-m)*o_prev instead of m*otilde + o_prev - a
   float* logit;             // [2][sh][rows][key_slots]
   float* stat;              // [sh][rows][4] = lse_prev, lse_new, valid, -
+  const int32_t* exit_flags;  // [n_seq] or null: nonzero = skip the sequence (early exit)
 };
 
 __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int v) {
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a
   const int r = blockIdx.x, sh = blockIdx.y;
   const int H = kv.H, d = kv.d;
   const int s = sh / H, h = sh % H;
+  if (kv.exited(s)) return;                               // uniform per workgroup
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, p = lane & 15;
   const bool live = 8 * p < d;
   const int32_t* act_s = a.act ? a.act + static_cast<int64_t>(s) * a.n_act : nullptr;
@@ -317,6 +319,7 @@ __global__ __launch_bounds__(256) void k_rows_colmass(int32_t n_seq, int32_t H, 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 64 + lane;
   const int s = sh / H;
+  if (a.exit_flags && a.exit_flags[s]) return;           // uniform per workgroup
   const int64_t slots = LAZY ? a.n_keys : N;
   const bool live = t < slots;
   const int j = !live ? 0 : LAZY ? a.keys[static_cast<int64_t>(sh) * a.n_keys + t] : t;
@@ -367,6 +370,7 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
   uint8_t* ws = static_cast<uint8_t*>(x.workspace);
   a.logit = reinterpret_cast<float*>(ws + p.off_logit);
   a.stat = reinterpret_cast<float*>(ws + p.off_stat);
+  a.exit_flags = kv.exit_flags;
   const bool lazy = x.mode == FL_ATTEND_LAZY;
   const int sh = kv.n_seq * kv.H;
   const bool fuse = lazy && x.fuse_commit;

@@ -92,6 +92,9 @@ struct KvView {
   uint64_t scales[FL_MAX_VERSIONS + 1];
   int32_t bits;                                  // bits per delta code: 4 or 2
   int32_t gshift;                                // log2(lanes per scale group): 2 (group 32) or 3 (64)
+  const int32_t* exit_flags;                     // [n_seq] or null: nonzero = the sequence has exited
+
+  __device__ __forceinline__ bool exited(int s) const { return exit_flags && exit_flags[s]; }
 
   // the slots of token j of sequence s in layers 2, 3, ... (entry l-2)
   __device__ __forceinline__ const int32_t* slot_row(int s, int j) const {

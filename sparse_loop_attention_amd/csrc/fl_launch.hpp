@@ -10,6 +10,7 @@ namespace fl {
 KvView make_view(const fl_kv_desc& d, const fl_kv_layout& lay);
 
 hipError_t launch_select(const fl_select_args& a, hipStream_t st);
+hipError_t launch_exit_check(const fl_exit_args& a, hipStream_t st);
 hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t st);
 
 // Workspace layout of an attend call, shared by sizing and launching.

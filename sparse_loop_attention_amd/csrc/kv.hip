@@ -16,10 +16,11 @@ namespace fl {
 // `slots` points at column l-2 of the slot table, rows `pitch` apart.
 __global__ __launch_bounds__(256) void k_slot_map(int32_t* __restrict__ slots, int32_t pitch, int32_t N,
                                                   const int32_t* __restrict__ act, int32_t n_act,
-                                                  int32_t slot_base, int32_t reset) {
+                                                  int32_t slot_base, int32_t reset,
+                                                  const int32_t* __restrict__ exit_flags) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int s = blockIdx.y;
-  if (j >= N) return;
+  if (j >= N || (exit_flags && exit_flags[s])) return;
   const int32_t* a = act + static_cast<int64_t>(s) * n_act;
   int lo = 0, hi = n_act;
   while (lo < hi) {
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(256) void k_commit(KvView kv, uint8_t* __restrict__
   const int64_t sr = (item >> 1) / H;
   const int r = static_cast<int>(sr % n_act);
   const int s = static_cast<int>(sr / n_act);
+  if (kv.exited(s)) return;                                     // uniform per 16-lane group
   const int j = act[static_cast<int64_t>(s) * n_act + r];
   const int64_t src_rows = src_compact ? n_act : kv.N;
   const int64_t src_row = src_compact ? r : j;
@@ -61,7 +63,7 @@ hipError_t launch_commit(const fl_commit_args& a, const KvView& kv, hipStream_t 
     TimedLaunch t(st, "slot_map");
     hipLaunchKernelGGL(k_slot_map, g, dim3(256), 0, st,
                        reinterpret_cast<int32_t*>(arena + kv.slot_table) + (a.version - 2), kv.slot_pitch, kv.N,
-                       a.active_idx, a.n_active, a.slot_base, a.reset_map);
+                       a.active_idx, a.n_active, a.slot_base, a.reset_map, a.exit_flags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -16,25 +16,8 @@ namespace fl {
 // Each lane streams 8 elements (16 B of bf16) per step, 4 steps in flight.
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(256) void k_delta_norm(const void* __restrict__ h_cur,
-                                                    const void* __restrict__ h_prev, int64_t n_rows,
-                                                    int64_t hidden, const int32_t* __restrict__ cand,
-                                                    int32_t n_cand, double* __restrict__ scores) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= n_rows) return;
-  if (cand != nullptr) {
-    int lo = 0, hi = n_cand;                      // first index with cand[idx] >= row
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (cand[mid] < row) lo = mid + 1; else hi = mid;
-    }
-    if (lo >= n_cand || cand[lo] != row) {        // carried row: unchanged, scores exactly 0
-      if (lane == 0) scores[row] = 0.0;
-      return;
-    }
-  }
-  const int64_t base = row * hidden;
+__device__ __forceinline__ double row_change(const void* __restrict__ h_cur, const void* __restrict__ h_prev,
+                                             int64_t base, int64_t hidden, int lane) {
   double acc = 0.0;
   constexpr int kUnroll = 4;
   int64_t e = static_cast<int64_t>(lane) * 8;
@@ -63,8 +46,70 @@ __global__ __launch_bounds__(256) void k_delta_norm(const void* __restrict__ h_c
       acc = fma(t, t, acc);
     }
   }
-  acc = wave_sum_f64(acc);
+  return wave_sum_f64(acc);                       // every lane holds the row's sum
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_delta_norm(const void* __restrict__ h_cur,
+                                                    const void* __restrict__ h_prev, int64_t n_rows,
+                                                    int64_t hidden, const int32_t* __restrict__ cand,
+                                                    int32_t n_cand, double* __restrict__ scores) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  if (cand != nullptr) {
+    int lo = 0, hi = n_cand;                      // first index with cand[idx] >= row
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (cand[mid] < row) lo = mid + 1; else hi = mid;
+    }
+    if (lo >= n_cand || cand[lo] != row) {        // carried row: unchanged, scores exactly 0
+      if (lane == 0) scores[row] = 0.0;
+      return;
+    }
+  }
+  const double acc = row_change<DT>(h_cur, h_prev, row * hidden, hidden, lane);
   if (lane == 0) scores[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// early exit: one workgroup per sequence takes the largest change of its rows
+// (given scores, or the same float64 row sums as the token score) and sets
+// the sequence's flag when it is below the threshold.  A set flag stays set.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void k_exit_check(const double* __restrict__ scores, const void* __restrict__ h_cur,
+                                                    const void* __restrict__ h_prev, int32_t n_rows, int32_t hidden,
+                                                    double threshold, int32_t* __restrict__ flags,
+                                                    double* __restrict__ max_change) {
+  __shared__ double red[4];
+  const int s = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double m = 0.0;                                 // changes are >= 0; fmax drops NaN
+  if (scores) {
+    for (int r = threadIdx.x; r < n_rows; r += 256) m = fmax(m, scores[static_cast<int64_t>(s) * n_rows + r]);
+    for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+  } else {
+    for (int r = wave; r < n_rows; r += 4)
+      m = fmax(m, row_change<DT>(h_cur, h_prev, (static_cast<int64_t>(s) * n_rows + r) * hidden, hidden, lane));
+  }
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    if (max_change) max_change[s] = m;
+    if (m < threshold) flags[s] = 1;
+  }
+}
+
+hipError_t launch_exit_check(const fl_exit_args& a, hipStream_t st) {
+  TimedLaunch t(st, "exit_check");
+  if (a.h_dtype == FL_BF16 && !a.scores)
+    hipLaunchKernelGGL(k_exit_check<FL_BF16>, dim3(a.n_seq), dim3(256), 0, st, a.scores, a.h_cur, a.h_prev,
+                       a.n_rows, a.hidden, a.threshold, a.exit_flags, a.max_change);
+  else
+    hipLaunchKernelGGL(k_exit_check<FL_F32>, dim3(a.n_seq), dim3(256), 0, st, a.scores, a.h_cur, a.h_prev,
+                       a.n_rows, a.hidden, a.threshold, a.exit_flags, a.max_change);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

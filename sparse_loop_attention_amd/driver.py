@@ -55,18 +55,23 @@ class LoopRecord:
     lse: Optional[torch.Tensor] = None
     colmass: Optional[torch.Tensor] = None
     arena: Optional[torch.Tensor] = None
+    exited: Optional[torch.Tensor] = None      # early exit: flags after the loop
 
 
 class PrefillRun:
     """GPU state of one prefill workload (n_seq = 1) and its loop sequence."""
 
     def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], device="cuda", fuse: bool = True,
-                 formula: str = "column", freeze_keys: bool = False):
+                 formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None):
         """formula "column" (default) or "mixture"; freeze_keys reuses the first
-        lazy loop's key group in every later lazy loop."""
+        lazy loop's key group in every later lazy loop; exit_threshold enables
+        the early exit (the sequence stops before the first lazy loop whose
+        largest token change is below it)."""
         assert wl.n_seq == 1 and not wl.decode
         self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
         self.formula, self.freeze_keys = formula, freeze_keys
+        self.exit_threshold = exit_threshold
+        self.exit_flags = torch.zeros(1, dtype=torch.int32, device=device) if exit_threshold is not None else None
         n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
         dt = torch_dtype(wl)
         self.kv = abi.KVStore(1, H, d, n, wl.n_loops, dt, wl.layer_caps(), device,
@@ -104,7 +109,7 @@ class PrefillRun:
         commit = dict(k_new=self.inp[l]["k"], v_new=self.inp[l]["v"]) if self.fuse else None
         return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, self.q_cur_rows[:na], self.q_prev_rows[:na],
                                self.act[l], na, self.keys_l[l], self.o, self.lse, self.colmass, self.workspace,
-                               q_compact=True, commit=commit, formula=self.formula)
+                               q_compact=True, commit=commit, formula=self.formula, exit_flags=self.exit_flags)
 
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
@@ -122,6 +127,8 @@ class PrefillRun:
         wl, x = self.wl, self.inp[l]
         act, na = self.act[l], wl.n_active(l)
         abi.select_tokens(self.h_eff, self.h_prev, na, self.scores, act, cand)
+        if self.exit_flags is not None:          # early exit: no later library call touches the sequence
+            abi.exit_check(self.exit_flags, self.exit_threshold, scores=self.scores)
         first = wl.n_full + 1
         if self.freeze_keys and l > first:
             self.keys_l[l].copy_(self.keys_l[first])
@@ -135,7 +142,7 @@ class PrefillRun:
         torch.index_select(x["q"][0], 0, idx, out=self.q_cur_rows[:na])
         self.q_eff.index_copy_(0, idx, self.q_cur_rows[:na])
         if not self.fuse:
-            abi.kv_commit(self.kv, l, act, x["k"], x["v"])
+            abi.kv_commit(self.kv, l, act, x["k"], x["v"], exit_flags=self.exit_flags)
         abi.attend(self._attend_args(l))
         return act
 
@@ -144,6 +151,8 @@ class PrefillRun:
         T = wl.n_loops if upto is None else upto
         recs: List[LoopRecord] = []
         cand = None
+        if self.exit_flags is not None:
+            self.exit_flags.zero_()
         for l in range(1, T + 1):
             if l <= wl.n_full:
                 self.full_loop(l)
@@ -158,6 +167,8 @@ class PrefillRun:
             if record:
                 rec.o, rec.lse, rec.colmass = self.o.clone(), self.lse.clone(), self.colmass.clone()
                 rec.arena = self.kv.arena.clone()
+                if self.exit_flags is not None:
+                    rec.exited = self.exit_flags.clone()
             recs.append(rec)
         return recs
 
@@ -166,10 +177,14 @@ class DecodeRun:
     """Decode workload: n_seq sequences, one new query per sequence and loop."""
 
     def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], ctx_sets: Dict[int, List[np.ndarray]],
-                 device="cuda", fuse: bool = True, formula: str = "column", freeze_keys: bool = False):
+                 device="cuda", fuse: bool = True, formula: str = "column", freeze_keys: bool = False,
+                 exit_threshold: Optional[float] = None):
         assert wl.decode
         self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
         self.formula, self.freeze_keys = formula, freeze_keys
+        self.exit_threshold = exit_threshold
+        self.exit_flags = (torch.zeros(wl.n_seq, dtype=torch.int32, device=device)
+                           if exit_threshold is not None else None)
         S, n, H, d = wl.n_seq, wl.n_tokens, wl.n_heads, wl.head_dim
         dt = torch_dtype(wl)
         self.kv = abi.KVStore(S, H, d, n, wl.n_loops, dt, wl.layer_caps(), device,
@@ -201,7 +216,7 @@ class DecodeRun:
             commit = dict(k_new=x["k"], v_new=x["v"], slot_base=self.ctx[l].shape[1], reset=False)
         return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, x["q"], self.inp[l - 1]["q"], self.last, 1,
                                self.keys, self.o, self.lse, self.colmass, ws, q_compact=True, o_compact=True,
-                               commit=commit, formula=self.formula)
+                               commit=commit, formula=self.formula, exit_flags=self.exit_flags)
 
     def build_context(self) -> None:
         for l in range(1, self.wl.n_loops + 1):
@@ -211,17 +226,23 @@ class DecodeRun:
     def loop(self, l: int) -> None:
         wl, x = self.wl, self.inp[l]
         slot_base = 0 if l == 1 else self.ctx[l].shape[1]
+        if l >= 2 and self.exit_flags is not None:   # early exit of each sequence, from its new token's change
+            abi.exit_check(self.exit_flags, self.exit_threshold, h_cur=self.inp[l - 1]["h"], h_prev=self.inp[l - 2]["h"])
         if l == 1 or not self.fuse:
-            abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False)
+            abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False,
+                          exit_flags=self.exit_flags)
         if l >= 2 and not (self.freeze_keys and l > 2):
             abi.select_keys(self.colmass, wl.n_keys, self.keys)
         abi.attend(self._args(l, self.workspace))
 
     def run(self, record: bool = False) -> List[LoopRecord]:
         recs = []
+        if self.exit_flags is not None:
+            self.exit_flags.zero_()
         for l in range(1, self.wl.n_loops + 1):
             self.loop(l)
             if record:
                 recs.append(LoopRecord(keys=self.keys.clone() if l >= 2 else None, o=self.o.clone(),
-                                       lse=self.lse.clone(), colmass=self.colmass.clone()))
+                                       lse=self.lse.clone(), colmass=self.colmass.clone(),
+                                       exited=None if self.exit_flags is None else self.exit_flags.clone()))
         return recs

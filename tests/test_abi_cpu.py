@@ -24,11 +24,11 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(abi.EXPORTS)
-    assert abi.abi_version() == 3
+    assert abi.abi_version() == 4
 
 
 def _desc(wl, group=32, bits=4):
@@ -177,3 +177,39 @@ def test_attend_formula_validation(L):
     a.mode, a.version, a.active_idx, a.n_active = abi.FL_ATTEND_FULL, 1, None, 256
     a.formula = abi.FL_FORMULA_MIXTURE
     assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG          # FULL: column only
+
+
+def test_exit_check_validation(L):
+    a = abi.fl_exit_args()
+    assert L.flashloop_exit_check(C.byref(a), None) == abi.FL_ERR_ARG              # NULL flags
+    assert b"exit_flags" in L.flashloop_last_error()
+    a.exit_flags, a.n_seq, a.n_rows = 256, 0, 10
+    assert L.flashloop_exit_check(C.byref(a), None) == abi.FL_ERR_ARG              # n_seq 0
+    a.n_seq = 2
+    assert L.flashloop_exit_check(C.byref(a), None) == abi.FL_ERR_ARG              # no scores, no h
+    a.h_cur = a.h_prev = 256
+    a.h_dtype, a.hidden = abi.FL_BF16, 12
+    assert L.flashloop_exit_check(C.byref(a), None) == abi.FL_ERR_UNSUPPORTED      # hidden % 8
+    a.exit_flags = 258
+    assert L.flashloop_exit_check(C.byref(a), None) == abi.FL_ERR_ARG              # misaligned flags
+    a.exit_flags, a.hidden, a.n_rows = 256, 64, 0
+    assert L.flashloop_exit_check(C.byref(a), None) == abi.FL_ERR_ARG              # n_rows 0
+
+
+def test_exit_flags_alignment(L):
+    d = _desc(configs.TINY)
+    d.arena, d.arena_bytes = 256, abi.kv_arena_bytes(d)
+    c = abi.fl_commit_args()
+    c.kv = C.pointer(d)
+    c.version, c.n_active = 1, 5
+    c.active_idx, c.k_new, c.v_new = 256, 256, 256
+    c.exit_flags = 258
+    assert L.flashloop_kv_commit(C.byref(c), None) == abi.FL_ERR_ARG
+    assert b"exit_flags" in L.flashloop_last_error()
+    a = abi.fl_attend_args()
+    a.kv = C.pointer(d)
+    a.mode, a.version, a.n_active = abi.FL_ATTEND_LAZY, 2, 0
+    a.q_cur = a.q_prev = a.o = a.lse = a.colmass = 256
+    a.key_idx, a.n_keys = 256, 26
+    a.exit_flags = 258
+    assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG
