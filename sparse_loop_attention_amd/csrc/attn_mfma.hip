@@ -134,7 +134,10 @@ __device__ __forceinline__ int vt_pos(int k16) {
 // commit is fused, the commit blocks (16 head rows each) and the slot-table
 // blocks (256 tokens each).  The gather never reads what the fused commit
 // writes (layer `version`): an active key's version is derived from k_new/v_new.
-template <int DT, int D, bool LAZY, bool FUSE>
+// U key slots of a 16-lane group walk their chains together (U = 4: four
+// times the loads in flight, for grids too small to fill the chip; U = 1
+// keeps the registers, and so the occupancy, of large grids).
+template <int DT, int D, bool LAZY, bool FUSE, int U>
 __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArgs cm) {
   __shared__ uint16_t sv[2][64][D + 2];
   const int n_tiles = a.n_keys_pad / 64;
@@ -178,53 +181,70 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
   if (kv.exited(s)) return;                               // uniform per workgroup
   const bool live = 8 * p < D;
   const int32_t* act_s = FUSE ? a.act + static_cast<int64_t>(s) * a.n_rows : nullptr;
+  // the 16-lane group's 4 key slots, U at a time (recon_kv keeps every slot
+  // and record load of the U keys in flight at once)
 #pragma unroll 1
-  for (int kk = 0; kk < 4; ++kk) {
-    const int local = g * 4 + kk;
-    const int t = tile * 64 + local;
-    int j = -1;
-    if (t < a.n_keys) j = a.key_idx ? a.key_idx[static_cast<int64_t>(sh) * a.n_keys + t] : t;
-    float x[8] = {}, xp[8] = {};
-    const int64_t krow = (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * p;
-    if (live) {
-      float y[8] = {}, yp[8] = {};
-      if (FUSE) {
-        // versions v-1 from the chain, version v from this loop's new rows
-        if (j >= 0) {
-          // a reset commit clears layer v for the tokens it does not write; otherwise
-          // layer v may hold earlier commits' records (an active key's own entry is
-          // overridden below)
-          const int vw = cm.reset ? a.version - 1 : a.version;
-          recon8<DT>(kv, 0, s, h, j, vw, p, x, cm.reset ? nullptr : xp);
-          recon8<DT>(kv, 1, s, h, j, vw, p, y, cm.reset ? nullptr : yp);
-          if (cm.reset) {
+  for (int k0 = 0; k0 < 4; k0 += U) {
+    int jj[U];
+    bool ok[U];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { xp[e] = x[e]; yp[e] = y[e]; }
-          }
-        }
-        const int ra = j >= 0 ? find_active(act_s, a.n_rows, j) : -1;
+    for (int kk = 0; kk < U; ++kk) {
+      const int t = tile * 64 + g * 4 + k0 + kk;
+      int j = -1;
+      if (t < a.n_keys) j = a.key_idx ? a.key_idx[static_cast<int64_t>(sh) * a.n_keys + t] : t;
+      jj[kk] = j;
+      ok[kk] = live && j >= 0;
+    }
+    float x[U][8], y[U][8], xp[U][8], yp[U][8];
+    if (FUSE) {
+      // versions v-1 from the chain, version v from this loop's new rows.  A
+      // reset commit clears layer v for the tokens it does not write; otherwise
+      // layer v may hold earlier commits' records (an active key's own entry is
+      // overridden below).
+      if (cm.reset) {
+        recon_kv<DT, U, false>(kv, s, h, jj, ok, a.version - 1, p, x, y, xp, yp);
+#pragma unroll
+        for (int kk = 0; kk < U; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { xp[kk][e] = x[kk][e]; yp[kk][e] = y[kk][e]; }
+      } else {
+        recon_kv<DT, U, true>(kv, s, h, jj, ok, a.version, p, x, y, xp, yp);
+      }
+#pragma unroll
+      for (int kk = 0; kk < U; ++kk) {
+        const int ra = ok[kk] ? find_active(act_s, a.n_rows, jj[kk]) : -1;
         if (ra >= 0) {
           const int64_t src_rows = cm.src_compact ? a.n_rows : kv.N;
-          const int64_t src = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? ra : j)) * kv.H + h) * D + 8 * p;
+          const int64_t src =
+              ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? ra : jj[kk])) * kv.H + h) * D + 8 * p;
           float kn[8], vn[8];
           load8<DT>(cm.k_new, src, kn);
           load8<DT>(cm.v_new, src, vn);
-          advance8(kv, kn, xp, true, x);
-          advance8(kv, vn, yp, true, y);
+          advance8(kv, kn, xp[kk], true, x[kk]);
+          advance8(kv, vn, yp[kk], true, y[kk]);
         }
-      } else {
-        if (j >= 0) recon8<DT>(kv, 0, s, h, j, a.version, p, x, LAZY ? xp : nullptr);
-        if (j >= 0) recon8<DT>(kv, 1, s, h, j, a.version, p, y, LAZY ? yp : nullptr);
       }
-      store8<FL_BF16>(a.kc, krow, x);
-      if (LAZY) store8<FL_BF16>(a.kp, krow, xp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[0][local][8 * p + e] = v_operand_bits(y[e]);
-        if (LAZY) sv[1][local][8 * p + e] = v_operand_bits(yp[e]);
-      }
+    } else if (LAZY) {
+      recon_kv<DT, U, true>(kv, s, h, jj, ok, a.version, p, x, y, xp, yp);
+    } else {
+      recon_kv<DT, U, false>(kv, s, h, jj, ok, a.version, p, x, y, xp, yp);
     }
-    if (p == 0) a.kidx[static_cast<int64_t>(sh) * a.n_keys_pad + t] = j >= 0 ? j : INT_MAX;
+#pragma unroll
+    for (int kk = 0; kk < U; ++kk) {
+      const int local = g * 4 + k0 + kk;
+      const int t = tile * 64 + local;
+      if (live) {
+        const int64_t krow = (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * p;
+        store8<FL_BF16>(a.kc, krow, x[kk]);
+        if (LAZY) store8<FL_BF16>(a.kp, krow, xp[kk]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sv[0][local][8 * p + e] = v_operand_bits(y[kk][e]);
+          if (LAZY) sv[1][local][8 * p + e] = v_operand_bits(yp[kk][e]);
+        }
+      }
+      if (p == 0) a.kidx[static_cast<int64_t>(sh) * a.n_keys_pad + t] = jj[kk] >= 0 ? jj[kk] : INT_MAX;
+    }
   }
   __syncthreads();
   // V^T: thread handles (dim, 8 consecutive stored positions)
@@ -1169,7 +1189,13 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   dim3 gg(static_cast<unsigned>(gblocks));
   {
     TimedLaunch t(st, fuse ? "gather_commit_lazy" : lazy ? "gather_lazy" : "gather_full");
-#define FL_GATHER(DTV, LZ, FU) hipLaunchKernelGGL((k_gather<DTV, D, LZ, FU>), gg, dim3(256), 0, st, kv, a, cm)
+    // four keys per chain walk when the gather blocks alone leave CUs idle
+    const bool wide = static_cast<int64_t>(sh) * (a.n_keys_pad / 64) < 512;
+#define FL_GATHER(DTV, LZ, FU)                                                                  \
+  do {                                                                                         \
+    if (wide) hipLaunchKernelGGL((k_gather<DTV, D, LZ, FU, 4>), gg, dim3(256), 0, st, kv, a, cm); \
+    else hipLaunchKernelGGL((k_gather<DTV, D, LZ, FU, 1>), gg, dim3(256), 0, st, kv, a, cm);      \
+  } while (0)
     if (kv.dtype == FL_BF16) {
       if (fuse) FL_GATHER(FL_BF16, true, true);
       else if (lazy) FL_GATHER(FL_BF16, true, false);

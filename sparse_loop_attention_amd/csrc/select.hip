@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
   constexpr int kBits = sizeof(KeyT) * 8;
   __shared__ int hist[256];
   __shared__ int scan_tmp[kTopkWaves + 1];
-  __shared__ int sel_bin, sel_above;
+  __shared__ int sel_bin, sel_above, sel_count;
 
   const int64_t seg = blockIdx.x;
   const ScoreT* src = scores + seg * seg_len;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
     key[e] = i < seg_len ? order_key(src[i]) : KeyT(0);
   }
 
-  if (tid == 0) { sel_bin = 0; sel_above = 0; }
+  if (tid == 0) { sel_bin = 0; sel_above = 0; sel_count = 0; }
   KeyT prefix = 0, pmask = 0;
   int k_rem = k;                                      // how many still to take at/below prefix
   for (int shift = kBits - 8; shift >= 0; shift -= 8) {
@@ -223,26 +223,31 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
         if (lane >= o) incl += t;
       }
       int above = incl - s;                           // count in bins strictly above my 4
-      int found = -1, found_above = 0;
+      int found = -1, found_above = 0, found_count = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (found < 0 && above < k_rem && above + c[i] >= k_rem) { found = 255 - 4 * lane - i; found_above = above; }
+        if (found < 0 && above < k_rem && above + c[i] >= k_rem) {
+          found = 255 - 4 * lane - i; found_above = above; found_count = c[i];
+        }
         above += c[i];
       }
-      if (found >= 0) { sel_bin = found; sel_above = found_above; }
+      if (found >= 0) { sel_bin = found; sel_above = found_above; sel_count = found_count; }
     }
     __syncthreads();
     const int b = sel_bin;
     k_rem -= sel_above;
     prefix |= static_cast<KeyT>(b) << shift;
     pmask |= static_cast<KeyT>(0xFF) << shift;
+    const bool whole_bin = sel_count == k_rem;        // every key of the crossing bin is taken
     __syncthreads();
+    if (whole_bin) break;
   }
-  // prefix is now the exact key of the k-th largest; take every key above it and
-  // the first k_rem keys equal to it in index order.
+  // prefix is the k-th largest key on the bits of pmask (all of them unless
+  // the crossing bin was taken whole); take every key above it there and the
+  // first k_rem keys equal to it in index order.
   int n_eq = 0;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) n_eq += (first + e < seg_len && key[e] == prefix) ? 1 : 0;
+  for (int e = 0; e < EPT; ++e) n_eq += (first + e < seg_len && (key[e] & pmask) == prefix) ? 1 : 0;
   int tot;
   int eq_before = block_excl_scan(n_eq, scan_tmp, tot);
   int n_sel = 0;
@@ -251,8 +256,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       if (first + e >= seg_len) continue;
-      if (key[e] > prefix) ++n_sel;
-      else if (key[e] == prefix) { if (eq_rank < k_rem) ++n_sel; ++eq_rank; }
+      const KeyT km = key[e] & pmask;
+      if (km > prefix) ++n_sel;
+      else if (km == prefix) { if (eq_rank < k_rem) ++n_sel; ++eq_rank; }
     }
   }
   int pos = block_excl_scan(n_sel, scan_tmp, tot);
@@ -262,8 +268,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
     for (int e = 0; e < EPT; ++e) {
       if (first + e >= seg_len) continue;
       bool take = false;
-      if (key[e] > prefix) take = true;
-      else if (key[e] == prefix) { take = eq_rank < k_rem; ++eq_rank; }
+      const KeyT km = key[e] & pmask;
+      if (km > prefix) take = true;
+      else if (km == prefix) { take = eq_rank < k_rem; ++eq_rank; }
       if (take) {
         if (pos < k) dst[pos] = static_cast<int32_t>(first + e);
         ++pos;
