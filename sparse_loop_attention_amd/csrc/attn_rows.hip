@@ -59,8 +59,12 @@ constexpr size_t kRowColMaxLds = 40960; // largest logit array (bytes) kept in L
 // wave 0 first writes the row's K and V records of head h (and, for head 0,
 // the row's share of the slot-table column).  With COL the workgroup owns
 // the only active row of its sequence and updates the column mass itself.
-template <int DT, bool LAZY, bool FUSE, bool COL>
+// BASE (full loops over version 1): keys are the base rows, with no chain to
+// walk; the smaller register footprint doubles the waves per CU, and with
+// them the loads in flight.
+template <int DT, bool LAZY, bool FUSE, bool COL, bool BASE = false>
 __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a, CommitArgs cm) {
+  static_assert(!(BASE && LAZY), "BASE serves full loops");
   constexpr int kU = LAZY ? 2 : 4;                        // keys per 16-lane group and step
   const int r = blockIdx.x, sh = blockIdx.y;
   const int H = kv.H, d = kv.d;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a
       i32x4 sl = i32x4{-1, -1, -1, -1};
       if (t < t_end) {
         jj = LAZY ? sel[t] : t;
-        if (a.version >= 2) sl = *reinterpret_cast<const i32x4*>(kv.slot_row(s, jj));
+        if (!BASE && a.version >= 2) sl = *reinterpret_cast<const i32x4*>(kv.slot_row(s, jj));
         if (FUSE) ra = find_active(act_s, a.n_act, jj);
       }
       s_j[wave][lane] = jj;
@@ -184,6 +188,18 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a
             }
             advance8(kv, kn, kp[u], live, kc[u]);
             advance8(kv, vn, vp[u], live, vc[u]);
+          }
+        }
+      } else if (BASE) {
+        const int64_t row = (static_cast<int64_t>(s) * H + h) * kv.N;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (ok[u]) {
+            load8<DT>(kv.arena + kv.base[0], (row + j[u]) * d + 8 * p, kc[u]);
+            load8<DT>(kv.arena + kv.base[1], (row + j[u]) * d + 8 * p, vc[u]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kc[u][e] = vc[u][e] = 0.0f;
           }
         }
       } else {
@@ -389,18 +405,21 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
   }
   {
     TimedLaunch t(st, fuse ? "rows_attend_commit_lazy" : lazy ? "rows_attend_lazy" : "rows_attend_full");
-#define FL_ROWS(DTV, LZ, FU, CO) \
-  hipLaunchKernelGGL((k_rows_wg<DTV, LZ, FU, CO>), g1, dim3(64 * kRowWaves), lds, st, kv, a, cm)
-#define FL_ROWS_COL(DTV, LZ, FU) \
-  do { if (col) FL_ROWS(DTV, LZ, FU, true); else FL_ROWS(DTV, LZ, FU, false); } while (0)
+#define FL_ROWS(DTV, LZ, FU, CO, BA) \
+  hipLaunchKernelGGL((k_rows_wg<DTV, LZ, FU, CO, BA>), g1, dim3(64 * kRowWaves), lds, st, kv, a, cm)
+#define FL_ROWS_COL(DTV, LZ, FU, BA) \
+  do { if (col) FL_ROWS(DTV, LZ, FU, true, BA); else FL_ROWS(DTV, LZ, FU, false, BA); } while (0)
+    const bool base = !lazy && x.version == 1;
     if (kv.dtype == FL_BF16) {
-      if (fuse) FL_ROWS_COL(FL_BF16, true, true);
-      else if (lazy) FL_ROWS_COL(FL_BF16, true, false);
-      else FL_ROWS_COL(FL_BF16, false, false);
+      if (fuse) FL_ROWS_COL(FL_BF16, true, true, false);
+      else if (lazy) FL_ROWS_COL(FL_BF16, true, false, false);
+      else if (base) FL_ROWS_COL(FL_BF16, false, false, true);
+      else FL_ROWS_COL(FL_BF16, false, false, false);
     } else {
-      if (fuse) FL_ROWS_COL(FL_F32, true, true);
-      else if (lazy) FL_ROWS_COL(FL_F32, true, false);
-      else FL_ROWS_COL(FL_F32, false, false);
+      if (fuse) FL_ROWS_COL(FL_F32, true, true, false);
+      else if (lazy) FL_ROWS_COL(FL_F32, true, false, false);
+      else if (base) FL_ROWS_COL(FL_F32, false, false, true);
+      else FL_ROWS_COL(FL_F32, false, false, false);
     }
 #undef FL_ROWS_COL
 #undef FL_ROWS
