@@ -42,11 +42,23 @@ struct RowArgs {
   const int32_t* exit_flags;  // [n_seq] or null: nonzero = skip the sequence (early exit)
 };
 
-__device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int v) {
-  int lo = 0, hi = n;
+// Number of entries of the ascending array a[0..n) that are <= v, by a
+// 64-way search across the wave: each round the lanes probe 64 evenly spaced
+// entries and the ballot of "<= v" (a prefix of the lanes) narrows the range
+// 64-fold, so 820 entries take two rounds of loads instead of ten dependent
+// ones.  Every lane of the wave must call it; every lane gets the result.
+__device__ __forceinline__ int wave_count_le(const int32_t* a, int n, int v) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;                                     // the count lies in [lo, hi]
   while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] <= v) lo = mid + 1; else hi = mid;
+    const int step = (hi - lo + 63) / 64;
+    const int pos = lo + lane * step;
+    const uint64_t le = __ballot(pos < hi && a[pos] <= v);
+    const int c = __popcll(le);                           // entries lo, lo+step, ... lo+(c-1)*step are <= v
+    if (c == 0) return lo;
+    const int top = min(hi, lo + c * step);               // entries from here on are > v
+    lo = lo + (c - 1) * step + 1;
+    hi = top;
   }
   return lo;
 }
@@ -75,7 +87,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void k_rows_wg(KvView kv, RowArgs a
   const int32_t* act_s = a.act ? a.act + static_cast<int64_t>(s) * a.n_act : nullptr;
   const int i = act_s ? act_s[r] : r;
   const int32_t* sel = LAZY ? a.keys + static_cast<int64_t>(sh) * a.n_keys : nullptr;
-  const int cnt = LAZY ? upper_bound_i32(sel, a.n_keys, i) : i + 1;     // visible key slots
+  const int cnt = LAZY ? wave_count_le(sel, a.n_keys, i) : i + 1;      // visible key slots
 
   extern __shared__ float s_lg[];                         // COL: logits [LAZY ? 2 : 1][key_slots]
   __shared__ int s_j[kRowWaves][64];

@@ -14,16 +14,19 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));   // 16-byte int vector (
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
+// Two float32 -> two bfloat16, round to nearest even (one v_cvt_pk_bf16_f32);
+// a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 // float32 -> bfloat16 bits, round to nearest even (inputs are finite).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 // Value of f rounded to the nearest bfloat16 (ties to even), as float32.
-__device__ __forceinline__ float round_bf16(float f) {
-  return __uint_as_float(static_cast<uint32_t>(f32_to_bf16(f)) << 16);
-}
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(pack_bf16x2(f, 0.0f) << 16); }
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
   _Float16 v = __builtin_bit_cast(_Float16, h);
   return static_cast<float>(v);
@@ -66,8 +69,7 @@ __device__ __forceinline__ void store8(void* base, int64_t elem, const float in[
     u32x4_t w;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16(in[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16(in[2 * i + 1])) << 16);
+      w[i] = pack_bf16x2(in[2 * i], in[2 * i + 1]);
     *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(base) + elem) = w;
   } else {
     f32x4_t* p = reinterpret_cast<f32x4_t*>(static_cast<float*>(base) + elem);
@@ -143,7 +145,11 @@ template <int DT>
 __device__ __forceinline__ void to_working8(float x[8]) {
   if constexpr (DT == FL_BF16) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = round_bf16(x[e]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      x[2 * i] = __uint_as_float(w << 16);
+      x[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
+    }
   }
 }
 
