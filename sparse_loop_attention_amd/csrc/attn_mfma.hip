@@ -76,6 +76,7 @@ struct MfmaArgs {
   int32_t fsplit_u, f_items, f_tiles;   // workgroups and row tiles per head
   float4* fpart;            // [sh][f_items][D/8 + 1][512] partial acc, (max, sum)
   int32_t* fcount;          // [sh][f_tiles] parts finished (zeroed by the gather launch)
+  int32_t* ccount;          // [sh][n_keys_pad / 256] column-mass ranges finished (zeroed by the gather), or null
   // early exit: sequences with a nonzero flag are skipped by every kernel
   const int32_t* exit_flags;  // [n_seq] or null
   int32_t heads;
@@ -145,6 +146,8 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
   const int g = threadIdx.x >> 4, p = threadIdx.x & 15;
   if (a.fcount && b == 0)                                 // the forward pass's arrival counters
     for (int i = threadIdx.x; i < a.n_sh * a.f_tiles; i += 256) a.fcount[i] = 0;
+  if (a.ccount && b == 0)                                 // the column-mass ranges' counters
+    for (int i = threadIdx.x; i < a.n_sh * (a.n_keys_pad / 256); i += 256) a.ccount[i] = 0;
   if (FUSE && b >= a.n_sh * n_tiles) {
     b -= a.n_sh * n_tiles;
     const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2;
@@ -934,6 +937,43 @@ __device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H
   __syncthreads();                                           // the buffers are reused by the next pass
 }
 
+// The workgroup's column sums (lane pair halves already added).  One row
+// range: written at once.  Several: each range stores its partial sums; with
+// a.ccount the range that finishes last adds them in range order and writes
+// the column mass (all ranges of a head run on one XCD, whose L2 every CU
+// shares: the stores are acknowledged before the count, and the sums are read
+// past this CU's L1), otherwise k_colmass_reduce does.  Every thread of the
+// workgroup calls it.
+template <bool LAZY>
+__device__ __forceinline__ void col_finish(const MfmaArgs& a, int N, int chunk, int sh, int kblk, int t, int kj,
+                                           float acc, int* s_arrived) {
+  const int tid = threadIdx.x, hh = (tid & 63) >> 5;
+  if (a.col_chunks == 1) {
+    if (hh == 0 && t < a.n_keys) {
+      float* dst = a.colmass + static_cast<int64_t>(sh) * N + kj;
+      if (LAZY) *dst += acc; else *dst = acc;
+    }
+    return;
+  }
+  if (hh == 0) a.col_part[(static_cast<int64_t>(chunk) * a.n_sh + sh) * a.n_keys_pad + t] = acc;
+  if (!a.ccount) return;
+  __builtin_amdgcn_s_waitcnt(0);                          // this lane's store acknowledged
+  __syncthreads();
+  if (tid == 0)
+    *s_arrived = __hip_atomic_fetch_add(a.ccount + static_cast<int64_t>(sh) * (a.n_keys_pad / 256) + kblk, 1,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*s_arrived != a.col_chunks - 1 || tid >= 256) return;
+  const int tk = kblk * 256 + tid;
+  if (tk >= a.n_keys) return;
+  float sum = 0.0f;
+  for (int ch = 0; ch < a.col_chunks; ++ch)
+    sum += __hip_atomic_load(a.col_part + (static_cast<int64_t>(ch) * a.n_sh + sh) * a.n_keys_pad + tk,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float* dst = a.colmass + static_cast<int64_t>(sh) * N + a.kidx[static_cast<int64_t>(sh) * a.n_keys_pad + tk];
+  if (LAZY) *dst += sum; else *dst = sum;
+}
+
 template <int D, bool LAZY>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_eu(4))) void k_mfma_colmass(int32_t H, int32_t N, MfmaArgs a) {
   using T = ColTiles<D>;
@@ -979,7 +1019,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_
   }
   acc += __shfl_xor(acc, 32, 64);
   if (hh != 0) return;
-  if (a.col_chunks > 1) {
+  if (a.col_chunks > 1) {                                    // added by k_colmass_reduce
     a.col_part[(static_cast<int64_t>(chunk) * a.n_sh + sh) * a.n_keys_pad + t] = acc;
   } else if (t < a.n_keys) {
     float* dst = a.colmass + static_cast<int64_t>(sh) * N + kj;
@@ -1002,7 +1042,7 @@ __global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t
   __shared__ __attribute__((aligned(16))) uint16_t sq[2][QT * QS];
   __shared__ __attribute__((aligned(16))) float sb[2][QT];
   __shared__ __attribute__((aligned(16))) int stok[2][QT];
-  __shared__ int s_start;
+  __shared__ int s_start, s_arrived;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
@@ -1122,9 +1162,7 @@ __global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t
     __syncthreads();
   }
   acc += __shfl_xor(acc, 32, 64);
-  if (hh != 0) return;
-  if (a.col_chunks > 1) a.col_part[(static_cast<int64_t>(chunk) * a.n_sh + sh) * a.n_keys_pad + t] = acc;
-  else if (t < a.n_keys) a.colmass[static_cast<int64_t>(sh) * N + kj] = acc;
+  col_finish<false>(a, N, chunk, sh, kblk, t, kj, acc, &s_arrived);
 }
 
 // Sums the per-chunk partial column masses in chunk order.
@@ -1167,6 +1205,8 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
 
   a.n_sh = static_cast<int32_t>(sh);
   a.heads = kv.H;
+  // set before the gather launch, which zeroes the counters
+  a.ccount = p.col_fused ? reinterpret_cast<int32_t*>(ws + p.off_ccount) : nullptr;
   a.exit_flags = kv.exit_flags;
   if (!lazy && p.fsplit_u > 0) {
     a.fsplit_u = p.fsplit_u;
@@ -1242,7 +1282,7 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     if (lazy) hipLaunchKernelGGL((k_mfma_colmass<D, true>), gc, dim3(512), 0, st, kv.H, kv.N, a);
     else hipLaunchKernelGGL((k_colmass_full_rows<D>), gc, dim3(512), 0, st, kv.H, kv.N, a);
   }
-  if (a.col_chunks > 1) {
+  if (a.col_chunks > 1 && !a.ccount) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = static_cast<int64_t>(a.n_sh) * a.n_keys_pad;
     dim3 gr(static_cast<unsigned>((n + 255) / 256));

@@ -130,6 +130,13 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     if (p.col_chunks < 1) p.col_chunks = 1;
     p.off_part = off;
     if (p.col_chunks > 1) off = align256(off + static_cast<uint64_t>(p.col_chunks) * sh * kpad * 4);
+    // full loops: the ranges of one key block run on one XCD when there are
+    // >= 8 heads, and the last one to finish adds the partial sums (one
+    // counter per block).  Lazy loops keep the reduction launch: the fused
+    // ending cost the two-pass kernel more registers than the launch saves.
+    p.col_fused = !lazy && p.col_chunks > 1 && sh >= 8;
+    p.off_ccount = off;
+    if (p.col_fused) off = align256(off + sh * (kpad / 256) * 4);
     p.off_logit = off;
     // forward key split of full loops: one partial (acc, max, sum of every
     // lane of the 512-thread workgroup) per workgroup, one counter per row tile

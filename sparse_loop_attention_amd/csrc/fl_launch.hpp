@@ -26,7 +26,8 @@ struct AttendPlan {
   // f_items workgroups per (sequence, head), f_tiles row tiles
   int fsplit_u, f_items, f_tiles;
   // byte offsets in the workspace
-  uint64_t off_part, off_logit, off_stat, off_gather, off_fpart, off_fcount, off_total;
+  uint64_t off_part, off_logit, off_stat, off_gather, off_fpart, off_fcount, off_ccount, off_total;
+  bool col_fused;       // several row ranges: the last range to finish adds them (no reduction launch)
 };
 // Forward key split of a full loop (0 = none) for n_sh (sequence, head) rows of
 // n_rows rows; the same answer at sizing and at launch.
