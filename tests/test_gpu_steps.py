@@ -36,7 +36,8 @@ def rel_err_ok(got, want, tol=2e-2):
 
 # --------------------------------------------------------------------------- select
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("n,hidden,k", [(1, 8, 1), (300, 64, 75), (4096, 2048, 820), (5000, 5280, 1500)])
+@pytest.mark.parametrize("n,hidden,k", [(1, 8, 1), (300, 64, 75), (4096, 2048, 820), (5000, 5280, 1500),
+                                         (65536, 64, 6554)])
 def test_select_tokens(dtype, n, hidden, k):
     rng = np.random.default_rng(n + hidden)
     h_prev = rng.standard_normal((n, hidden)).astype(np.float32)
@@ -78,7 +79,8 @@ def test_select_tokens_candidates():
 
 
 @pytest.mark.parametrize("n_seg,seg_len,k", [(1, 1, 1), (1, 256, 26), (16, 4096, 410), (3, 32768, 3277),
-                                             (512, 8192, 820), (55, 16384, 1639), (2, 1000, 1000), (2, 700, 0)])
+                                             (512, 8192, 820), (55, 16384, 1639), (2, 1000, 1000), (2, 700, 0),
+                                             (1, 65536, 6554), (4, 65536, 1)])
 def test_select_keys(n_seg, seg_len, k):
     rng = np.random.default_rng(seg_len + k)
     c = rng.random((n_seg, seg_len)).astype(np.float32) * 5
@@ -92,6 +94,20 @@ def test_select_keys(n_seg, seg_len, k):
     torch.cuda.synchronize()
     want = oracle.select_keys(c, k) if k else np.zeros((n_seg, 0), np.int32)
     assert np.array_equal(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("k", [1, 37, 500, 2047])
+def test_select_keys_spread_exponents(k):
+    """Values spread over many binades: the crossing bin is usually taken whole
+    after one or two radix passes, which ends the selection early."""
+    rng = np.random.default_rng(k)
+    c = (rng.random((3, 2048)) + 1.0) * np.exp2(rng.integers(-60, 60, (3, 2048)))
+    c[1] = -c[1]                                                   # all negative
+    c = c.astype(np.float32)
+    out = torch.empty(3, k, dtype=torch.int32, device=DEV)
+    abi.select_keys(torch.from_numpy(c).to(DEV), k, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.select_keys(c, k))
 
 
 def test_select_keys_all_equal():
