@@ -160,12 +160,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds_waves, int& total
   return res;
 }
 
+// Keys stay in registers as 32-bit words: the whole order key of a float, the
+// high word of a double's.  A double's low word is reloaded from the scores
+// (a read served by the L2) only where a pass or the final comparison needs
+// it, i.e. for keys whose high word ties the selected prefix; every other key
+// is decided by its high word.
 template <typename ScoreT, int EPT>
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict__ scores,
                                                        int64_t seg_len, int32_t k,
                                                        int32_t* __restrict__ out_idx) {
-  using KeyT = decltype(order_key(ScoreT{}));
-  constexpr int kBits = sizeof(KeyT) * 8;
+  constexpr bool WIDE = sizeof(ScoreT) == 8;
+  constexpr int kBits = WIDE ? 64 : 32;
   __shared__ int hist[256];
   __shared__ int scan_tmp[kTopkWaves + 1];
   __shared__ int sel_bin, sel_above, sel_count;
@@ -181,23 +186,31 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
     for (int64_t i = tid; i < seg_len; i += kTopkThreads) dst[i] = static_cast<int32_t>(i);
     return;
   }
-  KeyT key[EPT];
+  uint32_t hi[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const int64_t i = first + e;
-    key[e] = i < seg_len ? order_key(src[i]) : KeyT(0);
+    hi[e] = i < seg_len ? static_cast<uint32_t>(order_key(src[i]) >> (WIDE ? 32 : 0)) : 0u;
   }
+  auto lo_of = [&](int e) -> uint32_t { return static_cast<uint32_t>(order_key(src[first + e])); };
 
   if (tid == 0) { sel_bin = 0; sel_above = 0; sel_count = 0; }
-  KeyT prefix = 0, pmask = 0;
+  uint32_t pre_hi = 0, msk_hi = 0, pre_lo = 0, msk_lo = 0;   // the selected prefix and its bits
   int k_rem = k;                                      // how many still to take at/below prefix
   for (int shift = kBits - 8; shift >= 0; shift -= 8) {
+    const bool low = WIDE && shift < 32;              // a pass over the low word
+    const int sh = low || !WIDE ? shift : shift - 32;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const bool act = (first + e < seg_len) && ((key[e] & pmask) == prefix);
-      const int bin = static_cast<int>((key[e] >> shift) & 0xFF);
+      bool act = (first + e < seg_len) && ((hi[e] & msk_hi) == pre_hi);
+      uint32_t word = hi[e];
+      if (low && act) {
+        word = lo_of(e);
+        act = (word & msk_lo) == pre_lo;
+      }
+      const int bin = static_cast<int>((word >> sh) & 0xFF);
       // fast path: every active lane of the wave falls into one bin
       const uint64_t m = __ballot(act);
       if (m == 0) continue;
@@ -234,20 +247,28 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
       if (found >= 0) { sel_bin = found; sel_above = found_above; sel_count = found_count; }
     }
     __syncthreads();
-    const int b = sel_bin;
+    const uint32_t b = static_cast<uint32_t>(sel_bin);
     k_rem -= sel_above;
-    prefix |= static_cast<KeyT>(b) << shift;
-    pmask |= static_cast<KeyT>(0xFF) << shift;
+    if (low) { pre_lo |= b << sh; msk_lo |= 0xFFu << sh; }
+    else { pre_hi |= b << sh; msk_hi |= 0xFFu << sh; }
     const bool whole_bin = sel_count == k_rem;        // every key of the crossing bin is taken
     __syncthreads();
     if (whole_bin) break;
   }
-  // prefix is the k-th largest key on the bits of pmask (all of them unless
-  // the crossing bin was taken whole); take every key above it there and the
-  // first k_rem keys equal to it in index order.
+  // The prefix is the k-th largest key on the bits fixed so far (all of them
+  // unless the crossing bin was taken whole); take every key above it there
+  // and the first k_rem keys equal to it in index order.  cmp: +1 above, 0
+  // equal, -1 below.
+  auto cmp = [&](int e) -> int {
+    const uint32_t h = hi[e] & msk_hi;
+    if (h != pre_hi) return h > pre_hi ? 1 : -1;
+    if (!WIDE || msk_lo == 0) return 0;
+    const uint32_t l = lo_of(e) & msk_lo;
+    return l > pre_lo ? 1 : (l == pre_lo ? 0 : -1);
+  };
   int n_eq = 0;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) n_eq += (first + e < seg_len && (key[e] & pmask) == prefix) ? 1 : 0;
+  for (int e = 0; e < EPT; ++e) n_eq += (first + e < seg_len && cmp(e) == 0) ? 1 : 0;
   int tot;
   int eq_before = block_excl_scan(n_eq, scan_tmp, tot);
   int n_sel = 0;
@@ -256,9 +277,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       if (first + e >= seg_len) continue;
-      const KeyT km = key[e] & pmask;
-      if (km > prefix) ++n_sel;
-      else if (km == prefix) { if (eq_rank < k_rem) ++n_sel; ++eq_rank; }
+      const int c = cmp(e);
+      if (c > 0) ++n_sel;
+      else if (c == 0) { if (eq_rank < k_rem) ++n_sel; ++eq_rank; }
     }
   }
   int pos = block_excl_scan(n_sel, scan_tmp, tot);
@@ -267,10 +288,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       if (first + e >= seg_len) continue;
+      const int c = cmp(e);
       bool take = false;
-      const KeyT km = key[e] & pmask;
-      if (km > prefix) take = true;
-      else if (km == prefix) { take = eq_rank < k_rem; ++eq_rank; }
+      if (c > 0) take = true;
+      else if (c == 0) { take = eq_rank < k_rem; ++eq_rank; }
       if (take) {
         if (pos < k) dst[pos] = static_cast<int32_t>(first + e);
         ++pos;
