@@ -81,6 +81,7 @@ int plan_fwd_split(int64_t n_sh, int64_t n_rows) {
   const auto key = std::make_pair(n_sh, n_rows);
   const auto it = memo.find(key);
   if (it != memo.end()) return it->second;
+  if (memo.size() >= 4096) memo.clear();                // shapes seen by a long-running caller
   const int64_t kt_max = fwd_key_tiles(n_rows, T - 1);
   int best = 0;
   double best_t = fwd_makespan(n_sh, n_rows, 0);
