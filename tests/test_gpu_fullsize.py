@@ -209,3 +209,41 @@ def test_fullsize_decode_sampled_sequences():
             _within(g.o.cpu().numpy()[s], r["o"], f"seq {s} loop {l} o")
             _within(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
             _within(g.colmass.cpu().numpy()[s], r["colmass"], f"seq {s} loop {l} colmass")
+
+
+def test_fullsize_decode_early_exit():
+    """Early exit (reading E1) at the decode workload's full size: every
+    sequence's flag after every loop against the decisions taken from its new
+    token's exact squared changes, and sequences 0 and 31 end to end against
+    the oracle with the same threshold."""
+    wl = configs.DECODE
+    syn = SyntheticLoops(wl)
+    ctx_sets = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)}
+    data, inputs, hs = {}, {}, {}
+    dt = driver.torch_dtype(wl)
+    for l, x in syn:
+        inputs[l] = {k: driver.to_device(v, dt, DEV) for k, v in x.items()}
+        data[l] = {k: v[[0, wl.n_seq - 1]].copy() for k, v in x.items()}     # sequences 0 and 31
+        hs[l] = x["h"].astype(np.float64).copy()                           # [S, 1, hidden]
+    change = np.array([[((hs[l - 1][s] - hs[l - 2][s]) ** 2).sum() for l in range(2, wl.n_loops + 1)]
+                       for s in range(wl.n_seq)])
+    vals = np.sort(change.ravel())
+    i = int(np.searchsorted(vals, 10.0))                                  # a threshold near 10, between two changes
+    tau = math.sqrt(vals[i - 1] * vals[i])
+    assert np.all(np.abs(vals - tau) > 1e-6 * tau)
+    ran = [wl.n_loops if not (change[s] < tau).any() else 1 + int(np.argmax(change[s] < tau))
+           for s in range(wl.n_seq)]
+    assert min(ran) < wl.n_loops < max(ran) + 1 and len(set(ran)) > 1
+    run = driver.DecodeRun(wl, inputs, ctx_sets, DEV, exit_threshold=tau)
+    run.build_context()
+    recs = run.run(record=True)
+    torch.cuda.synchronize()
+    for l in range(1, wl.n_loops + 1):
+        flags = recs[l - 1].exited.cpu().numpy()
+        assert flags.tolist() == [int(l > ran[s]) for s in range(wl.n_seq)], f"loop {l}"
+    for si, s in enumerate((0, wl.n_seq - 1)):
+        ref, _ = oracle.run_decode_seq(wl, None, si, {l: ctx_sets[l][s] for l in ctx_sets}, data, exit_threshold=tau)
+        assert len(ref) == ran[s]
+        _within(recs[-1].o.cpu().numpy()[s], ref[-1]["o"], f"seq {s} o")
+        _within(recs[-1].lse.cpu().numpy()[s], ref[-1]["lse"], f"seq {s} lse")
+        _within(recs[-1].colmass.cpu().numpy()[s], ref[-1]["colmass"], f"seq {s} colmass")
