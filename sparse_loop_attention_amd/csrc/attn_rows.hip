@@ -18,50 +18,10 @@
 #include "fl_common.hpp"
 #include "fl_commit.hpp"
 #include "fl_launch.hpp"
+#include "fl_rows.hpp"
 #include "fl_timing.hpp"
 
 namespace fl {
-
-struct RowArgs {
-  const void* q_cur;
-  const void* q_prev;
-  int32_t q_compact, o_compact;
-  const int32_t* act;
-  int32_t n_act;
-  const int32_t* keys;      // LAZY: [n_seq*H][n_keys]
-  int32_t n_keys;
-  float* o;
-  float* lse;
-  float* colmass;
-  int32_t version;
-  float scale;              // 1/sqrt(d)
-  int64_t key_slots;        // logit row length (n_keys or N)
-  int32_t mixture;          // LAZY: o = m*otilde + (1-m)*o_prev instead of m*otilde + o_prev - a
-  float* logit;             // [2][sh][rows][key_slots]
-  float* stat;              // [sh][rows][4] = lse_prev, lse_new, valid, -
-  const int32_t* exit_flags;  // [n_seq] or null: nonzero = skip the sequence (early exit)
-};
-
-// Number of entries of the ascending array a[0..n) that are <= v, by a
-// 64-way search across the wave: each round the lanes probe 64 evenly spaced
-// entries and the ballot of "<= v" (a prefix of the lanes) narrows the range
-// 64-fold, so 820 entries take two rounds of loads instead of ten dependent
-// ones.  Every lane of the wave must call it; every lane gets the result.
-__device__ __forceinline__ int wave_count_le(const int32_t* a, int n, int v) {
-  const int lane = threadIdx.x & 63;
-  int lo = 0, hi = n;                                     // the count lies in [lo, hi]
-  while (lo < hi) {
-    const int step = (hi - lo + 63) / 64;
-    const int pos = lo + lane * step;
-    const uint64_t le = __ballot(pos < hi && a[pos] <= v);
-    const int c = __popcll(le);                           // entries lo, lo+step, ... lo+(c-1)*step are <= v
-    if (c == 0) return lo;
-    const int top = min(hi, lo + c * step);               // entries from here on are > v
-    lo = lo + (c - 1) * step + 1;
-    hi = top;
-  }
-  return lo;
-}
 
 constexpr int kRowWaves = 8;          // waves per workgroup
 constexpr size_t kRowColMaxLds = 40960; // largest logit array (bytes) kept in LDS
@@ -414,6 +374,10 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
     cm.k_new = x.k_new; cm.v_new = x.v_new;
     cm.src_compact = x.kv_layout == FL_ROWS_COMPACT;
     cm.slot_base = x.commit_slot_base; cm.reset = x.commit_reset;
+  }
+  if (lazy) {
+    hipError_t e = hipSuccess;
+    if (launch_decode_lazy(a, kv, cm, fuse, st, &e)) return e;
   }
   {
     TimedLaunch t(st, fuse ? "rows_attend_commit_lazy" : lazy ? "rows_attend_lazy" : "rows_attend_full");
