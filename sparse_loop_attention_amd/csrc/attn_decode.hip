@@ -40,6 +40,7 @@ constexpr int kDecWaves = 8;
 constexpr int kDecD = 128;                 // head_dim of this kernel
 constexpr int kDecMaxKeys = 1536;          // staged keys per (sequence, head): 28 bytes of LDS each
 constexpr int kDecMaxLayers = 4;           // delta layers walked (versions 2..5)
+constexpr size_t kDecMaxFullLds = 40960;   // full loop: logits of every key (N <= 10240) in LDS
 constexpr uint32_t kOut = 0x80000000u;     // an offset past every range: the load returns zeros
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 
@@ -337,6 +338,149 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
   const float f = mt / Zt;
   for (int t = tid; t < cnt; t += 64 * kDecWaves)
     c[s_j[t]] += f * __expf(lg_cur[t] - Mt) - __expf(lg_prev[t] - lse_prev);
+}
+
+// Full (dense) loop over the base of one new token per sequence: keys 0..i
+// of the bf16 base, no delta chain.  Key t goes to 16-lane group t mod 32 in
+// steps of 32*U keys (each step of the workgroup reads 32*U consecutive key
+// rows); the next step's U keys per group are in flight while the current
+// ones compute.  The base rows are bf16 already, so the logits are dot2
+// products of the loaded words and only V is widened.
+template <int U>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void k_decode_full(KvView kv, RowArgs a) {
+  const int sh = blockIdx.x;
+  const int H = kv.H;
+  const int s = sh / H, h = sh % H;
+  if (kv.exited(s)) return;                               // uniform per workgroup
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, p = lane & 15;
+  const int i = a.act[s];                                 // the sequence's only row
+  const int cnt = i + 1;                                  // keys 0..i
+
+  extern __shared__ float s_lgf[];                        // [N] logits
+  __shared__ float s_mz[kDecWaves][2];
+  __shared__ float s_ac[kDecWaves][kDecD];
+
+  const uint8_t* A = kv.arena;
+  const int64_t row_bytes = static_cast<int64_t>(kv.N) * kDecD * 2;
+  const int64_t rowb = (static_cast<int64_t>(s) * H + h) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rK = range_of(A + kv.base[0] + rowb, static_cast<uint32_t>(row_bytes));
+  const __amdgpu_buffer_rsrc_t rV = range_of(A + kv.base[1] + rowb, static_cast<uint32_t>(row_bytes));
+  const uint32_t lane_b = 16 * p;
+  const int64_t qoff = ((static_cast<int64_t>(s) * (a.q_compact ? 1 : kv.N) + (a.q_compact ? 0 : i)) * H + h) * kDecD;
+  const u32x4_t qc = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q_cur) + qoff + 8 * p);
+  const int64_t orow = (static_cast<int64_t>(s) * (a.o_compact ? 1 : kv.N) + (a.o_compact ? 0 : i)) * H + h;
+
+  struct Rows { u32x4_t kb[U], vb[U]; };
+  auto issue = [&](int k, Rows& r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = wave * 4 + g + 32 * (U * k + u);
+      const uint32_t ob = t < cnt ? static_cast<uint32_t>(t) * (kDecD * 2) + lane_b : kOut;
+      r.kb[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rK, ob, 0, 0));
+      r.vb[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rV, ob, 0, 0));
+    }
+  };
+  float M = -INFINITY, Z = 0.0f;
+  float acc[8] = {};
+  auto consume = [&](int k, const Rows& r) {
+    float sc[U];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = wave * 4 + g + 32 * (U * k + u);
+      const uint32_t kw[4] = {r.kb[u][0], r.kb[u][1], r.kb[u][2], r.kb[u][3]};
+      sc[u] = group_sum<16>(dot_bf16x8(kw, qc)) * a.scale;
+      if (t < cnt) {
+        if (p == 0) s_lgf[t] = sc[u];
+        tmax = fmaxf(tmax, sc[u]);
+      } else {
+        sc[u] = -INFINITY;                                 // past the row: weight 0
+      }
+    }
+    if (tmax == -INFINITY) return;                        // uniform per 16-lane group
+    const float Mn = fmaxf(M, tmax);
+    const float corr = __expf(M - Mn);
+    Z *= corr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= corr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = __expf(sc[u] - Mn);
+      Z += w;
+      const uint32_t vw[4] = {r.vb[u][0], r.vb[u][1], r.vb[u][2], r.vb[u][3]};
+      axpy_bf16x8(acc, 1.0f, w, vw);
+    }
+    M = Mn;
+  };
+
+  const int nsteps = cnt > wave * 4 ? (cnt - wave * 4 + 32 * U - 1) / (32 * U) : 0;
+  Rows ra, rb;
+  issue(0, ra);
+  for (int k = 0; k < nsteps; k += 2) {
+    issue(k + 1, rb);
+    consume(k, ra);
+    if (k + 1 >= nsteps) break;
+    issue(k + 2, ra);
+    consume(k + 1, rb);
+  }
+
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float Mo = __shfl_xor(M, o, 64);
+    const float Zo = __shfl_xor(Z, o, 64);
+    const float Mn = fmaxf(M, Mo);
+    const float c1 = (M == -INFINITY) ? 0.0f : __expf(M - Mn);
+    const float c2 = (Mo == -INFINITY) ? 0.0f : __expf(Mo - Mn);
+    Z = Z * c1 + Zo * c2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * c1 + __shfl_xor(acc[e], o, 64) * c2;
+    M = Mn;
+  }
+  if (lane == 0) { s_mz[wave][0] = M; s_mz[wave][1] = Z; }
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_ac[wave][8 * p + e] = acc[e];
+  }
+  __syncthreads();
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) Mt = fmaxf(Mt, s_mz[w][0]);
+  float Zt = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    const float cw = (s_mz[w][0] == -INFINITY) ? 0.0f : __expf(s_mz[w][0] - Mt);
+    Zt = fmaf(s_mz[w][1], cw, Zt);
+  }
+  if (tid < kDecD) {
+    float ov = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float cw = (s_mz[w][0] == -INFINITY) ? 0.0f : __expf(s_mz[w][0] - Mt);
+      ov = fmaf(s_ac[w][tid], cw, ov);
+    }
+    a.o[orow * kDecD + tid] = ov / Zt;
+  }
+  const float lnew = Mt + __logf(Zt);
+  if (tid == 0) {
+    a.lse[orow] = lnew;
+    float* st = a.stat + static_cast<int64_t>(sh) * 4;
+    st[0] = lnew; st[1] = lnew; st[2] = 1.0f; st[3] = 0.0f;
+  }
+  // column mass of the only row: c_j = p_ij, 0 past the row
+  float* c = a.colmass + static_cast<int64_t>(sh) * kv.N;
+  for (int t = tid; t < kv.N; t += 64 * kDecWaves) c[t] = t < cnt ? __expf(s_lgf[t] - lnew) : 0.0f;
+}
+
+bool launch_decode_full(const RowArgs& a, const KvView& kv, hipStream_t st, hipError_t* err) {
+  if (kv.dtype != FL_BF16 || kv.d != kDecD || a.n_act != 1 || a.act == nullptr || a.version != 1 ||
+      static_cast<size_t>(kv.N) * 4 > kDecMaxFullLds || static_cast<uint64_t>(kv.N) * kDecD * 2 > 0x7FFFFFFFull)
+    return false;
+  const int sh = kv.n_seq * kv.H;
+  TimedLaunch t(st, "rows_attend_full");
+  hipLaunchKernelGGL((k_decode_full<2>), dim3(sh), dim3(64 * kDecWaves), static_cast<size_t>(kv.N) * 4, st, kv, a);
+  *err = hipGetLastError();
+  return true;
 }
 
 bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm, bool fuse, hipStream_t st,

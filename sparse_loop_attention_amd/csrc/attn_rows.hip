@@ -375,9 +375,9 @@ hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPl
     cm.src_compact = x.kv_layout == FL_ROWS_COMPACT;
     cm.slot_base = x.commit_slot_base; cm.reset = x.commit_reset;
   }
-  if (lazy) {
+  {
     hipError_t e = hipSuccess;
-    if (launch_decode_lazy(a, kv, cm, fuse, st, &e)) return e;
+    if (lazy ? launch_decode_lazy(a, kv, cm, fuse, st, &e) : launch_decode_full(a, kv, st, &e)) return e;
   }
   {
     TimedLaunch t(st, fuse ? "rows_attend_commit_lazy" : lazy ? "rows_attend_lazy" : "rows_attend_full");

@@ -52,5 +52,8 @@ __device__ __forceinline__ int wave_count_le(const int32_t* a, int n, int v) {
 // and sets *err.
 bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm, bool fuse, hipStream_t st,
                         hipError_t* err);
+// The full loop over the base (version 1) of one row per sequence, same
+// shape limits (head_dim 128, bf16, N <= 10240); false when outside them.
+bool launch_decode_full(const RowArgs& a, const KvView& kv, hipStream_t st, hipError_t* err);
 
 }  // namespace fl

@@ -4,8 +4,8 @@ read straight from the base + delta chain) against the CPU oracle.
 Covers every delta depth of the decode kernel (versions 2..5), both scale
 groups, rows in the middle of the sequence (keys after the row are not
 visible), a row that sees no selected key, the fused commit with and without
-reset, and key counts on both sides of the kernel's LDS staging limit (1536
-keys).  Bars: codes and slot tables bit-exact; o, lse, column mass within
+reset, key counts on both sides of the kernel's LDS staging limit (1536
+keys), and the full loop over the base on both sides of its LDS limit.  Bars: codes and slot tables bit-exact; o, lse, column mass within
 2e-2 x RMS; the fused commit bit-identical to commit-then-attend.
 """
 import math
@@ -211,3 +211,32 @@ def test_decode_fused_commit_equals_commit_then_attend(reset):
     for k in aa:
         assert torch.equal(aa[k], ab[k]), k
     assert torch.equal(oa, ob) and torch.equal(la, lb) and torch.equal(ca, cb)
+
+
+@pytest.mark.parametrize("n", [700, 10240, 10241])
+def test_decode_full_loop(n):
+    """Full loop over the base (version 1) for one row per sequence: the last
+    token, a middle row and the first token; N on both sides of the limit of
+    logits kept in LDS (10240)."""
+    rng = np.random.default_rng(n)
+    S, H, d = 3, 2, 128
+    sts, kv = _build(rng, S, n, H, d, 1, 32, {})
+    rows = [n - 1, n // 3, 0]
+    q = np.stack([round_bf16(rng.standard_normal((1, H, d)).astype(np.float32) * 1.5) for _ in range(S)])
+    o = torch.zeros(S, 1, H, d, device=DEV)
+    lse = torch.zeros(S, 1, H, device=DEV)
+    c = torch.full((S, H, n), 7.0, device=DEV)
+    act = torch.tensor(np.asarray(rows, np.int32)[:, None], device=DEV)
+    a = abi.attend_args(kv, abi.FL_ATTEND_FULL, 1, _dev(q), None, act, 1, None, o, lse, c, None,
+                        q_compact=True, o_compact=True)
+    ws = torch.empty(max(256, abi.attend_workspace_bytes(a)), dtype=torch.uint8, device=DEV)
+    a = abi.attend_args(kv, abi.FL_ATTEND_FULL, 1, _dev(q), None, act, 1, None, o, lse, c, ws,
+                        q_compact=True, o_compact=True)
+    abi.attend(a)
+    torch.cuda.synchronize()
+    for s, st in enumerate(sts):
+        o_r, lse_r, c_r = oracle.full_attention(q[s], _rec(st, "k", 1), _rec(st, "v", 1), np.array([rows[s]]))
+        _close(o[s].cpu().numpy(), o_r, f"seq {s} o")
+        _close(lse[s].cpu().numpy(), lse_r, f"seq {s} lse")
+        _close(c[s].cpu().numpy(), c_r, f"seq {s} colmass")
+        assert torch.all(c[s][:, rows[s] + 1:] == 0)           # nothing past the row
