@@ -478,7 +478,7 @@ bool launch_decode_full(const RowArgs& a, const KvView& kv, hipStream_t st, hipE
     return false;
   const int sh = kv.n_seq * kv.H;
   TimedLaunch t(st, "rows_attend_full");
-  hipLaunchKernelGGL((k_decode_full<2>), dim3(sh), dim3(64 * kDecWaves), static_cast<size_t>(kv.N) * 4, st, kv, a);
+  hipLaunchKernelGGL((k_decode_full<4>), dim3(sh), dim3(64 * kDecWaves), static_cast<size_t>(kv.N) * 4, st, kv, a);
   *err = hipGetLastError();
   return true;
 }

@@ -186,12 +186,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
     for (int64_t i = tid; i < seg_len; i += kTopkThreads) dst[i] = static_cast<int32_t>(i);
     return;
   }
+  // all loads first, at clamped (in-range) positions, so that they are in
+  // flight together; a guarded load per element makes each wait for the last
+  ScoreT raw[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) raw[e] = src[min(first + e, seg_len - 1)];
   uint32_t hi[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int64_t i = first + e;
-    hi[e] = i < seg_len ? static_cast<uint32_t>(order_key(src[i]) >> (WIDE ? 32 : 0)) : 0u;
-  }
+  for (int e = 0; e < EPT; ++e)
+    hi[e] = first + e < seg_len ? static_cast<uint32_t>(order_key(raw[e]) >> (WIDE ? 32 : 0)) : 0u;
   auto lo_of = [&](int e) -> uint32_t { return static_cast<uint32_t>(order_key(src[first + e])); };
 
   if (tid == 0) { sel_bin = 0; sel_above = 0; sel_count = 0; }
