@@ -1,5 +1,5 @@
 // Lazy attention of one new token per sequence (decode) straight from the
-// base + 4-bit delta chain, with the commit of the token's records fused in.
+// base + low-bit delta chain, with the commit of the token's records fused in.
 //
 // Page "FlashLoop: Fast and Memory-Efficient Looped Transformers via Lazy
 // Updates", section "FlashLoop combines three kinds of savings": paragraph 2
@@ -20,11 +20,11 @@
 //  * loads are buffer loads against per-sequence ranges: a layer without a
 //    record for the key gets an offset past the range and reads zeros (code 0,
 //    scale 0), so the chain walk has no branches;
-//  * dequantisation is exact and cheap: a pair of 4-bit codes (elements k and
-//    k+4) becomes two binary16 values 1024 + u (u = code + 8) by OR-ing in a
-//    fixed exponent, 1032 is subtracted in binary16 (exact), and fma_mix adds
-//    code * scale (exact) to the float32 chain with one rounding, the same
-//    sum the store defines;
+//  * dequantisation is exact and cheap: a pair of 4-bit (or 2-bit) codes
+//    (elements k and k+4) becomes two binary16 values 1024 + u (u = code + 8,
+//    or + 2) by OR-ing in a fixed exponent, 1032 (1026) is subtracted in
+//    binary16 (exact), and fma_mix adds code * scale (exact) to the float32
+//    chain with one rounding, the same sum the store defines;
 //  * logits are dot2 products of bf16 pairs: the reconstruction rounded to
 //    bf16 (the working dtype) against the bf16 query.
 #include "fl_common.hpp"
@@ -68,15 +68,21 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4_t w, float x[8]) {
   }
 }
 
-// x[e] += code_e * scale for the 8 4-bit two's-complement codes of `codes`
-// (element e in bits [4e, 4e+4)); exact products, one float32 rounding each.
-__device__ __forceinline__ void add_layer4(uint32_t codes, uint32_t sbits, float x[8]) {
-  const uint32_t u = codes ^ 0x88888888u;                            // u = code + 8, in 0..15
+// x[e] += code_e * scale for the 8 BITS-wide two's-complement codes of
+// `codes` (element e in bits [BITS*e, BITS*e + BITS)); exact products, one
+// float32 rounding each.  4-bit: fields k and k+4 sit 16 bits apart already;
+// 2-bit: the two code bytes are spread to bytes 0 and 2 first.
+template <int BITS>
+__device__ __forceinline__ void add_layer(uint32_t codes, uint32_t sbits, float x[8]) {
+  constexpr uint32_t kMask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+  constexpr float kBias = 1024.0f + (1 << (BITS - 1));               // 1024 + the offset of u
+  const uint32_t w = BITS == 4 ? codes : (codes & 0xFFu) | ((codes & 0xFF00u) << 8);
+  const uint32_t u = w ^ (BITS == 4 ? 0x88888888u : 0x00AA00AAu);    // u = code + 2^(BITS-1)
   const float s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sbits)));
-  const f16x2_t bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+  const f16x2_t bias = {static_cast<_Float16>(kBias), static_cast<_Float16>(kBias)};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t pr = ((u >> (4 * k)) & 0x000F000Fu) | 0x64006400u;   // (1024 + u_k, 1024 + u_{k+4})
+    const uint32_t pr = ((u >> (BITS * k)) & kMask) | 0x64006400u;     // (1024 + u_k, 1024 + u_{k+4})
     const f16x2_t c = __builtin_bit_cast(f16x2_t, pr) - bias;           // (code_k, code_{k+4})
     x[k] = fmaf(s, static_cast<float>(c[0]), x[k]);
     x[k + 4] = fmaf(s, static_cast<float>(c[1]), x[k + 4]);
@@ -112,7 +118,7 @@ __device__ __forceinline__ void axpy_bf16x8(float acc[8], float c, float w, cons
 
 // NL = version - 1 delta layers (versions 2..v); the previous version is the
 // chain through layer NL - 1.
-template <int NL, bool FUSE>
+template <int NL, bool FUSE, int BITS>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(4)))
 void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
   const int sh = blockIdx.x;
@@ -166,7 +172,8 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
   const __amdgpu_buffer_rsrc_t rK = range_of(A + kv.base[0] + rowb, static_cast<uint32_t>(row_bytes));
   const __amdgpu_buffer_rsrc_t rV = range_of(A + kv.base[1] + rowb, static_cast<uint32_t>(row_bytes));
   const int ng = kDecD >> (3 + kv.gshift);                // scales per record: 4 (group 32) or 2 (group 64)
-  const uint32_t rec_code_bytes = H * kDecD;              // K and V codes of every head of one slot
+  constexpr uint32_t kCodeBytes = kDecD * BITS / 8;       // codes of one head row
+  const uint32_t rec_code_bytes = H * 2 * kCodeBytes;    // K and V codes of every head of one slot
   const uint32_t rec_scale_bytes = H * 4 * ng;            // K and V scales of every head of one slot
   __amdgpu_buffer_rsrc_t rC[NL], rS[NL];
   uint32_t cap[NL];
@@ -178,7 +185,7 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
                      cap[l] * rec_scale_bytes);
   }
   const uint32_t lane_b = 16 * p;
-  const uint32_t lane_c = h * kDecD + 4 * p;              // K codes; V codes 64 bytes on
+  const uint32_t lane_c = h * 2 * kCodeBytes + BITS * p;  // K codes; V codes kCodeBytes on
   const uint32_t lane_s = h * 4 * ng + 2 * (p >> kv.gshift);  // K scale; V scale 2*ng bytes on
   // a reset commit clears layer v for every token it does not write: the walk stops at v-1
   const bool walk_v = !(FUSE && cm.reset);
@@ -206,8 +213,13 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
       const bool use = ok && slot < cap[l] && (l + 1 < NL || walk_v);
       const uint32_t oc = use ? slot * rec_code_bytes + lane_c : kOut;
       const uint32_t os = use ? slot * rec_scale_bytes + lane_s : kOut;
-      r.kc[l] = __builtin_amdgcn_raw_buffer_load_b32(rC[l], oc, 0, 0);
-      r.vc[l] = __builtin_amdgcn_raw_buffer_load_b32(rC[l], oc + kDecD / 2, 0, 0);
+      if (BITS == 4) {
+        r.kc[l] = __builtin_amdgcn_raw_buffer_load_b32(rC[l], oc, 0, 0);
+        r.vc[l] = __builtin_amdgcn_raw_buffer_load_b32(rC[l], oc + kCodeBytes, 0, 0);
+      } else {
+        r.kc[l] = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rC[l], oc, 0, 0));
+        r.vc[l] = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rC[l], oc + kCodeBytes, 0, 0));
+      }
       r.ks[l] = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rS[l], os, 0, 0));
       r.vs[l] = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rS[l], os + 2 * ng, 0, 0));
     }
@@ -223,7 +235,7 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
     uint32_t pk[4];
     unpack_bf16x8(r.kb, x);
 #pragma unroll
-    for (int l = 0; l + 1 < NL; ++l) add_layer4(r.kc[l], r.ks[l], x);
+    for (int l = 0; l + 1 < NL; ++l) add_layer<BITS>(r.kc[l], r.ks[l], x);
     round_pack8(x, pk);
     const float sp = group_sum<16>(dot_bf16x8(pk, qp)) * a.scale;
     int64_t src = 0;
@@ -236,7 +248,7 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = xo[e];
     } else {
-      add_layer4(r.kc[NL - 1], r.ks[NL - 1], x);
+      add_layer<BITS>(r.kc[NL - 1], r.ks[NL - 1], x);
     }
     round_pack8(x, pk);
     const float sc = group_sum<16>(dot_bf16x8(pk, qc)) * a.scale;
@@ -250,7 +262,7 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
     M = Mn;
     unpack_bf16x8(r.vb, x);
 #pragma unroll
-    for (int l = 0; l + 1 < NL; ++l) add_layer4(r.vc[l], r.vs[l], x);
+    for (int l = 0; l + 1 < NL; ++l) add_layer<BITS>(r.vc[l], r.vs[l], x);
     round_pack8(x, pk);
     axpy_bf16x8(accp, 1.0f, pp, pk);
     if (active) {
@@ -260,7 +272,7 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = xo[e];
     } else {
-      add_layer4(r.vc[NL - 1], r.vs[NL - 1], x);
+      add_layer<BITS>(r.vc[NL - 1], r.vs[NL - 1], x);
     }
     round_pack8(x, pk);
     axpy_bf16x8(acc, corr, w, pk);
@@ -486,7 +498,8 @@ bool launch_decode_full(const RowArgs& a, const KvView& kv, hipStream_t st, hipE
 bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm, bool fuse, hipStream_t st,
                         hipError_t* err) {
   const int nl = a.version - 1;
-  if (kv.dtype != FL_BF16 || kv.d != kDecD || kv.bits != 4 || a.n_act != 1 || nl < 1 || nl > kDecMaxLayers ||
+  if (kv.dtype != FL_BF16 || kv.d != kDecD || (kv.bits != 4 && kv.bits != 2) || a.n_act != 1 || nl < 1 ||
+      nl > kDecMaxLayers ||
       a.n_keys > kDecMaxKeys)
     return false;
   // every range must fit a buffer descriptor, with offsets below 2^31
@@ -499,10 +512,14 @@ bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm
   const int sh = kv.n_seq * kv.H;
   const size_t lds = static_cast<size_t>(a.n_keys) * (16 + 4 + 4 + 4);
   TimedLaunch t(st, fuse ? "rows_attend_commit_lazy" : "rows_attend_lazy");
-#define FL_DEC(NLV)                                                                                         \
-  do {                                                                                                      \
-    if (fuse) hipLaunchKernelGGL((k_decode_lazy<NLV, true>), dim3(sh), dim3(64 * kDecWaves), lds, st, kv, a, cm); \
-    else hipLaunchKernelGGL((k_decode_lazy<NLV, false>), dim3(sh), dim3(64 * kDecWaves), lds, st, kv, a, cm);     \
+#define FL_DEC_B(NLV, B)                                                                                   \
+  do {                                                                                                       \
+    if (fuse) hipLaunchKernelGGL((k_decode_lazy<NLV, true, B>), dim3(sh), dim3(64 * kDecWaves), lds, st, kv, a, cm); \
+    else hipLaunchKernelGGL((k_decode_lazy<NLV, false, B>), dim3(sh), dim3(64 * kDecWaves), lds, st, kv, a, cm);     \
+  } while (0)
+#define FL_DEC(NLV)                                         \
+  do {                                                      \
+    if (kv.bits == 4) FL_DEC_B(NLV, 4); else FL_DEC_B(NLV, 2); \
   } while (0)
   switch (nl) {
     case 1: FL_DEC(1); break;
@@ -511,6 +528,7 @@ bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm
     default: FL_DEC(4); break;
   }
 #undef FL_DEC
+#undef FL_DEC_B
   *err = hipGetLastError();
   return true;
 }

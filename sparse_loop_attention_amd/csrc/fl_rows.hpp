@@ -47,7 +47,7 @@ __device__ __forceinline__ int wave_count_le(const int32_t* a, int n, int v) {
 }
 
 // Lazy attention of one active row per sequence (decode) on a bf16 store
-// with 4-bit deltas and head_dim 128, at versions 2..5.  Returns false (and
+// with 4- or 2-bit deltas and head_dim 128, at versions 2..5.  Returns false (and
 // launches nothing) when the call is outside that shape; otherwise launches
 // and sets *err.
 bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm, bool fuse, hipStream_t st,

@@ -2,7 +2,7 @@
 read straight from the base + delta chain) against the CPU oracle.
 
 Covers every delta depth of the decode kernel (versions 2..5), both scale
-groups, rows in the middle of the sequence (keys after the row are not
+groups and both code widths (4 and 2 bits), rows in the middle of the sequence (keys after the row are not
 visible), a row that sees no selected key, the fused commit with and without
 reset, key counts on both sides of the kernel's LDS staging limit (1536
 keys), and the full loop over the base on both sides of its LDS limit.  Bars: codes and slot tables bit-exact; o, lse, column mass within
@@ -34,7 +34,7 @@ def _close(got, want, what):
     assert err <= 2e-2 * rms, f"{what}: max err {err:.3e} > 2e-2 * RMS {rms:.3e}"
 
 
-def _build(rng, S, n, H, d, versions, group, sizes, caps=None):
+def _build(rng, S, n, H, d, versions, group, sizes, caps=None, bits=4):
     """S sequences, each an oracle store and the same records in one GPU
     store; layer l holds `sizes[l]` random tokens per sequence (slots
     0..sizes[l]-1 of caps[l])."""
@@ -42,7 +42,7 @@ def _build(rng, S, n, H, d, versions, group, sizes, caps=None):
     sts, kin, vin = [], {l: [] for l in range(1, versions + 1)}, {l: [] for l in range(1, versions + 1)}
     acts = {l: [] for l in range(2, versions + 1)}
     for _ in range(S):
-        st = oracle.KVStore(n, H, d, group=group)
+        st = oracle.KVStore(n, H, d, group=group, bits=bits)
         k = round_bf16(rng.standard_normal((n, H, d)).astype(np.float32))
         v = round_bf16(rng.standard_normal((n, H, d)).astype(np.float32))
         st.commit(1, np.arange(n), k, v)
@@ -55,7 +55,8 @@ def _build(rng, S, n, H, d, versions, group, sizes, caps=None):
             st.commit(l, act, k[act], v[act])
             kin[l].append(k.copy()); vin[l].append(v.copy()); acts[l].append(act)
         sts.append(st)
-    kv = abi.KVStore(S, H, d, n, versions, BF, [caps[l] for l in range(2, versions + 1)], DEV, group=group)
+    kv = abi.KVStore(S, H, d, n, versions, BF, [caps[l] for l in range(2, versions + 1)], DEV, group=group,
+                     delta_bits=bits)
     abi.kv_commit(kv, 1, torch.arange(n, dtype=torch.int32, device=DEV).repeat(S, 1),
                   _dev(np.stack(kin[1])), _dev(np.stack(vin[1])))
     for l in range(2, versions + 1):
@@ -130,12 +131,13 @@ def _check_against_oracle(sts, state, rows, keys, version, o, lse, c):
         _close(c[s].cpu().numpy(), c_r, f"seq {s} colmass")
 
 
-@pytest.mark.parametrize("version,group", [(2, 32), (3, 32), (4, 32), (5, 32), (3, 64), (5, 64)])
-def test_decode_depths_and_groups(version, group):
-    rng = np.random.default_rng(100 * version + group)
+@pytest.mark.parametrize("version,group,bits", [(2, 32, 4), (3, 32, 4), (4, 32, 4), (5, 32, 4), (3, 64, 4),
+                                                (5, 64, 4), (2, 32, 2), (4, 32, 2), (5, 64, 2)])
+def test_decode_depths_and_groups(version, group, bits):
+    rng = np.random.default_rng(100 * version + group + bits)
     S, n, H, d, nk = 3, 640, 2, 128, 64
     sizes = {l: [n, 300, 150, 40][l - 2] for l in range(2, version + 1)}
-    sts, kv = _build(rng, S, n, H, d, version, group, sizes)
+    sts, kv = _build(rng, S, n, H, d, version, group, sizes, bits=bits)
     rows = [n - 1, 333, 17]                                   # the last token, the middle, near the start
     keys = _keys(rng, S, H, n, nk, rows, force=rows)
     state = _row_state(rng, sts, rows, version, keys, H, d)
