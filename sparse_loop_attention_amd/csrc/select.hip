@@ -129,6 +129,12 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 
 constexpr int kTopkThreads = 1024;
+// Histogram replicas: lane l counts into copy l mod kTopkReplicas of a bin
+// (copies of one bin adjacent, so they sit in different LDS banks).  In the
+// first passes most keys share a few bins (one exponent range), and
+// per-lane atomics on one counter serialise; with the copies at most
+// 64 / kTopkReplicas lanes of a wave meet on one address.
+constexpr int kTopkReplicas = 8;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
 // Exclusive scan of one int per thread across the workgroup; returns the total.
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
                                                        int32_t* __restrict__ out_idx) {
   constexpr bool WIDE = sizeof(ScoreT) == 8;
   constexpr int kBits = WIDE ? 64 : 32;
-  __shared__ int hist[256];
+  __shared__ __align__(16) int hist[256 * kTopkReplicas];
   __shared__ int scan_tmp[kTopkWaves + 1];
   __shared__ int sel_bin, sel_above, sel_count;
 
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
   for (int shift = kBits - 8; shift >= 0; shift -= 8) {
     const bool low = WIDE && shift < 32;              // a pass over the low word
     const int sh = low || !WIDE ? shift : shift - 32;
-    if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < 256 * kTopkReplicas; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -221,9 +227,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
       const int lbin = __shfl(bin, leader, 64);
       const uint64_t same = __ballot(act && bin == lbin);
       if (same == m) {
-        if (lane == leader) atomicAdd(&hist[lbin], __popcll(m));
+        if (lane == leader) atomicAdd(&hist[lbin * kTopkReplicas], __popcll(m));
       } else if (act) {
-        atomicAdd(&hist[bin], 1);
+        atomicAdd(&hist[bin * kTopkReplicas + (lane & (kTopkReplicas - 1))], 1);
       }
     }
     __syncthreads();
@@ -231,7 +237,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
       // lane L owns bins 255-4L .. 252-4L (descending)
       int c[4], s = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; s += c[i]; }
+      for (int i = 0; i < 4; ++i) {
+        const int4* hb = reinterpret_cast<const int4*>(hist + (255 - 4 * lane - i) * kTopkReplicas);
+        c[i] = 0;
+#pragma unroll
+        for (int r = 0; r < kTopkReplicas / 4; ++r) c[i] += (hb[r].x + hb[r].y) + (hb[r].z + hb[r].w);
+        s += c[i];
+      }
       int incl = s;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
