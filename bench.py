@@ -153,9 +153,15 @@ def measured_traffic(timer, workload):
     return {}
 
 
-def roofline(timings, work, steps, decode=False, workload=""):
+def roofline(timings, work, steps, decode=False, workload="", kernel=None):
+    """Roofline of `kernel`, or of the kernel with the largest share of the step."""
     table = KERNEL_WORK_DECODE if decode else KERNEL_WORK
-    name, (ms, launches) = max(timings.items(), key=lambda kv: kv[1][0])
+    if kernel is None:
+        name, (ms, launches) = max(timings.items(), key=lambda kv: kv[1][0])
+    elif kernel in timings:
+        name, (ms, launches) = kernel, timings[kernel]
+    else:
+        return None
     avg_ms = ms / max(launches, 1)
     entry = {"kernel": name, "launches_per_step": launches / steps, "avg_launch_ms": avg_ms}
     if name in table:
@@ -395,6 +401,8 @@ def main():
     lazy_ms = sum(ms for name, (ms, _) in timings.items()
                   if name.endswith("_lazy") or name in ("delta_norm", "topk", "commit_delta", "slot_map",
                                                         "rows_colmass", "colmass_reduce")) / args.steps
+    lazy_kernel = next((k for k in ("mfma_fwd_lazy", "rows_attend_commit_lazy", "rows_attend_lazy") if k in timings),
+                       None)
     out = {
         "metric": "active-token loop-steps/sec + KV GB/s; % of HBM / bf16-MFMA roofline",
         "value": value,
@@ -413,6 +421,10 @@ def main():
         "lazy_active_token_steps_per_s": (work["lazy_rows"] / (lazy_ms / 1e3)) if lazy_ms > 0 else None,
         "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in sorted(timings.items())},
         "roofline": roofline(timings, work, args.steps, wl.decode, label),
+        # the lazy loops' attention on its own: the gathered-tile MFMA kernel
+        # (prefill) or the chain read (decode), loops after the full ones
+        "roofline_lazy_attention": (roofline(timings, work, args.steps, wl.decode, label, kernel=lazy_kernel)
+                                    if lazy_kernel else None),
     }
     if args.cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
