@@ -121,9 +121,21 @@ __device__ __forceinline__ void axpy_bf16x8(float acc[8], float c, float w, cons
 template <int NL, bool FUSE, int BITS>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(4)))
 void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
-  const int sh = blockIdx.x;
   const int H = kv.H;
-  const int s = sh / H, h = sh % H;
+  // all heads of a sequence on one XCD (workgroup b runs on XCD b % 8): the
+  // slot rows of keys that several heads select are then read once into
+  // that XCD's L2
+  int s, h;
+  if (kv.n_seq >= 8) {
+    const int local = blockIdx.x >> 3;
+    s = (blockIdx.x & 7) + 8 * (local / H);
+    h = local % H;
+    if (s >= kv.n_seq) return;
+  } else {
+    s = blockIdx.x / H;
+    h = blockIdx.x % H;
+  }
+  const int sh = s * H + h;
   if (kv.exited(s)) return;                               // uniform per workgroup
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, p = lane & 15;
   const int nk = a.n_keys;
@@ -509,7 +521,7 @@ bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm
     const uint64_t cap = static_cast<uint64_t>(kv.cap[l]);
     if (cap * kv.H * kDecD > lim) return false;
   }
-  const int sh = kv.n_seq * kv.H;
+  const int sh = kv.n_seq >= 8 ? (kv.n_seq + 7) / 8 * 8 * kv.H : kv.n_seq * kv.H;   // grid (see the kernel's mapping)
   const size_t lds = static_cast<size_t>(a.n_keys) * (16 + 4 + 4 + 4);
   TimedLaunch t(st, fuse ? "rows_attend_commit_lazy" : "rows_attend_lazy");
 #define FL_DEC_B(NLV, B)                                                                                   \

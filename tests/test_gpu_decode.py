@@ -242,3 +242,19 @@ def test_decode_full_loop(n):
         _close(lse[s].cpu().numpy(), lse_r, f"seq {s} lse")
         _close(c[s].cpu().numpy(), c_r, f"seq {s} colmass")
         assert torch.all(c[s][:, rows[s] + 1:] == 0)           # nothing past the row
+
+
+@pytest.mark.parametrize("S", [8, 10])
+def test_decode_many_sequences(S):
+    """From 8 sequences on, the heads of a sequence share an XCD; a count
+    that is not a multiple of 8 leaves workgroups with no sequence."""
+    rng = np.random.default_rng(S)
+    n, H, d, nk, version = 500, 3, 128, 50, 4
+    sts, kv = _build(rng, S, n, H, d, version, 32, {2: n, 3: 100, 4: 60})
+    rows = [int(x) for x in rng.integers(0, n, S)]
+    rows[0] = n - 1
+    keys = _keys(rng, S, H, n, nk, rows, force=rows)
+    state = _row_state(rng, sts, rows, version, keys, H, d)
+    q1, q0, act, kt, o, lse, c = _gpu_inputs(state, rows, keys)
+    _attend(kv, version, q1, q0, act, kt, o, lse, c)
+    _check_against_oracle(sts, state, rows, keys, version, o, lse, c)
