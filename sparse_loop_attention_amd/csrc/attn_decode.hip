@@ -12,7 +12,8 @@
 //
 //  * one workgroup of 8 waves per (sequence, head); two fit on a CU (at most
 //    128 VGPRs), so every workgroup of a 32 x 16 decode batch is resident at
-//    once;
+//    once; all heads of a sequence run on one XCD, whose L2 then serves the
+//    slot rows of keys that several heads select;
 //  * the selected keys' positions and slot rows are staged in LDS first, then
 //    key t goes to 16-lane group t mod 32 (lane p owns elements [8p, 8p+8));
 //    each group issues the loads of its next key before it works on the
@@ -27,6 +28,8 @@
 //    chain with one rounding, the same sum the store defines;
 //  * logits are dot2 products of bf16 pairs: the reconstruction rounded to
 //    bf16 (the working dtype) against the bf16 query.
+// The full decode loop over the base (version 1) has a streaming kernel of
+// its own below (k_decode_full).
 #include "fl_common.hpp"
 #include "fl_commit.hpp"
 #include "fl_rows.hpp"
@@ -52,7 +55,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_of(const uint8_t* p, uin
 }
 
 // Raw loads of one key for this lane: base rows (8 bf16 each) and, per delta
-// layer, the K and V codes (8 x 4 bits) and scales (binary16 bits).
+// layer, the K and V codes (8 codes of 4 or 2 bits) and scales (binary16 bits).
 template <int NL>
 struct KeyLoads {
   u32x4_t kb, vb;
