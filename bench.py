@@ -268,14 +268,17 @@ def quality(wl):
         for freeze in (False, True):
             run = driver.PrefillRun(wl, inputs, "cuda", formula=formula, freeze_keys=freeze)
             rows = []
+            q_eff = None                   # every row's query as of its last active loop
             for l in range(1, wl.n_loops + 1):
                 if l <= wl.n_full:
                     run.full_loop(l)
                     cand = None
+                    q_eff = inputs[l]["q"][0].clone()
                     continue
                 act = run.lazy_loop(l, cand)
                 cand = act
-                abi.attend(abi.attend_args(run.kv, abi.FL_ATTEND_FULL, l, run.q_eff, None, None, n, None,
+                q_eff.index_copy_(0, act.long(), inputs[l]["q"][0].index_select(0, act.long()))
+                abi.attend(abi.attend_args(run.kv, abi.FL_ATTEND_FULL, l, q_eff, None, None, n, None,
                                            o_ref, lse_ref, c_ref, run.workspace))
                 torch.cuda.synchronize()
                 diff = (run.o - o_ref).double()

@@ -8,10 +8,14 @@ loop, selects keys from the previous loop's column mass, commits int4 deltas
 of the active tokens and runs mass-corrected attention.
 
 The per-loop inputs come from a synthetic stand-in for the shared block (the
-model weights are not available): its new h and Q rows are copied into the
-effective-state buffers only for the active rows, which is how the carried
-rows of a looped model keep their previous state.  That copy is the model's
-work, not the method's, and is done with a torch index copy.
+model weights are not available), which produces every row of h and Q per
+loop; a looped model recomputes only the active rows and carries the others.
+The active sets are nested (loop l ranks the rows of loop l-1's set), so a
+row that is a candidate in loop l was active in every earlier loop: its
+effective state is the previous loops' output for that row.  The token scores
+therefore read h of loops l-1 and l-2 directly, and the previous queries of
+the active rows are those of loop l-1, gathered with a torch index select
+(the model's work, not the method's).
 """
 from __future__ import annotations
 
@@ -76,11 +80,6 @@ class PrefillRun:
         dt = torch_dtype(wl)
         self.kv = abi.KVStore(1, H, d, n, wl.n_loops, dt, wl.layer_caps(), device,
                               group=wl.group, delta_bits=wl.delta_bits)
-        # effective hidden state (carried rows keep their value) and, at the rows
-        # of the last active set, its value one loop earlier
-        self.h_eff = torch.empty(n, H * d, dtype=dt, device=device)
-        self.h_prev = torch.empty_like(self.h_eff)
-        self.q_eff = torch.empty(n, H, d, dtype=dt, device=device)
         na_max = max([wl.n_active(l) for l in range(wl.n_full + 1, wl.n_loops + 1)] or [1])
         self.q_cur_rows = torch.empty(na_max, H, d, dtype=dt, device=device)
         self.q_prev_rows = torch.empty(na_max, H, d, dtype=dt, device=device)
@@ -113,20 +112,15 @@ class PrefillRun:
 
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
-        x, wl = self.inp[l], self.wl
-        if l == wl.n_full and wl.n_loops > wl.n_full:
-            # the effective state the lazy loops start from (model stand-in:
-            # the block's outputs of the last full loop and the loop before)
-            self.h_prev.copy_(self.inp[l - 1]["h"][0])
-            self.h_eff.copy_(x["h"][0])
-            self.q_eff.copy_(x["q"][0])
+        x = self.inp[l]
         abi.kv_commit(self.kv, l, self.all_rows, x["k"], x["v"])
         abi.attend(self._attend_args(l))
 
     def lazy_loop(self, l: int, cand: Optional[torch.Tensor]) -> torch.Tensor:
         wl, x = self.wl, self.inp[l]
         act, na = self.act[l], wl.n_active(l)
-        abi.select_tokens(self.h_eff, self.h_prev, na, self.scores, act, cand)
+        # the change of the candidate rows during loop l-1 (every row after the full loops)
+        abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, self.scores, act, cand)
         if self.exit_flags is not None:          # early exit: no later library call touches the sequence
             abi.exit_check(self.exit_flags, self.exit_threshold, scores=self.scores)
         first = wl.n_full + 1
@@ -134,13 +128,10 @@ class PrefillRun:
             self.keys_l[l].copy_(self.keys_l[first])
         else:
             abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
-        # model stand-in: the shared block recomputes the active rows only
+        # model stand-in: the active rows' queries of this loop and of loop l-1
         idx = act.long()
-        self.h_prev.index_copy_(0, idx, self.h_eff.index_select(0, idx))
-        self.h_eff.index_copy_(0, idx, x["h"][0].index_select(0, idx))
-        torch.index_select(self.q_eff, 0, idx, out=self.q_prev_rows[:na])
+        torch.index_select(self.inp[l - 1]["q"][0], 0, idx, out=self.q_prev_rows[:na])
         torch.index_select(x["q"][0], 0, idx, out=self.q_cur_rows[:na])
-        self.q_eff.index_copy_(0, idx, self.q_cur_rows[:na])
         if not self.fuse:
             abi.kv_commit(self.kv, l, act, x["k"], x["v"], exit_flags=self.exit_flags)
         abi.attend(self._attend_args(l))
