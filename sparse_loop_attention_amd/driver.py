@@ -13,9 +13,8 @@ loop; a looped model recomputes only the active rows and carries the others.
 The active sets are nested (loop l ranks the rows of loop l-1's set), so a
 row that is a candidate in loop l was active in every earlier loop: its
 effective state is the previous loops' output for that row.  The token scores
-therefore read h of loops l-1 and l-2 directly, and the previous queries of
-the active rows are those of loop l-1, gathered with a torch index select
-(the model's work, not the method's).
+therefore read h of loops l-1 and l-2 directly, and attention reads the active
+rows' queries of loops l and l-1 by token from those loops' outputs.
 """
 from __future__ import annotations
 
@@ -80,9 +79,6 @@ class PrefillRun:
         dt = torch_dtype(wl)
         self.kv = abi.KVStore(1, H, d, n, wl.n_loops, dt, wl.layer_caps(), device,
                               group=wl.group, delta_bits=wl.delta_bits)
-        na_max = max([wl.n_active(l) for l in range(wl.n_full + 1, wl.n_loops + 1)] or [1])
-        self.q_cur_rows = torch.empty(na_max, H, d, dtype=dt, device=device)
-        self.q_prev_rows = torch.empty(na_max, H, d, dtype=dt, device=device)
         self.o = torch.empty(n, H, d, dtype=torch.float32, device=device)
         self.lse = torch.empty(n, H, dtype=torch.float32, device=device)
         self.colmass = torch.empty(H, n, dtype=torch.float32, device=device)
@@ -106,9 +102,10 @@ class PrefillRun:
                                    None, self.o, self.lse, self.colmass, self.workspace)
         na = wl.n_active(l)
         commit = dict(k_new=self.inp[l]["k"], v_new=self.inp[l]["v"]) if self.fuse else None
-        return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, self.q_cur_rows[:na], self.q_prev_rows[:na],
+        # the active rows' queries of loops l and l-1, read by token
+        return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, self.inp[l]["q"], self.inp[l - 1]["q"],
                                self.act[l], na, self.keys_l[l], self.o, self.lse, self.colmass, self.workspace,
-                               q_compact=True, commit=commit, formula=self.formula, exit_flags=self.exit_flags)
+                               commit=commit, formula=self.formula, exit_flags=self.exit_flags)
 
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
@@ -128,10 +125,6 @@ class PrefillRun:
             self.keys_l[l].copy_(self.keys_l[first])
         else:
             abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
-        # model stand-in: the active rows' queries of this loop and of loop l-1
-        idx = act.long()
-        torch.index_select(self.inp[l - 1]["q"][0], 0, idx, out=self.q_prev_rows[:na])
-        torch.index_select(x["q"][0], 0, idx, out=self.q_cur_rows[:na])
         if not self.fuse:
             abi.kv_commit(self.kv, l, act, x["k"], x["v"], exit_flags=self.exit_flags)
         abi.attend(self._attend_args(l))
