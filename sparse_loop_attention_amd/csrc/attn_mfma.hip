@@ -76,6 +76,7 @@ struct MfmaArgs {
   int32_t fsplit_u, f_items, f_tiles;   // workgroups and row tiles per head
   float4* fpart;            // [sh][f_items][D/8 + 1][512] partial acc, (max, sum)
   int32_t* fcount;          // [sh][f_tiles] parts finished (zeroed by the gather launch)
+  int32_t fpair;            // full loops: workgroups per head taking an early and a late 128-row half (0 = off)
   int32_t* ccount;          // [sh][n_keys_pad / 256] column-mass ranges finished (zeroed by the gather), or null
   // early exit: sequences with a nonzero flag are skipped by every kernel
   const int32_t* exit_flags;  // [n_seq] or null
@@ -317,12 +318,16 @@ struct FwdTiles {
 
 
 // NOPV: the pass needs only the probability mass (no V tiles, no PV product).
-template <int D, int NW, int KT_, bool FIXED, bool NOPV = false>
+// WLIM: the wave computes only its first my_n of the workgroup's n_tiles key
+// tiles (the rest lie past its rows' causal limit) and afterwards only helps
+// stage the tiles the other waves still use.
+template <int D, int NW, int KT_, bool FIXED, bool NOPV = false, bool WLIM = false>
 __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const uint16_t* kbase, const uint16_t* vbase,
                                          const int32_t* kx, uint16_t (*sk)[FwdTiles<D, NW, KT_>::KBUF],
                                          uint16_t (*sv)[FwdTiles<D, NW, KT_>::VBUF], int (*skx)[KT_],
                                          const bf16x8 (&qf)[D / 16], int tok, int tok_first, int tok_last, bool blk_full,
-                                         float c1, float b_fix, f32x16 (&acc)[D / 32], float& ref, float& lsum) {
+                                         float c1, float b_fix, f32x16 (&acc)[D / 32], float& ref, float& lsum,
+                                         int my_n = 0) {
   using T = FwdTiles<D, NW, KT_>;
   constexpr int KT = T::KT, NT = T::NT, KS = T::KS, VS = T::VS;
   (void)NT;
@@ -426,7 +431,7 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
   __syncthreads();
   f32x16 S0[NKB], S1[NKB];
   f16x8 P[NCC];
-  qk(0, S0);
+  if (!WLIM || my_n > 0) qk(0, S0);
   __syncthreads();
 
   // iteration t: QK(t+1) into Sn, PV(t-1) with P, softmax(t) of Sc into P;
@@ -565,21 +570,46 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     resc_prev = resc_cur;
     alpha_prev = alpha_cur;
   };
-  step(0, S0, S1, true);
+  // a wave past its own tiles: the PV product of its last tile (whose V
+  // buffer is overwritten only at the end of the next step), then staging
+  auto idle = [&](int t) {
+    if (!NOPV && t == my_n && my_n > 0) {
+      if (resc_prev) rescale(alpha_prev);
+      pv_acc((t - 1) & 1, P);
+    }
+    load_k(t & 1, min(t + 2, n_tiles - 1));
+    if (!NOPV) load_v(t & 1, t);
+    flush_k();
+    if (!NOPV) flush_v();
+    store_kx(t + 2);
+    __syncthreads();
+  };
+  auto run = [&](int t, f32x16 (&Sc)[NKB], f32x16 (&Sn)[NKB], bool first) {
+    if (!WLIM || t < my_n) step(t, Sc, Sn, first);
+    else idle(t);
+  };
+  run(0, S0, S1, true);
   int t = 1;
   for (; t + 1 < n_tiles; t += 2) {
-    step(t, S1, S0, false);
-    step(t + 1, S0, S1, false);
+    run(t, S1, S0, false);
+    run(t + 1, S0, S1, false);
   }
-  if (t < n_tiles) step(t, S1, S0, false);
-  if (NOPV) return;
+  if (t < n_tiles) run(t, S1, S0, false);
+  if (NOPV || (WLIM && my_n < n_tiles)) return;
   if (resc_prev) rescale(alpha_prev);                      // PV of the last tile
   pv_acc((n_tiles - 1) & 1, P);
 }
 
 // MIX (lazy only): the mixture formula o = m*otilde + (1-m)*o_prev; the
 // previous-loop pass then needs only the mass.
-template <int D, int NW, int KT_, bool LAZY, bool MIX = false>
+// PAIR (full loops, 256-row shape): the rows are cut into 128-row halves and a
+// workgroup takes half j on waves 0-3 and half (last - j) on waves 4-7, so
+// every workgroup sees about the same number of causal (row, key) pairs.  A
+// wave stops computing at its own rows' last key tile; waves w and w + 4
+// share a SIMD, so once the early half is done the late half runs alone
+// there.  Used when the grid is a single round of workgroups, whose time is
+// otherwise that of the last row tile.
+template <int D, int NW, int KT_, bool LAZY, bool MIX = false, bool PAIR = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2))) void k_mfma_fwd(int32_t H, int32_t N, MfmaArgs a) {
   using T = FwdTiles<D, NW, KT_>;
   constexpr int KT = T::KT;
@@ -589,14 +619,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][T::VBUF];
   __shared__ __attribute__((aligned(16))) int skx[4][KT];
   __shared__ int s_last, s_arrived;
+  __shared__ int s_wcount[NW];
   constexpr int NT = 64 * NW;
   // the key split serves full loops in the 256-row, 64-key-tile shape
-  constexpr bool kSplit = !LAZY && ROWS == 256 && KT == 64;
+  constexpr bool kSplit = !LAZY && ROWS == 256 && KT == 64 && !PAIR;
+  static_assert(!PAIR || (!LAZY && ROWS == 256 && KT == 64), "paired halves: full loops, 256-row shape");
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
   int sh, qtile, item = 0, part = 0, parts = 1;
-  if (kSplit && a.fsplit_u > 0) {
+  int r0, wg_last;                                         // first row of this wave, last row of the workgroup
+  if (PAIR) {
+    int j;
+    if (!map_block(a.n_sh, a.fpair, sh, j)) return;
+    const int halves = (a.n_rows + 127) / 128, late = halves - 1 - j;
+    r0 = wave < 4 ? j * 128 + wave * 32 : late == j ? a.n_rows : late * 128 + (wave - 4) * 32;
+    wg_last = min(a.n_rows, (late + 1) * 128) - 1;
+  } else if (kSplit && a.fsplit_u > 0) {
     // workgroups in launch order: row tiles heaviest first, the parts of a
     // tile one after another
     int rev;
@@ -613,9 +652,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   } else if (!map_block(a.n_sh, (a.n_rows + ROWS - 1) / ROWS, sh, qtile)) {
     return;
   }
+  if (!PAIR) {
+    r0 = qtile * ROWS + wave * 32;
+    wg_last = min(a.n_rows, (qtile + 1) * ROWS) - 1;
+  }
   const int s = sh / H, h = sh % H;
   if (a.exited(s)) return;
-  const int r0 = qtile * ROWS + wave * 32;                // first row of this wave
   const int r = r0 + c;
   const bool vrow = r < a.n_rows;
   const int tok = vrow ? row_token(a, s, r) : -1;         // -1: every key is masked
@@ -625,14 +667,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   const float c1 = a.scale * kLog2e;                      // logits in log2 units
 
   const int32_t* kx = a.kidx + static_cast<int64_t>(sh) * a.n_keys_pad;
-  if (tid == 0) {                                          // key slots visible to the workgroup's last row
-    const int last_tok = row_token(a, s, min(a.n_rows, (qtile + 1) * ROWS) - 1);
+  // key slots visible to a row: those with a token at or before its own
+  auto visible = [&](int row) {
+    const int last_tok = row_token(a, s, row);
     int lo = 0, hi = a.n_keys;
     while (lo < hi) { const int mid = (lo + hi) >> 1; if (kx[mid] <= last_tok) lo = mid + 1; else hi = mid; }
-    s_last = lo;
+    return lo;
+  };
+  int my_n = 0, n_vis;                                     // PAIR: this wave's own key tiles
+  if (PAIR) {
+    if (lane == 0) s_wcount[wave] = r0 < a.n_rows ? visible(min(r0 + 31, a.n_rows - 1)) : 0;
+    __syncthreads();
+    n_vis = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) n_vis = max(n_vis, s_wcount[w]);
+    my_n = (s_wcount[wave] + KT - 1) / KT;
+  } else {
+    if (tid == 0) s_last = visible(wg_last);               // key slots visible to the workgroup's last row
+    __syncthreads();
+    n_vis = s_last;
   }
-  __syncthreads();
-  const int n_tiles = (s_last + KT - 1) / KT;
+  const int n_tiles = (n_vis + KT - 1) / KT;
 
   const int64_t rows_q = a.q_compact ? a.n_rows : N;
   const int64_t qr = a.q_compact ? r : tok;
@@ -655,9 +710,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
     load_q(a.q_cur, qf);
     // a part covers key tiles [t_lo, t_hi) of the row tile
     const int t_lo = part * n_tiles / parts, t_hi = (part + 1) * n_tiles / parts;
-    fwd_pass<D, NW, KT_, false>(a, t_hi - t_lo, a.kc + kofs + static_cast<int64_t>(t_lo) * KT * D,
-                                a.vtc + kofs + t_lo * KT, kx + t_lo * KT, sk, sv, skx, qf, tok, tok_first,
-                                tok_last, blk_full, c1, 0.0f, acc, ref, lsum);
+    fwd_pass<D, NW, KT_, false, false, PAIR>(a, t_hi - t_lo, a.kc + kofs + static_cast<int64_t>(t_lo) * KT * D,
+                                              a.vtc + kofs + t_lo * KT, kx + t_lo * KT, sk, sv, skx, qf, tok,
+                                              tok_first, tok_last, blk_full, c1, 0.0f, acc, ref, lsum, my_n);
     if (kSplit && parts > 1) {
       // every part stores its partial state (acc against its own reference
       // max, the max, the lane's sum); the part that finishes last merges all
@@ -1215,6 +1270,7 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     a.fpart = reinterpret_cast<float4*>(ws + p.off_fpart);
     a.fcount = reinterpret_cast<int32_t*>(ws + p.off_fcount);
   }
+  if (!lazy) a.fpair = p.fpair;
   const bool fuse = lazy && x.fuse_commit;
   CommitArgs cm{};
   int64_t gblocks = static_cast<int64_t>(sh) * (a.n_keys_pad / 64);
@@ -1256,8 +1312,8 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   const int64_t wg128 = static_cast<int64_t>(a.n_sh) * ((a.n_rows + 127) / 128);
   const int cfg = (!lazy || wg256 >= 512) ? 0 : wg128 >= 512 ? 1 : 2;
   const int rows_per = cfg == 0 ? 256 : cfg == 1 ? 128 : 64;
-  if (a.fsplit_u > 0 && cfg != 0) return hipErrorInvalidConfiguration;   // the split assumes 256-row tiles
-  dim3 gf(mapped_grid(a.n_sh, a.fsplit_u > 0 ? a.f_items : (a.n_rows + rows_per - 1) / rows_per));
+  if ((a.fsplit_u > 0 || a.fpair > 0) && cfg != 0) return hipErrorInvalidConfiguration;   // 256-row tiles only
+  dim3 gf(mapped_grid(a.n_sh, a.fsplit_u > 0 ? a.f_items : a.fpair > 0 ? a.fpair : (a.n_rows + rows_per - 1) / rows_per));
   {
     TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
     const bool mix = lazy && x.formula == FL_FORMULA_MIXTURE;
@@ -1267,7 +1323,8 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     else if (lazy) hipLaunchKernelGGL((k_mfma_fwd<D, NWV, KTV, true>), gf, dim3(THREADS), 0, st, kv.H, kv.N, a); \
     else hipLaunchKernelGGL((k_mfma_fwd<D, NWV, KTV, false>), gf, dim3(THREADS), 0, st, kv.H, kv.N, a);          \
   } while (0)
-    if (cfg == 0) FL_FWD(8, 64, 512);
+    if (a.fpair > 0) hipLaunchKernelGGL((k_mfma_fwd<D, 8, 64, false, false, true>), gf, dim3(512), 0, st, kv.H, kv.N, a);
+    else if (cfg == 0) FL_FWD(8, 64, 512);
     else if (cfg == 1) FL_FWD(4, 32, 256);
     else FL_FWD(2, 32, 128);
 #undef FL_FWD

@@ -95,6 +95,12 @@ int plan_fwd_split(int64_t n_sh, int64_t n_rows) {
   return best;
 }
 
+int plan_fwd_pair(int64_t n_sh, int64_t n_rows) {
+  const int64_t halves = (n_rows + 127) / 128, per = (halves + 1) / 2;
+  if (halves < 2 || n_sh * per > kXcds * kCusPerXcd) return 0;
+  return static_cast<int>(per);
+}
+
 hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);
 hipError_t launch_mfma(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);
 
@@ -144,6 +150,7 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     p.fsplit_u = lazy ? 0 : plan_fwd_split(static_cast<int64_t>(sh), p.rows);
     p.f_tiles = static_cast<int>((rows + 255) / 256);
     p.f_items = p.fsplit_u > 0 ? fwd_split_items(p.rows, p.fsplit_u) : p.f_tiles;
+    p.fpair = lazy || p.fsplit_u > 0 ? 0 : plan_fwd_pair(static_cast<int64_t>(sh), p.rows);
     p.off_fpart = off;
     p.off_fcount = off;
     if (p.fsplit_u > 0) {

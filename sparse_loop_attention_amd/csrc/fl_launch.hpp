@@ -25,6 +25,9 @@ struct AttendPlan {
   // of at most fsplit_u tiles, each a workgroup of its own (0 = no split);
   // f_items workgroups per (sequence, head), f_tiles row tiles
   int fsplit_u, f_items, f_tiles;
+  // MFMA path, full loops in one round of workgroups: workgroups per (sequence,
+  // head) that each take an early and a late 128-row half (0 = not used)
+  int fpair;
   // byte offsets in the workspace
   uint64_t off_part, off_logit, off_stat, off_gather, off_fpart, off_fcount, off_ccount, off_total;
   bool col_fused;       // several row ranges: the last range to finish adds them (no reduction launch)
@@ -34,6 +37,9 @@ struct AttendPlan {
 int plan_fwd_split(int64_t n_sh, int64_t n_rows);
 // Workgroups per (sequence, head) of the forward pass under key split u.
 int fwd_split_items(int64_t n_rows, int u);
+// Workgroups per (sequence, head) of a full loop's forward pass with paired
+// 128-row halves, or 0 where the grid would exceed one round of workgroups.
+int plan_fwd_pair(int64_t n_sh, int64_t n_rows);
 AttendPlan plan_attend(const fl_attend_args& a);
 hipError_t launch_attend(const fl_attend_args& a, const KvView& kv, const AttendPlan& p, hipStream_t st);
 

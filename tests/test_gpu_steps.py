@@ -257,6 +257,31 @@ def test_attend_full_key_split(d, n, H):
             assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("d,n,H", [(64, 2048, 32), (128, 1900, 32), (128, 4000, 16)])
+def test_attend_full_paired_halves(d, n, H):
+    """Full loops whose grid is one round of workgroups: each workgroup takes
+    an early and a late 128-row half (the second case has an odd number of
+    halves, so one workgroup per head has only the early one; the third ends
+    in a ragged half), and each wave stops at its own rows' last key tile."""
+    rng = np.random.default_rng(2000 + n)
+    dtype = torch.bfloat16
+    st, kv, rnd = _setup_attend(rng, n, H, d, dtype, {})
+    q = rnd(rng.standard_normal((n, H, d)).astype(np.float32) * 1.5)
+    o = torch.zeros(1, n, H, d, device=DEV)
+    lse = torch.zeros(1, n, H, device=DEV)
+    c = torch.full((1, H, n), 7.0, device=DEV)
+    a = abi.attend_args(kv, abi.FL_ATTEND_FULL, 1, to_dev(q[None], dtype), None, None, n, None, o, lse, c)
+    ws = torch.full((abi.attend_workspace_bytes(a),), 0xA5, dtype=torch.uint8, device=DEV)
+    a = abi.attend_args(kv, abi.FL_ATTEND_FULL, 1, to_dev(q[None], dtype), None, None, n, None, o, lse, c, ws)
+    abi.attend(a)
+    torch.cuda.synchronize()
+    o_r, lse_r, c_r = oracle.full_attention(q, oracle.to_working_dtype(st.reconstruct("k", 1), "bf16"),
+                                            oracle.to_working_dtype(st.reconstruct("v", 1), "bf16"), np.arange(n))
+    for got, want in ((o[0], o_r), (lse[0], lse_r), (c[0], c_r)):
+        ok, err, rms = rel_err_ok(got.cpu().numpy(), want)
+        assert ok, (err, rms)
+
+
 @pytest.mark.parametrize("dtype,d,n,na,ns", [(torch.float32, 64, 256, 64, 26), (torch.bfloat16, 128, 512, 103, 52),
                                              (torch.bfloat16, 96, 300, 300, 300), (torch.bfloat16, 128, 700, 1, 70),
                                              (torch.bfloat16, 128, 2000, 600, 200), (torch.bfloat16, 64, 1500, 1500, 150),
