@@ -194,13 +194,16 @@ fl_status flashloop_select(const fl_select_args* args, void* stream);
 /* (1 - m_i)*o_i (a_i is not needed); lse and colmass are updated as above.  */
 /* o, lse and colmass are updated in place; rows that are not active are not */
 /* read or written.  Any key tensor entry not described above is untouched.  */
-/* Fused commit (LAZY, fuse_commit != 0; paragraph 4: the KV update and      */
+/* Fused commit (fuse_commit != 0; paragraph 4: the KV update and           */
 /* compression are fused with the compute): the call also does what          */
 /* flashloop_kv_commit(version, active_idx, k_new, v_new, commit_slot_base,  */
 /* commit_reset) would do, inside its first kernel; keys that are active in  */
 /* this loop derive version `version` from k_new/v_new with the commit's own */
-/* float32 arithmetic instead of reading the records being written, so the   */
-/* store and every output equal commit-then-attend bit for bit.              */
+/* float32 arithmetic (version 1: the rows as given) instead of reading the  */
+/* records being written, so the store and every output equal                */
+/* commit-then-attend bit for bit.  FULL mode with a NULL active_idx commits */
+/* every token; where a FULL call takes the per-row path (float32 stores,   */
+/* fewer than 64 rows) the commit runs as its own kernel first.              */
 /* ------------------------------------------------------------------------ */
 typedef struct {
   int32_t mode;                 /* fl_attend_mode */
@@ -219,7 +222,7 @@ typedef struct {
   float* colmass;               /* [n_seq][H][N] float32 */
   void* workspace;              /* device, >= flashloop_attend_workspace_bytes(args) */
   uint64_t workspace_bytes;
-  /* fused commit (LAZY only) */
+  /* fused commit */
   int32_t fuse_commit;
   const void* k_new;            /* [n_seq][R][H][d] base_dtype, R per kv_layout */
   const void* v_new;

@@ -237,7 +237,7 @@ def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx,
                 key_idx, o, lse, colmass, workspace=None, q_compact=False, o_compact=False,
                 commit=None, formula: str = "column", exit_flags=None) -> fl_attend_args:
     """`commit` = dict(k_new=, v_new=, compact=False, slot_base=0, reset=True) fuses the
-    KV commit of this loop into the call (LAZY only); `formula` is "column" or
+    KV commit of this loop into the call; `formula` is "column" or
     "mixture" (LAZY only); `exit_flags` (int32 [n_seq]) skips exited sequences."""
     a = fl_attend_args()
     a.mode, a.kv, a.version = mode, C.pointer(kv.desc), version

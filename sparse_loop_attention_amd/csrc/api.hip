@@ -218,12 +218,11 @@ static fl_status check_attend(const fl_attend_args* a, fl_kv_layout* lay) {
     return fail(FL_ERR_ARG, "attend: formula %d (FULL needs FL_FORMULA_COLUMN)", a->formula);
   if (a->exit_flags && !aligned(a->exit_flags, 4)) return fail(FL_ERR_ARG, "attend: exit_flags must be 4-byte aligned");
   if (a->fuse_commit) {
-    if (!lazy) return fail(FL_ERR_ARG, "attend: fuse_commit needs LAZY mode");
     if (!a->k_new || !a->v_new || !aligned(a->k_new, 16) || !aligned(a->v_new, 16))
       return fail(FL_ERR_ARG, "attend: fused commit needs 16-byte aligned k_new and v_new");
     if (a->kv_layout != FL_ROWS_BY_TOKEN && a->kv_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "attend: kv_layout");
-    if (a->commit_slot_base < 0 ||
-        static_cast<int64_t>(a->commit_slot_base) + a->n_active > d.layer_cap[a->version])
+    if (a->version >= 2 && (a->commit_slot_base < 0 ||
+                            static_cast<int64_t>(a->commit_slot_base) + a->n_active > d.layer_cap[a->version]))
       return fail(FL_ERR_ARG, "attend: commit slots %d..%d exceed layer_cap[%d] = %d", a->commit_slot_base,
                   a->commit_slot_base + a->n_active, a->version, d.layer_cap[a->version]);
   }
@@ -259,6 +258,19 @@ fl_status flashloop_attend(const fl_attend_args* a, void* stream) {
                 (unsigned long long)p.off_total, (unsigned long long)a->workspace_bytes);
   fl::KvView kv = fl::make_view(*a->kv, lay);
   kv.exit_flags = a->exit_flags;
+  if (a->fuse_commit && a->mode == FL_ATTEND_FULL && !p.mfma) {
+    // the per-row path fuses only LAZY commits: commit first, on the same stream
+    fl_commit_args c{};
+    c.kv = a->kv; c.version = a->version;
+    c.active_idx = a->active_idx;                 // null: every token (the commit kernels take it so)
+    c.n_active = a->n_active;
+    c.slot_base = a->commit_slot_base; c.reset_map = a->commit_reset;
+    c.k_new = a->k_new; c.v_new = a->v_new;
+    c.src_layout = a->kv_layout;
+    c.exit_flags = a->exit_flags;
+    hipError_t e = fl::launch_commit(c, kv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attend launch");
+  }
   hipError_t e = fl::launch_attend(*a, kv, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attend launch");
   return ok();

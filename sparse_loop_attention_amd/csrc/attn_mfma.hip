@@ -151,7 +151,9 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
     for (int i = threadIdx.x; i < a.n_sh * (a.n_keys_pad / 256); i += 256) a.ccount[i] = 0;
   if (FUSE && b >= a.n_sh * n_tiles) {
     b -= a.n_sh * n_tiles;
-    const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2;
+    // lazy loops: blocks of their own write the active rows' records (the
+    // selected keys are other tokens); a full loop's key groups write them
+    const int64_t items = LAZY ? static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2 : 0;
     const int n_cb = static_cast<int>((items + 15) / 16);
     if (b < n_cb) {                                       // records of the active rows
       const int64_t item = static_cast<int64_t>(b) * 16 + g;
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
       const int64_t sr = (item >> 1) / kv.H;
       const int r = static_cast<int>(sr % a.n_rows), s = static_cast<int>(sr / a.n_rows);
       if (kv.exited(s)) return;                           // uniform per 16-lane group
-      const int j = a.act[static_cast<int64_t>(s) * a.n_rows + r];
+      const int j = a.act ? a.act[static_cast<int64_t>(s) * a.n_rows + r] : r;
       const int64_t src_rows = cm.src_compact ? a.n_rows : kv.N;
       const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? r : j)) * kv.H + h) * D;
       commit_row<DT>(kv, cm.arena, a.version, s, j, h, which, cm.slot_base + r, which ? cm.v_new : cm.k_new,
@@ -172,8 +174,8 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
     const int per_seq = (kv.N + 255) / 256;
     const int s = b / per_seq;
     const int j = (b % per_seq) * 256 + threadIdx.x;
-    if (s >= kv.n_seq || j >= kv.N || kv.exited(s)) return;
-    const int ra = find_active(a.act + static_cast<int64_t>(s) * a.n_rows, a.n_rows, j);
+    if (a.version < 2 || s >= kv.n_seq || j >= kv.N || kv.exited(s)) return;
+    const int ra = a.act ? find_active(a.act + static_cast<int64_t>(s) * a.n_rows, a.n_rows, j) : j;
     int32_t* dst = reinterpret_cast<int32_t*>(cm.arena + kv.slot_table) +
                    (static_cast<int64_t>(s) * kv.N + j) * kv.slot_pitch + (a.version - 2);
     if (ra >= 0) *dst = cm.slot_base + ra;
@@ -184,7 +186,8 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
   const int s = sh / kv.H, h = sh % kv.H;
   if (kv.exited(s)) return;                               // uniform per workgroup
   const bool live = 8 * p < D;
-  const int32_t* act_s = FUSE ? a.act + static_cast<int64_t>(s) * a.n_rows : nullptr;
+  // fused commit: the active rows (null: every token, row = token)
+  const int32_t* act_s = FUSE && a.act ? a.act + static_cast<int64_t>(s) * a.n_rows : nullptr;
   // the 16-lane group's 4 key slots, U at a time (recon_kv keeps every slot
   // and record load of the U keys in flight at once)
 #pragma unroll 1
@@ -204,8 +207,21 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
       // versions v-1 from the chain, version v from this loop's new rows.  A
       // reset commit clears layer v for the tokens it does not write; otherwise
       // layer v may hold earlier commits' records (an active key's own entry is
-      // overridden below).
-      if (cm.reset) {
+      // overridden below).  In a full loop every active row is one of the
+      // keys, whose group writes its record (version 1: the base row) while
+      // deriving the key's new version; version 1 of the other tokens is the
+      // stored base.
+      int ra[U];
+#pragma unroll
+      for (int kk = 0; kk < U; ++kk)
+        ra[kk] = !ok[kk] ? -1 : act_s ? find_active(act_s, a.n_rows, jj[kk]) : jj[kk];
+      const bool base_commit = !LAZY && a.version == 1;
+      if (base_commit) {
+        bool rd[U];
+#pragma unroll
+        for (int kk = 0; kk < U; ++kk) rd[kk] = ok[kk] && ra[kk] < 0;
+        recon_kv<DT, U, false>(kv, s, h, jj, rd, 1, p, x, y, xp, yp);
+      } else if (cm.reset) {
         recon_kv<DT, U, false>(kv, s, h, jj, ok, a.version - 1, p, x, y, xp, yp);
 #pragma unroll
         for (int kk = 0; kk < U; ++kk)
@@ -216,16 +232,28 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
       }
 #pragma unroll
       for (int kk = 0; kk < U; ++kk) {
-        const int ra = ok[kk] ? find_active(act_s, a.n_rows, jj[kk]) : -1;
-        if (ra >= 0) {
+        if (ra[kk] >= 0) {
           const int64_t src_rows = cm.src_compact ? a.n_rows : kv.N;
           const int64_t src =
-              ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? ra : jj[kk])) * kv.H + h) * D + 8 * p;
+              ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? ra[kk] : jj[kk])) * kv.H + h) * D + 8 * p;
           float kn[8], vn[8];
           load8<DT>(cm.k_new, src, kn);
           load8<DT>(cm.v_new, src, vn);
-          advance8(kv, kn, xp[kk], true, x[kk]);
-          advance8(kv, vn, yp[kk], true, y[kk]);
+          if (base_commit) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { x[kk][e] = kn[e]; y[kk][e] = vn[e]; }
+            if (live) {
+              const int64_t be = ((static_cast<int64_t>(s) * kv.H + h) * kv.N + jj[kk]) * D + 8 * p;
+              store8<DT>(cm.arena + kv.base[0], be, kn);
+              store8<DT>(cm.arena + kv.base[1], be, vn);
+            }
+          } else if (!LAZY) {
+            commit_advance8(kv, cm.arena, a.version, s, cm.slot_base + ra[kk], h, 0, kn, xp[kk], live, p, x[kk]);
+            commit_advance8(kv, cm.arena, a.version, s, cm.slot_base + ra[kk], h, 1, vn, yp[kk], live, p, y[kk]);
+          } else {
+            advance8(kv, kn, xp[kk], true, x[kk]);
+            advance8(kv, vn, yp[kk], true, y[kk]);
+          }
         }
       }
     } else if (LAZY) {
@@ -1271,7 +1299,7 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     a.fcount = reinterpret_cast<int32_t*>(ws + p.off_fcount);
   }
   if (!lazy) a.fpair = p.fpair;
-  const bool fuse = lazy && x.fuse_commit;
+  const bool fuse = x.fuse_commit;
   CommitArgs cm{};
   int64_t gblocks = static_cast<int64_t>(sh) * (a.n_keys_pad / 64);
   if (fuse) {
@@ -1280,11 +1308,12 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     cm.src_compact = x.kv_layout == FL_ROWS_COMPACT;
     cm.slot_base = x.commit_slot_base; cm.reset = x.commit_reset;
     const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2;
-    gblocks += (items + 15) / 16 + static_cast<int64_t>(kv.n_seq) * ((kv.N + 255) / 256);
+    if (lazy) gblocks += (items + 15) / 16;                                  // the active rows' records
+    if (x.version >= 2) gblocks += static_cast<int64_t>(kv.n_seq) * ((kv.N + 255) / 256);   // slot column
   }
   dim3 gg(static_cast<unsigned>(gblocks));
   {
-    TimedLaunch t(st, fuse ? "gather_commit_lazy" : lazy ? "gather_lazy" : "gather_full");
+    TimedLaunch t(st, fuse ? (lazy ? "gather_commit_lazy" : "gather_commit_full") : lazy ? "gather_lazy" : "gather_full");
     // four keys per chain walk when the gather blocks alone leave CUs idle
     const bool wide = static_cast<int64_t>(sh) * (a.n_keys_pad / 64) < 512;
 #define FL_GATHER(DTV, LZ, FU)                                                                  \
@@ -1293,12 +1322,14 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     else hipLaunchKernelGGL((k_gather<DTV, D, LZ, FU, 1>), gg, dim3(256), 0, st, kv, a, cm);      \
   } while (0)
     if (kv.dtype == FL_BF16) {
-      if (fuse) FL_GATHER(FL_BF16, true, true);
+      if (lazy && fuse) FL_GATHER(FL_BF16, true, true);
       else if (lazy) FL_GATHER(FL_BF16, true, false);
+      else if (fuse) FL_GATHER(FL_BF16, false, true);
       else FL_GATHER(FL_BF16, false, false);
     } else {
-      if (fuse) FL_GATHER(FL_F32, true, true);
+      if (lazy && fuse) FL_GATHER(FL_F32, true, true);
       else if (lazy) FL_GATHER(FL_F32, true, false);
+      else if (fuse) FL_GATHER(FL_F32, false, true);
       else FL_GATHER(FL_F32, false, false);
     }
 #undef FL_GATHER

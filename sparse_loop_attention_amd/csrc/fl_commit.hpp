@@ -56,6 +56,32 @@ __device__ __forceinline__ void advance8(const KvView& kv, const float x_new[8],
   add_codes8(packed, kv.bits, sc, x_out);
 }
 
+// Commits a head row whose version l-1 is x_prev and whose new value is x_new
+// into layer l >= 2 at record slot `slot` (what commit_row writes), and
+// returns version l in x_out (what a reader of the record reconstructs).
+// Called by a whole 16-lane group; lane p owns elements [8p, 8p+8).
+__device__ __forceinline__ void commit_advance8(const KvView& kv, uint8_t* arena_w, int l, int s, int slot, int h,
+                                                int which, const float x_new[8], const float x_prev[8], bool live,
+                                                int p, float x_out[8]) {
+  float delta[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) delta[e] = x_new[e] - x_prev[e];
+  uint32_t packed;
+  uint16_t sbits;
+  float sc;
+  quantize8(kv, delta, live, packed, sbits, sc);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x_out[e] = x_prev[e];
+  add_codes8(packed, kv.bits, sc, x_out);
+  if (!live) return;
+  const int64_t rec = kv.record(l, s, slot, h, which);
+  uint8_t* cb = arena_w + kv.codes[l] + rec * (kv.d * kv.bits / 8) + p * kv.bits;
+  if (kv.bits == 4) *reinterpret_cast<uint32_t*>(cb) = packed;
+  else *reinterpret_cast<uint16_t*>(cb) = static_cast<uint16_t>(packed);
+  if ((p & ((1 << kv.gshift) - 1)) == 0)
+    reinterpret_cast<uint16_t*>(arena_w + kv.scales[l])[kv.scale_index(rec, p)] = sbits;
+}
+
 // Position of token j in the ascending active list act[0..n), or -1.
 __device__ __forceinline__ int find_active(const int32_t* act, int n, int j) {
   int lo = 0, hi = n;

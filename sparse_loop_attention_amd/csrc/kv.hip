@@ -13,7 +13,8 @@
 namespace fl {
 
 // slot(l, s, j) = slot_base + r if active_idx[s][r] == j, else -1 (reset) / untouched;
-// `slots` points at column l-2 of the slot table, rows `pitch` apart.
+// `slots` points at column l-2 of the slot table, rows `pitch` apart.  A null
+// `act` means every token is active (n_act == N, r == j).
 __global__ __launch_bounds__(256) void k_slot_map(int32_t* __restrict__ slots, int32_t pitch, int32_t N,
                                                   const int32_t* __restrict__ act, int32_t n_act,
                                                   int32_t slot_base, int32_t reset,
@@ -21,18 +22,23 @@ __global__ __launch_bounds__(256) void k_slot_map(int32_t* __restrict__ slots, i
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int s = blockIdx.y;
   if (j >= N || (exit_flags && exit_flags[s])) return;
+  int32_t* dst = slots + (static_cast<int64_t>(s) * N + j) * pitch;
+  if (!act) {
+    *dst = slot_base + static_cast<int32_t>(j);
+    return;
+  }
   const int32_t* a = act + static_cast<int64_t>(s) * n_act;
   int lo = 0, hi = n_act;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (a[mid] < j) lo = mid + 1; else hi = mid;
   }
-  int32_t* dst = slots + (static_cast<int64_t>(s) * N + j) * pitch;
   if (lo < n_act && a[lo] == j) *dst = slot_base + lo;
   else if (reset) *dst = -1;
 }
 
-// One 16-lane group per (sequence, active row, head, K|V) row.
+// One 16-lane group per (sequence, active row, head, K|V) row (a null `act`:
+// every token, row r = token r).
 template <int DT>
 __global__ __launch_bounds__(256) void k_commit(KvView kv, uint8_t* __restrict__ arena_w, int32_t l,
                                                 const int32_t* __restrict__ act, int32_t n_act,
@@ -49,7 +55,7 @@ __global__ __launch_bounds__(256) void k_commit(KvView kv, uint8_t* __restrict__
   const int r = static_cast<int>(sr % n_act);
   const int s = static_cast<int>(sr / n_act);
   if (kv.exited(s)) return;                                     // uniform per 16-lane group
-  const int j = act[static_cast<int64_t>(s) * n_act + r];
+  const int j = act ? act[static_cast<int64_t>(s) * n_act + r] : r;
   const int64_t src_rows = src_compact ? n_act : kv.N;
   const int64_t src_row = src_compact ? r : j;
   const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + src_row) * H + h) * kv.d;

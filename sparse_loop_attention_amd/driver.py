@@ -98,8 +98,10 @@ class PrefillRun:
     def _attend_args(self, l: int):
         wl = self.wl
         if l <= wl.n_full:
+            # every row; with fusion the call also commits every token's K/V
+            commit = dict(k_new=self.inp[l]["k"], v_new=self.inp[l]["v"]) if self.fuse else None
             return abi.attend_args(self.kv, abi.FL_ATTEND_FULL, l, self.inp[l]["q"], None, None, wl.n_tokens,
-                                   None, self.o, self.lse, self.colmass, self.workspace)
+                                   None, self.o, self.lse, self.colmass, self.workspace, commit=commit)
         na = wl.n_active(l)
         commit = dict(k_new=self.inp[l]["k"], v_new=self.inp[l]["v"]) if self.fuse else None
         # the active rows' queries of loops l and l-1, read by token
@@ -110,7 +112,8 @@ class PrefillRun:
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
         x = self.inp[l]
-        abi.kv_commit(self.kv, l, self.all_rows, x["k"], x["v"])
+        if not self.fuse:
+            abi.kv_commit(self.kv, l, self.all_rows, x["k"], x["v"])
         abi.attend(self._attend_args(l))
 
     def lazy_loop(self, l: int, cand: Optional[torch.Tensor]) -> torch.Tensor:

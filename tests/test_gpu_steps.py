@@ -257,6 +257,55 @@ def test_attend_full_key_split(d, n, H):
             assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("dtype,n,H,d,version,subset,reset", [
+    (torch.bfloat16, 700, 3, 128, 1, False, True),     # the base of every token (NULL active_idx)
+    (torch.bfloat16, 700, 3, 128, 2, False, True),
+    (torch.bfloat16, 700, 3, 64, 3, True, False),      # some rows, into a layer that already holds records
+    (torch.bfloat16, 640, 2, 96, 3, True, True),
+    (torch.float32, 300, 2, 64, 2, False, True),       # per-row path: the commit runs as its own kernel
+])
+def test_attend_full_fused_commit(dtype, n, H, d, version, subset, reset):
+    """A FULL call with the commit fused writes the same store and gives the
+    same o, lse and column mass, bit for bit, as commit-then-attend."""
+    rng = np.random.default_rng(3000 + n + version)
+    rnd = bf16_round if dtype == torch.bfloat16 else (lambda x: x.astype(np.float32))
+    xs = {l: [rnd(rng.standard_normal((1, n, H, d)) * (1.0 + 0.1 * l)) for _ in range(2)] for l in (1, 2, 3)}
+    q = rnd(rng.standard_normal((1, n, H, d)) * 1.5)
+    rows = np.sort(rng.choice(n, size=n // 3, replace=False)) if subset else np.arange(n)
+    early = None if reset else np.sort(rng.choice(np.setdiff1d(np.arange(n), rows), size=40, replace=False))
+    dev_rows = torch.from_numpy(rows.astype(np.int32)).to(DEV)[None]
+    outs = []
+    for fuse in (False, True):
+        kv = abi.KVStore(1, H, d, n, 3, dtype, [n, n], DEV)
+        kv.arena.zero_()
+        every = torch.arange(n, dtype=torch.int32, device=DEV)[None]
+        for l in range(1, version):
+            abi.kv_commit(kv, l, every, to_dev(xs[l][0], dtype), to_dev(xs[l][1], dtype))
+        slot_base = 0
+        if not reset:                                      # records of other tokens already in the layer
+            abi.kv_commit(kv, version, torch.from_numpy(early.astype(np.int32)).to(DEV)[None],
+                          to_dev(xs[version][0] * 0.5, dtype), to_dev(xs[version][1] * 0.5, dtype))
+            slot_base = len(early)
+        k_new, v_new = to_dev(xs[version][0], dtype), to_dev(xs[version][1], dtype)
+        o = torch.zeros(1, n, H, d, device=DEV)
+        lse = torch.zeros(1, n, H, device=DEV)
+        c = torch.full((1, H, n), 7.0, device=DEV)
+        act = dev_rows if subset else None
+        commit = dict(k_new=k_new, v_new=v_new, slot_base=slot_base, reset=reset) if fuse else None
+        if not fuse:
+            abi.kv_commit(kv, version, dev_rows, k_new, v_new, slot_base=slot_base, reset_map=reset)
+        a = abi.attend_args(kv, abi.FL_ATTEND_FULL, version, to_dev(q, dtype), None, act, len(rows), None, o, lse,
+                            c, commit=commit)
+        ws = torch.empty(max(abi.attend_workspace_bytes(a), 256), dtype=torch.uint8, device=DEV)
+        a = abi.attend_args(kv, abi.FL_ATTEND_FULL, version, to_dev(q, dtype), None, act, len(rows), None, o, lse,
+                            c, ws, commit=commit)
+        abi.attend(a)
+        torch.cuda.synchronize()
+        outs.append((kv.arena.cpu(), o.cpu(), lse.cpu(), c.cpu()))
+    for x, y, name in zip(outs[0], outs[1], ("arena", "o", "lse", "colmass")):
+        assert torch.equal(x, y), name
+
+
 @pytest.mark.parametrize("d,n,H", [(64, 2048, 32), (128, 1900, 32), (128, 4000, 16)])
 def test_attend_full_paired_halves(d, n, H):
     """Full loops whose grid is one round of workgroups: each workgroup takes
