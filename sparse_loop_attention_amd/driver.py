@@ -15,6 +15,11 @@ row that is a candidate in loop l was active in every earlier loop: its
 effective state is the previous loops' output for that row.  The token scores
 therefore read h of loops l-1 and l-2 directly, and attention reads the active
 rows' queries of loops l and l-1 by token from those loops' outputs.
+
+The token selection of a loop depends only on the hidden states and on the
+previous loop's active set, not on any attention result, so PrefillRun issues
+it on a second stream (default priority) that runs ahead of the attention
+chain; a loop's attention waits for its own selection only.
 """
 from __future__ import annotations
 
@@ -65,11 +70,13 @@ class PrefillRun:
     """GPU state of one prefill workload (n_seq = 1) and its loop sequence."""
 
     def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], device="cuda", fuse: bool = True,
-                 formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None):
+                 formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None,
+                 overlap: bool = True):
         """formula "column" (default) or "mixture"; freeze_keys reuses the first
         lazy loop's key group in every later lazy loop; exit_threshold enables
         the early exit (the sequence stops before the first lazy loop whose
-        largest token change is below it)."""
+        largest token change is below it); overlap runs the token selection on
+        a second stream."""
         assert wl.n_seq == 1 and not wl.decode
         self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
         self.formula, self.freeze_keys = formula, freeze_keys
@@ -82,7 +89,11 @@ class PrefillRun:
         self.o = torch.empty(n, H, d, dtype=torch.float32, device=device)
         self.lse = torch.empty(n, H, dtype=torch.float32, device=device)
         self.colmass = torch.empty(H, n, dtype=torch.float32, device=device)
-        self.scores = torch.empty(n, dtype=torch.float64, device=device)
+        # one score buffer per lazy loop: a loop's selection may run before the
+        # previous loop's readers of its scores
+        self.scores_l = {l: torch.empty(n, dtype=torch.float64, device=device)
+                         for l in range(wl.n_full + 1, wl.n_loops + 1)}
+        self.side = torch.cuda.Stream(device=device) if overlap else None
         self.all_rows = torch.arange(n, dtype=torch.int32, device=device)
         self.act = {l: torch.empty(wl.n_active(l), dtype=torch.int32, device=device)
                     for l in range(wl.n_full + 1, wl.n_loops + 1)}
@@ -118,11 +129,16 @@ class PrefillRun:
 
     def lazy_loop(self, l: int, cand: Optional[torch.Tensor]) -> torch.Tensor:
         wl, x = self.wl, self.inp[l]
-        act, na = self.act[l], wl.n_active(l)
+        act, na, scores = self.act[l], wl.n_active(l), self.scores_l[l]
         # the change of the candidate rows during loop l-1 (every row after the full loops)
-        abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, self.scores, act, cand)
+        if self.side is not None:
+            with torch.cuda.stream(self.side):
+                abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, scores, act, cand)
+            torch.cuda.current_stream().wait_stream(self.side)
+        else:
+            abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, scores, act, cand)
         if self.exit_flags is not None:          # early exit: no later library call touches the sequence
-            abi.exit_check(self.exit_flags, self.exit_threshold, scores=self.scores)
+            abi.exit_check(self.exit_flags, self.exit_threshold, scores=scores)
         first = wl.n_full + 1
         if self.freeze_keys and l > first:
             self.keys_l[l].copy_(self.keys_l[first])
@@ -140,6 +156,9 @@ class PrefillRun:
         cand = None
         if self.exit_flags is not None:
             self.exit_flags.zero_()
+        if self.side is not None:
+            # the selection buffers are reused: earlier steps' readers finish first
+            self.side.wait_stream(torch.cuda.current_stream())
         for l in range(1, T + 1):
             if l <= wl.n_full:
                 self.full_loop(l)
@@ -150,13 +169,15 @@ class PrefillRun:
                 cand = act
                 rec = LoopRecord(rows=act.clone() if record else None,
                                  keys=self.keys_l[l].clone() if record else None,
-                                 scores=self.scores.clone() if record else None)
+                                 scores=self.scores_l[l].clone() if record else None)
             if record:
                 rec.o, rec.lse, rec.colmass = self.o.clone(), self.lse.clone(), self.colmass.clone()
                 rec.arena = self.kv.arena.clone()
                 if self.exit_flags is not None:
                     rec.exited = self.exit_flags.clone()
             recs.append(rec)
+        if self.side is not None:
+            torch.cuda.current_stream().wait_stream(self.side)
         return recs
 
 
