@@ -19,7 +19,9 @@ rows' queries of loops l and l-1 by token from those loops' outputs.
 The token selection of a loop depends only on the hidden states and on the
 previous loop's active set, not on any attention result, so PrefillRun issues
 it on a second stream (default priority) that runs ahead of the attention
-chain; a loop's attention waits for its own selection only.
+chain; a loop's attention waits for its own selection only.  Each wait costs
+a cross-stream synchronisation, which only pays where the attention chain
+keeps the GPU busy meanwhile (4096 tokens or more).
 """
 from __future__ import annotations
 
@@ -71,12 +73,12 @@ class PrefillRun:
 
     def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], device="cuda", fuse: bool = True,
                  formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None,
-                 overlap: bool = True):
+                 overlap: Optional[bool] = None):
         """formula "column" (default) or "mixture"; freeze_keys reuses the first
         lazy loop's key group in every later lazy loop; exit_threshold enables
         the early exit (the sequence stops before the first lazy loop whose
         largest token change is below it); overlap runs the token selection on
-        a second stream."""
+        a second stream (None: from 4096 tokens up)."""
         assert wl.n_seq == 1 and not wl.decode
         self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
         self.formula, self.freeze_keys = formula, freeze_keys
@@ -93,6 +95,8 @@ class PrefillRun:
         # previous loop's readers of its scores
         self.scores_l = {l: torch.empty(n, dtype=torch.float64, device=device)
                          for l in range(wl.n_full + 1, wl.n_loops + 1)}
+        if overlap is None:
+            overlap = n >= 4096
         self.side = torch.cuda.Stream(device=device) if overlap else None
         self.all_rows = torch.arange(n, dtype=torch.int32, device=device)
         self.act = {l: torch.empty(wl.n_active(l), dtype=torch.int32, device=device)

@@ -110,21 +110,25 @@ def _arena_parts(kv, wl):
                          ids=["tiny", "single_layer_512", "deep_320"])
 def test_fused_commit_equals_commit_then_attend(wl):
     """The commit fused into the attention call writes the same store and gives
-    the same outputs, bit for bit, as a separate commit followed by attend."""
+    the same outputs, bit for bit, as a separate commit followed by attend;
+    so does the run with the token selection on a second stream."""
     inputs = driver.upload_loops(wl, SyntheticLoops(wl), DEV)
     res = []
-    for fuse in (False, True):
-        run = driver.PrefillRun(wl, inputs, DEV, fuse=fuse)
+    for fuse, overlap in ((False, False), (True, False), (True, True)):
+        run = driver.PrefillRun(wl, inputs, DEV, fuse=fuse, overlap=overlap)
         run.kv.arena.zero_()
         recs = run.run(record=True)
         torch.cuda.synchronize()
         res.append((recs, _arena_parts(run.kv, wl)))
-    (ra, aa), (rb, ab) = res
-    for k in aa:
-        assert torch.equal(aa[k], ab[k]), k
-    for l in range(wl.n_loops):
-        assert torch.equal(ra[l].o, rb[l].o) and torch.equal(ra[l].lse, rb[l].lse)
-        assert torch.equal(ra[l].colmass, rb[l].colmass)
+    (ra, aa) = res[0]
+    for rb, ab in res[1:]:
+        for k in aa:
+            assert torch.equal(aa[k], ab[k]), k
+        for l in range(wl.n_loops):
+            assert torch.equal(ra[l].o, rb[l].o) and torch.equal(ra[l].lse, rb[l].lse)
+            assert torch.equal(ra[l].colmass, rb[l].colmass)
+            if ra[l].rows is not None:
+                assert torch.equal(ra[l].rows, rb[l].rows) and torch.equal(ra[l].scores, rb[l].scores)
 
 
 def test_fused_commit_decode_equals_unfused():
