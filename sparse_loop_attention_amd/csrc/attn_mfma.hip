@@ -68,8 +68,11 @@ struct MfmaArgs {
   int32_t* kidx;            // [sh][n_keys_pad], INT_MAX for padding
   float* stat;              // [sh][n_rows][4] = lse_prev, lse_new, valid, token
   int32_t n_sh;             // n_seq * H
-  // column mass: rows split into col_chunks ranges of col_rows rows
-  int32_t col_chunks, col_rows;
+  // column mass: rows split into col_chunks ranges of col_rows rows; or, with
+  // col_var_rows > 0 (full loops, rows = tokens = key slots), key block b's
+  // rows [256 b, n_rows) split into ranges of col_var_rows rows, col_items
+  // (block, range) items per head in all, at most col_chunks per block
+  int32_t col_chunks, col_rows, col_var_rows, col_items;
   float* col_part;          // [col_chunks][sh][n_keys_pad] partial sums (col_chunks > 1)
   // forward key split (full loops): the key tiles of row tile t are cut into
   // ceil(tiles / fsplit_u) parts, one workgroup each (fsplit_u = 0: none)
@@ -1029,7 +1032,7 @@ __device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H
 // workgroup calls it.
 template <bool LAZY>
 __device__ __forceinline__ void col_finish(const MfmaArgs& a, int N, int chunk, int sh, int kblk, int t, int kj,
-                                           float acc, int* s_arrived) {
+                                           float acc, int* s_arrived, int n_parts) {
   const int tid = threadIdx.x, hh = (tid & 63) >> 5;
   if (a.col_chunks == 1) {
     if (hh == 0 && t < a.n_keys) {
@@ -1046,11 +1049,11 @@ __device__ __forceinline__ void col_finish(const MfmaArgs& a, int N, int chunk, 
     *s_arrived = __hip_atomic_fetch_add(a.ccount + static_cast<int64_t>(sh) * (a.n_keys_pad / 256) + kblk, 1,
                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (*s_arrived != a.col_chunks - 1 || tid >= 256) return;
+  if (*s_arrived != n_parts - 1 || tid >= 256) return;
   const int tk = kblk * 256 + tid;
   if (tk >= a.n_keys) return;
   float sum = 0.0f;
-  for (int ch = 0; ch < a.col_chunks; ++ch)
+  for (int ch = 0; ch < n_parts; ++ch)
     sum += __hip_atomic_load(a.col_part + (static_cast<int64_t>(ch) * a.n_sh + sh) * a.n_keys_pad + tk,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float* dst = a.colmass + static_cast<int64_t>(sh) * N + a.kidx[static_cast<int64_t>(sh) * a.n_keys_pad + tk];
@@ -1130,10 +1133,26 @@ __global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
   const int n_kblk = a.n_keys_pad / KB;
-  int sh, item;
-  if (!map_block(a.n_sh, n_kblk * a.col_chunks, sh, item)) return;
-  const int chunk = item % a.col_chunks;
-  const int kblk = n_kblk - 1 - item / a.col_chunks;      // early keys see the most rows: start them first
+  int sh, item, chunk, kblk, c_lo, n_parts;
+  if (a.col_var_rows > 0) {
+    // items heavy first: key blocks in order, each block's ranges in order
+    if (!map_block(a.n_sh, a.col_items, sh, item)) return;
+    int rem = a.col_items - 1 - item;
+    for (kblk = 0;; ++kblk) {
+      n_parts = (a.n_rows - kblk * KB + a.col_var_rows - 1) / a.col_var_rows;
+      if (rem < n_parts || kblk == n_kblk - 1) break;
+      rem -= n_parts;
+    }
+    chunk = rem;
+    c_lo = kblk * KB + chunk * a.col_var_rows;
+  } else {
+    if (!map_block(a.n_sh, n_kblk * a.col_chunks, sh, item)) return;
+    chunk = item % a.col_chunks;
+    kblk = n_kblk - 1 - item / a.col_chunks;              // early keys see the most rows: start them first
+    c_lo = chunk * a.col_rows;
+    n_parts = a.col_chunks;
+  }
+  const int c_rows = a.col_var_rows > 0 ? a.col_var_rows : a.col_rows;
   const int s = sh / H, h = sh % H;
   if (a.exited(s)) return;
   const int t0 = kblk * KB + wave * 32;
@@ -1156,8 +1175,7 @@ __global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t
     s_start = lo;
   }
   __syncthreads();
-  const int c_lo = chunk * a.col_rows;
-  const int r_end = min(a.n_rows, c_lo + a.col_rows);
+  const int r_end = min(a.n_rows, c_lo + c_rows);
   const int r_begin = max(c_lo, (s_start / QT) * QT);
   const int n_tiles = r_end > r_begin ? (r_end - r_begin + QT - 1) / QT : 0;
   const int64_t rows_q = a.q_compact ? a.n_rows : N;
@@ -1245,7 +1263,7 @@ __global__ __launch_bounds__(512, 1) void k_colmass_full_rows(int32_t H, int32_t
     __syncthreads();
   }
   acc += __shfl_xor(acc, 32, 64);
-  col_finish<false>(a, N, chunk, sh, kblk, t, kj, acc, &s_arrived);
+  col_finish<false>(a, N, chunk, sh, kblk, t, kj, acc, &s_arrived, n_parts);
 }
 
 // Sums the per-chunk partial column masses in chunk order.
@@ -1362,9 +1380,11 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.col_chunks = p.col_chunks;
+  a.col_var_rows = p.col_var_rows;
+  a.col_items = p.col_items;
   a.col_rows = p.col_rows;
   a.col_part = reinterpret_cast<float*>(ws + p.off_part);
-  dim3 gc(mapped_grid(a.n_sh, a.n_keys_pad / 256 * a.col_chunks));
+  dim3 gc(mapped_grid(a.n_sh, a.col_var_rows > 0 ? a.col_items : a.n_keys_pad / 256 * a.col_chunks));
   {
     TimedLaunch t(st, lazy ? "mfma_colmass_lazy" : "mfma_colmass_full");
     if (lazy) hipLaunchKernelGGL((k_mfma_colmass<D, true>), gc, dim3(512), 0, st, kv.H, kv.N, a);

@@ -135,6 +135,26 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     p.col_rows = static_cast<int>((row_tiles + chunks - 1) / chunks * 64);
     p.col_chunks = static_cast<int>((rows + p.col_rows - 1) / p.col_rows);
     if (p.col_chunks < 1) p.col_chunks = 1;
+    // a full loop over every row (rows = tokens = key slots) on >= 8 heads
+    // sizes the ranges of each key block to its own rows (block b: rows from
+    // 256 b on), so no range is empty and the largest is small: the largest
+    // range length (a multiple of 64) that still gives >= 1024 items
+    p.col_var_rows = 0;
+    p.col_items = 0;
+    if (!lazy && !a.active_idx && p.col_chunks > 1 && sh >= 8) {
+      const uint64_t n_kblk = kpad / 256;
+      auto items_for = [&](uint64_t r) {
+        uint64_t n = 0;
+        for (uint64_t b = 0; b < n_kblk; ++b) n += (rows - 256 * b + r - 1) / r;
+        return n;
+      };
+      uint64_t r = 64 * row_tiles;
+      while (r > 64 && sh * items_for(r) < 1024) r -= 64;
+      p.col_var_rows = static_cast<int>(r);
+      p.col_items = static_cast<int>(items_for(r));
+      p.col_chunks = static_cast<int>((rows + r - 1) / r);
+      p.col_rows = static_cast<int>(r);
+    }
     p.off_part = off;
     if (p.col_chunks > 1) off = align256(off + static_cast<uint64_t>(p.col_chunks) * sh * kpad * 4);
     // full loops: the ranges of one key block run on one XCD when there are

@@ -21,6 +21,9 @@ struct AttendPlan {
   int splits;           // unused (0)
   int col_chunks;       // MFMA path: row ranges of the column-mass pass
   int col_rows;         // rows per range (a multiple of 64)
+  // full loops over every row: ranges of col_var_rows rows per key block,
+  // col_items (block, range) items per (sequence, head) (0 = fixed ranges)
+  int col_var_rows, col_items;
   // MFMA path, full loops: the key tiles of a 256-row tile are cut into parts
   // of at most fsplit_u tiles, each a workgroup of its own (0 = no split);
   // f_items workgroups per (sequence, head), f_tiles row tiles
