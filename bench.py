@@ -63,7 +63,9 @@ def _pairs(rows, keys_sorted):
 
 
 def work_model(wl, run):
-    """Algorithmic flops / bytes of one step, per kernel family."""
+    """Algorithmic flops / bytes of one step, per kernel family: 4d flops per visible
+    (row, key) pair in full loops and 8d in lazy ones (6d for the mixture formula),
+    2d (4d lazy) for the column mass, and the bytes each HBM-bound kernel must move."""
     import numpy as np
     H, d, N = wl.n_heads, wl.head_dim, wl.n_tokens
     es = 2 if wl.dtype == "bf16" else 4

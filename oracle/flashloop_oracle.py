@@ -17,7 +17,7 @@ reconstruction chain are evaluated in float32, because their results decide
 integers (the 4-bit codes) and the HIP path takes those decisions in float32;
 both sides therefore take the same decision in the same precision.
 
-Readings of points the page leaves open (all listed in the design doc):
+Readings of points the page leaves open:
   R1 tokens are ranked at loop l by the change of the previous loop,
      ||h_eff^(l-1) - h_eff^(l-2)||^2 (a loop cannot know its own change before
      computing it); squared L2 over the whole hidden row, float64.
