@@ -306,6 +306,46 @@ def test_attend_full_fused_commit(dtype, n, H, d, version, subset, reset):
         assert torch.equal(x, y), name
 
 
+def test_attend_full_fused_exit_flags():
+    """A FULL call (paired row halves, per-block column-mass ranges, fused
+    commit) over two sequences of which one has exited: the exited sequence's
+    o, lse, column mass and store are left as they were, and the other's equal
+    those of a call without flags, bit for bit."""
+    rng = np.random.default_rng(4242)
+    n, H, d, S = 2048, 16, 128, 2                         # 32 head rows x 8 row tiles: one round
+    dtype = torch.bfloat16
+    x1 = [bf16_round(rng.standard_normal((S, n, H, d))) for _ in range(2)]
+    x2 = [bf16_round(rng.standard_normal((S, n, H, d)) * 1.1) for _ in range(2)]
+    q = bf16_round(rng.standard_normal((S, n, H, d)) * 1.5)
+    outs = []
+    for flags in (None, [0, 1]):
+        kv = abi.KVStore(S, H, d, n, 2, dtype, [n], DEV)
+        kv.arena.zero_()
+        every = torch.arange(n, dtype=torch.int32, device=DEV)[None].repeat(S, 1).contiguous()
+        abi.kv_commit(kv, 1, every, to_dev(x1[0], dtype), to_dev(x1[1], dtype))
+        o = torch.zeros(S, n, H, d, device=DEV)
+        lse = torch.zeros(S, n, H, device=DEV)
+        c = torch.full((S, H, n), 7.0, device=DEV)
+        ef = None if flags is None else torch.tensor(flags, dtype=torch.int32, device=DEV)
+        commit = dict(k_new=to_dev(x2[0], dtype), v_new=to_dev(x2[1], dtype))
+        a = abi.attend_args(kv, abi.FL_ATTEND_FULL, 2, to_dev(q, dtype), None, None, n, None, o, lse, c,
+                            commit=commit, exit_flags=ef)
+        ws = torch.empty(abi.attend_workspace_bytes(a), dtype=torch.uint8, device=DEV)
+        a = abi.attend_args(kv, abi.FL_ATTEND_FULL, 2, to_dev(q, dtype), None, None, n, None, o, lse, c, ws,
+                            commit=commit, exit_flags=ef)
+        abi.attend(a)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu(), c.cpu(), kv.view("slot_map", 2).cpu(), kv.view("codes", 2).cpu(),
+                     kv.view("scales", 2).cpu()))
+    ref, got = outs
+    for x, y, name in zip(ref[:3], got[:3], ("o", "lse", "colmass")):
+        assert torch.equal(x[0], y[0]), name
+    assert torch.all(got[0][1] == 0) and torch.all(got[1][1] == 0) and torch.all(got[2][1] == 7.0)
+    for x, y, name in zip(ref[3:], got[3:], ("slots", "codes", "scales")):
+        assert torch.equal(x[0], y[0]), name
+        assert torch.all(y[1] == 0), name                 # never written for the exited sequence
+
+
 @pytest.mark.parametrize("d,n,H", [(64, 2048, 32), (128, 1900, 32), (128, 4000, 16)])
 def test_attend_full_paired_halves(d, n, H):
     """Full loops whose grid is one round of workgroups: each workgroup takes
