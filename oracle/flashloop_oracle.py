@@ -75,7 +75,11 @@ The page prints no worked example of the mass-corrected formula (R4); it is
 pinned by invariants that follow from the mathematics (full attention when
 every key is selected, the dense loop when every row and key is, a fixed point
 when nothing changed, mass preservation, single-key closed forms) and by a
-loop-level evaluation; see tests/test_oracle_attention.py.
+loop-level evaluation; see tests/test_oracle_attention.py.  The loop driver's
+wiring (which hidden states, queries and store versions each lazy loop reads)
+is pinned by the same invariants applied to whole runs of run_prefill
+(tests/test_oracle_prefill_driver.py) and of the decode driver
+(tests/test_oracle_driver.py).
 """
 from __future__ import annotations
 
@@ -88,7 +92,8 @@ import numpy as np
 __all__ = [
     "to_working_dtype", "token_scores", "topk_ascending", "select_keys", "f16_rne", "quantize_groups",
     "dequantize_groups", "pack_int4", "unpack_int4", "pack_codes", "unpack_codes", "KVStore", "full_attention",
-    "lazy_attention", "LoopState", "run_prefill", "run_prefill_chain", "build_decode_context",
+    "lazy_attention", "LoopState", "save_state", "load_state", "lazy_loop",
+    "run_prefill", "run_prefill_chain", "build_decode_context",
     "run_decode_loops", "run_decode_seq",
 ]
 
@@ -404,7 +409,10 @@ def lazy_attention(q_cur, q_prev, k_prev, v_prev, k_cur, v_cur, o_prev, lse_prev
 # --------------------------------------------------------------------------- #
 @dataclass
 class LoopState:
-    """Per-sequence state after a loop (everything carried for inactive rows)."""
+    """Per-sequence state after a loop (everything carried for inactive rows).
+
+    This is also the checkpoint a run resumes from (``run_prefill(resume=)``,
+    ``save_state`` / ``load_state``): every buffer the next loop reads."""
     loop: int
     h: Optional[np.ndarray]        # [N, D] effective hidden state (prefill only)
     q: np.ndarray                  # [Nq, H, d] effective queries
@@ -414,6 +422,8 @@ class LoopState:
     store: KVStore
     records: Dict[int, dict] = field(default_factory=dict)   # loop -> details
     exited_at: Optional[int] = None                          # E1: the loop that was not run
+    h_prev: Optional[np.ndarray] = None                      # [N, D] h_eff of the loop before (prefill)
+    frozen_keys: Optional[np.ndarray] = None                 # V2: the first lazy loop's key group
 
 
 def _copy_state(st: LoopState) -> LoopState:
@@ -421,8 +431,80 @@ def _copy_state(st: LoopState) -> LoopState:
     return copy.deepcopy(st)
 
 
+def save_state(st: LoopState, path: str) -> None:
+    """Checkpoint of a LoopState as an .npz archive of plain arrays (no pickles)."""
+    arrs = {"loop": np.array(st.loop), "o": st.o, "lse": st.lse, "colmass": st.colmass, "q": st.q,
+            "store_shape": np.array([st.store.n, st.store.h, st.store.d, st.store.group, st.store.bits]),
+            "base_k": st.store.base["k"], "base_v": st.store.base["v"]}
+    for name in ("h", "h_prev", "frozen_keys"):
+        if getattr(st, name) is not None:
+            arrs[name] = getattr(st, name)
+    for l, layer in st.store.layers.items():
+        for which, recs in layer.items():
+            for r, rec in enumerate(recs):
+                for part in ("idx", "codes", "scales"):
+                    arrs[f"layer{l}_{which}_{r}_{part}"] = getattr(rec, part)
+    np.savez(path, **arrs)
+
+
+def load_state(path: str) -> LoopState:
+    """Inverse of save_state (records and exit information are not kept)."""
+    z = np.load(path, allow_pickle=False)
+    n, H, d, group, bits = (int(v) for v in z["store_shape"])
+    store = KVStore(n, H, d, group, bits)
+    store.base["k"][...] = z["base_k"]
+    store.base["v"][...] = z["base_v"]
+    layers: Dict[int, Dict[str, Dict[int, dict]]] = {}
+    for key in z.files:
+        if key.startswith("layer"):
+            head, which, r, part = key.split("_")
+            layers.setdefault(int(head[5:]), {}).setdefault(which, {}).setdefault(int(r), {})[part] = z[key]
+    for l in sorted(layers):
+        store.layers[l] = {w: [_Records(recs[r]["idx"], recs[r]["codes"], recs[r]["scales"]) for r in sorted(recs)]
+                           for w, recs in layers[l].items()}
+    get = lambda name: z[name] if name in z.files else None
+    return LoopState(int(z["loop"]), get("h"), z["q"], z["o"], z["lse"], z["colmass"], store,
+                     h_prev=get("h_prev"), frozen_keys=get("frozen_keys"))
+
+
+def lazy_loop(wl, st: LoopState, x: dict, l: int, seq: int = 0, formula: str = "column",
+              keys: Optional[np.ndarray] = None):
+    """One lazy loop l on the state ``st`` after loop l-1, in place ([FL/savings]
+    par. 1-3).  Steps, in the page's order: rank the tokens by the change their
+    hidden state made in loop l-1 and keep the top n_active (R1); choose each
+    head's keys from loop l-1's column mass (R3) unless ``keys`` is given; the
+    shared block recomputes only the active rows (the others carry h, Q, o, lse);
+    the active tokens write their K/V differences as layer l (R8); then
+    mass-corrected attention of the active rows on the selected keys (R4-R6),
+    whose previous-loop part uses the active rows' loop-(l-1) queries and the
+    store at version l-1, and whose current part uses their loop-l queries and
+    version l.  Returns the loop's record (rows, keys, scores, mass, ...)."""
+    u = token_scores(st.h, st.h_prev)
+    rows = topk_ascending(u, wl.n_active(l))
+    if keys is None:
+        keys = select_keys(st.colmass, wl.n_keys)
+    # the shared block recomputes only the active rows; others carry
+    st.h_prev = st.h.copy()
+    st.h[rows] = x["h"][seq][rows]
+    q_prev_rows = st.q[rows].copy()
+    st.q[rows] = x["q"][seq][rows]
+    k_prev_hat = to_working_dtype(st.store.reconstruct("k", l - 1), wl.dtype)
+    v_prev_hat = to_working_dtype(st.store.reconstruct("v", l - 1), wl.dtype)
+    recs = st.store.commit(l, rows, x["k"][seq][rows], x["v"][seq][rows])
+    k_hat = to_working_dtype(st.store.reconstruct("k", l), wl.dtype)
+    v_hat = to_working_dtype(st.store.reconstruct("v", l), wl.dtype)
+    o_r, lse_r, st.colmass, m, upd = lazy_attention(
+        st.q[rows], q_prev_rows, k_prev_hat, v_prev_hat, k_hat, v_hat,
+        st.o[rows], st.lse[rows], st.colmass, rows, keys, formula=formula)
+    st.o[rows] = o_r
+    st.lse[rows] = lse_r
+    st.loop = l
+    return dict(rows=rows, keys=keys, scores=u, mass=m, updated=upd, records=recs)
+
+
 def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: int = 0,
-                formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None):
+                formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None,
+                resume: Optional[LoopState] = None):
     """Run loops 1..T of a prefill workload on one sequence.
 
     ``loops`` yields (l, dict(h, q, k, v)) with l = 0..T, arrays shaped
@@ -431,59 +513,48 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
     keys, commit deltas of the active tokens and run mass-corrected attention
     ([FL/savings] par. 1-3).  ``formula`` and ``freeze_keys`` select the
     variants V1 and V2, ``exit_threshold`` the early exit E1 (module
-    docstring).  Returns the final LoopState (and, with keep=True, the list
-    of states after every loop that ran).
+    docstring).  ``resume`` continues from a checkpoint (the state after loop
+    resume.loop; ``loops`` may still start at 0, earlier loops are skipped).
+    Returns the final LoopState (and, with keep=True, the list of states
+    after every loop that ran).
     """
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
     T = wl.n_loops if upto is None else upto
-    store = KVStore(n, H, d, wl.group, wl.delta_bits)
-    h_eff = h_prev_eff = q_eff = None
-    o = lse = colmass = None
     history = []
-    st = None
-    frozen = None
+    if resume is None:
+        st, start = None, 0
+        h0 = None
+    else:
+        st, start = _copy_state(resume), resume.loop + 1
     for l, x in loops:
         if l > T:
             break
+        if l < start:
+            continue
         if l == 0:
-            h_eff = x["h"][seq].copy()
+            h0 = x["h"][seq].copy()
             continue
         rec = {}
         if l <= wl.n_full:
             rows = np.arange(n, dtype=np.int32)
-            h_prev_eff, h_eff = h_eff, x["h"][seq].copy()
-            q_eff = x["q"][seq].copy()
-            store.commit(l, rows, x["k"][seq], x["v"][seq])
-            kh = to_working_dtype(store.reconstruct("k", l), wl.dtype)
-            vh = to_working_dtype(store.reconstruct("v", l), wl.dtype)
-            o, lse, colmass = full_attention(q_eff, kh, vh, rows)
+            if st is None:
+                st = LoopState(0, h0, None, None, None, None, KVStore(n, H, d, wl.group, wl.delta_bits))
+            st.h_prev, st.h = st.h, x["h"][seq].copy()
+            st.q = x["q"][seq].copy()
+            st.store.commit(l, rows, x["k"][seq], x["v"][seq])
+            kh = to_working_dtype(st.store.reconstruct("k", l), wl.dtype)
+            vh = to_working_dtype(st.store.reconstruct("v", l), wl.dtype)
+            st.o, st.lse, st.colmass = full_attention(st.q, kh, vh, rows)
+            st.loop = l
             rec.update(rows=rows)
         else:
-            u = token_scores(h_eff, h_prev_eff)
-            if exit_threshold is not None and float(np.max(u)) < exit_threshold:
+            if exit_threshold is not None and float(np.max(token_scores(st.h, st.h_prev))) < exit_threshold:
                 st.exited_at = l                   # E1: loops l.. are not run
                 break
-            rows = topk_ascending(u, wl.n_active(l))
-            keys = frozen if frozen is not None else select_keys(colmass, wl.n_keys)
+            rec = lazy_loop(wl, st, x, l, seq, formula, keys=st.frozen_keys)
             if freeze_keys:
-                frozen = keys
-            # the shared block recomputes only the active rows; others carry
-            h_prev_eff = h_eff.copy()
-            h_eff[rows] = x["h"][seq][rows]
-            q_prev_rows = q_eff[rows].copy()
-            q_eff[rows] = x["q"][seq][rows]
-            k_prev_hat = to_working_dtype(store.reconstruct("k", l - 1), wl.dtype)
-            v_prev_hat = to_working_dtype(store.reconstruct("v", l - 1), wl.dtype)
-            recs = store.commit(l, rows, x["k"][seq][rows], x["v"][seq][rows])
-            k_hat = to_working_dtype(store.reconstruct("k", l), wl.dtype)
-            v_hat = to_working_dtype(store.reconstruct("v", l), wl.dtype)
-            o_r, lse_r, colmass, m, upd = lazy_attention(
-                q_eff[rows], q_prev_rows, k_prev_hat, v_prev_hat, k_hat, v_hat,
-                o[rows], lse[rows], colmass, rows, keys, formula=formula)
-            o[rows] = o_r
-            lse[rows] = lse_r
-            rec.update(rows=rows, keys=keys, scores=u, mass=m, updated=upd, records=recs)
-        st = LoopState(l, h_eff, q_eff, o, lse, colmass, store, {l: rec})
+                st.frozen_keys = rec["keys"]
+        st.records = {l: rec}
         if keep:
             history.append(_copy_state(st))
     return (st, history) if keep else st
