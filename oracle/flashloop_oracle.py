@@ -468,7 +468,7 @@ def load_state(path: str) -> LoopState:
 
 
 def lazy_loop(wl, st: LoopState, x: dict, l: int, seq: int = 0, formula: str = "column",
-              keys: Optional[np.ndarray] = None):
+              keys: Optional[np.ndarray] = None, operand_dtype: Optional[str] = None):
     """One lazy loop l on the state ``st`` after loop l-1, in place ([FL/savings]
     par. 1-3).  Steps, in the page's order: rank the tokens by the change their
     hidden state made in loop l-1 and keep the top n_active (R1); choose each
@@ -478,7 +478,10 @@ def lazy_loop(wl, st: LoopState, x: dict, l: int, seq: int = 0, formula: str = "
     mass-corrected attention of the active rows on the selected keys (R4-R6),
     whose previous-loop part uses the active rows' loop-(l-1) queries and the
     store at version l-1, and whose current part uses their loop-l queries and
-    version l.  Returns the loop's record (rows, keys, scores, mass, ...)."""
+    version l.  ``operand_dtype`` overrides the dtype attention's K^, V^ are
+    rounded to (R9; "fp32" keeps the float32 reconstruction, to measure what
+    the rounding costs).  Returns the loop's record (rows, keys, scores, mass, ...)."""
+    od = wl.dtype if operand_dtype is None else operand_dtype
     u = token_scores(st.h, st.h_prev)
     rows = topk_ascending(u, wl.n_active(l))
     if keys is None:
@@ -488,11 +491,11 @@ def lazy_loop(wl, st: LoopState, x: dict, l: int, seq: int = 0, formula: str = "
     st.h[rows] = x["h"][seq][rows]
     q_prev_rows = st.q[rows].copy()
     st.q[rows] = x["q"][seq][rows]
-    k_prev_hat = to_working_dtype(st.store.reconstruct("k", l - 1), wl.dtype)
-    v_prev_hat = to_working_dtype(st.store.reconstruct("v", l - 1), wl.dtype)
+    k_prev_hat = to_working_dtype(st.store.reconstruct("k", l - 1), od)
+    v_prev_hat = to_working_dtype(st.store.reconstruct("v", l - 1), od)
     recs = st.store.commit(l, rows, x["k"][seq][rows], x["v"][seq][rows])
-    k_hat = to_working_dtype(st.store.reconstruct("k", l), wl.dtype)
-    v_hat = to_working_dtype(st.store.reconstruct("v", l), wl.dtype)
+    k_hat = to_working_dtype(st.store.reconstruct("k", l), od)
+    v_hat = to_working_dtype(st.store.reconstruct("v", l), od)
     o_r, lse_r, st.colmass, m, upd = lazy_attention(
         st.q[rows], q_prev_rows, k_prev_hat, v_prev_hat, k_hat, v_hat,
         st.o[rows], st.lse[rows], st.colmass, rows, keys, formula=formula)
@@ -504,7 +507,7 @@ def lazy_loop(wl, st: LoopState, x: dict, l: int, seq: int = 0, formula: str = "
 
 def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: int = 0,
                 formula: str = "column", freeze_keys: bool = False, exit_threshold: Optional[float] = None,
-                resume: Optional[LoopState] = None):
+                resume: Optional[LoopState] = None, operand_dtype: Optional[str] = None):
     """Run loops 1..T of a prefill workload on one sequence.
 
     ``loops`` yields (l, dict(h, q, k, v)) with l = 0..T, arrays shaped
@@ -515,8 +518,9 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
     variants V1 and V2, ``exit_threshold`` the early exit E1 (module
     docstring).  ``resume`` continues from a checkpoint (the state after loop
     resume.loop; ``loops`` may still start at 0, earlier loops are skipped).
-    Returns the final LoopState (and, with keep=True, the list of states
-    after every loop that ran).
+    ``operand_dtype`` as in lazy_loop, for full loops too.  Returns the final
+    LoopState (and, with keep=True, the list of states after every loop that
+    ran).
     """
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
     T = wl.n_loops if upto is None else upto
@@ -542,8 +546,9 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
             st.h_prev, st.h = st.h, x["h"][seq].copy()
             st.q = x["q"][seq].copy()
             st.store.commit(l, rows, x["k"][seq], x["v"][seq])
-            kh = to_working_dtype(st.store.reconstruct("k", l), wl.dtype)
-            vh = to_working_dtype(st.store.reconstruct("v", l), wl.dtype)
+            od = wl.dtype if operand_dtype is None else operand_dtype
+            kh = to_working_dtype(st.store.reconstruct("k", l), od)
+            vh = to_working_dtype(st.store.reconstruct("v", l), od)
             st.o, st.lse, st.colmass = full_attention(st.q, kh, vh, rows)
             st.loop = l
             rec.update(rows=rows)
@@ -551,7 +556,7 @@ def run_prefill(wl, loops, upto: Optional[int] = None, keep: bool = False, seq: 
             if exit_threshold is not None and float(np.max(token_scores(st.h, st.h_prev))) < exit_threshold:
                 st.exited_at = l                   # E1: loops l.. are not run
                 break
-            rec = lazy_loop(wl, st, x, l, seq, formula, keys=st.frozen_keys)
+            rec = lazy_loop(wl, st, x, l, seq, formula, keys=st.frozen_keys, operand_dtype=operand_dtype)
             if freeze_keys:
                 st.frozen_keys = rec["keys"]
         st.records = {l: rec}
@@ -610,13 +615,17 @@ def build_decode_context(wl, seq_index: int, ctx_sets: Dict[int, np.ndarray], lo
 
 
 def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data, formula: str = "column",
-                     freeze_keys: bool = False, exit_threshold: Optional[float] = None):
+                     freeze_keys: bool = False, exit_threshold: Optional[float] = None,
+                     start: int = 1, upto: Optional[int] = None, state: Optional[dict] = None):
     """The T decode loops of the new token at position N-1 over a built
     context: loop 1 attends in full over version 1, loops l >= 2 select keys
     from that row's column mass, commit the token's own delta and run
     mass-corrected attention over version l (variants V1, V2 and the early
     exit E1 as in run_prefill; E1 reads the new token's hidden state,
-    ``loops_data[l]["h"]`` for l = 0..T).  Returns a list of per-loop dicts,
+    ``loops_data[l]["h"]`` for l = 0..T).  ``start``/``upto`` run loops
+    start..upto only; a start > 1 continues from ``state``, the dict that the
+    loop before returned (its o, lse, colmass, and keys under V2), with
+    ``store`` holding that loop's records.  Returns a list of per-loop dicts,
     one per loop that ran."""
     n = wl.n_tokens
     si = seq_index
@@ -625,7 +634,12 @@ def run_decode_loops(wl, store: KVStore, seq_index: int, loops_data, formula: st
     o = lse = colmass = None
     q_prev = None
     frozen = None
-    for l in range(1, wl.n_loops + 1):
+    if start > 1:
+        o, lse, colmass = (np.array(state[k], copy=True) for k in ("o", "lse", "colmass"))
+        q_prev = loops_data[start - 1]["q"][si].copy()
+        if freeze_keys and start > 2:
+            frozen = state["keys"]
+    for l in range(start, (wl.n_loops if upto is None else upto) + 1):
         x = loops_data[l]
         q = x["q"][si]                       # [1, H, d]
         if l >= 2 and exit_threshold is not None:

@@ -56,6 +56,50 @@ def upload_loops(wl: Workload, loops: SyntheticLoops, device="cuda") -> Dict[int
     return out
 
 
+class CallTimer:
+    """hipEvent pairs around each ABI call, on the stream the call is issued
+    on (diagnostics: the benchmark's per-call medians).  ``calls[name]`` holds
+    (start, end) event pairs; ``ms()`` waits for them."""
+
+    def __init__(self):
+        self.calls: Dict[str, list] = {}
+
+    def __call__(self, name: str):
+        timer = self
+
+        class _Span:
+            def __enter__(self):
+                self.a = torch.cuda.Event(enable_timing=True)
+                self.b = torch.cuda.Event(enable_timing=True)
+                self.a.record(torch.cuda.current_stream())
+                return self
+
+            def __exit__(self, *exc):
+                self.b.record(torch.cuda.current_stream())
+                timer.calls.setdefault(name, []).append((self.a, self.b))
+                return False
+
+        return _Span()
+
+    def ms(self) -> Dict[str, List[float]]:
+        torch.cuda.synchronize()
+        return {k: [a.elapsed_time(b) for a, b in v] for k, v in self.calls.items()}
+
+
+class _NoTimer:
+    def __call__(self, name: str):
+        return self
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+_NO_TIMER = _NoTimer()
+
+
 @dataclass
 class LoopRecord:
     rows: Optional[torch.Tensor] = None
@@ -109,6 +153,39 @@ class PrefillRun:
             if l in self.inp:                      # loops whose inputs were drawn
                 ws = max(ws, abi.attend_workspace_bytes(self._attend_args(l)))
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        self.timer = _NO_TIMER
+
+    # -------------------------------------------------------------- checkpoints
+    def state_tensors(self) -> Dict[str, torch.Tensor]:
+        """Every buffer a later loop reads: the outputs (o, lse, column mass),
+        the KV arena and the per-loop index sets and scores."""
+        out = {"o": self.o, "lse": self.lse, "colmass": self.colmass, "arena": self.kv.arena}
+        for l in self.act:
+            out[f"act{l}"], out[f"keys{l}"], out[f"scores{l}"] = self.act[l], self.keys_l[l], self.scores_l[l]
+        if self.exit_flags is not None:
+            out["exit_flags"] = self.exit_flags
+        return out
+
+    def snapshot(self, arena: bool = True) -> Dict[str, torch.Tensor]:
+        """Device copies of the state (see restore)."""
+        return {k: v.clone() for k, v in self.state_tensors().items() if arena or k != "arena"}
+
+    def restore(self, snap: Dict[str, torch.Tensor]) -> None:
+        cur = self.state_tensors()
+        for k, v in snap.items():
+            cur[k].copy_(v)
+
+    def save_state(self, path: str, loop: int) -> None:
+        """Checkpoint after loop `loop` (torch file of host tensors, no pickled objects)."""
+        torch.cuda.synchronize()
+        torch.save({"loop": torch.tensor(loop), **{k: v.cpu() for k, v in self.state_tensors().items()}}, path)
+
+    def load_state(self, path: str) -> int:
+        """Restores a checkpoint written by save_state; returns its loop."""
+        snap = torch.load(path, weights_only=True)
+        loop = int(snap.pop("loop"))
+        self.restore({k: v.to(self.dev) for k, v in snap.items()})
+        return loop
 
     def _attend_args(self, l: int):
         wl = self.wl
@@ -127,43 +204,54 @@ class PrefillRun:
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
         x = self.inp[l]
+        t = self.timer
         if not self.fuse:
-            abi.kv_commit(self.kv, l, self.all_rows, x["k"], x["v"])
-        abi.attend(self._attend_args(l))
+            with t(f"loop{l}.kv_commit"):
+                abi.kv_commit(self.kv, l, self.all_rows, x["k"], x["v"])
+        with t(f"loop{l}.attend"):
+            abi.attend(self._attend_args(l))
 
     def lazy_loop(self, l: int, cand: Optional[torch.Tensor]) -> torch.Tensor:
         wl, x = self.wl, self.inp[l]
         act, na, scores = self.act[l], wl.n_active(l), self.scores_l[l]
+        t = self.timer
         # the change of the candidate rows during loop l-1 (every row after the full loops)
         if self.side is not None:
-            with torch.cuda.stream(self.side):
+            with torch.cuda.stream(self.side), t(f"loop{l}.select_tokens"):
                 abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, scores, act, cand)
             torch.cuda.current_stream().wait_stream(self.side)
         else:
-            abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, scores, act, cand)
+            with t(f"loop{l}.select_tokens"):
+                abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, scores, act, cand)
         if self.exit_flags is not None:          # early exit: no later library call touches the sequence
             abi.exit_check(self.exit_flags, self.exit_threshold, scores=scores)
         first = wl.n_full + 1
         if self.freeze_keys and l > first:
             self.keys_l[l].copy_(self.keys_l[first])
         else:
-            abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
+            with t(f"loop{l}.select_keys"):
+                abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
         if not self.fuse:
-            abi.kv_commit(self.kv, l, act, x["k"], x["v"], exit_flags=self.exit_flags)
-        abi.attend(self._attend_args(l))
+            with t(f"loop{l}.kv_commit"):
+                abi.kv_commit(self.kv, l, act, x["k"], x["v"], exit_flags=self.exit_flags)
+        with t(f"loop{l}.attend"):
+            abi.attend(self._attend_args(l))
         return act
 
-    def run(self, upto: Optional[int] = None, record: bool = False) -> List[LoopRecord]:
+    def run(self, upto: Optional[int] = None, record: bool = False, start: int = 1) -> List[LoopRecord]:
+        """Loops start..upto (default: all).  start > 1 continues from the
+        state the buffers hold (the loops before it must have run, or a
+        checkpoint been restored)."""
         wl = self.wl
         T = wl.n_loops if upto is None else upto
         recs: List[LoopRecord] = []
-        cand = None
-        if self.exit_flags is not None:
+        cand = None if start <= wl.n_full + 1 else self.act[start - 1]
+        if self.exit_flags is not None and start == 1:
             self.exit_flags.zero_()
         if self.side is not None:
             # the selection buffers are reused: earlier steps' readers finish first
             self.side.wait_stream(torch.cuda.current_stream())
-        for l in range(1, T + 1):
+        for l in range(start, T + 1):
             if l <= wl.n_full:
                 self.full_loop(l)
                 cand = None
@@ -217,6 +305,21 @@ class DecodeRun:
         for l in range(1, wl.n_loops + 1):
             ws = max(ws, abi.attend_workspace_bytes(self._args(l, None)))
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        self.timer = _NO_TIMER
+
+    # -------------------------------------------------------------- checkpoints
+    def state_tensors(self) -> Dict[str, torch.Tensor]:
+        """Every buffer a later loop reads: the new token's outputs, its
+        column-mass rows, the key sets and the KV arena."""
+        out = {"o": self.o, "lse": self.lse, "colmass": self.colmass, "keys": self.keys, "arena": self.kv.arena}
+        if self.exit_flags is not None:
+            out["exit_flags"] = self.exit_flags
+        return out
+
+    snapshot = PrefillRun.snapshot
+    restore = PrefillRun.restore
+    save_state = PrefillRun.save_state
+    load_state = PrefillRun.load_state
 
     def _args(self, l, ws):
         x = self.inp[l]
@@ -237,21 +340,27 @@ class DecodeRun:
 
     def loop(self, l: int) -> None:
         wl, x = self.wl, self.inp[l]
+        t = self.timer
         slot_base = 0 if l == 1 else self.ctx[l].shape[1]
         if l >= 2 and self.exit_flags is not None:   # early exit of each sequence, from its new token's change
             abi.exit_check(self.exit_flags, self.exit_threshold, h_cur=self.inp[l - 1]["h"], h_prev=self.inp[l - 2]["h"])
         if l == 1 or not self.fuse:
-            abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False,
-                          exit_flags=self.exit_flags)
+            with t(f"loop{l}.kv_commit"):
+                abi.kv_commit(self.kv, l, self.last, x["k"], x["v"], slot_base=slot_base, reset_map=False,
+                              exit_flags=self.exit_flags)
         if l >= 2 and not (self.freeze_keys and l > 2):
-            abi.select_keys(self.colmass, wl.n_keys, self.keys)
-        abi.attend(self._args(l, self.workspace))
+            with t(f"loop{l}.select_keys"):
+                abi.select_keys(self.colmass, wl.n_keys, self.keys)
+        with t(f"loop{l}.attend"):
+            abi.attend(self._args(l, self.workspace))
 
-    def run(self, record: bool = False) -> List[LoopRecord]:
+    def run(self, record: bool = False, start: int = 1, upto: Optional[int] = None) -> List[LoopRecord]:
+        """Loops start..upto (default: all); start > 1 continues from the
+        state the buffers hold."""
         recs = []
-        if self.exit_flags is not None:
+        if self.exit_flags is not None and start == 1:
             self.exit_flags.zero_()
-        for l in range(1, self.wl.n_loops + 1):
+        for l in range(start, (self.wl.n_loops if upto is None else upto) + 1):
             self.loop(l)
             if record:
                 recs.append(LoopRecord(keys=self.keys.clone() if l >= 2 else None, o=self.o.clone(),

@@ -127,7 +127,8 @@ def _check_against_oracle(sts, state, rows, keys, version, o, lse, c):
             q1, q0, _rec(st, "k", version - 1), _rec(st, "v", version - 1), _rec(st, "k", version),
             _rec(st, "v", version), o0, lse0, c0, np.array([rows[s]]), keys[s])
         _close(o[s].cpu().numpy(), o_r, f"seq {s} o")
-        _close(lse[s].cpu().numpy(), lse_r, f"seq {s} lse")
+        err = float(np.abs(lse[s].cpu().numpy().astype(np.float64) - lse_r).max())
+        assert err <= 2e-2, f"seq {s} lse: max abs err {err:.3e}"
         _close(c[s].cpu().numpy(), c_r, f"seq {s} colmass")
 
 
@@ -239,7 +240,8 @@ def test_decode_full_loop(n):
     for s, st in enumerate(sts):
         o_r, lse_r, c_r = oracle.full_attention(q[s], _rec(st, "k", 1), _rec(st, "v", 1), np.array([rows[s]]))
         _close(o[s].cpu().numpy(), o_r, f"seq {s} o")
-        _close(lse[s].cpu().numpy(), lse_r, f"seq {s} lse")
+        err = float(np.abs(lse[s].cpu().numpy().astype(np.float64) - lse_r).max())
+        assert err <= 2e-2, f"seq {s} lse: max abs err {err:.3e}"
         _close(c[s].cpu().numpy(), c_r, f"seq {s} colmass")
         assert torch.all(c[s][:, rows[s] + 1:] == 0)           # nothing past the row
 

@@ -22,6 +22,12 @@ def _check_o(got, want, what):
     assert err <= 2e-2 * rms, f"{what}: max err {err:.3e} > 2e-2 * RMS {rms:.3e}"
     return err / rms
 
+def _check_abs(got, want, what, tol=2e-2):
+    """lse: max abs error (nats); an error of e rescales the next loop's p' by exp(e)."""
+    err = float(np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64)).max())
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol}"
+
+
 
 def _key_mismatch_is_near_tie(got, want, colmass):
     """Different key sets are allowed only where the column masses tie to 1e-5."""
@@ -68,7 +74,7 @@ def test_prefill_loops_match_oracle(wl):
                 assert np.array_equal(scales.view(np.uint16), rr.scales.view(np.uint16))
             kv.arena.copy_(arena_now)
         _check_o(g.o.cpu().numpy(), r.o, f"loop {l} o")
-        _check_o(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")
+        _check_abs(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")
         _check_o(g.colmass.cpu().numpy(), r.colmass, f"loop {l} colmass")
 
 
@@ -91,7 +97,7 @@ def test_decode_loops_match_oracle(n_seq, n):
             if l >= 2:
                 assert np.array_equal(g.keys.cpu().numpy()[s], r["keys"]), f"seq {s} loop {l} keys"
             _check_o(g.o.cpu().numpy()[s], r["o"], f"seq {s} loop {l} o")
-            _check_o(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
+            _check_abs(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
             _check_o(g.colmass.cpu().numpy()[s], r["colmass"], f"seq {s} loop {l} colmass")
 
 
@@ -168,7 +174,7 @@ def test_prefill_variants_match_oracle(wl, formula, freeze):
             assert np.array_equal(g.rows.cpu().numpy(), r.records[l]["rows"]), f"loop {l}: token sets differ"
             assert np.array_equal(g.keys.cpu().numpy(), r.records[l]["keys"]), f"loop {l}: key sets differ"
         _check_o(g.o.cpu().numpy(), r.o, f"loop {l} o")
-        _check_o(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")
+        _check_abs(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")
         _check_o(g.colmass.cpu().numpy(), r.colmass, f"loop {l} colmass")
 
 
@@ -191,7 +197,7 @@ def test_decode_variants_match_oracle(formula, freeze):
             if l >= 2:
                 assert np.array_equal(g.keys.cpu().numpy()[s], r["keys"]), f"seq {s} loop {l} keys"
             _check_o(g.o.cpu().numpy()[s], r["o"], f"seq {s} loop {l} o")
-            _check_o(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
+            _check_abs(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
             _check_o(g.colmass.cpu().numpy()[s], r["colmass"], f"seq {s} loop {l} colmass")
 
 
@@ -222,7 +228,7 @@ def test_prefill_delta_formats_match_oracle(wl, bits, group):
             assert np.array_equal(g.rows.cpu().numpy(), r.records[l]["rows"]), f"loop {l}: token sets differ"
             assert np.array_equal(g.keys.cpu().numpy(), r.records[l]["keys"]), f"loop {l}: key sets differ"
         _check_o(g.o.cpu().numpy(), r.o, f"loop {l} o")
-        _check_o(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")
+        _check_abs(g.lse.cpu().numpy(), r.lse, f"loop {l} lse")
         _check_o(g.colmass.cpu().numpy(), r.colmass, f"loop {l} colmass")
     kv = run.kv
     for l in range(2, wl.n_loops + 1):
@@ -253,5 +259,5 @@ def test_decode_delta_formats_match_oracle(bits, group):
             if l >= 2:
                 assert np.array_equal(g.keys.cpu().numpy()[s], r["keys"]), f"seq {s} loop {l} keys"
             _check_o(g.o.cpu().numpy()[s], r["o"], f"seq {s} loop {l} o")
-            _check_o(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
+            _check_abs(g.lse.cpu().numpy()[s], r["lse"], f"seq {s} loop {l} lse")
             _check_o(g.colmass.cpu().numpy()[s], r["colmass"], f"seq {s} loop {l} colmass")

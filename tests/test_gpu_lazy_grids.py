@@ -1,0 +1,132 @@
+"""Lazy attention on the large grids that the 32K and deep workloads run,
+against the oracle element by element (GPU, through the C ABI).
+
+With at least 512 workgroups of 256 rows a lazy call takes 256-row
+workgroups with 64-key tiles; with at least 512 of 128 rows it takes
+128-row/32-key ones; the gather walks one key at a time per 16-lane group
+once it has at least 512 blocks.  Four sequences of 16 heads (64 head rows),
+2560 tokens and 512 selected keys per head reach every one of these, with the
+commit of the active rows fused into the call as the benchmark runs it
+(page "FlashLoop: Fast and Memory-Efficient Looped Transformers via Lazy
+Updates", section "FlashLoop combines three kinds of savings", paragraphs 2-4).
+
+Inputs: the synthetic trajectory of the 32K workload (head_dim 128) or of the
+deep workload (head_dim 96), scaled to these sizes; loop 1 is a full loop on
+the oracle, whose state (o, lse, column mass) both sides start from.
+Bars: o within 2e-2 x RMS (max abs error), lse within 2e-2 absolute, column
+mass within 2e-2 x RMS; rows outside the active set untouched; every record
+of the fused commit bit-exact.
+"""
+import dataclasses
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_loop_attention_amd import abi, configs, driver
+from sparse_loop_attention_amd.synth import SyntheticLoops
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+S, H, N, NS = 4, 16, 2560, 512
+
+
+def _wl(d):
+    base = configs.LONG_PREFILL if d == 128 else configs.DEEP
+    return dataclasses.replace(configs.scaled(base, N, n_seq=S, n_heads=H), n_loops=2, n_full=1,
+                               head_dim=d, n_keys=NS)
+
+
+@functools.lru_cache(maxsize=2)
+def _state(d):
+    """Loops 1-2 of the trajectory and the oracle's loop-1 state per sequence."""
+    wl = _wl(d)
+    data = {l: {k: v.copy() for k, v in x.items()} for l, x in SyntheticLoops(wl)}
+    per_seq = []
+    for s in range(S):
+        st = oracle.KVStore(N, H, d, wl.group, wl.delta_bits)
+        st.commit(1, np.arange(N), data[1]["k"][s], data[1]["v"][s])
+        kh = oracle.to_working_dtype(st.reconstruct("k", 1), "bf16")
+        vh = oracle.to_working_dtype(st.reconstruct("v", 1), "bf16")
+        o0, lse0, c0 = oracle.full_attention(data[1]["q"][s], kh, vh, np.arange(N))
+        per_seq.append((o0, lse0, c0, oracle.select_keys(c0, NS)))
+    print(f"[lazy_grids] d={d}: oracle loop-1 state ready", flush=True)
+    return wl, data, per_seq
+
+
+def _err(got, want):
+    want = np.asarray(want, np.float64)
+    return float(np.abs(np.asarray(got, np.float64) - want).max()), math.sqrt(float(np.mean(want ** 2)))
+
+
+@pytest.mark.parametrize("d,na,formula", [(128, 2048, "column"), (128, 1024, "column"), (128, 2048, "mixture"),
+                                          (96, 2048, "column"), (96, 1024, "column"), (96, 1024, "mixture")],
+                         ids=["d128-256rows", "d128-128rows", "d128-256rows-mixture", "d96-256rows", "d96-128rows",
+                              "d96-128rows-mixture"])
+def test_lazy_large_grid_matches_oracle(d, na, formula):
+    wl, data, per_seq = _state(d)
+    rng = np.random.default_rng(na + d)
+    act = np.stack([np.sort(rng.choice(N, na, replace=False)) for _ in range(S)]).astype(np.int32)
+    keys = np.stack([p[3] for p in per_seq]).astype(np.int32)                   # [S, H, NS]
+    # the call's shape: 64 head rows, so the grids are the large ones
+    wg256, wg128 = S * H * ((na + 255) // 256), S * H * ((na + 127) // 128)
+    assert (wg256 >= 512) == (na == 2048) and wg128 >= 512 and S * H * ((NS + 255) // 256 * 256 // 64) >= 512
+    dt = torch.bfloat16
+    kv = abi.KVStore(S, H, d, N, 2, dt, [na], DEV, group=wl.group, delta_bits=wl.delta_bits)
+    every = torch.arange(N, dtype=torch.int32, device=DEV)[None].repeat(S, 1).contiguous()
+    x1, x2 = data[1], data[2]
+    dev = lambda a: driver.to_device(a, dt, DEV)
+    abi.kv_commit(kv, 1, every, dev(x1["k"]), dev(x1["v"]))
+    o0 = np.stack([p[0] for p in per_seq]).astype(np.float32)
+    lse0 = np.stack([p[1] for p in per_seq]).astype(np.float32)
+    c0 = np.stack([p[2] for p in per_seq]).astype(np.float32)
+    o = torch.from_numpy(o0).to(DEV)
+    lse = torch.from_numpy(lse0).to(DEV)
+    c = torch.from_numpy(c0).to(DEV)
+    act_d = torch.from_numpy(act).to(DEV)
+    keys_d = torch.from_numpy(keys).to(DEV)
+    commit = dict(k_new=dev(x2["k"]), v_new=dev(x2["v"]))
+    args = lambda ws: abi.attend_args(kv, abi.FL_ATTEND_LAZY, 2, dev(x2["q"]), dev(x1["q"]), act_d, na, keys_d,
+                                      o, lse, c, ws, commit=commit, formula=formula)
+    ws = torch.full((abi.attend_workspace_bytes(args(None)),), 0xA5, dtype=torch.uint8, device=DEV)
+    abi.attend(args(ws))
+    torch.cuda.synchronize()
+    got_o, got_lse, got_c = o.cpu().numpy(), lse.cpu().numpy(), c.cpu().numpy()
+    codes = kv.view("codes", 2).cpu().numpy()
+    scales = kv.view("scales", 2).cpu().numpy()
+    slots = kv.view("slot_map", 2).cpu().numpy()
+    worst = {"o": 0.0, "lse": 0.0, "c": 0.0}
+    for s in range(S):
+        o_prev, lse_prev, c_prev, ks = per_seq[s]
+        st = oracle.KVStore(N, H, d, wl.group, wl.delta_bits)
+        st.commit(1, np.arange(N), x1["k"][s], x1["v"][s])
+        kp = oracle.to_working_dtype(st.reconstruct("k", 1), "bf16")
+        vp = oracle.to_working_dtype(st.reconstruct("v", 1), "bf16")
+        recs = st.commit(2, act[s], x2["k"][s][act[s]], x2["v"][s][act[s]])
+        kc = oracle.to_working_dtype(st.reconstruct("k", 2), "bf16")
+        vc = oracle.to_working_dtype(st.reconstruct("v", 2), "bf16")
+        A = act[s]
+        o_r, lse_r, c_r, m, upd = oracle.lazy_attention(x2["q"][s][A], x1["q"][s][A], kp, vp, kc, vc,
+                                                        o_prev[A], lse_prev[A], c_prev, A, ks, formula=formula)
+        err, rms = _err(got_o[s][A], o_r)
+        assert err <= 2e-2 * rms, f"seq {s} o: {err:.3e} > 2e-2 * {rms:.3e}"
+        worst["o"] = max(worst["o"], err / rms)
+        others = np.setdiff1d(np.arange(N), A)
+        assert np.array_equal(got_o[s][others], o0[s][others]) and np.array_equal(got_lse[s][others], lse0[s][others])
+        err, _ = _err(got_lse[s][A], lse_r)
+        assert err <= 2e-2, f"seq {s} lse: max abs error {err:.3e}"
+        worst["lse"] = max(worst["lse"], err)
+        err, rms = _err(got_c[s], c_r)
+        assert err <= 2e-2 * rms, f"seq {s} colmass: {err:.3e} > 2e-2 * {rms:.3e}"
+        worst["c"] = max(worst["c"], err / rms)
+        want_slots = np.full(N, -1)
+        want_slots[A] = np.arange(na)
+        assert np.array_equal(slots[s], want_slots), f"seq {s} slots"
+        for wi, w in enumerate(("k", "v")):
+            assert np.array_equal(codes[s][:, :, wi], oracle.pack_codes(recs[w].codes, wl.delta_bits)), (s, w)
+            assert np.array_equal(scales[s][:, :, wi].view(np.uint16), recs[w].scales.view(np.uint16)), (s, w)
+    print(f"[lazy_grids] d={d} na={na} {formula}: max|do|/rms {worst['o']:.2e}, max|dlse| {worst['lse']:.2e}, "
+          f"max|dc|/rms {worst['c']:.2e}", flush=True)

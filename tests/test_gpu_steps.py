@@ -1,7 +1,8 @@
 """GPU parity of each ABI call against the CPU oracle on identical inputs.
 
-Bars: index sets and int4 codes bit-exact; attention outputs within
-2e-2 x RMS (max abs error); float64 token scores within 1e-13 relative.
+Bars: index sets and int4 codes bit-exact; attention outputs and column mass within
+2e-2 x RMS (max abs error), lse within 2e-2 absolute; float64 token scores
+within 1e-13 relative.
 """
 import math
 
@@ -32,6 +33,12 @@ def rel_err_ok(got, want, tol=2e-2):
     rms = math.sqrt(float(np.mean(want ** 2)))
     err = float(np.abs(got - want).max()) if want.size else 0.0
     return err <= tol * rms, err, rms
+
+
+def lse_abs_err(got, want):
+    """lse is compared in absolute terms (nats): an error of e rescales the
+    next loop's previous-loop probabilities by exp(e)."""
+    return float(np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64)).max())
 
 
 # --------------------------------------------------------------------------- select
@@ -221,9 +228,10 @@ def test_attend_full(dtype, d, n):
         o_r, lse_r, c_r = oracle.full_attention(q, oracle.to_working_dtype(st.reconstruct("k", version), wd),
                                                 oracle.to_working_dtype(st.reconstruct("v", version), wd),
                                                 np.arange(n))
-        for got, want in ((o[0], o_r), (lse[0], lse_r), (c[0], c_r)):
+        for got, want in ((o[0], o_r), (c[0], c_r)):
             ok, err, rms = rel_err_ok(got.cpu().numpy(), want)
             assert ok, (version, err, rms)
+        assert lse_abs_err(lse[0].cpu().numpy(), lse_r) <= 2e-2, version
 
 
 @pytest.mark.parametrize("d,n,H", [(128, 2048, 8), (64, 1024, 16), (96, 1800, 8), (128, 2500, 12)])
@@ -249,9 +257,10 @@ def test_attend_full_key_split(d, n, H):
         outs.append((o.cpu().numpy(), lse.cpu().numpy(), c.cpu().numpy()))
     o_r, lse_r, c_r = oracle.full_attention(q, oracle.to_working_dtype(st.reconstruct("k", 1), "bf16"),
                                             oracle.to_working_dtype(st.reconstruct("v", 1), "bf16"), np.arange(n))
-    for got, want in zip(outs[0], (o_r[None], lse_r[None], c_r[None])):
+    for got, want in zip((outs[0][0], outs[0][2]), (o_r[None], c_r[None])):
         ok, err, rms = rel_err_ok(got, want)
         assert ok, (err, rms)
+    assert lse_abs_err(outs[0][1], lse_r[None]) <= 2e-2
     for rep in (1, 2):
         for x, y in zip(outs[0], outs[rep]):
             assert np.array_equal(x, y)
@@ -366,9 +375,10 @@ def test_attend_full_paired_halves(d, n, H):
     torch.cuda.synchronize()
     o_r, lse_r, c_r = oracle.full_attention(q, oracle.to_working_dtype(st.reconstruct("k", 1), "bf16"),
                                             oracle.to_working_dtype(st.reconstruct("v", 1), "bf16"), np.arange(n))
-    for got, want in ((o[0], o_r), (lse[0], lse_r), (c[0], c_r)):
+    for got, want in ((o[0], o_r), (c[0], c_r)):
         ok, err, rms = rel_err_ok(got.cpu().numpy(), want)
         assert ok, (err, rms)
+    assert lse_abs_err(lse[0].cpu().numpy(), lse_r) <= 2e-2
 
 
 @pytest.mark.parametrize("dtype,d,n,na,ns", [(torch.float32, 64, 256, 64, 26), (torch.bfloat16, 128, 512, 103, 52),
@@ -406,7 +416,7 @@ def test_attend_lazy(dtype, d, n, na, ns):
     assert ok, ("o", err, rms)
     inactive = np.setdiff1d(np.arange(n), act)
     assert np.array_equal(got_o[inactive], o0.astype(np.float32)[inactive])      # untouched
-    ok, err, rms = rel_err_ok(lse[0].cpu().numpy()[act], lse_r)
-    assert ok, ("lse", err, rms)
+    err = float(np.abs(lse[0].cpu().numpy()[act].astype(np.float64) - lse_r).max())
+    assert err <= 2e-2, ("lse max abs error", err)
     ok, err, rms = rel_err_ok(c[0].cpu().numpy(), c_r)
     assert ok, ("colmass", err, rms)

@@ -126,3 +126,23 @@ def test_decode_with_every_key_equals_full_attention_each_loop():
     for l in range(2, wl.n_loops + 1):
         idx = np.concatenate([r.idx for r in store.layers[l]["k"]])
         assert np.array_equal(np.sort(idx), np.union1d(ctx[l], last))
+
+
+def test_decode_resume_equals_uninterrupted_run():
+    """run_decode_loops continued from the state after loop l (start = l + 1)
+    gives the uninterrupted run's loops bit for bit."""
+    import copy
+    from oracle import build_decode_context, run_decode_loops
+    wl = configs.scaled(configs.DECODE, 128, n_seq=2, n_heads=2)
+    syn = SyntheticLoops(wl)
+    ctx = {l: syn.context_active_sets(l)[0] for l in range(2, wl.n_loops + 1)}
+    data = {l: {k: v.copy() for k, v in x.items()} for l, x in SyntheticLoops(wl)}
+    store = build_decode_context(wl, 0, ctx, data)
+    whole = run_decode_loops(wl, copy.deepcopy(store), 0, data)
+    for cut in range(1, wl.n_loops):
+        st = copy.deepcopy(store)
+        head = run_decode_loops(wl, st, 0, data, upto=cut)
+        tail = run_decode_loops(wl, st, 0, data, start=cut + 1, state=head[-1])
+        for a, b in zip(whole, head + tail):
+            for k in ("o", "lse", "colmass"):
+                assert np.array_equal(a[k], b[k]), (cut, k)
