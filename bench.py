@@ -3,24 +3,30 @@
 
 One step = every loop of one workload, in order: the full early loops (commit
 the base or a dense delta layer, full causal attention with column mass) and
-the lazy loops (token selection, key selection, delta commit of the
-active tokens, mass-corrected attention), i.e. every step of the hot path
-over one batch of synthetic input already resident in HBM.  Deltas are
-stored as 4-bit codes with one binary16 scale per 32 elements unless
---delta-bits / --group ask for 2-bit codes or 64-element groups.
+the lazy loops (token selection, key selection, delta commit of the active
+tokens, mass-corrected attention), i.e. every step of the hot path over one
+batch of synthetic input already resident in HBM.  ``ms_per_step`` times K
+such steps without instrumentation.
 
-Metric: active-token loop-steps per second = (sum over the step's loops of the
-rows that loop computes: N in a full loop, n_active in a lazy loop) / step
-time, over K steps without instrumentation.  The JSON line also carries the
-lazy-loop rate, KV bytes per second, the roofline position of the dominant
-kernel (from hipEvent pairs around every launch, over a second run of the
-same K steps) and the CPU oracle timed on the host.
+The headline metric is the lazy loops' own rate: active-token loop-steps/s =
+(sum over the lazy loops of n_active) / (the lazy loops' time), where the
+lazy loops' time is the median, over R repetitions, of a hipEvent pair
+bracketing every library call of loops F+1..T, each repetition started from
+the same state after the full loops (a device checkpoint restored untimed).
+KV GB/s = (chain bytes read by the commit and the attention + delta bytes
+written) / the same time.  The JSON line also carries per-call medians (p10,
+p90) measured with each call on its own (no second stream), per-kernel
+hipEvent times, the roofline of the lazy loops' attention kernel (the
+gathered-tile MFMA forward in prefill, the chain read in decode; flops or
+bytes counted from the actual index sets) with the full loop's dominant
+kernel beside it, and the CPU oracle timed on the host on the same lazy loops.
 """
 from __future__ import annotations
 
 import argparse
+import copy
+import dataclasses
 import json
-import math
 import os
 import sys
 import time
@@ -31,17 +37,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+METRIC = "active-token loop-steps/sec + KV GB/s; % of HBM / bf16-MFMA roofline"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20, help="timed whole steps (every loop)")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="single_layer",
-                    help="tiny | single_layer | long_prefill | decode | deep")
+    ap.add_argument("--reps", type=int, default=50, help="repetitions of the lazy loops for the medians")
+    ap.add_argument("--workload", default="long_prefill",
+                    help="long_prefill (default) | single_layer | decode | deep | tiny")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the host oracle timing")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of each oracle sample")
     ap.add_argument("--delta-bits", type=int, default=4, choices=(2, 4),
                     help="bits per stored delta element of the lazy loops' KV versions")
     ap.add_argument("--group", type=int, default=32, choices=(32, 64),
@@ -51,8 +59,17 @@ def parse():
                          "the full loop count, and the loops each sequence ran")
     ap.add_argument("--quality", action="store_true",
                     help="instead of timing: error of every lazy loop against the dense loop, for the output "
-                         "formulas and key policies")
+                         "formulas and key policies, and the cost of bf16 attention operands")
     return ap.parse_args()
+
+
+def _pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, np.float64), q))
+
+
+def _stats(xs):
+    return {"median": _pct(xs, 50), "p10": _pct(xs, 10), "p90": _pct(xs, 90), "n": len(xs)}
 
 
 # --------------------------------------------------------------------------- work model
@@ -63,81 +80,67 @@ def _pairs(rows, keys_sorted):
 
 
 def work_model(wl, run):
-    """Algorithmic flops / bytes of one step, per kernel family: 4d flops per visible
-    (row, key) pair in full loops and 8d in lazy ones (6d for the mixture formula),
-    2d (4d lazy) for the column mass, and the bytes each HBM-bound kernel must move."""
+    """Algorithmic work of each lazy loop, counted from the run's actual index
+    sets: 8d flops per visible (row, selected key) pair in the attention (6d
+    for the mixture formula), 4d in its column-mass pass; chain bytes read by
+    the commit (the active tokens' previous version) and by the attention (the
+    selected keys' versions l-1 and l: base row + the records present in
+    layers 2..l-1, the layer-l version of an active key being derived from its
+    new row), delta records written.  Full loops: 4d flops per causal pair.
+    Decode: the lazy kernel reads each selected key's base rows and every
+    record it holds up to layer l (the context's layers are stored before the
+    loops run)."""
     import numpy as np
     H, d, N = wl.n_heads, wl.head_dim, wl.n_tokens
     es = 2 if wl.dtype == "bf16" else 4
     rec = d * wl.delta_bits // 8 + 2 * (d // wl.group)   # bytes of one delta record (one head row)
-    w = {"attn_full_flops": 0, "attn_lazy_flops": 0, "colmass_full_flops": 0, "colmass_lazy_flops": 0,
-         "select_bytes": 0, "commit_bytes": 0, "kv_bytes": 0, "lazy_rows": 0, "rows": 0}
+    fl = 6 if getattr(run, "formula", "column") == "mixture" else 8
+    out = {"loops": {}, "full": {}}
     if wl.decode:
         S = wl.n_seq
-        w["decode_full_bytes"] = w["decode_lazy_bytes"] = 0
-        for l in range(1, wl.n_loops + 1):
-            w["rows"] += S
-            if l == 1:
-                p = S * H * N
-                w["attn_full_flops"] += 4 * d * p
-                w["decode_full_bytes"] += S * H * N * d * es * 2
-            else:
-                keys = run.keys.cpu().numpy()
-                p = S * H * wl.n_keys
-                w["attn_lazy_flops"] += 8 * d * p
-                w["lazy_rows"] += S
-                # chain reads of the selected keys: base + one record per present layer, K and V
-                layers_present = 0
-                for s in range(S):
-                    for lp in range(2, l + 1):
-                        present = set(run.ctx[lp][s].cpu().numpy().tolist()) | {N - 1}
-                        layers_present += sum(int(j in present) for j in keys[s, 0])
-                w["decode_lazy_bytes"] += 2 * H * (S * wl.n_keys * d * es + layers_present * rec)
-        w["kv_bytes"] = w["decode_full_bytes"] + w["decode_lazy_bytes"]
-        return w
-    for l in range(1, wl.n_loops + 1):
+        present = {}
+        for l in range(2, wl.n_loops + 1):
+            m = np.zeros((S, N), bool)
+            ctx = run.ctx[l].cpu().numpy()
+            for s in range(S):
+                m[s, ctx[s]] = True
+            m[:, N - 1] = True                               # the new token writes a record every loop
+            present[l] = m
+        out["full"][1] = {"flops": 4 * d * S * H * N, "bytes": 2 * S * H * N * d * es}
+        keys = run.keys.cpu().numpy()                        # the last lazy loop's keys (per-loop sets: see run)
+        for l in range(2, wl.n_loops + 1):
+            ks = run.keys_by_loop[l] if hasattr(run, "keys_by_loop") else keys
+            n_rec = sum(int(np.take_along_axis(present[lp][:, None, :].repeat(H, 1), ks, 2).sum())
+                        for lp in range(2, l + 1))
+            attend = 2 * (S * H * ks.shape[-1] * d * es + n_rec * rec)
+            commit = 2 * H * S * (d * es + (l - 2) * rec)          # the new token has a record in every layer
+            out["loops"][l] = {"rows": S, "pairs": S * H * ks.shape[-1], "attn_flops": fl * d * S * H * ks.shape[-1],
+                               "attend_bytes": attend, "commit_chain_bytes": commit, "delta_bytes": 2 * H * S * rec}
+        return out
+    present = {}
+    for l in range(2, wl.n_loops + 1):
+        m = np.zeros(N, bool)
         if l <= wl.n_full:
-            p = H * N * (N + 1) // 2
-            w["rows"] += N
-            w["attn_full_flops"] += 4 * d * p
-            w["colmass_full_flops"] += 2 * d * p
-            w["commit_bytes"] += 2 * H * N * (d * es + (d * es + (l - 1) * rec if l > 1 else d * es))
+            m[:] = True
         else:
-            act = run.act[l].cpu().numpy()
-            keys = run.keys_l[l].cpu().numpy()
-            na = act.size
-            w["rows"] += na
-            w["lazy_rows"] += na
-            p = sum(_pairs(act, keys[h]) for h in range(H))
-            w["attn_lazy_flops"] += 8 * d * p
-            w["colmass_lazy_flops"] += 4 * d * p
-            cand = N if l == wl.n_full + 1 else wl.n_active(l - 1)
-            w["select_bytes"] += cand * H * d * es * 2 + N * 8 + N * 8 + H * N * 4 + H * wl.n_keys * 4
-            chain = 2 * H * na * (d * es + (l - 2) * rec)        # upper bound: every earlier layer present
-            w["commit_bytes"] += 2 * H * na * d * es + chain + 2 * H * na * rec
-            w["kv_bytes"] += chain + 2 * H * na * rec
-    return w
-
-
-KERNEL_WORK = {
-    # kernel name -> (work key, unit, bound)
-    "rows_attend_full": ("attn_full_flops", "TFLOP/s", "alu"),
-    "rows_attend_lazy": ("attn_lazy_flops", "TFLOP/s", "alu"),
-    "rows_attend_commit_lazy": ("attn_lazy_flops", "TFLOP/s", "alu"),
-    "rows_colmass": ("colmass_full_flops", "TFLOP/s", "alu"),
-    "mfma_fwd_full": ("attn_full_flops", "TFLOP/s", "mfma"),
-    "mfma_fwd_lazy": ("attn_lazy_flops", "TFLOP/s", "mfma"),
-    "mfma_colmass_full": ("colmass_full_flops", "TFLOP/s", "mfma"),
-    "mfma_colmass_lazy": ("colmass_lazy_flops", "TFLOP/s", "mfma"),
-    "delta_norm": ("select_bytes", "GB/s", "hbm"),
-    "commit_delta": ("commit_bytes", "GB/s", "hbm"),
-}
-# the decode workload's per-row kernels stream the stored context: HBM-bound
-KERNEL_WORK_DECODE = dict(KERNEL_WORK, **{
-    "rows_attend_full": ("decode_full_bytes", "GB/s", "hbm"),
-    "rows_attend_commit_lazy": ("decode_lazy_bytes", "GB/s", "hbm"),
-    "rows_attend_lazy": ("decode_lazy_bytes", "GB/s", "hbm"),
-})
+            m[run.act[l].cpu().numpy()] = True
+        present[l] = m
+    for l in range(1, wl.n_full + 1):
+        p = H * N * (N + 1) // 2
+        out["full"][l] = {"flops": 4 * d * p, "colmass_flops": 2 * d * p}
+    for l in range(wl.n_full + 1, wl.n_loops + 1):
+        act = run.act[l].cpu().numpy()
+        keys = run.keys_l[l].cpu().numpy()
+        p = sum(_pairs(act, keys[h]) for h in range(H))
+        chain_rec = lambda idx: sum(int(present[lp][idx].sum()) for lp in range(2, l))
+        commit = 2 * H * (act.size * d * es + chain_rec(act) * rec)
+        attend = 2 * sum(keys[h].size * d * es + chain_rec(keys[h]) * rec for h in range(H))
+        cand = N if l == wl.n_full + 1 else wl.n_active(l - 1)
+        out["loops"][l] = {"rows": int(act.size), "pairs": p, "attn_flops": fl * d * p, "colmass_flops": 4 * d * p,
+                           "attend_bytes": attend, "commit_chain_bytes": commit,
+                           "delta_bytes": 2 * H * act.size * rec,
+                           "select_bytes": cand * H * d * es * 2 + N * 8 + N * 8 + H * N * 4 + H * wl.n_keys * 4}
+    return out
 
 
 def measured_traffic(timer, workload):
@@ -152,99 +155,107 @@ def measured_traffic(timer, workload):
                 return {"traffic": None, "traffic_note": f"{rec['file']} is stale (sources changed)"}
             return {"traffic": rec["traffic_bytes"], "traffic_unit": "bytes per launch",
                     "traffic_source": rec["file"]}
-    return {}
+    return {"traffic": None}
 
 
-def roofline(timings, work, steps, decode=False, workload="", kernel=None):
-    """Roofline of `kernel`, or of the kernel with the largest share of the step."""
-    table = KERNEL_WORK_DECODE if decode else KERNEL_WORK
-    if kernel is None:
-        name, (ms, launches) = max(timings.items(), key=lambda kv: kv[1][0])
-    elif kernel in timings:
-        name, (ms, launches) = kernel, timings[kernel]
+def roofline_entry(kernel, work, ms, launches, unit, bound, label):
+    """Work per launch / average launch time, against MI355X's published peak."""
+    avg = ms / max(launches, 1)
+    if unit == "GB/s":
+        achieved, peak = work / launches / (avg / 1e3) / 1e9, HBM_PEAK_GBPS
     else:
-        return None
-    avg_ms = ms / max(launches, 1)
-    entry = {"kernel": name, "launches_per_step": launches / steps, "avg_launch_ms": avg_ms}
-    if name in table:
-        key, unit, bound = table[name]
-        per_step = work[key]
-        secs = ms / 1e3 / steps
-        if unit == "GB/s":
-            achieved = per_step / secs / 1e9
-            peak = HBM_PEAK_GBPS
-        else:
-            achieved = per_step / secs / 1e12
-            peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else FP32_VECTOR_PEAK_TFLOPS
-        entry.update({"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                      "frac": achieved / peak, "traffic": None})
-        entry.update(measured_traffic(name, workload))
-    else:
-        entry.update({"bound": None, "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None})
-    return entry
+        achieved = work / launches / (avg / 1e3) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else FP32_VECTOR_PEAK_TFLOPS
+    e = {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+         "avg_launch_ms": avg, "launches": launches, "work_per_launch": work / launches}
+    e.update(measured_traffic(kernel, label))
+    return e
 
 
 # --------------------------------------------------------------------------- CPU oracle
-def cpu_baseline(wl, target_s):
-    """The oracle, as it stands, on a bounded sample of the same workload.
-
-    Decode: the T loops of one sequence over its built context (the context
-    build is outside the timed work, as on the GPU).  Prefill: whole steps;
-    when one step of all heads would take well over the target, whole steps
-    of the same workload with fewer heads (same N, schedule and key count),
-    scaled by the head fraction (every part of a step is per head or
-    proportional to the hidden width).
-    """
-    import copy
+def _threads():
     from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle, as it stands, on the same lazy loops the metric times.
+
+    The full loops run first, untimed (the checkpoint the lazy loops start
+    from, as on the GPU).  Prefill: with N above 4096 the oracle runs one head
+    of every per-head step (key selection, commit, attention) while the token
+    selection scores every token's whole hidden row; the per-head part is
+    scaled by the head count (every step but the token selection is per head).
+    Decode: the lazy loops of one sequence over its built context.  Timed with
+    the BLAS thread pool at its default size and again with one thread.
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_limits
     import oracle
-    from sparse_loop_attention_amd import configs
     from sparse_loop_attention_amd.synth import SyntheticLoops
-    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    lazy = list(range(wl.n_full + 1, wl.n_loops + 1))
     if wl.decode:
         syn = SyntheticLoops(wl, seqs=(0,))
         data = {l: {k: v.copy() for k, v in x.items()} for l, x in syn}
         ctx = {l: syn.context_active_sets(l)[0] for l in range(2, wl.n_loops + 1)}
         store = oracle.build_decode_context(wl, 0, ctx, data)
-        n, busy = 0, 0.0
-        while busy < target_s:
+        head = oracle.run_decode_loops(wl, store, 0, data, upto=1)           # loop 1, untimed
+
+        def once():
             st = copy.deepcopy(store)
             t0 = time.perf_counter()
-            oracle.run_decode_loops(wl, st, 0, data)
-            busy += time.perf_counter() - t0
-            n += 1
-            print(f"[bench] oracle decode run {n}: {busy:.1f} s", file=sys.stderr, flush=True)
-        return {"value": n * wl.n_loops / busy, "unit": "active-token loop-steps/s", "cores": cores,
-                "kind": "oracle",
-                "sample": f"{n} run(s) of the {wl.n_loops} decode loops of 1 of {wl.n_seq} sequences "
-                          f"over its built context, {busy:.1f} s"}
-
-    def steps_of(w, budget):
-        data = [(l, {k: v.copy() for k, v in x.items()}) for l, x in SyntheticLoops(w)]
-        n, busy = 0, 0.0
-        while True:
-            t0 = time.perf_counter()
-            oracle.run_prefill(w, iter(data))
-            busy += time.perf_counter() - t0
-            n += 1
-            print(f"[bench] oracle step {n} ({w.n_heads} heads): {busy:.1f} s", file=sys.stderr, flush=True)
-            if busy >= budget:
-                return n, busy
-
-    H = wl.n_heads
-    rows_per_step = sum(wl.n_active(l) for l in range(1, wl.n_loops + 1))
-    probe = configs.scaled(wl, wl.n_tokens, n_heads=1)
-    n1, t1 = steps_of(probe, 0.0)
-    hs = H if t1 * H <= 1.5 * target_s else max(1, min(H, int(target_s // t1)))
-    if hs == 1 and t1 >= 0.5 * target_s:
-        n, dt = n1, t1
+            oracle.run_decode_loops(wl, st, 0, data, start=2, state=head[-1])
+            return time.perf_counter() - t0
+        rows = len(lazy)
+        what = f"the {len(lazy)} lazy decode loops of 1 of {wl.n_seq} sequences over its built context"
+        t_sel, hs = 0.0, wl.n_heads
     else:
-        n, dt = steps_of(wl if hs == H else configs.scaled(wl, wl.n_tokens, n_heads=hs), target_s)
-    what = "all heads" if hs == H else f"{hs} of its {H} heads, scaled by {hs}/{H}"
-    return {"value": n * rows_per_step / dt * hs / H, "unit": "active-token loop-steps/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{n} whole step(s) of the workload ({wl.n_loops} loops, N = {wl.n_tokens}) with {what}, "
-                      f"{dt:.1f} s"}
+        hs = wl.n_heads if wl.n_tokens <= 4096 else 1
+        raw = [(l, {k: v.copy() for k, v in x.items()}) for l, x in SyntheticLoops(wl)]
+        data = [(l, {k: (v if k == "h" else np.ascontiguousarray(v[:, :, :hs])) for k, v in x.items()})
+                for l, x in raw]
+        wl_s = dataclasses.replace(wl, n_heads=hs)
+        t0 = time.perf_counter()
+        ck = oracle.run_prefill(wl_s, iter(data), upto=wl.n_full)           # full loops, untimed
+        print(f"[bench] oracle full loops ({hs} heads, untimed): {time.perf_counter() - t0:.1f} s",
+              file=sys.stderr, flush=True)
+        hx = {l: x["h"][0] for l, x in raw}
+
+        def once():
+            t0 = time.perf_counter()
+            oracle.run_prefill(wl_s, iter(data), resume=ck)
+            return time.perf_counter() - t0
+
+        def selection():                   # the part that is not per head: every token's whole hidden row
+            t0 = time.perf_counter()
+            for l in lazy:
+                oracle.topk_ascending(oracle.token_scores(hx[l - 1], hx[l - 2]), wl.n_active(l))
+            return time.perf_counter() - t0
+        rows = sum(wl.n_active(l) for l in lazy)
+        what = (f"lazy loops {lazy[0]}-{lazy[-1]} (N = {wl.n_tokens}) after the untimed full loops, "
+                + ("all heads" if hs == wl.n_heads else
+                   f"{hs} of {wl.n_heads} heads for the per-head steps, scaled by {wl.n_heads}/{hs}, "
+                   f"token selection over the whole hidden row"))
+    out = {}
+    for threads in (None, 1):
+        with threadpool_limits(limits=threads):
+            cores = _threads()
+            n, busy = 0, 0.0
+            while busy < (target_s if threads is None else 0.5 * target_s) or n == 0:
+                busy += once()
+                n += 1
+            t_run = busy / n
+            t_sel = 0.0
+            if not wl.decode and hs < wl.n_heads:
+                t_sel = min(selection(), t_run)
+            t_step = t_sel + (t_run - t_sel) * wl.n_heads / hs
+        print(f"[bench] oracle, {cores} thread(s): {n} run(s), {t_run:.2f} s each", file=sys.stderr, flush=True)
+        out[threads] = {"value": rows / t_step, "unit": "active-token loop-steps/s", "cores": cores,
+                        "kind": "oracle", "sample": f"{n} run(s) of {what}; {t_run:.2f} s per run"
+                        + (f", of which {t_sel:.2f} s token selection" if t_sel else "")}
+    res = out[None]
+    res["single_thread"] = out[1]
+    return res
 
 
 # --------------------------------------------------------------------------- quality
@@ -255,10 +266,15 @@ def quality(wl):
     every row (the effective queries) over the store's version l, computed by
     the library's full mode; the error is ||o - o_dense|| / ||o_dense|| over
     all rows and over the loop's active rows, for each output formula and key
-    policy.
+    policy.  Also, at a size the oracle finishes in seconds (at most 1024
+    tokens and 4 heads), the GPU's largest error against the oracle with
+    attention's K^, V^ rounded to bf16 (the parity reference) and against the
+    oracle that attends to the float32 reconstruction: what bf16 operands cost.
     """
+    import numpy as np
     import torch
-    from sparse_loop_attention_amd import abi, driver
+    import oracle
+    from sparse_loop_attention_amd import abi, configs, driver
     from sparse_loop_attention_amd.synth import SyntheticLoops
     inputs = driver.upload_loops(wl, SyntheticLoops(wl), "cuda")
     n, H, d = wl.n_tokens, wl.n_heads, wl.head_dim
@@ -291,6 +307,21 @@ def quality(wl):
                              "rel_err_active": float(diff[idx].norm() / ref[idx].norm())})
             out[f"{formula}{'+frozen' if freeze else ''}"] = rows
             print(f"[bench] quality {formula} frozen={freeze} done", file=sys.stderr, flush=True)
+    small = configs.scaled(wl, min(n, 1024), n_heads=min(H, 4))
+    run = driver.PrefillRun(small, driver.upload_loops(small, SyntheticLoops(small), "cuda"), "cuda")
+    recs = run.run(record=True)
+    torch.cuda.synchronize()
+    ops = {}
+    for od in (None, "fp32"):
+        _, hist = oracle.run_prefill(small, iter(SyntheticLoops(small)), keep=True, operand_dtype=od)
+        per = []
+        for l in range(1, small.n_loops + 1):
+            want = hist[l - 1].o
+            got = recs[l - 1].o.cpu().numpy().astype(np.float64)
+            per.append({"loop": l, "max_abs_err_over_rms": float(np.abs(got - want).max() / np.sqrt(np.mean(want ** 2)))})
+        ops["bf16_operands" if od is None else "fp32_operands"] = per
+    out["gpu_vs_oracle_operands"] = {"workload": f"{small.name} scaled to N = {small.n_tokens}, {small.n_heads} heads",
+                                     **ops}
     return out
 
 
@@ -332,6 +363,80 @@ def exit_report(wl, tau, steps, warmup):
     return out
 
 
+# --------------------------------------------------------------------------- GPU timing
+# the lazy loops' attention kernel and the full loop's dominant kernel, by workload kind
+LAZY_KERNEL = {"prefill": ("mfma_fwd_lazy", "attn_flops", "TFLOP/s", "mfma"),
+               "decode": ("rows_attend_commit_lazy", "attend_bytes", "GB/s", "hbm"),
+               "fp32": ("rows_attend_commit_lazy", "attn_flops", "TFLOP/s", "alu")}
+FULL_KERNEL = {"prefill": ("mfma_fwd_full", "flops", "TFLOP/s", "mfma"),
+               "decode": ("rows_attend_full", "bytes", "GB/s", "hbm"),
+               "fp32": ("rows_attend_full", "flops", "TFLOP/s", "alu")}
+
+
+def make_run(wl, inputs, syn, overlap=None):
+    from sparse_loop_attention_amd import driver
+    if wl.decode:
+        ctx_sets = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)}
+        run = driver.DecodeRun(wl, inputs, ctx_sets, "cuda")
+        run.build_context()
+        return run
+    return driver.PrefillRun(wl, inputs, "cuda", overlap=overlap)
+
+
+def time_lazy_loops(run, wl, reps):
+    """Median (p10, p90) over `reps` of the lazy loops' time, each repetition
+    from the state after the full loops (restored untimed).  The lazy loops
+    rewrite their own layers and index sets, so the restored outputs (o, lse,
+    column mass) are all a repetition needs."""
+    import torch
+    first = wl.n_full + 1
+    run.run(upto=wl.n_full)
+    snap = run.snapshot(arena=False)
+    times = []
+    for _ in range(reps):
+        run.restore(snap)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run.run(start=first)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return times, snap
+
+
+def per_call_and_kernel_times(run, wl, snap, reps):
+    """Each library call of the lazy loops on its own (one stream): hipEvent
+    medians per call; and per lazy loop, the kernels' hipEvent times (a
+    second pass, so the kernel events do not add to the call times)."""
+    import torch
+    from sparse_loop_attention_amd import abi, driver
+    first = wl.n_full + 1
+    timer = driver.CallTimer()
+    run.timer = timer
+    for _ in range(reps):
+        run.restore(snap)
+        run.run(start=first)
+    calls = timer.ms()
+    run.timer = driver._NO_TIMER
+    per_loop = {l: {} for l in range(first, wl.n_loops + 1)}
+    keys_by_loop = {}
+    for _ in range(max(3, reps // 5)):
+        run.restore(snap)
+        for l in range(first, wl.n_loops + 1):
+            abi.timing_enable(True)
+            run.run(start=l, upto=l)
+            t = abi.timing_read()
+            abi.timing_enable(False)
+            for k, (ms, n) in t.items():
+                acc = per_loop[l].setdefault(k, [0.0, 0])
+                acc[0] += ms
+                acc[1] += n
+            if wl.decode:
+                keys_by_loop[l] = run.keys.cpu().numpy()
+    torch.cuda.synchronize()
+    return {k: _stats(v) for k, v in sorted(calls.items())}, per_loop, keys_by_loop
+
+
 # --------------------------------------------------------------------------- main
 def main():
     args = parse()
@@ -339,7 +444,6 @@ def main():
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
                                    "(the multi-GPU sharding is a design note, not code)"}))
         sys.exit(2)
-    import numpy as np
     import torch
     from sparse_loop_attention_amd import abi, configs, driver
     from sparse_loop_attention_amd.synth import SyntheticLoops
@@ -350,7 +454,6 @@ def main():
     wl = configs.WORKLOADS[args.workload]
     if wl.head_dim % args.group:
         raise SystemExit(f"--group {args.group} does not divide head_dim {wl.head_dim}")
-    import dataclasses
     wl = dataclasses.replace(wl, delta_bits=args.delta_bits, group=args.group)
     if args.exit_threshold is not None:
         print(json.dumps(exit_report(wl, args.exit_threshold, args.steps, args.warmup)), flush=True)
@@ -364,72 +467,103 @@ def main():
         return
     # traffic records name the workload, and the store format when it is not the default
     label = wl.name if (wl.delta_bits, wl.group) == (4, 32) else f"{wl.name}-{wl.delta_bits}b{wl.group}"
+    kind = "decode" if wl.decode else ("prefill" if wl.dtype == "bf16" else "fp32")
     print(f"[bench] workload {label}: generating inputs", file=sys.stderr, flush=True)
     syn = SyntheticLoops(wl)
-    if wl.decode:
-        ctx_sets = {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)}
-        inputs = driver.upload_loops(wl, syn, "cuda")
-        run = driver.DecodeRun(wl, inputs, ctx_sets, "cuda")
-        run.build_context()
-    else:
-        inputs = driver.upload_loops(wl, syn, "cuda")
-        run = driver.PrefillRun(wl, inputs, "cuda")
+    inputs = driver.upload_loops(wl, syn, "cuda")
+    run = make_run(wl, inputs, syn)
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         run.run()
     torch.cuda.synchronize()
-    # timed region: K steps as a caller runs them (no instrumentation)
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
+    # whole steps (every loop) as a caller runs them, no instrumentation
+    print(f"[bench] timing {args.steps} whole steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         run.run()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    # kernel durations: the same K steps again with a hipEvent pair around every
-    # launch, on the launch stream (the events add queue gaps between kernels,
-    # not kernel time, so the step time above is taken without them)
-    print(f"[bench] per-kernel hipEvent timing over {args.steps} steps", file=sys.stderr, flush=True)
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    # per-kernel hipEvent times over the same K whole steps
+    print(f"[bench] per-kernel hipEvent timing over {args.steps} whole steps", file=sys.stderr, flush=True)
     abi.timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for _ in range(args.steps):
         run.run()
     torch.cuda.synchronize()
-    ms_instrumented = (time.perf_counter() - t0) / args.steps * 1e3
-    timings = abi.timing_read()
+    step_kernels = abi.timing_read()
     abi.timing_enable(False)
+    # the metric: the lazy loops from the checkpoint after the full loops
+    print(f"[bench] lazy loops: {args.reps} repetitions", file=sys.stderr, flush=True)
+    lazy_times, snap = time_lazy_loops(run, wl, args.reps)
+    # each call on its own, then each loop's kernels (one stream)
+    print("[bench] per-call and per-kernel timing of the lazy loops", file=sys.stderr, flush=True)
+    solo = run if wl.decode else make_run(wl, inputs, syn, overlap=False)
+    if solo is not run:
+        solo.run(upto=wl.n_full)
+        solo.restore(snap)
+    calls, per_loop, keys_by_loop = per_call_and_kernel_times(solo, wl, snap, args.reps)
+    if wl.decode:
+        run.keys_by_loop = keys_by_loop
     work = work_model(wl, run)
-    value = work["rows"] * args.steps / elapsed
-    lazy_ms = sum(ms for name, (ms, _) in timings.items()
-                  if name.endswith("_lazy") or name in ("delta_norm", "topk", "commit_delta", "slot_map",
-                                                        "rows_colmass", "colmass_reduce")) / args.steps
-    lazy_kernel = next((k for k in ("mfma_fwd_lazy", "rows_attend_commit_lazy", "rows_attend_lazy") if k in timings),
-                       None)
+    lazy = sorted(work["loops"])
+    lazy_ms = _pct(lazy_times, 50)
+    rows = sum(work["loops"][l]["rows"] for l in lazy)
+    kv_bytes = sum(work["loops"][l]["attend_bytes"] + work["loops"][l]["commit_chain_bytes"]
+                   + work["loops"][l]["delta_bytes"] for l in lazy)
+    # roofline of the lazy loops' attention kernel, over all lazy loops and per loop
+    kname, wkey, unit, bound = LAZY_KERNEL[kind]
+    tot_ms = sum(per_loop[l].get(kname, [0.0, 0])[0] for l in lazy)
+    tot_n = sum(per_loop[l].get(kname, [0.0, 0])[1] for l in lazy)
+    reps_k = max(3, args.reps // 5)
+    tot_work = sum(work["loops"][l][wkey] for l in lazy) * reps_k
+    roof = roofline_entry(kname, tot_work, tot_ms, tot_n, unit, bound, label) if tot_n else None
+    if roof:
+        # HBM traffic: each loop's launch is its own kernel instance, with its own
+        # counter record (timer "<kernel>@<loop>"); per launch over the loops
+        traffic = [measured_traffic(f"{kname}@{l}", label) for l in lazy]
+        roof["traffic"] = (sum(t["traffic"] for t in traffic) / len(lazy)
+                           if all(t.get("traffic") is not None for t in traffic) else None)
+        roof["traffic_sources"] = [t.get("traffic_source") or t.get("traffic_note") for t in traffic]
+        roof.pop("traffic_source", None)
+        roof.pop("traffic_unit", None)
+        roof["scope"] = f"lazy loops {lazy[0]}-{lazy[-1]}: work summed over the loops / kernel time summed"
+        roof["per_loop"] = {}
+        for l, t in zip(lazy, traffic):
+            ms, n = per_loop[l].get(kname, [0.0, 0])
+            if n:
+                e = roofline_entry(kname, work["loops"][l][wkey] * reps_k, ms, n, unit, bound, label)
+                roof["per_loop"][str(l)] = {k: e[k] for k in ("achieved", "frac", "avg_launch_ms", "work_per_launch")}
+                roof["per_loop"][str(l)]["traffic"] = t.get("traffic")
+    fname, fkey, funit, fbound = FULL_KERNEL[kind]
+    full_roof = None
+    if fname in step_kernels:
+        ms, n = step_kernels[fname]
+        fwork = sum(work["full"][l][fkey] for l in work["full"]) * args.steps
+        full_roof = roofline_entry(fname, fwork, ms, n, funit, fbound, label)
     out = {
-        "metric": "active-token loop-steps/sec + KV GB/s; % of HBM / bf16-MFMA roofline",
-        "value": value,
+        "metric": METRIC,
+        "value": rows / (lazy_ms / 1e3),
         "unit": "active-token loop-steps/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "ms_per_step_with_kernel_events": ms_instrumented,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; shapes and change/heavy-key structure of the pages' workloads)",
         "config": {"workload": wl.name, "n_seq": wl.n_seq, "heads": wl.n_heads, "head_dim": wl.head_dim,
                    "seq_len": wl.n_tokens, "loops": wl.n_loops, "full_loops": wl.n_full,
-                   "active": list(wl.active), "keys": wl.n_keys,
-                   "delta_bits": wl.delta_bits, "group": wl.group},
-        "kv_GBps": work["kv_bytes"] / (elapsed / args.steps) / 1e9,
-        "lazy_active_token_steps_per_s": (work["lazy_rows"] / (lazy_ms / 1e3)) if lazy_ms > 0 else None,
-        "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in sorted(timings.items())},
-        "roofline": roofline(timings, work, args.steps, wl.decode, label),
-        # the lazy loops' attention on its own: the gathered-tile MFMA kernel
-        # (prefill) or the chain read (decode), loops after the full ones
-        "roofline_lazy_attention": (roofline(timings, work, args.steps, wl.decode, label, kernel=lazy_kernel)
-                                    if lazy_kernel else None),
+                   "active": list(wl.active), "keys": wl.n_keys, "delta_bits": wl.delta_bits, "group": wl.group},
+        "value_definition": "sum of n_active over the lazy loops / median time of the lazy loops' library calls "
+                            "(hipEvents, from the state after the full loops)",
+        "lazy_loops_ms": _stats(lazy_times),
+        "kv_GBps": kv_bytes / (lazy_ms / 1e3) / 1e9,
+        "kv_bytes_per_step": kv_bytes,
+        "abi_calls_ms": calls,
+        "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in sorted(step_kernels.items())},
+        "kernels_ms_per_lazy_loop": {str(l): {k: round(v[0] / reps_k, 4) for k, v in sorted(per_loop[l].items())}
+                                     for l in lazy},
+        "roofline": roof,
+        "roofline_full_loop": full_roof,
+        "work_per_lazy_loop": {str(l): {k: v for k, v in work["loops"][l].items()} for l in lazy},
     }
     if args.cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
