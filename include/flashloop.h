@@ -27,10 +27,11 @@
  *    call returns a non-zero fl_status, launches nothing, and
  *    flashloop_last_error() describes the problem.  A failed launch returns
  *    FL_ERR_HIP.  No C++ exception crosses this boundary.
- *  - The library holds no state besides a thread-local error message and the
- *    optional kernel-timing registry below; calls from several threads are
- *    safe.  Calls that write the same buffers on different streams race, as
- *    any two kernels would.
+ *  - The library holds no state besides a thread-local error message, the
+ *    optional kernel-timing registry below and the per-GPU scratch array of
+ *    flashloop_attend_noalloc; calls from several threads are safe.  Calls
+ *    that write the same buffers on different streams race, as any two
+ *    kernels would.
  */
 #ifndef FLASHLOOP_H
 #define FLASHLOOP_H
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FLASHLOOP_ABI_VERSION 4
+#define FLASHLOOP_ABI_VERSION 5
 #define FL_MAX_VERSIONS 32          /* versions 1..FL_MAX_VERSIONS */
 
 typedef enum {
@@ -236,6 +237,23 @@ typedef struct {
 
 uint64_t  flashloop_attend_workspace_bytes(const fl_attend_args* args);
 fl_status flashloop_attend(const fl_attend_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* flashloop_attend_noalloc -- flashloop_attend for callers that cannot     */
+/* allocate device memory (code under HIP graph capture, serving loops or    */
+/* harnesses that forbid hipMalloc).  Same arguments, same kernels, same     */
+/* results bit for bit; args->workspace and workspace_bytes are ignored and  */
+/* the call's scratch comes from an array the library holds on each GPU      */
+/* (FLASHLOOP_STATIC_SCRATCH_BYTES, resident from the library's load on that */
+/* GPU until the process ends).  The call allocates nothing.  A call whose   */
+/* scratch need (flashloop_attend_workspace_bytes) exceeds that size returns */
+/* FL_ERR_WORKSPACE before any launch.  The stream must belong to the        */
+/* current device (FL_ERR_ARG otherwise).  Every call on one GPU shares the  */
+/* array: calls that overlap on one GPU (several streams or threads) race;   */
+/* calls ordered on one stream do not.                                       */
+/* ------------------------------------------------------------------------ */
+#define FLASHLOOP_STATIC_SCRATCH_BYTES (128ull << 20)
+fl_status flashloop_attend_noalloc(const fl_attend_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* flashloop_exit_check -- early exit per sequence.                           */

@@ -27,7 +27,9 @@ FL_ROWS_BY_TOKEN, FL_ROWS_COMPACT = 0, 1
 
 EXPORTS = ("flashloop_kv_layout", "flashloop_kv_arena_bytes", "flashloop_kv_commit", "flashloop_select",
            "flashloop_attend_workspace_bytes", "flashloop_attend", "flashloop_last_error",
-           "flashloop_abi_version", "flashloop_timing_enable", "flashloop_timing_read", "flashloop_exit_check")
+           "flashloop_abi_version", "flashloop_timing_enable", "flashloop_timing_read", "flashloop_exit_check",
+           "flashloop_attend_noalloc")
+STATIC_SCRATCH_BYTES = 128 << 20        # FLASHLOOP_STATIC_SCRATCH_BYTES
 
 
 class fl_kv_desc(C.Structure):
@@ -99,6 +101,7 @@ def lib():
         L.flashloop_attend_workspace_bytes.argtypes = [C.POINTER(fl_attend_args)]
         L.flashloop_attend_workspace_bytes.restype = C.c_uint64
         L.flashloop_attend.argtypes = [C.POINTER(fl_attend_args), C.c_void_p]
+        L.flashloop_attend_noalloc.argtypes = [C.POINTER(fl_attend_args), C.c_void_p]
         L.flashloop_last_error.restype = C.c_char_p
         L.flashloop_abi_version.restype = C.c_int32
         L.flashloop_timing_enable.argtypes = [C.c_int32]
@@ -106,7 +109,7 @@ def lib():
         L.flashloop_timing_read.restype = C.c_int32
         L.flashloop_exit_check.argtypes = [C.POINTER(fl_exit_args), C.c_void_p]
         for f in ("flashloop_kv_layout", "flashloop_kv_commit", "flashloop_select", "flashloop_attend",
-                  "flashloop_exit_check"):
+                  "flashloop_exit_check", "flashloop_attend_noalloc"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -267,6 +270,11 @@ def attend_workspace_bytes(a: fl_attend_args) -> int:
 
 def attend(a: fl_attend_args, stream=None) -> None:
     _check(lib().flashloop_attend(C.byref(a), _stream(stream)))
+
+
+def attend_noalloc(a: fl_attend_args, stream=None) -> None:
+    """flashloop_attend on the library's own per-GPU scratch (a.workspace is ignored)."""
+    _check(lib().flashloop_attend_noalloc(C.byref(a), _stream(stream)))
 
 
 def exit_check(exit_flags: torch.Tensor, threshold: float, scores: Optional[torch.Tensor] = None,

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libflashloop.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "timing.hip", "select.hip", "kv.hip", "attn_rows.hip", "attn_decode.hip", "attn_plan.hip", "attn_mfma.hip"]
+SOURCES = ["api.hip", "timing.hip", "select.hip", "kv.hip", "attn_rows.hip", "attn_decode.hip", "attn_plan.hip", "attn_mfma.hip", "scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

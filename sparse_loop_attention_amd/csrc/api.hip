@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "flashloop.h"
 #include "fl_launch.hpp"
@@ -236,7 +237,7 @@ uint64_t flashloop_attend_workspace_bytes(const fl_attend_args* a) {
   return fl::plan_attend(*a).off_total;
 }
 
-fl_status flashloop_attend(const fl_attend_args* a, void* stream) {
+static fl_status attend_impl(const fl_attend_args* a, void* stream, bool static_scratch) {
   fl_kv_layout lay;
   fl_status st = check_attend(a, &lay);
   if (st != FL_OK) return st;
@@ -253,28 +254,45 @@ fl_status flashloop_attend(const fl_attend_args* a, void* stream) {
     return ok();
   }
   const fl::AttendPlan p = fl::plan_attend(*a);
-  if (p.off_total > 0 && (!a->workspace || a->workspace_bytes < p.off_total || !aligned(a->workspace, 256)))
+  fl_attend_args x = *a;
+  if (static_scratch) {
+    if (p.off_total > FLASHLOOP_STATIC_SCRATCH_BYTES)
+      return fail(FL_ERR_WORKSPACE, "attend_noalloc: the call needs %llu bytes of scratch, more than the %llu the "
+                  "library holds per GPU (use flashloop_attend with a workspace)",
+                  (unsigned long long)p.off_total, (unsigned long long)FLASHLOOP_STATIC_SCRATCH_BYTES);
+    void* ptr = nullptr;
+    hipError_t e = fl::static_scratch(static_cast<hipStream_t>(stream), &ptr);
+    if (e == hipErrorInvalidValue) return fail(FL_ERR_ARG, "attend_noalloc: the stream belongs to another device");
+    if (e != hipSuccess) return hip_fail(e, "attend_noalloc: scratch address");
+    x.workspace = ptr;
+    x.workspace_bytes = FLASHLOOP_STATIC_SCRATCH_BYTES;
+  } else if (p.off_total > 0 && (!a->workspace || a->workspace_bytes < p.off_total || !aligned(a->workspace, 256))) {
     return fail(FL_ERR_WORKSPACE, "attend: workspace needs %llu bytes (256-byte aligned), got %llu",
                 (unsigned long long)p.off_total, (unsigned long long)a->workspace_bytes);
+  }
   fl::KvView kv = fl::make_view(*a->kv, lay);
   kv.exit_flags = a->exit_flags;
-  if (a->fuse_commit && a->mode == FL_ATTEND_FULL && !p.mfma) {
+  if (x.fuse_commit && x.mode == FL_ATTEND_FULL && !p.mfma) {
     // the per-row path fuses only LAZY commits: commit first, on the same stream
     fl_commit_args c{};
-    c.kv = a->kv; c.version = a->version;
-    c.active_idx = a->active_idx;                 // null: every token (the commit kernels take it so)
-    c.n_active = a->n_active;
-    c.slot_base = a->commit_slot_base; c.reset_map = a->commit_reset;
-    c.k_new = a->k_new; c.v_new = a->v_new;
-    c.src_layout = a->kv_layout;
-    c.exit_flags = a->exit_flags;
+    c.kv = x.kv; c.version = x.version;
+    c.active_idx = x.active_idx;                  // null: every token (the commit kernels take it so)
+    c.n_active = x.n_active;
+    c.slot_base = x.commit_slot_base; c.reset_map = x.commit_reset;
+    c.k_new = x.k_new; c.v_new = x.v_new;
+    c.src_layout = x.kv_layout;
+    c.exit_flags = x.exit_flags;
     hipError_t e = fl::launch_commit(c, kv, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attend launch");
   }
-  hipError_t e = fl::launch_attend(*a, kv, p, static_cast<hipStream_t>(stream));
+  hipError_t e = fl::launch_attend(x, kv, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attend launch");
   return ok();
 }
+
+fl_status flashloop_attend(const fl_attend_args* a, void* stream) { return attend_impl(a, stream, false); }
+
+fl_status flashloop_attend_noalloc(const fl_attend_args* a, void* stream) { return attend_impl(a, stream, true); }
 
 fl_status flashloop_exit_check(const fl_exit_args* a, void* stream) {
   if (!a) return fail(FL_ERR_ARG, "exit args are NULL");

@@ -45,5 +45,8 @@ int fwd_split_items(int64_t n_rows, int u);
 int plan_fwd_pair(int64_t n_sh, int64_t n_rows);
 AttendPlan plan_attend(const fl_attend_args& a);
 hipError_t launch_attend(const fl_attend_args& a, const KvView& kv, const AttendPlan& p, hipStream_t st);
+// Device address of the library's static scratch on the stream's device
+// (FLASHLOOP_STATIC_SCRATCH_BYTES; scratch.hip).
+hipError_t static_scratch(hipStream_t st, void** out);
 
 }  // namespace fl

@@ -24,11 +24,11 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(abi.EXPORTS)
-    assert abi.abi_version() == 4
+    assert abi.abi_version() == 5
 
 
 def _desc(wl, group=32, bits=4):
@@ -213,3 +213,22 @@ def test_exit_flags_alignment(L):
     a.key_idx, a.n_keys = 256, 26
     a.exit_flags = 258
     assert L.flashloop_attend(C.byref(a), None) == abi.FL_ERR_ARG
+
+
+def test_attend_noalloc_rejects_beyond_its_scratch(L):
+    """flashloop_attend_noalloc checks the call's scratch need against the
+    library's per-GPU array before any HIP call: the 32K full loop (gathered
+    tiles of every key) does not fit and is rejected; invalid arguments are
+    rejected as by flashloop_attend."""
+    wl = configs.LONG_PREFILL
+    d = _desc(wl)
+    d.arena, d.arena_bytes = 256, abi.kv_arena_bytes(d)
+    a = abi.fl_attend_args()
+    a.kv = C.pointer(d)
+    a.mode, a.version, a.n_active = abi.FL_ATTEND_FULL, 1, wl.n_tokens
+    a.q_cur = a.o = a.lse = a.colmass = 256
+    assert L.flashloop_attend_workspace_bytes(C.byref(a)) > abi.STATIC_SCRATCH_BYTES
+    assert L.flashloop_attend_noalloc(C.byref(a), None) == abi.FL_ERR_WORKSPACE
+    assert b"scratch" in L.flashloop_last_error()
+    a.mode = 9
+    assert L.flashloop_attend_noalloc(C.byref(a), None) == abi.FL_ERR_ARG
