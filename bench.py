@@ -565,6 +565,30 @@ def main():
         "roofline_full_loop": full_roof,
         "work_per_lazy_loop": {str(l): {k: v for k, v in work["loops"][l].items()} for l in lazy},
     }
+    if wl.decode:
+        # the same lazy loops as one flashloop_decode_loops launch (every loop's
+        # key selection, commit and attention in one kernel), from the same state
+        print(f"[bench] lazy loops in one launch: {args.reps} repetitions", file=sys.stderr, flush=True)
+        one = driver.DecodeRun(wl, inputs, {l: syn.context_active_sets(l) for l in range(2, wl.n_loops + 1)},
+                               "cuda", single_launch=True)
+        one.build_context()
+        one_times, _ = time_lazy_loops(one, wl, args.reps)
+        abi.timing_enable(True)
+        for _ in range(reps_k):
+            one.restore(snap)
+            one.run(start=wl.n_full + 1)
+        torch.cuda.synchronize()
+        t1 = abi.timing_read()
+        abi.timing_enable(False)
+        ms1, n1 = t1.get("decode_loops", (0.0, 0))
+        attend_bytes = sum(work["loops"][l]["attend_bytes"] for l in lazy)
+        out["single_launch"] = {
+            "lazy_loops_ms": _stats(one_times),
+            "value": rows / (_pct(one_times, 50) / 1e3),
+            "kernel": "decode_loops", "avg_launch_ms": ms1 / max(n1, 1),
+            "achieved_GBps": attend_bytes / (ms1 / max(n1, 1) / 1e3) / 1e9 if n1 else None,
+            "note": "the lazy loops' chain reads (attend_bytes summed over the loops) per launch of the one kernel",
+        }
     if args.cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

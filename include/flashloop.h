@@ -239,6 +239,49 @@ uint64_t  flashloop_attend_workspace_bytes(const fl_attend_args* args);
 fl_status flashloop_attend(const fl_attend_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* flashloop_decode_loops -- lazy decode loops first..last in one launch.    */
+/* (section "FlashLoop combines three kinds of savings", paragraphs 2-4:     */
+/* keys chosen from the previous loop's statistics, a base plus low-bit      */
+/* corrections, the update and compression fused with the compute)          */
+/* One new token per sequence (active_idx[s]).  The call does what, for      */
+/* l = first..last in order, flashloop_select(KEYS, colmass -> the top       */
+/* n_keys per (sequence, head)) followed by flashloop_attend(LAZY, version  */
+/* l, q_cur = q[l], q_prev = q[l-1], fused commit of k_new[l], v_new[l] at   */
+/* slot commit_slot_base[l], commit_reset 0) would do, with the same key     */
+/* sets and the same output bits, in one kernel: each (sequence, head)       */
+/* keeps its column-mass row, key list and the token's K/V versions on chip  */
+/* from loop to loop.  Per-loop queries and new rows are inputs (the shared  */
+/* block that produces them is outside this library).                        */
+/* In: o, lse, colmass after loop first-1 (and the store through it); out:   */
+/* after loop last.  key_idx_out (optional) receives each loop's keys.       */
+/* Limits (FL_ERR_UNSUPPORTED): bf16 store, head_dim 128, 4- or 2-bit codes, */
+/* last <= 5, n_keys <= 1536, n_tokens <= 8192.  exit_flags are read once,   */
+/* at entry (a flagged sequence is skipped for every loop).  No workspace.   */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const fl_kv_desc* kv;
+  int32_t first_version;        /* >= 2 */
+  int32_t last_version;         /* first_version..n_versions, <= 5 */
+  const void* q[FL_MAX_VERSIONS + 1];       /* q[l] for l = first-1..last: device [n_seq][R][H][d] bf16 */
+  int32_t q_layout;             /* fl_row_layout: R = N (row = token) or R = 1 */
+  const int32_t* active_idx;    /* [n_seq] device: the new token's position */
+  int32_t n_keys;               /* 1..N keys per (sequence, head) and loop */
+  float* o;                     /* [n_seq][R][H][d] */
+  float* lse;                   /* [n_seq][R][H] */
+  int32_t o_layout;             /* fl_row_layout */
+  float* colmass;               /* [n_seq][H][N] */
+  const void* k_new[FL_MAX_VERSIONS + 1];   /* k_new[l], v_new[l] for l = first..last: [n_seq][R][H][d] bf16 */
+  const void* v_new[FL_MAX_VERSIONS + 1];
+  int32_t kv_layout;            /* fl_row_layout of k_new / v_new */
+  int32_t commit_slot_base[FL_MAX_VERSIONS + 1];  /* [l]: the token's record slot in layer l (< layer_cap[l]) */
+  int32_t* key_idx_out;         /* optional [last-first+1][n_seq][H][n_keys] device */
+  int32_t formula;              /* fl_formula */
+  const int32_t* exit_flags;    /* optional [n_seq] device */
+} fl_decode_loops_args;
+
+fl_status flashloop_decode_loops(const fl_decode_loops_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* flashloop_attend_noalloc -- flashloop_attend for callers that cannot     */
 /* allocate device memory (code under HIP graph capture, serving loops or    */
 /* harnesses that forbid hipMalloc).  Same arguments, same kernels, same     */

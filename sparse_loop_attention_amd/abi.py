@@ -28,7 +28,7 @@ FL_ROWS_BY_TOKEN, FL_ROWS_COMPACT = 0, 1
 EXPORTS = ("flashloop_kv_layout", "flashloop_kv_arena_bytes", "flashloop_kv_commit", "flashloop_select",
            "flashloop_attend_workspace_bytes", "flashloop_attend", "flashloop_last_error",
            "flashloop_abi_version", "flashloop_timing_enable", "flashloop_timing_read", "flashloop_exit_check",
-           "flashloop_attend_noalloc")
+           "flashloop_attend_noalloc", "flashloop_decode_loops")
 STATIC_SCRATCH_BYTES = 128 << 20        # FLASHLOOP_STATIC_SCRATCH_BYTES
 
 
@@ -77,6 +77,18 @@ class fl_exit_args(C.Structure):
                 ("exit_flags", C.c_void_p), ("max_change", C.c_void_p)]
 
 
+V = MAX_VERSIONS + 1
+
+
+class fl_decode_loops_args(C.Structure):
+    _fields_ = [("kv", C.POINTER(fl_kv_desc)), ("first_version", C.c_int32), ("last_version", C.c_int32),
+                ("q", C.c_void_p * V), ("q_layout", C.c_int32), ("active_idx", C.c_void_p), ("n_keys", C.c_int32),
+                ("o", C.c_void_p), ("lse", C.c_void_p), ("o_layout", C.c_int32), ("colmass", C.c_void_p),
+                ("k_new", C.c_void_p * V), ("v_new", C.c_void_p * V), ("kv_layout", C.c_int32),
+                ("commit_slot_base", C.c_int32 * V), ("key_idx_out", C.c_void_p), ("formula", C.c_int32),
+                ("exit_flags", C.c_void_p)]
+
+
 class FlashLoopError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"flashloop status {status}: {msg}")
@@ -102,6 +114,7 @@ def lib():
         L.flashloop_attend_workspace_bytes.restype = C.c_uint64
         L.flashloop_attend.argtypes = [C.POINTER(fl_attend_args), C.c_void_p]
         L.flashloop_attend_noalloc.argtypes = [C.POINTER(fl_attend_args), C.c_void_p]
+        L.flashloop_decode_loops.argtypes = [C.POINTER(fl_decode_loops_args), C.c_void_p]
         L.flashloop_last_error.restype = C.c_char_p
         L.flashloop_abi_version.restype = C.c_int32
         L.flashloop_timing_enable.argtypes = [C.c_int32]
@@ -109,7 +122,7 @@ def lib():
         L.flashloop_timing_read.restype = C.c_int32
         L.flashloop_exit_check.argtypes = [C.POINTER(fl_exit_args), C.c_void_p]
         for f in ("flashloop_kv_layout", "flashloop_kv_commit", "flashloop_select", "flashloop_attend",
-                  "flashloop_exit_check", "flashloop_attend_noalloc"):
+                  "flashloop_exit_check", "flashloop_attend_noalloc", "flashloop_decode_loops"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -275,6 +288,33 @@ def attend(a: fl_attend_args, stream=None) -> None:
 def attend_noalloc(a: fl_attend_args, stream=None) -> None:
     """flashloop_attend on the library's own per-GPU scratch (a.workspace is ignored)."""
     _check(lib().flashloop_attend_noalloc(C.byref(a), _stream(stream)))
+
+
+def decode_loops(kv: KVStore, first: int, last: int, q: dict, active_idx: torch.Tensor, n_keys: int,
+                 o: torch.Tensor, lse: torch.Tensor, colmass: torch.Tensor, k_new: dict, v_new: dict,
+                 slot_base: dict, keys_out: Optional[torch.Tensor] = None, q_compact: bool = True,
+                 o_compact: bool = True, kv_compact: bool = False, formula: str = "column",
+                 exit_flags: Optional[torch.Tensor] = None, stream=None) -> None:
+    """flashloop_decode_loops: lazy decode loops first..last in one launch.
+    q[l] for l = first-1..last, k_new[l], v_new[l], slot_base[l] for
+    l = first..last (dicts of tensors / ints, indexed by loop)."""
+    a = fl_decode_loops_args()
+    a.kv = C.pointer(kv.desc)
+    a.first_version, a.last_version = first, last
+    for l in range(first - 1, last + 1):
+        a.q[l] = _ptr(q[l])
+    for l in range(first, last + 1):
+        a.k_new[l], a.v_new[l] = _ptr(k_new[l]), _ptr(v_new[l])
+        a.commit_slot_base[l] = slot_base[l]
+    a.q_layout = FL_ROWS_COMPACT if q_compact else FL_ROWS_BY_TOKEN
+    a.o_layout = FL_ROWS_COMPACT if o_compact else FL_ROWS_BY_TOKEN
+    a.kv_layout = FL_ROWS_COMPACT if kv_compact else FL_ROWS_BY_TOKEN
+    a.active_idx, a.n_keys = _ptr(active_idx), n_keys
+    a.o, a.lse, a.colmass = _ptr(o), _ptr(lse), _ptr(colmass)
+    a.key_idx_out = _ptr(keys_out)
+    a.formula = FORMULAS[formula]
+    a.exit_flags = _ptr(exit_flags)
+    _check(lib().flashloop_decode_loops(C.byref(a), _stream(stream)))
 
 
 def exit_check(exit_flags: torch.Tensor, threshold: float, scores: Optional[torch.Tensor] = None,

@@ -11,6 +11,7 @@
 
 #include "flashloop.h"
 #include "fl_launch.hpp"
+#include "fl_rows.hpp"
 
 namespace {
 
@@ -293,6 +294,63 @@ static fl_status attend_impl(const fl_attend_args* a, void* stream, bool static_
 fl_status flashloop_attend(const fl_attend_args* a, void* stream) { return attend_impl(a, stream, false); }
 
 fl_status flashloop_attend_noalloc(const fl_attend_args* a, void* stream) { return attend_impl(a, stream, true); }
+
+fl_status flashloop_decode_loops(const fl_decode_loops_args* a, void* stream) {
+  if (!a) return fail(FL_ERR_ARG, "decode_loops args are NULL");
+  fl_kv_layout lay;
+  fl_status st = check_arena(a->kv, &lay);
+  if (st != FL_OK) return st;
+  const fl_kv_desc& d = *a->kv;
+  if (a->first_version < 2 || a->last_version < a->first_version || a->last_version > d.n_versions)
+    return fail(FL_ERR_ARG, "decode_loops: versions %d..%d invalid (2 <= first <= last <= %d)", a->first_version,
+                a->last_version, d.n_versions);
+  if (a->n_keys < 1 || a->n_keys > d.n_tokens) return fail(FL_ERR_ARG, "decode_loops: n_keys outside 1..n_tokens");
+  if (!a->active_idx || !aligned(a->active_idx, 4)) return fail(FL_ERR_ARG, "decode_loops: NULL active_idx");
+  if (!a->o || !a->lse || !a->colmass || !aligned(a->o, 16))
+    return fail(FL_ERR_ARG, "decode_loops: NULL or misaligned o, lse or colmass");
+  if (a->q_layout != FL_ROWS_BY_TOKEN && a->q_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "decode_loops: q_layout");
+  if (a->o_layout != FL_ROWS_BY_TOKEN && a->o_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "decode_loops: o_layout");
+  if (a->kv_layout != FL_ROWS_BY_TOKEN && a->kv_layout != FL_ROWS_COMPACT) return fail(FL_ERR_ARG, "decode_loops: kv_layout");
+  if (a->formula != FL_FORMULA_COLUMN && a->formula != FL_FORMULA_MIXTURE) return fail(FL_ERR_ARG, "decode_loops: formula");
+  if (a->exit_flags && !aligned(a->exit_flags, 4)) return fail(FL_ERR_ARG, "decode_loops: exit_flags must be 4-byte aligned");
+  if (a->key_idx_out && !aligned(a->key_idx_out, 4)) return fail(FL_ERR_ARG, "decode_loops: key_idx_out misaligned");
+  for (int l = a->first_version - 1; l <= a->last_version; ++l)
+    if (!a->q[l] || !aligned(a->q[l], 16)) return fail(FL_ERR_ARG, "decode_loops: q[%d] NULL or misaligned", l);
+  for (int l = a->first_version; l <= a->last_version; ++l) {
+    if (!a->k_new[l] || !a->v_new[l] || !aligned(a->k_new[l], 16) || !aligned(a->v_new[l], 16))
+      return fail(FL_ERR_ARG, "decode_loops: k_new[%d] / v_new[%d] NULL or misaligned", l, l);
+    if (a->commit_slot_base[l] < 0 || a->commit_slot_base[l] >= d.layer_cap[l])
+      return fail(FL_ERR_ARG, "decode_loops: commit_slot_base[%d] = %d outside layer_cap[%d] = %d", l,
+                  a->commit_slot_base[l], l, d.layer_cap[l]);
+  }
+  fl::KvView kv = fl::make_view(d, lay);
+  kv.exit_flags = a->exit_flags;
+  fl::DecLoopsArgs x{};
+  x.arena = static_cast<uint8_t*>(d.arena);
+  x.act = a->active_idx;
+  x.first = a->first_version;
+  x.last = a->last_version;
+  for (int l = 0; l <= FL_MAX_VERSIONS; ++l) {
+    x.q[l] = a->q[l];
+    x.k_new[l] = a->k_new[l];
+    x.v_new[l] = a->v_new[l];
+    x.slot_base[l] = a->commit_slot_base[l];
+  }
+  x.q_compact = a->q_layout == FL_ROWS_COMPACT;
+  x.o_compact = a->o_layout == FL_ROWS_COMPACT;
+  x.kv_compact = a->kv_layout == FL_ROWS_COMPACT;
+  x.n_keys = a->n_keys;
+  x.o = a->o; x.lse = a->lse; x.colmass = a->colmass;
+  x.keys_out = a->key_idx_out;
+  x.scale = 1.0f / sqrtf(static_cast<float>(d.head_dim));
+  x.mixture = a->formula == FL_FORMULA_MIXTURE;
+  hipError_t e = hipSuccess;
+  if (!fl::launch_decode_loops(x, kv, static_cast<hipStream_t>(stream), &e))
+    return fail(FL_ERR_UNSUPPORTED, "decode_loops: needs a bf16 store, head_dim 128, 4- or 2-bit codes, versions "
+                "up to 5, n_keys <= 1536 and n_tokens <= 8192");
+  if (e != hipSuccess) return hip_fail(e, "decode_loops launch");
+  return ok();
+}
 
 fl_status flashloop_exit_check(const fl_exit_args* a, void* stream) {
   if (!a) return fail(FL_ERR_ARG, "exit args are NULL");

@@ -34,6 +34,7 @@
 #include "fl_commit.hpp"
 #include "fl_rows.hpp"
 #include "fl_timing.hpp"
+#include "fl_topk.hpp"
 
 namespace fl {
 
@@ -43,6 +44,7 @@ constexpr int kDecWaves = 8;
 constexpr int kDecD = 128;                 // head_dim of this kernel
 constexpr int kDecMaxKeys = 1536;          // staged keys per (sequence, head): 28 bytes of LDS each
 constexpr int kDecMaxLayers = 4;           // delta layers walked (versions 2..5)
+constexpr int kDecLoopsMaxN = 8192;        // multi-loop kernel: the column-mass row (32 KB) in LDS
 constexpr size_t kDecMaxFullLds = 40960;   // full loop: logits of every key (N <= 10240) in LDS
 constexpr uint32_t kOut = 0x80000000u;     // an offset past every range: the load returns zeros
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
@@ -119,73 +121,39 @@ __device__ __forceinline__ void axpy_bf16x8(float acc[8], float c, float w, cons
 
 }  // namespace
 
-// NL = version - 1 delta layers (versions 2..v); the previous version is the
-// chain through layer NL - 1.
-template <int NL, bool FUSE, int BITS>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(4)))
-void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
+// One lazy loop, version v = NL + 1, of one (sequence s, head h) row: the
+// selected keys' positions and slot rows are staged in LDS (s_j, s_sl; the
+// first cnt are visible).  Updates the row's output o_row (global) and its
+// column-mass row c_row (global, or LDS in the multi-loop kernel) and returns
+// whether the row updated and its new lse.  The sequence's new token i takes
+// version v from k_new/v_new and the commit arithmetic (FUSE), or versions
+// v-1 and v from trk_prev/trk_cur ([K, V][kDecD] float32 in LDS; TRACK: the
+// multi-loop kernel keeps the token's chain on chip, its records being
+// written by this same workgroup).  Every thread of the workgroup calls it.
+struct StepOut {
+  bool valid;
+  float lse;
+};
+
+// z is 0; the multi-loop kernel passes an opaque 0 made at the start of each
+// version's code, so that the layer table is read there (reads at fixed
+// kernel-argument offsets would be shared by every version's code and kept
+// live throughout, in scalar registers that then spill).
+template <int NL, bool FUSE, int BITS, bool TRACK>
+__device__ __forceinline__ StepOut lazy_step(const KvView& kv, const CommitArgs& cm, int s, int h, int i,
+                                             const void* q_cur, const void* q_prev, int q_compact, float scale,
+                                             int mixture, float* o_row, float lse_prev, const int32_t* s_j,
+                                             const i32x4* s_sl, int cnt, float* lg_cur, float* lg_prev,
+                                             float (*s_mzm)[3], float (*s_acc)[2][kDecD], float* c_row,
+                                             const float* trk_prev, const float* trk_cur, int z = 0) {
   const int H = kv.H;
-  // all heads of a sequence on one XCD (workgroup b runs on XCD b % 8): the
-  // slot rows of keys that several heads select are then read once into
-  // that XCD's L2
-  int s, h;
-  if (kv.n_seq >= 8) {
-    const int local = blockIdx.x >> 3;
-    s = (blockIdx.x & 7) + 8 * (local / H);
-    h = local % H;
-    if (s >= kv.n_seq) return;
-  } else {
-    s = blockIdx.x / H;
-    h = blockIdx.x % H;
-  }
-  const int sh = s * H + h;
-  if (kv.exited(s)) return;                               // uniform per workgroup
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, p = lane & 15;
-  const int nk = a.n_keys;
-  const int i = a.act[s];                                 // the sequence's only active row
-  const int32_t* sel = a.keys + static_cast<int64_t>(sh) * nk;
-
-  extern __shared__ __align__(16) uint8_t s_dyn[];
-  i32x4* s_sl = reinterpret_cast<i32x4*>(s_dyn);         // [nk] slot rows (layers 2..5)
-  int32_t* s_j = reinterpret_cast<int32_t*>(s_sl + nk);  // [nk] key positions
-  float* lg_cur = reinterpret_cast<float*>(s_j + nk);    // [nk] logits, this loop
-  float* lg_prev = lg_cur + nk;                           // [nk] logits, previous loop
-  __shared__ float s_mzm[kDecWaves][3];
-  __shared__ float s_acc[kDecWaves][2][kDecD];
-
-  if (FUSE && wave == kDecWaves - 1) {
-    // this row's records of layer `version` (groups 0, 1: K, V) and, for
-    // head 0, its slot-table entry; the other waves stage the keys meanwhile
-    if (g < 2) {
-      const int64_t src_rows = cm.src_compact ? 1 : kv.N;
-      const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? 0 : i)) * H + h) * kDecD;
-      commit_row<FL_BF16>(kv, cm.arena, a.version, s, i, h, g, cm.slot_base, g ? cm.v_new : cm.k_new, src_elem, p);
-    }
-    if (h == 0) {
-      int32_t* col = reinterpret_cast<int32_t*>(cm.arena + kv.slot_table) + (a.version - 2);
-      if (cm.reset) {
-        for (int jj = lane; jj < kv.N; jj += 64)
-          col[(static_cast<int64_t>(s) * kv.N + jj) * kv.slot_pitch] = jj == i ? cm.slot_base : -1;
-      } else if (lane == 0) {
-        col[(static_cast<int64_t>(s) * kv.N + i) * kv.slot_pitch] = cm.slot_base;
-      }
-    }
-  } else {
-    for (int t = tid; t < nk; t += 64 * (FUSE ? kDecWaves - 1 : kDecWaves)) {
-      const int j = sel[t];
-      s_j[t] = j;
-      s_sl[t] = *reinterpret_cast<const i32x4*>(kv.slot_row(s, j));
-    }
-  }
-  __syncthreads();
-  const int cnt = wave_count_le(s_j, nk, i);              // visible keys: a prefix of the ascending list
-
   // per-sequence ranges of the base rows and of each layer's records
   const uint8_t* A = kv.arena;
   const int64_t row_bytes = static_cast<int64_t>(kv.N) * kDecD * 2;
   const int64_t rowb = (static_cast<int64_t>(s) * H + h) * row_bytes;
-  const __amdgpu_buffer_rsrc_t rK = range_of(A + kv.base[0] + rowb, static_cast<uint32_t>(row_bytes));
-  const __amdgpu_buffer_rsrc_t rV = range_of(A + kv.base[1] + rowb, static_cast<uint32_t>(row_bytes));
+  const __amdgpu_buffer_rsrc_t rK = range_of(A + kv.base[z] + rowb, static_cast<uint32_t>(row_bytes));
+  const __amdgpu_buffer_rsrc_t rV = range_of(A + kv.base[z + 1] + rowb, static_cast<uint32_t>(row_bytes));
   const int ng = kDecD >> (3 + kv.gshift);                // scales per record: 4 (group 32) or 2 (group 64)
   constexpr uint32_t kCodeBytes = kDecD * BITS / 8;       // codes of one head row
   const uint32_t rec_code_bytes = H * 2 * kCodeBytes;    // K and V codes of every head of one slot
@@ -194,9 +162,10 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
   uint32_t cap[NL];
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
-    cap[l] = static_cast<uint32_t>(kv.cap[l + 2]);
-    rC[l] = range_of(A + kv.codes[l + 2] + static_cast<int64_t>(s) * cap[l] * rec_code_bytes, cap[l] * rec_code_bytes);
-    rS[l] = range_of(A + kv.scales[l + 2] + static_cast<int64_t>(s) * cap[l] * rec_scale_bytes,
+    cap[l] = static_cast<uint32_t>(kv.cap[l + 2 + z]);
+    rC[l] = range_of(A + kv.codes[l + 2 + z] + static_cast<int64_t>(s) * cap[l] * rec_code_bytes,
+                     cap[l] * rec_code_bytes);
+    rS[l] = range_of(A + kv.scales[l + 2 + z] + static_cast<int64_t>(s) * cap[l] * rec_scale_bytes,
                      cap[l] * rec_scale_bytes);
   }
   const uint32_t lane_b = 16 * p;
@@ -205,19 +174,16 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
   // a reset commit clears layer v for every token it does not write: the walk stops at v-1
   const bool walk_v = !(FUSE && cm.reset);
 
-  const int64_t qoff = ((static_cast<int64_t>(s) * (a.q_compact ? 1 : kv.N) + (a.q_compact ? 0 : i)) * H + h) * kDecD;
-  const u32x4_t qc = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q_cur) + qoff + 8 * p);
-  const u32x4_t qp = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q_prev) + qoff + 8 * p);
-  const int64_t orow = (static_cast<int64_t>(s) * (a.o_compact ? 1 : kv.N) + (a.o_compact ? 0 : i)) * H + h;
-  float* o_row = a.o + orow * kDecD;
-  float* lse_ptr = a.lse + orow;
-  const float lse_prev = *lse_ptr;
+  const int64_t qoff = ((static_cast<int64_t>(s) * (q_compact ? 1 : kv.N) + (q_compact ? 0 : i)) * H + h) * kDecD;
+  const u32x4_t qc = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q_cur) + qoff + 8 * p);
+  const u32x4_t qp = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q_prev) + qoff + 8 * p);
 
   auto issue = [&](int k, KeyLoads<NL>& r) {
     const int t = wave * 4 + g + 32 * k;
-    const bool ok = t < cnt;
-    const int tt = ok ? t : 0;
+    const int tt = t < cnt ? t : 0;
     const int j = s_j[tt];
+    // TRACK: the new token's versions come from LDS, its loads read zeros
+    const bool ok = t < cnt && !(TRACK && j == i);
     const i32x4 sl = s_sl[tt];
     const uint32_t ob = ok ? static_cast<uint32_t>(j) * (kDecD * 2) + lane_b : kOut;
     r.kb = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rK, ob, 0, 0));
@@ -245,16 +211,24 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
   auto consume = [&](int k, const KeyLoads<NL>& r) {
     const int t = wave * 4 + g + 32 * k;
     if (t >= cnt) return;                                 // uniform per 16-lane group
-    const bool active = FUSE && s_j[t] == i;              // the new token: version v from k_new / v_new
+    const bool active = (FUSE || TRACK) && s_j[t] == i;   // the new token: version v from its new row
     float x[8];
     uint32_t pk[4];
-    unpack_bf16x8(r.kb, x);
+    if (TRACK && active) {
 #pragma unroll
-    for (int l = 0; l + 1 < NL; ++l) add_layer<BITS>(r.kc[l], r.ks[l], x);
+      for (int e = 0; e < 8; ++e) x[e] = trk_prev[8 * p + e];
+    } else {
+      unpack_bf16x8(r.kb, x);
+#pragma unroll
+      for (int l = 0; l + 1 < NL; ++l) add_layer<BITS>(r.kc[l], r.ks[l], x);
+    }
     round_pack8(x, pk);
-    const float sp = group_sum<16>(dot_bf16x8(pk, qp)) * a.scale;
+    const float sp = group_sum<16>(dot_bf16x8(pk, qp)) * scale;
     int64_t src = 0;
-    if (active) {
+    if (TRACK && active) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = trk_cur[8 * p + e];
+    } else if (active) {
       const int64_t src_rows = cm.src_compact ? 1 : kv.N;
       src = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? 0 : i)) * H + h) * kDecD + 8 * p;
       float xn[8], xo[8];
@@ -266,7 +240,7 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
       add_layer<BITS>(r.kc[NL - 1], r.ks[NL - 1], x);
     }
     round_pack8(x, pk);
-    const float sc = group_sum<16>(dot_bf16x8(pk, qc)) * a.scale;
+    const float sc = group_sum<16>(dot_bf16x8(pk, qc)) * scale;
     if (p == 0) { lg_cur[t] = sc; lg_prev[t] = sp; }
     const float Mn = fmaxf(M, sc);
     const float corr = __expf(M - Mn);
@@ -275,12 +249,20 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
     Z = fmaf(Z, corr, w);
     m += pp;
     M = Mn;
-    unpack_bf16x8(r.vb, x);
+    if (TRACK && active) {
 #pragma unroll
-    for (int l = 0; l + 1 < NL; ++l) add_layer<BITS>(r.vc[l], r.vs[l], x);
+      for (int e = 0; e < 8; ++e) x[e] = trk_prev[kDecD + 8 * p + e];
+    } else {
+      unpack_bf16x8(r.vb, x);
+#pragma unroll
+      for (int l = 0; l + 1 < NL; ++l) add_layer<BITS>(r.vc[l], r.vs[l], x);
+    }
     round_pack8(x, pk);
     axpy_bf16x8(accp, 1.0f, pp, pk);
-    if (active) {
+    if (TRACK && active) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = trk_cur[kDecD + 8 * p + e];
+    } else if (active) {
       float xn[8], xo[8];
       load8<FL_BF16>(cm.v_new, src, xn);
       advance8(kv, xn, x, true, xo);
@@ -351,20 +333,208 @@ void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
       ov = fmaf(s_acc[w][0][tid], cw, ov);
       av += s_acc[w][1][tid];
     }
-    if (valid) o_row[tid] = fmaf(mt / Zt, ov, a.mixture ? (1.0f - mt) * o_row[tid] : o_row[tid] - av);
+    if (valid) o_row[tid] = fmaf(mt / Zt, ov, mixture ? (1.0f - mt) * o_row[tid] : o_row[tid] - av);
   }
   const float lnew = valid ? Mt + __logf(Zt) - __logf(mt) : lse_prev;
-  if (tid == 0) {
-    if (valid) *lse_ptr = lnew;
-    float* st = a.stat + static_cast<int64_t>(sh) * 4;
-    st[0] = lse_prev; st[1] = lnew; st[2] = valid ? 1.0f : 0.0f; st[3] = 0.0f;
-  }
   // column mass of the row: c_j += p_ij - p'_ij over the visible selected keys
-  if (!valid) return;
-  float* c = a.colmass + static_cast<int64_t>(sh) * kv.N;
-  const float f = mt / Zt;
-  for (int t = tid; t < cnt; t += 64 * kDecWaves)
-    c[s_j[t]] += f * __expf(lg_cur[t] - Mt) - __expf(lg_prev[t] - lse_prev);
+  if (valid) {
+    const float f = mt / Zt;
+    for (int t = tid; t < cnt; t += 64 * kDecWaves)
+      c_row[s_j[t]] += f * __expf(lg_cur[t] - Mt) - __expf(lg_prev[t] - lse_prev);
+  }
+  return {valid, lnew};
+}
+
+// (sequence, head) of a decode workgroup: all heads of a sequence on one XCD
+// (workgroup b runs on XCD b % 8), whose L2 then serves the slot rows of keys
+// that several heads select.  False for padding workgroups.
+__device__ __forceinline__ bool dec_map(const KvView& kv, int& s, int& h) {
+  const int H = kv.H;
+  if (kv.n_seq >= 8) {
+    const int local = blockIdx.x >> 3;
+    s = (blockIdx.x & 7) + 8 * (local / H);
+    h = local % H;
+    return s < kv.n_seq;
+  }
+  s = blockIdx.x / H;
+  h = blockIdx.x % H;
+  return true;
+}
+
+// NL = version - 1 delta layers (versions 2..v); the previous version is the
+// chain through layer NL - 1.
+template <int NL, bool FUSE, int BITS>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void k_decode_lazy(KvView kv, RowArgs a, CommitArgs cm) {
+  const int H = kv.H;
+  int s, h;
+  if (!dec_map(kv, s, h)) return;
+  const int sh = s * H + h;
+  if (kv.exited(s)) return;                               // uniform per workgroup
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, p = lane & 15;
+  const int nk = a.n_keys;
+  const int i = a.act[s];                                 // the sequence's only active row
+  const int32_t* sel = a.keys + static_cast<int64_t>(sh) * nk;
+
+  extern __shared__ __align__(16) uint8_t s_dyn[];
+  i32x4* s_sl = reinterpret_cast<i32x4*>(s_dyn);         // [nk] slot rows (layers 2..5)
+  int32_t* s_j = reinterpret_cast<int32_t*>(s_sl + nk);  // [nk] key positions
+  float* lg_cur = reinterpret_cast<float*>(s_j + nk);    // [nk] logits, this loop
+  float* lg_prev = lg_cur + nk;                           // [nk] logits, previous loop
+  __shared__ float s_mzm[kDecWaves][3];
+  __shared__ float s_acc[kDecWaves][2][kDecD];
+
+  if (FUSE && wave == kDecWaves - 1) {
+    // this row's records of layer `version` (groups 0, 1: K, V) and, for
+    // head 0, its slot-table entry; the other waves stage the keys meanwhile
+    if (g < 2) {
+      const int64_t src_rows = cm.src_compact ? 1 : kv.N;
+      const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? 0 : i)) * H + h) * kDecD;
+      commit_row<FL_BF16>(kv, cm.arena, a.version, s, i, h, g, cm.slot_base, g ? cm.v_new : cm.k_new, src_elem, p);
+    }
+    if (h == 0) {
+      int32_t* col = reinterpret_cast<int32_t*>(cm.arena + kv.slot_table) + (a.version - 2);
+      if (cm.reset) {
+        for (int jj = lane; jj < kv.N; jj += 64)
+          col[(static_cast<int64_t>(s) * kv.N + jj) * kv.slot_pitch] = jj == i ? cm.slot_base : -1;
+      } else if (lane == 0) {
+        col[(static_cast<int64_t>(s) * kv.N + i) * kv.slot_pitch] = cm.slot_base;
+      }
+    }
+  } else {
+    for (int t = tid; t < nk; t += 64 * (FUSE ? kDecWaves - 1 : kDecWaves)) {
+      const int j = sel[t];
+      s_j[t] = j;
+      s_sl[t] = *reinterpret_cast<const i32x4*>(kv.slot_row(s, j));
+    }
+  }
+  __syncthreads();
+  const int cnt = wave_count_le(s_j, nk, i);              // visible keys: a prefix of the ascending list
+  const int64_t orow = (static_cast<int64_t>(s) * (a.o_compact ? 1 : kv.N) + (a.o_compact ? 0 : i)) * H + h;
+  float* lse_ptr = a.lse + orow;
+  const float lse_prev = *lse_ptr;
+  const StepOut r = lazy_step<NL, FUSE, BITS, false>(kv, cm, s, h, i, a.q_cur, a.q_prev, a.q_compact, a.scale,
+                                                     a.mixture, a.o + orow * kDecD, lse_prev, s_j, s_sl, cnt,
+                                                     lg_cur, lg_prev, s_mzm, s_acc,
+                                                     a.colmass + static_cast<int64_t>(sh) * kv.N, nullptr, nullptr);
+  if (tid == 0) {
+    if (r.valid) *lse_ptr = r.lse;
+    float* st = a.stat + static_cast<int64_t>(sh) * 4;
+    st[0] = lse_prev; st[1] = r.lse; st[2] = r.valid ? 1.0f : 0.0f; st[3] = 0.0f;
+  }
+}
+
+// LDS of the multi-loop kernel besides its dynamic part (the column-mass row
+// and the staged keys).
+struct LoopsShared {
+  float mzm[kDecWaves][3];
+  float acc[kDecWaves][2][kDecD];
+  float trk[2][2][kDecD];               // the new token's versions: [version parity][K, V][d]
+  float lse;
+  TopkLds<64 * kDecWaves> topk;
+};
+
+// Loop L of the multi-loop kernel (L is a template argument so that the
+// per-loop pointers are read at fixed kernel-argument offsets).
+template <int L, int BITS, int EPT>
+__device__ __forceinline__ void loops_iter(const KvView& kv, const DecLoopsArgs& a, int s, int h, int i,
+                                           int64_t orow, float* s_c, i32x4* s_sl, int32_t* s_j, float* lg_cur,
+                                           float* lg_prev, LoopsShared& sm) {
+  const int H = kv.H, N = kv.N, nk = a.n_keys, sh = s * H + h;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, p = lane & 15;
+  int z;                                                  // an opaque 0 (see lazy_step)
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  __syncthreads();                                        // the previous loop's column mass is in place
+  topk_block<float, EPT, 64 * kDecWaves>(N, nk, [&](int64_t t) { return s_c[t]; },
+                                         [&](int pos, int32_t idx) { s_j[pos] = idx; }, sm.topk);
+  __syncthreads();
+  const float* trk_prev = &sm.trk[(L - 1) & 1][0][0];
+  float* trk_cur = &sm.trk[L & 1][0][0];
+  if (wave == kDecWaves - 1) {
+    // the token's layer-L records (groups 0, 1: K, V) from its version L-1,
+    // and version L for this loop; head 0 also sets its slot-table entry
+    if (g < 2) {
+      const int64_t src_rows = a.kv_compact ? 1 : N;
+      const int64_t src = ((static_cast<int64_t>(s) * src_rows + (a.kv_compact ? 0 : i)) * H + h) * kDecD + 8 * p;
+      float xn[8], xp[8], xo[8];
+      load8<FL_BF16>(g ? a.v_new[L + z] : a.k_new[L + z], src, xn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xp[e] = trk_prev[g * kDecD + 8 * p + e];
+      commit_advance8(kv, a.arena, L, s, a.slot_base[L + z], h, g, xn, xp, true, p, xo);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) trk_cur[g * kDecD + 8 * p + e] = xo[e];
+    }
+    if (h == 0 && lane == 0)
+      reinterpret_cast<int32_t*>(a.arena + kv.slot_table)[(static_cast<int64_t>(s) * N + i) * kv.slot_pitch + (L - 2)] =
+          a.slot_base[L + z];
+  } else {
+    for (int t = tid; t < nk; t += 64 * (kDecWaves - 1))
+      s_sl[t] = *reinterpret_cast<const i32x4*>(kv.slot_row(s, s_j[t]));
+  }
+  if (a.keys_out) {
+    int32_t* ko = a.keys_out + (static_cast<int64_t>(L - a.first) * kv.n_seq * H + sh) * nk;
+    for (int t = tid; t < nk; t += 64 * kDecWaves) ko[t] = s_j[t];
+  }
+  __syncthreads();
+  const int cnt = wave_count_le(s_j, nk, i);
+  const float lse_prev = sm.lse;
+  CommitArgs cm{};
+  const StepOut r = lazy_step<L - 1, false, BITS, true>(kv, cm, s, h, i, a.q[L + z], a.q[L - 1 + z], a.q_compact,
+                                                        a.scale, a.mixture, a.o + orow * kDecD, lse_prev, s_j, s_sl,
+                                                        cnt, lg_cur, lg_prev, sm.mzm, sm.acc, s_c, trk_prev, trk_cur, z);
+  __syncthreads();                                        // every thread has read the previous lse
+  if (tid == 0) sm.lse = r.lse;
+}
+
+// Lazy loops first..last of one new token per sequence in one launch (one
+// workgroup per (sequence, head), as k_decode_lazy).  Per loop: the keys are
+// the top n_keys of the row's column mass (kept in LDS from loop to loop),
+// the token's layer-l record is written (and its version l derived) by the
+// last wave while the others stage the keys' slot rows, then the step above
+// runs with the token's versions l-1 and l taken from LDS.  The column-mass
+// row and lse leave the chip once, after the last loop.  Keys are the same
+// sets, and every output the same bits, as loops of select_keys +
+// k_decode_lazy.
+template <int BITS, int EPT>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void k_decode_loops(KvView kv, DecLoopsArgs a) {
+  const int H = kv.H;
+  int s, h;
+  if (!dec_map(kv, s, h)) return;
+  const int sh = s * H + h;
+  if (kv.exited(s)) return;                               // uniform per workgroup
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, p = lane & 15;
+  const int nk = a.n_keys, N = kv.N;
+  const int i = a.act[s];
+
+  extern __shared__ __align__(16) uint8_t s_dyn[];
+  float* s_c = reinterpret_cast<float*>(s_dyn);                  // [N] column-mass row
+  i32x4* s_sl = reinterpret_cast<i32x4*>(s_c + ((N + 3) & ~3));  // [nk] slot rows
+  int32_t* s_j = reinterpret_cast<int32_t*>(s_sl + nk);          // [nk] key positions
+  float* lg_cur = reinterpret_cast<float*>(s_j + nk);
+  float* lg_prev = lg_cur + nk;
+  __shared__ LoopsShared sm;
+
+  float* c_glob = a.colmass + static_cast<int64_t>(sh) * N;
+  for (int t = tid; t < N; t += 64 * kDecWaves) s_c[t] = c_glob[t];
+  const int64_t orow = (static_cast<int64_t>(s) * (a.o_compact ? 1 : N) + (a.o_compact ? 0 : i)) * H + h;
+  if (tid == 0) sm.lse = a.lse[orow];
+  // the token's version first-1 (its records so far were written by earlier calls)
+  if (wave == 0 && g < 2) {
+    float x[8] = {};
+    recon8<FL_BF16>(kv, g, s, h, i, a.first - 1, p, x, nullptr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.trk[(a.first - 1) & 1][g][8 * p + e] = x[e];
+  }
+  // straight-line code per version (a loop over the versions made the
+  // compiler keep every loop-invariant argument live across all of them)
+  if (a.first <= 2 && 2 <= a.last) loops_iter<2, BITS, EPT>(kv, a, s, h, i, orow, s_c, s_sl, s_j, lg_cur, lg_prev, sm);
+  if (a.first <= 3 && 3 <= a.last) loops_iter<3, BITS, EPT>(kv, a, s, h, i, orow, s_c, s_sl, s_j, lg_cur, lg_prev, sm);
+  if (a.first <= 4 && 4 <= a.last) loops_iter<4, BITS, EPT>(kv, a, s, h, i, orow, s_c, s_sl, s_j, lg_cur, lg_prev, sm);
+  if (a.first <= 5 && 5 <= a.last) loops_iter<5, BITS, EPT>(kv, a, s, h, i, orow, s_c, s_sl, s_j, lg_cur, lg_prev, sm);
+  __syncthreads();
+  for (int t = tid; t < N; t += 64 * kDecWaves) c_glob[t] = s_c[t];
+  if (tid == 0) a.lse[orow] = sm.lse;
 }
 
 // Full (dense) loop over the base of one new token per sequence: keys 0..i
@@ -544,6 +714,32 @@ bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm
   }
 #undef FL_DEC
 #undef FL_DEC_B
+  *err = hipGetLastError();
+  return true;
+}
+
+bool launch_decode_loops(const DecLoopsArgs& a, const KvView& kv, hipStream_t st, hipError_t* err) {
+  if (kv.dtype != FL_BF16 || kv.d != kDecD || (kv.bits != 4 && kv.bits != 2) || a.first < 2 ||
+      a.last - 1 > kDecMaxLayers || a.last < a.first || a.n_keys > kDecMaxKeys || kv.N > kDecLoopsMaxN)
+    return false;
+  const uint64_t lim = 0x7FFFFFFFull;
+  if (static_cast<uint64_t>(kv.N) * kDecD * 2 > lim) return false;
+  for (int l = 2; l <= a.last; ++l)
+    if (static_cast<uint64_t>(kv.cap[l]) * kv.H * kDecD > lim) return false;
+  const int sh = kv.n_seq >= 8 ? (kv.n_seq + 7) / 8 * 8 * kv.H : kv.n_seq * kv.H;
+  const size_t lds = static_cast<size_t>((kv.N + 3) & ~3) * 4 + static_cast<size_t>(a.n_keys) * (16 + 4 + 4 + 4);
+  TimedLaunch t(st, "decode_loops");
+  // the column-mass row takes the dynamic LDS past the default limit
+#define FL_LOOPS(B, E)                                                                                      \
+  do {                                                                                                       \
+    const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(k_decode_loops<B, E>),           \
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)); \
+    if (ea != hipSuccess) { *err = ea; return true; }                                                        \
+    hipLaunchKernelGGL((k_decode_loops<B, E>), dim3(sh), dim3(64 * kDecWaves), lds, st, kv, a);             \
+  } while (0)
+  static_assert(kDecLoopsMaxN <= 64 * kDecWaves * 16, "16 column-mass entries per thread");
+  if (kv.bits == 4) FL_LOOPS(4, 16); else FL_LOOPS(2, 16);
+#undef FL_LOOPS
   *err = hipGetLastError();
   return true;
 }

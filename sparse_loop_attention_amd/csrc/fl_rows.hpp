@@ -56,4 +56,26 @@ bool launch_decode_lazy(const RowArgs& a, const KvView& kv, const CommitArgs& cm
 // shape limits (head_dim 128, bf16, N <= 10240); false when outside them.
 bool launch_decode_full(const RowArgs& a, const KvView& kv, hipStream_t st, hipError_t* err);
 
+// Lazy decode loops first..last in one launch (flashloop_decode_loops).
+struct DecLoopsArgs {
+  uint8_t* arena;                          // writable arena (the token's records, its slot entries)
+  const int32_t* act;                      // [n_seq] the new token's position
+  int32_t first, last;                     // loops (versions) first..last
+  const void* q[FL_MAX_VERSIONS + 1];      // q[l], l = first-1..last
+  const void* k_new[FL_MAX_VERSIONS + 1];  // the token's new rows, l = first..last
+  const void* v_new[FL_MAX_VERSIONS + 1];
+  int32_t slot_base[FL_MAX_VERSIONS + 1];  // the token's record slot in layer l
+  int32_t q_compact, o_compact, kv_compact;
+  int32_t n_keys;
+  float* o;
+  float* lse;
+  float* colmass;
+  int32_t* keys_out;                       // [last-first+1][n_seq*H][n_keys] or null
+  float scale;
+  int32_t mixture;
+};
+// Shape limits: bf16 store, head_dim 128, 4- or 2-bit codes, versions up to
+// 5, n_keys <= 1536, N <= 8192.  Returns false (nothing launched) outside them.
+bool launch_decode_loops(const DecLoopsArgs& a, const KvView& kv, hipStream_t st, hipError_t* err);
+
 }  // namespace fl

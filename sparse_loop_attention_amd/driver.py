@@ -278,8 +278,15 @@ class DecodeRun:
 
     def __init__(self, wl: Workload, inputs: Dict[int, Dict[str, torch.Tensor]], ctx_sets: Dict[int, List[np.ndarray]],
                  device="cuda", fuse: bool = True, formula: str = "column", freeze_keys: bool = False,
-                 exit_threshold: Optional[float] = None):
+                 exit_threshold: Optional[float] = None, single_launch: bool = False):
+        """single_launch runs the lazy loops 2..T as one flashloop_decode_loops
+        call (key selection, commit and attention of every loop in one kernel)
+        instead of select_keys + attend per loop; it re-selects keys every loop
+        and takes no early exit between loops."""
         assert wl.decode
+        if single_launch and (freeze_keys or exit_threshold is not None or not fuse):
+            raise ValueError("single_launch: no frozen keys, no early exit, commit fused")
+        self.single_launch = single_launch
         self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
         self.formula, self.freeze_keys = formula, freeze_keys
         self.exit_threshold = exit_threshold
@@ -301,6 +308,9 @@ class DecodeRun:
         self.lse = torch.empty(S, 1, H, dtype=torch.float32, device=device)
         self.colmass = torch.empty(S, H, n, dtype=torch.float32, device=device)
         self.keys = torch.empty(S, H, wl.n_keys, dtype=torch.int32, device=device)
+        # single launch: every lazy loop's keys [loop - 2][S][H][n_keys]
+        self.keys_all = (torch.empty(max(wl.n_loops - 1, 1), S, H, wl.n_keys, dtype=torch.int32, device=device)
+                         if single_launch else None)
         ws = 0
         for l in range(1, wl.n_loops + 1):
             ws = max(ws, abi.attend_workspace_bytes(self._args(l, None)))
@@ -354,12 +364,36 @@ class DecodeRun:
         with t(f"loop{l}.attend"):
             abi.attend(self._args(l, self.workspace))
 
+    def lazy_loops_single(self, first: int, last: int) -> None:
+        """Lazy loops first..last in one flashloop_decode_loops call."""
+        wl, x = self.wl, self.inp
+        with self.timer(f"loops{first}-{last}.decode_loops"):
+            abi.decode_loops(self.kv, first, last, {l: x[l]["q"] for l in range(first - 1, last + 1)}, self.last,
+                             wl.n_keys, self.o, self.lse, self.colmass, {l: x[l]["k"] for l in range(first, last + 1)},
+                             {l: x[l]["v"] for l in range(first, last + 1)},
+                             {l: self.ctx[l].shape[1] for l in range(first, last + 1)},
+                             keys_out=self.keys_all[first - 2:last - 1], formula=self.formula)
+
     def run(self, record: bool = False, start: int = 1, upto: Optional[int] = None) -> List[LoopRecord]:
         """Loops start..upto (default: all); start > 1 continues from the
         state the buffers hold."""
         recs = []
         if self.exit_flags is not None and start == 1:
             self.exit_flags.zero_()
+        if self.single_launch:
+            last = self.wl.n_loops if upto is None else upto
+            if start == 1:
+                self.loop(1)
+                if record:
+                    recs.append(LoopRecord(o=self.o.clone(), lse=self.lse.clone(), colmass=self.colmass.clone()))
+            first = max(2, start)
+            if first <= last:
+                self.lazy_loops_single(first, last)
+                if record:                  # the keys of every loop; the outputs after the last
+                    for l in range(first, last + 1):
+                        recs.append(LoopRecord(keys=self.keys_all[l - 2].clone()))
+                    recs[-1].o, recs[-1].lse, recs[-1].colmass = self.o.clone(), self.lse.clone(), self.colmass.clone()
+            return recs
         for l in range(start, (self.wl.n_loops if upto is None else upto) + 1):
             self.loop(l)
             if record:

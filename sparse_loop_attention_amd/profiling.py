@@ -14,6 +14,14 @@ text summaries of rocprofv3 output (kernel statistics, HBM traffic).
         carries a hash of the library sources so that a reader can tell
         whether the kernel changed since the counters were taken.
 
+    python -m sparse_loop_attention_amd.profiling counters --dir DIR [--dir DIR ...]
+            --kernel LABEL=SUBSTR [--kernel ...] --title T --command C
+        per-dispatch averages of every counter found in one or more
+        `rocprofv3 --pmc` runs, per kernel, with derived ratios (MFMA busy
+        share of the CUs' busy SIMD cycles, MFMA operations against the
+        kernel's algorithmic flops, LDS bank-conflict share, VALU and
+        transcendental instructions per MFMA).
+
 Traffic summaries are markdown files under profiles/ holding one line
 `traffic-record: {json}` that bench.py reads.
 """
@@ -138,6 +146,59 @@ def cmd_traffic(a):
     print("\n".join(out))
 
 
+def all_counters(d: str, kernel_substr: str):
+    """{counter: [value per dispatch]} of kernels whose name contains kernel_substr."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = set()
+    with open(_counter_csv(d)) as fh:
+        for r in csv.DictReader(fh):
+            if kernel_substr not in r["Kernel_Name"]:
+                continue
+            vals[r["Counter_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+            names.add(r["Kernel_Name"])
+    return {c: [v[k] for k in sorted(v)] for c, v in vals.items()}, sorted(names)
+
+
+def cmd_counters(a):
+    out = [f"# {a.title}", "", "Commands (from the repository root, one MI355X; one `--pmc` set per run):", "",
+           "```", a.command, "```", ""]
+    for spec in a.kernel:
+        label, sub = spec.split("=", 1)
+        merged, names = {}, set()
+        for d in a.dir:
+            c, n = all_counters(d, sub)
+            names.update(n)
+            for k, v in c.items():
+                merged[k] = sum(v) / len(v)
+        if not merged:
+            out += [f"## {label}", "", f"no dispatch of `{sub}`", ""]
+            continue
+        out += [f"## {label}", "", f"kernel: `{sorted(names)[0][:140]}`", "", "| counter | per dispatch |", "|---|---|"]
+        for k in sorted(merged):
+            out.append(f"| {k} | {merged[k]:.4g} |")
+        g = merged.get
+        derived = []
+        if g("SQ_VALU_MFMA_BUSY_CYCLES") and g("SQ_BUSY_CU_CYCLES"):
+            # busy CU quad-cycles x 4 cycles x 4 SIMDs = busy SIMD cycles
+            derived.append(("MFMA busy / busy SIMD cycles", g("SQ_VALU_MFMA_BUSY_CYCLES") / (16 * g("SQ_BUSY_CU_CYCLES"))))
+        if g("SQ_LDS_BANK_CONFLICT") and g("SQ_ACTIVE_INST_LDS"):
+            derived.append(("LDS bank-conflict cycles / LDS active cycles",
+                            g("SQ_LDS_BANK_CONFLICT") / (4 * g("SQ_ACTIVE_INST_LDS"))))
+        if g("SQ_INSTS_MFMA"):
+            for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"):
+                if g(k):
+                    derived.append((f"{k} per MFMA instruction", g(k) / g("SQ_INSTS_MFMA")))
+        mops = sum(g(k) or 0.0 for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"))
+        if mops:
+            derived.append(("MFMA flops (MOPS x 512)", mops * 512))
+        if g("SQ_VALU_MFMA_COEXEC_CYCLES") and g("SQ_VALU_MFMA_BUSY_CYCLES"):
+            derived.append(("VALU co-issued during MFMA / MFMA busy", g("SQ_VALU_MFMA_COEXEC_CYCLES") / g("SQ_VALU_MFMA_BUSY_CYCLES")))
+        if derived:
+            out += ["", "| derived | value |", "|---|---|"] + [f"| {k} | {v:.4g} |" for k, v in derived]
+        out.append("")
+    print("\n".join(out))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -154,8 +215,13 @@ def main(argv=None):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     t.add_argument("--cal-kernel", default="copyBuffer")
     t.add_argument("--cal-bytes", type=float, default=float(1 << 30))
+    k = sub.add_parser("counters")
+    k.add_argument("--dir", action="append", required=True)
+    k.add_argument("--kernel", action="append", required=True, help="LABEL=name substring")
+    k.add_argument("--title", required=True)
+    k.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

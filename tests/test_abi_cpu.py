@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(abi.EXPORTS)
@@ -232,3 +232,28 @@ def test_attend_noalloc_rejects_beyond_its_scratch(L):
     assert b"scratch" in L.flashloop_last_error()
     a.mode = 9
     assert L.flashloop_attend_noalloc(C.byref(a), None) == abi.FL_ERR_ARG
+
+
+def test_decode_loops_validation(L):
+    """flashloop_decode_loops rejects invalid arguments before any launch."""
+    wl = configs.DECODE
+    d = _desc(wl)
+    d.arena, d.arena_bytes = 256, abi.kv_arena_bytes(d)
+    a = abi.fl_decode_loops_args()
+    assert L.flashloop_decode_loops(C.byref(a), None) == abi.FL_ERR_ARG              # no descriptor
+    a.kv = C.pointer(d)
+    a.first_version, a.last_version, a.n_keys = 1, 4, 820
+    assert L.flashloop_decode_loops(C.byref(a), None) == abi.FL_ERR_ARG              # first < 2
+    a.first_version = 2
+    a.active_idx, a.o, a.lse, a.colmass = 256, 256, 256, 256
+    assert L.flashloop_decode_loops(C.byref(a), None) == abi.FL_ERR_ARG              # q[1..4] missing
+    assert b"q[1]" in L.flashloop_last_error()
+    for l in range(1, 5):
+        a.q[l] = 256
+    for l in range(2, 5):
+        a.k_new[l] = a.v_new[l] = 256
+        a.commit_slot_base[l] = wl.layer_caps()[l - 2]                               # one past the capacity
+    assert L.flashloop_decode_loops(C.byref(a), None) == abi.FL_ERR_ARG
+    assert b"commit_slot_base" in L.flashloop_last_error()
+    a.last_version = 5
+    assert L.flashloop_decode_loops(C.byref(a), None) == abi.FL_ERR_ARG              # beyond n_versions
