@@ -233,7 +233,16 @@ typedef struct {
   int32_t formula;              /* fl_formula (LAZY); FULL requires FL_FORMULA_COLUMN */
   const int32_t* exit_flags;    /* optional [n_seq] device: sequences with a nonzero flag are
                                    skipped (o, lse, colmass and store left as they are) */
+  int32_t* dev_status;          /* optional [1] device, caller-zeroed: the kernels OR in FL_DEV_* bits
+                                   when a run-time check fails (the call's outputs are then unreliable) */
 } fl_attend_args;
+
+/* Bits of fl_attend_args.dev_status.  FL_DEV_XCD_SPLIT: a full loop whose
+ * forward pass or column mass is split into parts over several workgroups
+ * relies on every part of a head running on one XCD, whose L2 is where the
+ * parts' partial results meet (they are not written back past it); a part
+ * that ran on another XCD sets this bit. */
+#define FL_DEV_XCD_SPLIT 1
 
 uint64_t  flashloop_attend_workspace_bytes(const fl_attend_args* args);
 fl_status flashloop_attend(const fl_attend_args* args, void* stream);

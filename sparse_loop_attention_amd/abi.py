@@ -24,6 +24,7 @@ FORMULAS = {"column": FL_FORMULA_COLUMN, "mixture": FL_FORMULA_MIXTURE}
 FL_SEL_TOKENS, FL_SEL_KEYS = 0, 1
 FL_ATTEND_FULL, FL_ATTEND_LAZY = 0, 1
 FL_ROWS_BY_TOKEN, FL_ROWS_COMPACT = 0, 1
+FL_DEV_XCD_SPLIT = 1
 
 EXPORTS = ("flashloop_kv_layout", "flashloop_kv_arena_bytes", "flashloop_kv_commit", "flashloop_select",
            "flashloop_attend_workspace_bytes", "flashloop_attend", "flashloop_last_error",
@@ -68,7 +69,7 @@ class fl_attend_args(C.Structure):
                 ("colmass", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_uint64),
                 ("fuse_commit", C.c_int32), ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("kv_layout", C.c_int32),
                 ("commit_slot_base", C.c_int32), ("commit_reset", C.c_int32), ("formula", C.c_int32),
-                ("exit_flags", C.c_void_p)]
+                ("exit_flags", C.c_void_p), ("dev_status", C.c_void_p)]
 
 
 class fl_exit_args(C.Structure):
@@ -251,10 +252,11 @@ def select_keys(key_scores: torch.Tensor, k: int, out_idx: torch.Tensor, stream=
 # --------------------------------------------------------------------------- attend
 def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx, n_active: int,
                 key_idx, o, lse, colmass, workspace=None, q_compact=False, o_compact=False,
-                commit=None, formula: str = "column", exit_flags=None) -> fl_attend_args:
+                commit=None, formula: str = "column", exit_flags=None, dev_status=None) -> fl_attend_args:
     """`commit` = dict(k_new=, v_new=, compact=False, slot_base=0, reset=True) fuses the
     KV commit of this loop into the call; `formula` is "column" or
-    "mixture" (LAZY only); `exit_flags` (int32 [n_seq]) skips exited sequences."""
+    "mixture" (LAZY only); `exit_flags` (int32 [n_seq]) skips exited sequences; `dev_status`
+    (int32 [1], zeroed by the caller) receives FL_DEV_* bits of failed run-time checks."""
     a = fl_attend_args()
     a.mode, a.kv, a.version = mode, C.pointer(kv.desc), version
     a.q_cur, a.q_prev = _ptr(q_cur), _ptr(q_prev)
@@ -274,6 +276,7 @@ def attend_args(kv: KVStore, mode: int, version: int, q_cur, q_prev, active_idx,
         a.commit_reset = int(commit.get("reset", True))
     a.formula = FORMULAS[formula]
     a.exit_flags = _ptr(exit_flags)
+    a.dev_status = _ptr(dev_status)
     return a
 
 

@@ -30,6 +30,7 @@
 //              the column sums are lane-local; fixed order, no atomics (row
 //              ranges are added by a small reduction kernel).
 #include <climits>
+#include <cstdlib>
 #include <type_traits>
 
 #include "fl_common.hpp"
@@ -78,9 +79,15 @@ struct MfmaArgs {
   // ceil(tiles / fsplit_u) parts, one workgroup each (fsplit_u = 0: none)
   int32_t fsplit_u, f_items, f_tiles;   // workgroups and row tiles per head
   float4* fpart;            // [sh][f_items][D/8 + 1][512] partial acc, (max, sum)
-  int32_t* fcount;          // [sh][f_tiles] parts finished (zeroed by the gather launch)
+  int32_t* fcount;          // [2][sh][f_tiles] parts finished, then the XCDs they ran on (zeroed by the gather)
   int32_t fpair;            // full loops: workgroups per head taking an early and a late 128-row half (0 = off)
-  int32_t* ccount;          // [sh][n_keys_pad / 256] column-mass ranges finished (zeroed by the gather), or null
+  int32_t* ccount;          // [2][sh][n_keys_pad / 256] column-mass ranges finished, then the XCDs they ran on
+                            // (bit x: XCD x), zeroed by the gather; or null
+  // run-time check of the split reductions above: every part of a head must
+  // run on one XCD (its L2 is where the parts' partial sums meet); a part on
+  // another XCD sets FL_DEV_XCD_SPLIT in *dev_status (optional)
+  int32_t* dev_status;
+  int32_t xcd_test;         // nonzero: report part p's XCD as (XCD ^ (p & 1)), to test the check
   // early exit: sequences with a nonzero flag are skipped by every kernel
   const int32_t* exit_flags;  // [n_seq] or null
   int32_t heads;
@@ -122,6 +129,25 @@ __host__ __device__ inline int mapped_grid(int n_sh, int n_tiles) {
   return n_sh >= 8 ? 8 * ((n_sh + 7) / 8) * n_tiles : n_sh * n_tiles;
 }
 
+// The XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
+  return x;
+}
+
+// Part `part` of a split reduction records its XCD in *mask before it counts
+// its arrival; the last part (after its own record) compares the mask with
+// its own XCD.  Called by one thread per workgroup.
+__device__ __forceinline__ uint32_t xcd_bit(const MfmaArgs& a, int part) {
+  return 1u << (a.xcd_test ? (xcc_id() ^ static_cast<uint32_t>(part & 1)) : xcc_id());
+}
+__device__ __forceinline__ void xcd_check(const MfmaArgs& a, int32_t* mask, uint32_t mine) {
+  const uint32_t all = static_cast<uint32_t>(__hip_atomic_load(mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (all != mine && a.dev_status)
+    __hip_atomic_fetch_or(a.dev_status, FL_DEV_XCD_SPLIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ int row_token(const MfmaArgs& a, int s, int r) {
   return a.act ? a.act[static_cast<int64_t>(s) * a.n_rows + r] : r;
 }
@@ -148,10 +174,10 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
   const int n_tiles = a.n_keys_pad / 64;
   int b = blockIdx.x;
   const int g = threadIdx.x >> 4, p = threadIdx.x & 15;
-  if (a.fcount && b == 0)                                 // the forward pass's arrival counters
-    for (int i = threadIdx.x; i < a.n_sh * a.f_tiles; i += 256) a.fcount[i] = 0;
-  if (a.ccount && b == 0)                                 // the column-mass ranges' counters
-    for (int i = threadIdx.x; i < a.n_sh * (a.n_keys_pad / 256); i += 256) a.ccount[i] = 0;
+  if (a.fcount && b == 0)                                 // the forward pass's arrival counters and XCD masks
+    for (int i = threadIdx.x; i < 2 * a.n_sh * a.f_tiles; i += 256) a.fcount[i] = 0;
+  if (a.ccount && b == 0)                                 // the column-mass ranges' counters and XCD masks
+    for (int i = threadIdx.x; i < 2 * a.n_sh * (a.n_keys_pad / 256); i += 256) a.ccount[i] = 0;
   if (FUSE && b >= a.n_sh * n_tiles) {
     b -= a.n_sh * n_tiles;
     // lazy loops: blocks of their own write the active rows' records (the
@@ -765,11 +791,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
       mine[(D / 8) * NT + tid] = make_float4(ref, lsum, 0.0f, 0.0f);
       __builtin_amdgcn_s_waitcnt(0);                       // this lane's stores acknowledged
       __syncthreads();
-      if (tid == 0)
-        s_arrived = __hip_atomic_fetch_add(a.fcount + static_cast<int64_t>(sh) * a.f_tiles + qtile, 1,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int32_t* cnt = a.fcount + static_cast<int64_t>(sh) * a.f_tiles + qtile;
+      int32_t* xmask = cnt + static_cast<int64_t>(a.n_sh) * a.f_tiles;
+      const uint32_t xbit = xcd_bit(a, part);
+      if (tid == 0) {
+        __hip_atomic_fetch_or(xmask, static_cast<int32_t>(xbit), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        s_arrived = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       __syncthreads();
       if (s_arrived != parts - 1) return;
+      if (tid == 0) xcd_check(a, xmask, xbit);
       auto ld4 = [](const float4* q) {
         const float* f = reinterpret_cast<const float*>(q);
         return make_float4(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
@@ -1045,11 +1077,18 @@ __device__ __forceinline__ void col_finish(const MfmaArgs& a, int N, int chunk, 
   if (!a.ccount) return;
   __builtin_amdgcn_s_waitcnt(0);                          // this lane's store acknowledged
   __syncthreads();
-  if (tid == 0)
-    *s_arrived = __hip_atomic_fetch_add(a.ccount + static_cast<int64_t>(sh) * (a.n_keys_pad / 256) + kblk, 1,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int32_t* cnt = a.ccount + static_cast<int64_t>(sh) * (a.n_keys_pad / 256) + kblk;
+  int32_t* xmask = cnt + static_cast<int64_t>(a.n_sh) * (a.n_keys_pad / 256);
+  const uint32_t xbit = xcd_bit(a, chunk);
+  if (tid == 0) {
+    __hip_atomic_fetch_or(xmask, static_cast<int32_t>(xbit), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    *s_arrived = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
-  if (*s_arrived != n_parts - 1 || tid >= 256) return;
+  if (*s_arrived != n_parts - 1) return;
+  if (tid == 0) xcd_check(a, xmask, xbit);
+  if (tid >= 256) return;
   const int tk = kblk * 256 + tid;
   if (tk >= a.n_keys) return;
   float sum = 0.0f;
@@ -1280,6 +1319,14 @@ __global__ __launch_bounds__(256) void k_colmass_reduce(int32_t N, MfmaArgs a) {
 }
 
 // --------------------------------------------------------------------------- launch
+// FLASHLOOP_TEST_XCD_SPLIT=1 makes the split reductions' XCD check see
+// different XCDs for odd and even parts, so that a test can see the check
+// report (the results themselves are unaffected).
+static int32_t xcd_test_flag() {
+  const char* e = getenv("FLASHLOOP_TEST_XCD_SPLIT");
+  return e && e[0] == '1';
+}
+
 template <int D>
 static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st) {
   const bool lazy = x.mode == FL_ATTEND_LAZY;
@@ -1309,6 +1356,8 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   // set before the gather launch, which zeroes the counters
   a.ccount = p.col_fused ? reinterpret_cast<int32_t*>(ws + p.off_ccount) : nullptr;
   a.exit_flags = kv.exit_flags;
+  a.dev_status = x.dev_status;
+  a.xcd_test = xcd_test_flag();
   if (!lazy && p.fsplit_u > 0) {
     a.fsplit_u = p.fsplit_u;
     a.f_items = p.f_items;

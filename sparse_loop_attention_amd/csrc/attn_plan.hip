@@ -163,8 +163,8 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     // counter per block).  Lazy loops keep the reduction launch: the fused
     // ending cost the two-pass kernel more registers than the launch saves.
     p.col_fused = !lazy && p.col_chunks > 1 && sh >= 8;
-    p.off_ccount = off;
-    if (p.col_fused) off = align256(off + sh * (kpad / 256) * 4);
+    p.off_ccount = off;                                  // counters, then as many XCD masks
+    if (p.col_fused) off = align256(off + 2 * sh * (kpad / 256) * 4);
     p.off_logit = off;
     // forward key split of full loops: one partial (acc, max, sum of every
     // lane of the 512-thread workgroup) per workgroup, one counter per row tile
@@ -176,8 +176,8 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     p.off_fcount = off;
     if (p.fsplit_u > 0) {
       off = align256(off + sh * p.f_items * (D / 8 + 1) * 512 * 16);   // D/8 float4 of acc + (max, sum)
-      p.off_fcount = off;
-      off = align256(off + sh * p.f_tiles * 4);
+      p.off_fcount = off;                                // counters, then as many XCD masks
+      off = align256(off + 2 * sh * p.f_tiles * 4);
     }
     p.off_total = off;
     return p;

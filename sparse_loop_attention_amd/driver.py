@@ -147,6 +147,8 @@ class PrefillRun:
                     for l in range(wl.n_full + 1, wl.n_loops + 1)}
         self.keys_l = {l: torch.empty(H, wl.n_keys, dtype=torch.int32, device=device)
                        for l in range(wl.n_full + 1, wl.n_loops + 1)}
+        # FL_DEV_* bits of failed run-time checks in the attention kernels (0: none)
+        self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
         self.workspace = None
         ws = 0
         for l in range(1, wl.n_loops + 1):
@@ -193,13 +195,15 @@ class PrefillRun:
             # every row; with fusion the call also commits every token's K/V
             commit = dict(k_new=self.inp[l]["k"], v_new=self.inp[l]["v"]) if self.fuse else None
             return abi.attend_args(self.kv, abi.FL_ATTEND_FULL, l, self.inp[l]["q"], None, None, wl.n_tokens,
-                                   None, self.o, self.lse, self.colmass, self.workspace, commit=commit)
+                                   None, self.o, self.lse, self.colmass, self.workspace, commit=commit,
+                                   dev_status=self.dev_status)
         na = wl.n_active(l)
         commit = dict(k_new=self.inp[l]["k"], v_new=self.inp[l]["v"]) if self.fuse else None
         # the active rows' queries of loops l and l-1, read by token
         return abi.attend_args(self.kv, abi.FL_ATTEND_LAZY, l, self.inp[l]["q"], self.inp[l - 1]["q"],
                                self.act[l], na, self.keys_l[l], self.o, self.lse, self.colmass, self.workspace,
-                               commit=commit, formula=self.formula, exit_flags=self.exit_flags)
+                               commit=commit, formula=self.formula, exit_flags=self.exit_flags,
+                               dev_status=self.dev_status)
 
     # ------------------------------------------------------------------ loops
     def full_loop(self, l: int) -> None:
