@@ -35,6 +35,30 @@ def rel_err_ok(got, want, tol=2e-2):
     return err <= tol * rms, err, rms
 
 
+GUARD = 4096                     # elements before and after a guarded buffer (16 KiB of float32)
+SENTINEL = -12345.5
+
+
+def guarded(shape, fill, dtype=torch.float32):
+    """A device buffer of `shape` (a view) inside a larger allocation whose
+    GUARD elements on either side hold SENTINEL: writes past the buffer show
+    up in check_guards.  fill: the buffer's contents (NaN for outputs a call
+    must write completely, so that an unwritten element shows up)."""
+    n = int(np.prod(shape))
+    full = torch.full((n + 2 * GUARD,), SENTINEL, dtype=dtype, device=DEV)
+    view = full[GUARD:GUARD + n].view(*shape)
+    if isinstance(fill, torch.Tensor):
+        view.copy_(fill)
+    else:
+        view.fill_(fill)
+    return full, view
+
+
+def check_guards(full):
+    g = full.cpu()
+    assert torch.all(g[:GUARD] == SENTINEL) and torch.all(g[-GUARD:] == SENTINEL), "write outside the buffer"
+
+
 def lse_abs_err(got, want):
     """lse is compared in absolute terms (nats): an error of e rescales the
     next loop's previous-loop probabilities by exp(e)."""
@@ -215,15 +239,22 @@ def test_attend_full(dtype, d, n):
     sets = {2: np.arange(n)}
     st, kv, rnd = _setup_attend(rng, n, H, d, dtype, sets)
     q = rnd(rng.standard_normal((n, H, d)).astype(np.float32) * 1.5)
-    o = torch.zeros(1, n, H, d, device=DEV)
-    lse = torch.zeros(1, n, H, device=DEV)
-    c = torch.full((1, H, n), 7.0, device=DEV)
     for version in (1, 2):
+        # outputs NaN-filled (a FULL call writes every o, lse and column-mass
+        # entry) inside guard regions; the workspace too has guards
+        og, o = guarded((1, n, H, d), float("nan"))
+        lg, lse = guarded((1, n, H), float("nan"))
+        cg, c = guarded((1, H, n), float("nan"))
         a = abi.attend_args(kv, abi.FL_ATTEND_FULL, version, to_dev(q[None], dtype), None, None, n, None, o, lse, c)
-        ws = torch.empty(abi.attend_workspace_bytes(a), dtype=torch.uint8, device=DEV)
+        wsg = torch.full((abi.attend_workspace_bytes(a) + 2 * 256,), 0x5A, dtype=torch.uint8, device=DEV)
+        ws = wsg[256:-256]
         a = abi.attend_args(kv, abi.FL_ATTEND_FULL, version, to_dev(q[None], dtype), None, None, n, None, o, lse, c, ws)
         abi.attend(a)
         torch.cuda.synchronize()
+        for g in (og, lg, cg):
+            check_guards(g)
+        assert torch.all(wsg[:256] == 0x5A) and torch.all(wsg[-256:] == 0x5A), "write outside the workspace"
+        assert not (torch.isnan(o).any() or torch.isnan(lse).any() or torch.isnan(c).any()), "unwritten output"
         wd = "bf16" if dtype == torch.bfloat16 else "fp32"
         o_r, lse_r, c_r = oracle.full_attention(q, oracle.to_working_dtype(st.reconstruct("k", version), wd),
                                                 oracle.to_working_dtype(st.reconstruct("v", version), wd),
@@ -397,9 +428,9 @@ def test_attend_lazy(dtype, d, n, na, ns):
     rec = lambda w, l: oracle.to_working_dtype(st.reconstruct(w, l), wd)
     o0, lse0, c0 = oracle.full_attention(q0, rec("k", 1), rec("v", 1), np.arange(n))
     keys = oracle.select_keys(c0, ns)
-    o = torch.from_numpy(o0.astype(np.float32)[None]).to(DEV)
-    lse = torch.from_numpy(lse0.astype(np.float32)[None]).to(DEV)
-    c = torch.from_numpy(c0.astype(np.float32)[None]).to(DEV)
+    og, o = guarded((1, n, H, d), torch.from_numpy(o0.astype(np.float32)[None]))
+    lg, lse = guarded((1, n, H), torch.from_numpy(lse0.astype(np.float32)[None]))
+    cg, c = guarded((1, H, n), torch.from_numpy(c0.astype(np.float32)[None]))
     qc = to_dev(q1[act][None], dtype)
     qp = to_dev(q0[act][None], dtype)
     a = abi.attend_args(kv, abi.FL_ATTEND_LAZY, 2, qc, qp, torch.from_numpy(act).to(DEV)[None], na,
@@ -409,6 +440,8 @@ def test_attend_lazy(dtype, d, n, na, ns):
                         torch.from_numpy(keys).to(DEV)[None], o, lse, c, ws, q_compact=True)
     abi.attend(a)
     torch.cuda.synchronize()
+    for g in (og, lg, cg):
+        check_guards(g)
     o_r, lse_r, c_r, m, upd = oracle.lazy_attention(
         q1[act], q0[act], rec("k", 1), rec("v", 1), rec("k", 2), rec("v", 2), o0[act], lse0[act], c0, act, keys)
     got_o = o[0].cpu().numpy()
