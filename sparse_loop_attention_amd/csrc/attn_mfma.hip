@@ -80,6 +80,10 @@ struct MfmaArgs {
   int32_t fsplit_u, f_items, f_tiles;   // workgroups and row tiles per head
   float4* fpart;            // [sh][f_items][D/8 + 1][512] partial acc, (max, sum)
   int32_t* fcount;          // [2][sh][f_tiles] parts finished, then the XCDs they ran on (zeroed by the gather)
+  // lazy loops with the passes split (non-null): the previous-loop pass's
+  // mass m per row [sh][n_rows]; fpart/fcount/f_tiles then hold the
+  // current-loop pass's partials and the arrivals per row tile
+  float* lmass;
   int32_t fpair;            // full loops: workgroups per head taking an early and a late 128-row half (0 = off)
   int32_t* ccount;          // [2][sh][n_keys_pad / 256] column-mass ranges finished, then the XCDs they ran on
                             // (bit x: XCD x), zeroed by the gather; or null
@@ -128,6 +132,17 @@ __device__ __forceinline__ bool map_block(int n_sh, int n_tiles, int& sh, int& t
 __host__ __device__ inline int mapped_grid(int n_sh, int n_tiles) {
   return n_sh >= 8 ? 8 * ((n_sh + 7) / 8) * n_tiles : n_sh * n_tiles;
 }
+
+// A float4 read at device scope (past this CU's L1): data another workgroup
+// of the XCD stored and acknowledged before counting its arrival.
+__device__ __forceinline__ float4 ld4_agent(const float4* q) {
+  const float* f = reinterpret_cast<const float*>(q);
+  return make_float4(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     __hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float4 ld4_agent_f(const float* p) { return ld4_agent(reinterpret_cast<const float4*>(p)); }
 
 // The XCD (accelerator complex die) this wave runs on.
 __device__ __forceinline__ uint32_t xcc_id() {
@@ -684,7 +699,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31;
-  int sh, qtile, item = 0, part = 0, parts = 1;
+  int sh, qtile, item = 0, part = 0, parts = 1, lrole = 0;
   int r0, wg_last;                                         // first row of this wave, last row of the workgroup
   if (PAIR) {
     int j;
@@ -706,6 +721,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
       i -= parts;
     }
     part = i;
+  } else if (LAZY && a.lmass) {
+    // two workgroups per row tile, the previous-loop pass (role 1) first
+    int t2;
+    if (!map_block(a.n_sh, 2 * a.f_tiles, sh, t2)) return;
+    qtile = t2 >> 1;
+    lrole = t2 & 1;
   } else if (!map_block(a.n_sh, (a.n_rows + ROWS - 1) / ROWS, sh, qtile)) {
     return;
   }
@@ -854,63 +875,134 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   // lse_prev gives the mass m and contribution a; o_prev - a is written back
   // at once, and pass 2 (current loop, online softmax) adds m * otilde.
   const float b_prev = vrow ? a.lse[(static_cast<int64_t>(s) * rows_o + orow) * H + h] * kLog2e : 0.0f;
+  // o <- o_prev - a (or (1 - m) o_prev), from o as read by ld
+  auto prev_update = [&](bool valid, float m, auto ld) {
+    if (!valid) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dim = db * 32 + 8 * q4 + 4 * hh;
+        float4 op = ld(o_ptr + dim);
+        if (MIX) {
+          const float keep = 1.0f - m;
+          op.x *= keep; op.y *= keep; op.z *= keep; op.w *= keep;
+        } else {
+          op.x -= acc[db][4 * q4 + 0];
+          op.y -= acc[db][4 * q4 + 1];
+          op.z -= acc[db][4 * q4 + 2];
+          op.w -= acc[db][4 * q4 + 3];
+        }
+        *reinterpret_cast<float4*>(o_ptr + dim) = op;
+      }
+  };
+  // o <- o + (m / z) acc, the new lse and the row statistics
+  auto cur_finish = [&](bool valid, float m, float z, auto ld) {
+    if (valid) {
+      const float f = z > 0.0f ? m / z : 0.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int dim = db * 32 + 8 * q4 + 4 * hh;
+          float4 op = ld(o_ptr + dim);
+          op.x = fmaf(f, acc[db][4 * q4 + 0], op.x);
+          op.y = fmaf(f, acc[db][4 * q4 + 1], op.y);
+          op.z = fmaf(f, acc[db][4 * q4 + 2], op.z);
+          op.w = fmaf(f, acc[db][4 * q4 + 3], op.w);
+          *reinterpret_cast<float4*>(o_ptr + dim) = op;
+        }
+    }
+    if (vrow && hh == 0) {
+      // new lse in log2 units: M + log2 Z - log2 m
+      const float b = valid ? ref + __log2f(z) - __log2f(m) : b_prev;
+      if (valid) *lse_ptr = b * kLn2;
+      *reinterpret_cast<float4*>(st_ptr) =
+          make_float4(valid ? b_prev : INFINITY, valid ? b : INFINITY, valid ? 1.0f : 0.0f, __int_as_float(tok));
+    }
+  };
+  auto ld_plain = [](const float* p) { return *reinterpret_cast<const float4*>(p); };
+  if (a.lmass) {
+    // The two passes as two workgroups of one XCD (map_block: whole heads
+    // per XCD).  The previous-loop pass writes o_prev - a and m at once; the
+    // workgroup that ends last applies the current-loop pass, from its own
+    // registers or from the partial (acc, max, sum) the current-loop pass
+    // stored.  Stores are acknowledged before the arrival count, and the
+    // other workgroup's data is read past this CU's L1 (device-scope loads).
+    constexpr int SLOT = (D / 8 + 1) * NT;
+    int32_t* cnt = a.fcount + static_cast<int64_t>(sh) * a.f_tiles + qtile;
+    int32_t* xmask = cnt + static_cast<int64_t>(a.n_sh) * a.f_tiles;
+    float4* part = a.fpart + (static_cast<int64_t>(sh) * a.f_tiles + qtile) * SLOT;
+    float* mrow = a.lmass + static_cast<int64_t>(sh) * a.n_rows + r;
+    const uint32_t xbit = xcd_bit(a, lrole);
+    auto arrive = [&]() {
+      __builtin_amdgcn_s_waitcnt(0);                       // this lane's stores acknowledged
+      __syncthreads();
+      if (tid == 0) {
+        __hip_atomic_fetch_or(xmask, static_cast<int32_t>(xbit), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        s_arrived = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      return s_arrived;
+    };
+    float m;
+    bool valid;
+    if (lrole == 1) {
+      load_q(a.q_prev, qf);
+      fwd_pass<D, NW, KT_, true, MIX>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok, tok_first,
+                                      tok_last, blk_full, c1, b_prev, acc, ref, lsum);
+      m = lsum + __shfl_xor(lsum, 32, 64);
+      valid = vrow && m > 0.0f;
+      prev_update(valid, m, ld_plain);
+      if (vrow && hh == 0) *mrow = m;
+      if (arrive() == 0) return;                           // the current-loop pass ends the tile
+      if (tid == 0) xcd_check(a, xmask, xbit);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v = ld4_agent(part + (db * 4 + q4) * NT + tid);
+          acc[db][4 * q4 + 0] = v.x; acc[db][4 * q4 + 1] = v.y;
+          acc[db][4 * q4 + 2] = v.z; acc[db][4 * q4 + 3] = v.w;
+        }
+      const float4 st = ld4_agent(part + (D / 8) * NT + tid);
+      ref = st.x;
+      lsum = st.y;
+    } else {
+      load_q(a.q_cur, qf);
+      fwd_pass<D, NW, KT_, false>(a, n_tiles, a.kc + kofs, a.vtc + kofs, kx, sk, sv, skx, qf, tok, tok_first,
+                                  tok_last, blk_full, c1, 0.0f, acc, ref, lsum);
+      if (tid == 0) s_arrived = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (s_arrived == 0) {                                // the previous-loop pass still runs: leave a partial
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            part[(db * 4 + q4) * NT + tid] =
+                make_float4(acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]);
+        part[(D / 8) * NT + tid] = make_float4(ref, lsum, 0.0f, 0.0f);
+        if (arrive() == 0) return;                         // the previous-loop pass ends the tile
+      }
+      if (tid == 0) xcd_check(a, xmask, xbit);
+      m = vrow ? __hip_atomic_load(mrow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+      valid = vrow && m > 0.0f;
+    }
+    cur_finish(valid, m, lsum + __shfl_xor(lsum, 32, 64), ld4_agent_f);
+    return;
+  }
   load_q(a.q_prev, qf);
   fwd_pass<D, NW, KT_, true, MIX>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok, tok_first,
                                   tok_last, blk_full, c1, b_prev, acc, ref, lsum);
   const float m = lsum + __shfl_xor(lsum, 32, 64);
   const bool valid = vrow && m > 0.0f;
-  if (valid && MIX) {
-    const float keep = 1.0f - m;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int dim = db * 32 + 8 * q4 + 4 * hh;
-        float4 op = *reinterpret_cast<const float4*>(o_ptr + dim);
-        op.x *= keep; op.y *= keep; op.z *= keep; op.w *= keep;
-        *reinterpret_cast<float4*>(o_ptr + dim) = op;
-      }
-  } else if (valid) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int dim = db * 32 + 8 * q4 + 4 * hh;
-        float4 op = *reinterpret_cast<const float4*>(o_ptr + dim);
-        op.x -= acc[db][4 * q4 + 0];
-        op.y -= acc[db][4 * q4 + 1];
-        op.z -= acc[db][4 * q4 + 2];
-        op.w -= acc[db][4 * q4 + 3];
-        *reinterpret_cast<float4*>(o_ptr + dim) = op;
-      }
-  }
+  prev_update(valid, m, ld_plain);
   __syncthreads();                                         // pass 2 reuses the tile buffers
   load_q(a.q_cur, qf);
   fwd_pass<D, NW, KT_, false>(a, n_tiles, a.kc + kofs, a.vtc + kofs, kx, sk, sv, skx, qf, tok, tok_first, tok_last,
                          blk_full, c1, 0.0f, acc, ref, lsum);
-  const float z = lsum + __shfl_xor(lsum, 32, 64);
-  if (valid) {
-    const float f = z > 0.0f ? m / z : 0.0f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int dim = db * 32 + 8 * q4 + 4 * hh;
-        float4 op = *reinterpret_cast<const float4*>(o_ptr + dim);
-        op.x = fmaf(f, acc[db][4 * q4 + 0], op.x);
-        op.y = fmaf(f, acc[db][4 * q4 + 1], op.y);
-        op.z = fmaf(f, acc[db][4 * q4 + 2], op.z);
-        op.w = fmaf(f, acc[db][4 * q4 + 3], op.w);
-        *reinterpret_cast<float4*>(o_ptr + dim) = op;
-      }
-  }
-  if (vrow && hh == 0) {
-    // new lse in log2 units: M + log2 Z - log2 m
-    const float b = valid ? ref + __log2f(z) - __log2f(m) : b_prev;
-    if (valid) *lse_ptr = b * kLn2;
-    *reinterpret_cast<float4*>(st_ptr) =
-        make_float4(valid ? b_prev : INFINITY, valid ? b : INFINITY, valid ? 1.0f : 0.0f, __int_as_float(tok));
-  }
+  cur_finish(valid, m, lsum + __shfl_xor(lsum, 32, 64), ld_plain);
 }
 
 // --------------------------------------------------------------------------- colmass
@@ -1366,6 +1458,12 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     a.fcount = reinterpret_cast<int32_t*>(ws + p.off_fcount);
   }
   if (!lazy) a.fpair = p.fpair;
+  if (lazy && p.lsplit) {
+    a.f_tiles = p.f_tiles;
+    a.fpart = reinterpret_cast<float4*>(ws + p.off_fpart);
+    a.fcount = reinterpret_cast<int32_t*>(ws + p.off_fcount);
+    a.lmass = reinterpret_cast<float*>(ws + p.off_lmass);
+  }
   const bool fuse = x.fuse_commit;
   CommitArgs cm{};
   int64_t gblocks = static_cast<int64_t>(sh) * (a.n_keys_pad / 64);
@@ -1403,15 +1501,14 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 256-row workgroups with 64-key tiles for full loops and for lazy loops
-  // that fill the chip, else 128-row workgroups with 32-key tiles, or 64-row
-  // ones for lazy grids too small even for those (more, lighter workgroups)
-  const int64_t wg256 = static_cast<int64_t>(a.n_sh) * ((a.n_rows + 255) / 256);
-  const int64_t wg128 = static_cast<int64_t>(a.n_sh) * ((a.n_rows + 127) / 128);
-  const int cfg = (!lazy || wg256 >= 512) ? 0 : wg128 >= 512 ? 1 : 2;
-  const int rows_per = cfg == 0 ? 256 : cfg == 1 ? 128 : 64;
+  // 256-row workgroups with 64-key tiles for full loops; a lazy loop's shape
+  // is planned (plan_lazy_cfg)
+  const int cfg = lazy ? p.lazy_cfg : 0;
+  const int rows_per = lazy_cfg_rows(cfg);
   if ((a.fsplit_u > 0 || a.fpair > 0) && cfg != 0) return hipErrorInvalidConfiguration;   // 256-row tiles only
-  dim3 gf(mapped_grid(a.n_sh, a.fsplit_u > 0 ? a.f_items : a.fpair > 0 ? a.fpair : (a.n_rows + rows_per - 1) / rows_per));
+  const int row_tiles = (a.n_rows + rows_per - 1) / rows_per;
+  if (a.lmass && a.f_tiles != row_tiles) return hipErrorInvalidConfiguration;
+  dim3 gf(mapped_grid(a.n_sh, a.fsplit_u > 0 ? a.f_items : a.fpair > 0 ? a.fpair : a.lmass ? 2 * row_tiles : row_tiles));
   {
     TimedLaunch t(st, lazy ? "mfma_fwd_lazy" : "mfma_fwd_full");
     const bool mix = lazy && x.formula == FL_FORMULA_MIXTURE;

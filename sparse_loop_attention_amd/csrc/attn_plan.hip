@@ -5,6 +5,7 @@
 // active rows (prefill loops); the per-row path serves float32 stores and
 // calls with few rows per head (decode), where a 32-row MFMA tile would idle.
 #include <algorithm>
+#include <cstdlib>
 #include <functional>
 #include <map>
 #include <mutex>
@@ -101,6 +102,36 @@ int plan_fwd_pair(int64_t n_sh, int64_t n_rows) {
   return static_cast<int>(per);
 }
 
+// 256-row workgroups with 64-key tiles for lazy loops that fill the chip,
+// else 128-row workgroups with 32-key tiles, or 64-row ones for grids too
+// small even for those (more, lighter workgroups).
+int plan_lazy_cfg(int64_t n_sh, int64_t n_rows) {
+  const int64_t wg256 = n_sh * ((n_rows + 255) / 256);
+  const int64_t wg128 = n_sh * ((n_rows + 127) / 128);
+  return wg256 >= 512 ? 0 : wg128 >= 512 ? 1 : 2;
+}
+
+// The two passes of a lazy row tile as two workgroups: twice the workgroups
+// and no pipeline restart between the passes; the two meet in the L2 of
+// their XCD, which holds for >= 8 (sequence, head) rows (whole heads per XCD).
+// Measured on 16 heads x 128: it pays where the grid is under one round of
+// workgroups but more than one per CU (32768 rows, 2621 active, 64-row
+// shape: 234 -> 212 us), and costs where the grid already takes rounds
+// (9830 active, 256-row shape: 558 -> 617 us; 4915, 128-row: 333 -> 341 us)
+// or is below one workgroup per CU (820 active: 35 -> 40 us).
+// FLASHLOOP_LAZY_SPLIT=0 or =1 turns it off or on wherever it is possible.
+static bool plan_lazy_split(int64_t n_sh, int64_t n_rows, int cfg) {
+  if (n_sh < kXcds) return false;
+  const char* e = getenv("FLASHLOOP_LAZY_SPLIT");
+  if (e && e[0] == '0') return false;
+  if (e && e[0] == '1') return true;
+  const int64_t rows_per = lazy_cfg_rows(cfg);
+  const int64_t wgs = n_sh * ((n_rows + rows_per - 1) / rows_per);
+  const int64_t per_cu = cfg == 0 ? 1 : cfg == 1 ? 2 : 4;            // resident workgroups per CU
+  const int64_t cus = kXcds * kCusPerXcd;
+  return wgs > cus && wgs < per_cu * cus;
+}
+
 hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);
 hipError_t launch_mfma(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);
 
@@ -172,9 +203,22 @@ AttendPlan plan_attend(const fl_attend_args& a) {
     p.f_tiles = static_cast<int>((rows + 255) / 256);
     p.f_items = p.fsplit_u > 0 ? fwd_split_items(p.rows, p.fsplit_u) : p.f_tiles;
     p.fpair = lazy || p.fsplit_u > 0 ? 0 : plan_fwd_pair(static_cast<int64_t>(sh), p.rows);
+    p.lazy_cfg = lazy ? plan_lazy_cfg(static_cast<int64_t>(sh), p.rows) : 0;
+    p.lsplit = lazy && plan_lazy_split(static_cast<int64_t>(sh), p.rows, p.lazy_cfg);
     p.off_fpart = off;
     p.off_fcount = off;
-    if (p.fsplit_u > 0) {
+    p.off_lmass = off;
+    if (p.lsplit) {
+      // one partial (acc, max, sum of every lane) per row tile, written by the
+      // current-loop pass when it ends before the previous-loop pass
+      const uint64_t rows_per = lazy_cfg_rows(p.lazy_cfg), nt = 2 * rows_per;
+      p.f_tiles = static_cast<int>((rows + rows_per - 1) / rows_per);
+      off = align256(off + sh * p.f_tiles * (D / 8 + 1) * nt * 16);
+      p.off_fcount = off;                                // counters, then as many XCD masks
+      off = align256(off + 2 * sh * p.f_tiles * 4);
+      p.off_lmass = off;
+      off = align256(off + sh * rows * 4);
+    } else if (p.fsplit_u > 0) {
       off = align256(off + sh * p.f_items * (D / 8 + 1) * 512 * 16);   // D/8 float4 of acc + (max, sum)
       p.off_fcount = off;                                // counters, then as many XCD masks
       off = align256(off + 2 * sh * p.f_tiles * 4);

@@ -31,8 +31,15 @@ struct AttendPlan {
   // MFMA path, full loops in one round of workgroups: workgroups per (sequence,
   // head) that each take an early and a late 128-row half (0 = not used)
   int fpair;
+  // MFMA path, lazy loops: forward workgroup shape (0: 256 rows and 64-key
+  // tiles, 1: 128 and 32, 2: 64 and 32); with lsplit the two passes of a row
+  // tile run as two workgroups (f_tiles row tiles per head; partials in
+  // off_fpart, counters in off_fcount, the mass of the previous-loop pass in
+  // off_lmass)
+  int lazy_cfg;
+  bool lsplit;
   // byte offsets in the workspace
-  uint64_t off_part, off_logit, off_stat, off_gather, off_fpart, off_fcount, off_ccount, off_total;
+  uint64_t off_part, off_logit, off_stat, off_gather, off_fpart, off_fcount, off_ccount, off_lmass, off_total;
   bool col_fused;       // several row ranges: the last range to finish adds them (no reduction launch)
 };
 // Forward key split of a full loop (0 = none) for n_sh (sequence, head) rows of
@@ -43,6 +50,9 @@ int fwd_split_items(int64_t n_rows, int u);
 // Workgroups per (sequence, head) of a full loop's forward pass with paired
 // 128-row halves, or 0 where the grid would exceed one round of workgroups.
 int plan_fwd_pair(int64_t n_sh, int64_t n_rows);
+// Forward workgroup shape of a lazy loop (AttendPlan::lazy_cfg) and its rows.
+int plan_lazy_cfg(int64_t n_sh, int64_t n_rows);
+constexpr int lazy_cfg_rows(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 128 : 64; }
 AttendPlan plan_attend(const fl_attend_args& a);
 hipError_t launch_attend(const fl_attend_args& a, const KvView& kv, const AttendPlan& p, hipStream_t st);
 // Device address of the library's static scratch on the stream's device

@@ -129,6 +129,85 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict_
                                         [&](int pos, int32_t idx) { dst[pos] = idx; }, lds);
 }
 
+// Token top-k of a later lazy loop, whose candidate rows (the previous
+// loop's active set, ascending) are the only rows that may have changed:
+// every other row scores exactly 0.  If at least k candidates score above 0,
+// the k largest rows are the k largest candidates (all the others score 0,
+// below them; ties between candidates still go to the lower row), so the
+// selection runs over the candidates alone.  Otherwise, or if a candidate
+// scores below 0 or NaN (orders the general selection defines), it leaves
+// out_idx[0] = -1 and k_topk_rest selects over every row.  k >= 1.
+template <int EPT>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_cand(const double* __restrict__ scores,
+                                                            const int32_t* __restrict__ cand, int32_t n_cand,
+                                                            int32_t k, int32_t* __restrict__ out_idx) {
+  __shared__ TopkLds<kTopkThreads> lds;
+  __shared__ int s_pos, s_bad;
+  if (threadIdx.x == 0) { s_pos = 0; s_bad = 0; }
+  __syncthreads();
+  int pos = 0, bad = 0;
+  for (int i = threadIdx.x; i < n_cand; i += kTopkThreads) {
+    const double v = scores[cand[i]];
+    pos += v > 0.0 ? 1 : 0;
+    bad |= v >= 0.0 ? 0 : 1;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    pos += __shfl_xor(pos, o, 64);
+    bad |= __shfl_xor(bad, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&s_pos, pos);
+    atomicOr(&s_bad, bad);
+  }
+  __syncthreads();
+  if (s_bad || s_pos < k) {
+    if (threadIdx.x == 0) out_idx[0] = -1;
+    return;
+  }
+  topk_block<double, EPT, kTopkThreads>(n_cand, k, [&](int64_t i) { return scores[cand[i]]; },
+                                        [&](int p, int32_t i) { out_idx[p] = cand[i]; }, lds);
+}
+
+// The general token top-k, where k_topk_cand left out_idx[0] = -1.
+template <int EPT>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_rest(const double* __restrict__ scores, int64_t n, int32_t k,
+                                                            int32_t* __restrict__ out_idx) {
+  __shared__ TopkLds<kTopkThreads> lds;
+  __shared__ int s_needed;
+  if (threadIdx.x == 0) s_needed = out_idx[0] < 0;
+  __syncthreads();
+  if (!s_needed) return;
+  topk_block<double, EPT, kTopkThreads>(n, k, [&](int64_t i) { return scores[i]; },
+                                        [&](int p, int32_t i) { out_idx[p] = i; }, lds);
+}
+
+static hipError_t launch_topk_cand(const double* scores, const int32_t* cand, int32_t n_cand, int64_t n, int32_t k,
+                                   int32_t* out, hipStream_t st) {
+  const int64_t per_c = (n_cand + kTopkThreads - 1) / kTopkThreads, per = (n + kTopkThreads - 1) / kTopkThreads;
+  dim3 grid(1), block(kTopkThreads);
+  bool done = false;
+#define FL_CAND_CASE(E)                                                                          \
+  if (!done && per_c <= E) {                                                                     \
+    TimedLaunch t(st, "topk");                                                                   \
+    hipLaunchKernelGGL(k_topk_cand<E>, grid, block, 0, st, scores, cand, n_cand, k, out);       \
+    done = true;                                                                                 \
+  }
+  FL_CAND_CASE(1) FL_CAND_CASE(2) FL_CAND_CASE(4) FL_CAND_CASE(8) FL_CAND_CASE(16) FL_CAND_CASE(32) FL_CAND_CASE(64)
+#undef FL_CAND_CASE
+  if (!done) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+#define FL_REST_CASE(E)                                                                          \
+  if (per <= E) {                                                                                \
+    TimedLaunch t(st, "topk_rest");                                                              \
+    hipLaunchKernelGGL(k_topk_rest<E>, grid, block, 0, st, scores, n, k, out);                  \
+    return hipGetLastError();                                                                    \
+  }
+  FL_REST_CASE(1) FL_REST_CASE(2) FL_REST_CASE(4) FL_REST_CASE(8) FL_REST_CASE(16) FL_REST_CASE(32) FL_REST_CASE(64)
+#undef FL_REST_CASE
+  return hipErrorInvalidValue;
+}
+
 template <typename ScoreT>
 static hipError_t launch_topk(const ScoreT* scores, int64_t n_seg, int64_t seg_len, int32_t k,
                               int32_t* out, hipStream_t st) {
@@ -160,6 +239,8 @@ hipError_t launch_select(const fl_select_args& a, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.cand_idx && a.k > 0)
+      return launch_topk_cand(a.scores, a.cand_idx, a.n_cand, a.n_rows, a.k, a.out_idx, st);
     return launch_topk<double>(a.scores, 1, a.n_rows, a.k, a.out_idx, st);
   }
   return launch_topk<float>(a.key_scores, a.n_seg, a.seg_len, a.k, a.out_idx, st);

@@ -4,9 +4,12 @@ against the oracle element by element (GPU, through the C ABI).
 With at least 512 workgroups of 256 rows a lazy call takes 256-row
 workgroups with 64-key tiles; with at least 512 of 128 rows it takes
 128-row/32-key ones; the gather walks one key at a time per 16-lane group
-once it has at least 512 blocks.  Four sequences of 16 heads (64 head rows),
-2560 tokens and 512 selected keys per head reach every one of these, with the
-commit of the active rows fused into the call as the benchmark runs it
+once it has at least 512 blocks; below that, 64-row workgroups.  The two
+passes of a row tile run as two workgroups (partials met in L2) where the
+grid is under one round of workgroups but over one per CU, and wherever
+FLASHLOOP_LAZY_SPLIT=1 asks for it.  Four sequences of 16 heads (64 head
+rows), 2560 tokens and 512 selected keys per head reach every one of these,
+with the commit of the active rows fused into the call as the benchmark runs it
 (page "FlashLoop: Fast and Memory-Efficient Looped Transformers via Lazy
 Updates", section "FlashLoop combines three kinds of savings", paragraphs 2-4).
 
@@ -62,18 +65,27 @@ def _err(got, want):
     return float(np.abs(np.asarray(got, np.float64) - want).max()), math.sqrt(float(np.mean(want ** 2)))
 
 
-@pytest.mark.parametrize("d,na,formula", [(128, 2048, "column"), (128, 1024, "column"), (128, 2048, "mixture"),
-                                          (96, 2048, "column"), (96, 1024, "column"), (96, 1024, "mixture")],
-                         ids=["d128-256rows", "d128-128rows", "d128-256rows-mixture", "d96-256rows", "d96-128rows",
-                              "d96-128rows-mixture"])
-def test_lazy_large_grid_matches_oracle(d, na, formula):
+@pytest.mark.parametrize("d,na,formula,split", [
+    (128, 2048, "column", None), (128, 1024, "column", None), (128, 2048, "mixture", None),
+    (96, 2048, "column", None), (96, 1024, "column", None), (96, 1024, "mixture", None),
+    (128, 896, "column", None), (128, 896, "column", "0"), (96, 896, "mixture", None),
+    (128, 2048, "column", "1"), (128, 2048, "mixture", "1"), (96, 1024, "column", "1")],
+    ids=["d128-256rows", "d128-128rows", "d128-256rows-mixture", "d96-256rows", "d96-128rows",
+         "d96-128rows-mixture", "d128-64rows-split", "d128-64rows-nosplit", "d96-64rows-split-mixture",
+         "d128-256rows-split", "d128-256rows-split-mixture", "d96-128rows-split"])
+def test_lazy_large_grid_matches_oracle(d, na, formula, split, monkeypatch):
+    if split is not None:
+        monkeypatch.setenv("FLASHLOOP_LAZY_SPLIT", split)
+    else:
+        monkeypatch.delenv("FLASHLOOP_LAZY_SPLIT", raising=False)
     wl, data, per_seq = _state(d)
     rng = np.random.default_rng(na + d)
     act = np.stack([np.sort(rng.choice(N, na, replace=False)) for _ in range(S)]).astype(np.int32)
     keys = np.stack([p[3] for p in per_seq]).astype(np.int32)                   # [S, H, NS]
     # the call's shape: 64 head rows, so the grids are the large ones
     wg256, wg128 = S * H * ((na + 255) // 256), S * H * ((na + 127) // 128)
-    assert (wg256 >= 512) == (na == 2048) and wg128 >= 512 and S * H * ((NS + 255) // 256 * 256 // 64) >= 512
+    assert (wg256 >= 512) == (na == 2048) and (wg128 >= 512) == (na >= 1024)
+    assert S * H * ((NS + 255) // 256 * 256 // 64) >= 512
     dt = torch.bfloat16
     kv = abi.KVStore(S, H, d, N, 2, dt, [na], DEV, group=wl.group, delta_bits=wl.delta_bits)
     every = torch.arange(N, dtype=torch.int32, device=DEV)[None].repeat(S, 1).contiguous()
@@ -128,5 +140,5 @@ def test_lazy_large_grid_matches_oracle(d, na, formula):
         for wi, w in enumerate(("k", "v")):
             assert np.array_equal(codes[s][:, :, wi], oracle.pack_codes(recs[w].codes, wl.delta_bits)), (s, w)
             assert np.array_equal(scales[s][:, :, wi].view(np.uint16), recs[w].scales.view(np.uint16)), (s, w)
-    print(f"[lazy_grids] d={d} na={na} {formula}: max|do|/rms {worst['o']:.2e}, max|dlse| {worst['lse']:.2e}, "
+    print(f"[lazy_grids] d={d} na={na} {formula} split={split}: max|do|/rms {worst['o']:.2e}, max|dlse| {worst['lse']:.2e}, "
           f"max|dc|/rms {worst['c']:.2e}", flush=True)

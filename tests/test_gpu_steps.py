@@ -91,22 +91,30 @@ def test_select_tokens(dtype, n, hidden, k):
     assert np.array_equal(got, oracle.topk_ascending(u_ref, k))
 
 
-def test_select_tokens_candidates():
-    rng = np.random.default_rng(3)
-    n, hidden = 2000, 256
+@pytest.mark.parametrize("n,hidden,n_cand,n_still,ks", [
+    (2000, 256, 300, 0, (1, 150, 300, 400)),       # 400 > candidates: zeros by index
+    (2000, 256, 300, 100, (150, 200, 250, 300)),   # 100 candidates unchanged: k > 200 takes zeros by index
+    (32768, 64, 9830, 0, (4915, 9830)),            # the 32K workload's later loops
+    (65536, 16, 40000, 7, (20000, 39999))])
+def test_select_tokens_candidates(n, hidden, n_cand, n_still, ks):
+    """Later lazy loops: only the candidate rows may change, every other row
+    scores exactly 0; the selection runs over the candidates while at least k
+    of them score above 0, else over every row."""
+    rng = np.random.default_rng(n + n_cand + n_still)
     h_prev = rng.standard_normal((n, hidden)).astype(np.float32)
-    cand = np.sort(rng.choice(n, 300, replace=False)).astype(np.int32)
+    cand = np.sort(rng.choice(n, n_cand, replace=False)).astype(np.int32)
     h_cur = h_prev.copy()
-    h_cur[cand] += rng.standard_normal((300, hidden)).astype(np.float32)
+    moved = cand[rng.permutation(n_cand)[n_still:]]
+    h_cur[moved] += rng.standard_normal((len(moved), hidden)).astype(np.float32)
     scores = torch.full((n,), -1.0, dtype=torch.float64, device=DEV)
-    for k in (1, 150, 300, 400):                                   # 400 > candidates: zeros by index
-        out = torch.empty(k, dtype=torch.int32, device=DEV)
+    u_ref = oracle.token_scores(h_cur, h_prev)
+    for k in ks:
+        out = torch.full((k,), -7, dtype=torch.int32, device=DEV)
         abi.select_tokens(to_dev(h_cur, torch.float32), to_dev(h_prev, torch.float32), k, scores, out,
                           torch.from_numpy(cand).to(DEV))
         torch.cuda.synchronize()
-        u_ref = oracle.token_scores(h_cur, h_prev)
         np.testing.assert_allclose(scores.cpu().numpy(), u_ref, rtol=1e-13)
-        assert np.array_equal(out.cpu().numpy(), oracle.topk_ascending(u_ref, k))
+        assert np.array_equal(out.cpu().numpy(), oracle.topk_ascending(u_ref, k)), k
 
 
 @pytest.mark.parametrize("n_seg,seg_len,k", [(1, 1, 1), (1, 256, 26), (16, 4096, 410), (3, 32768, 3277),
