@@ -129,6 +129,22 @@ __device__ __forceinline__ bool map_block(int n_sh, int n_tiles, int& sh, int& t
   tile = n_tiles - 1 - b % n_tiles;
   return sh < n_sh;
 }
+// Lazy loops with the two passes as two workgroups (n_sh >= 8): each XCD
+// takes the previous-loop passes (role 1) of all its heads' row tiles, heavy
+// first, then their current-loop passes in the same order, so that a row
+// tile's current-loop pass starts well after its previous-loop pass (which
+// it then finds done: no partial state to store).  Grid: mapped_grid(n_sh,
+// 2 * n_tiles).
+__device__ __forceinline__ bool map_split(int n_sh, int n_tiles, int& sh, int& tile, int& role) {
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int per_role = (n_sh + 7) / 8 * n_tiles;            // items of one role on this XCD
+  role = local < per_role ? 1 : 0;
+  const int rem = local % per_role;
+  sh = xcd + 8 * (rem / n_tiles);
+  tile = n_tiles - 1 - rem % n_tiles;
+  return sh < n_sh;
+}
 __host__ __device__ inline int mapped_grid(int n_sh, int n_tiles) {
   return n_sh >= 8 ? 8 * ((n_sh + 7) / 8) * n_tiles : n_sh * n_tiles;
 }
@@ -722,11 +738,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
     }
     part = i;
   } else if (LAZY && a.lmass) {
-    // two workgroups per row tile, the previous-loop pass (role 1) first
-    int t2;
-    if (!map_block(a.n_sh, 2 * a.f_tiles, sh, t2)) return;
-    qtile = t2 >> 1;
-    lrole = t2 & 1;
+    if (!map_split(a.n_sh, a.f_tiles, sh, qtile, lrole)) return;
   } else if (!map_block(a.n_sh, (a.n_rows + ROWS - 1) / ROWS, sh, qtile)) {
     return;
   }

@@ -112,14 +112,15 @@ int plan_lazy_cfg(int64_t n_sh, int64_t n_rows) {
 }
 
 // The two passes of a lazy row tile as two workgroups: twice the workgroups
-// and no pipeline restart between the passes; the two meet in the L2 of
-// their XCD, which holds for >= 8 (sequence, head) rows (whole heads per XCD).
-// Measured on 16 heads x 128: it pays where the grid is under one round of
-// workgroups but more than one per CU (32768 rows, 2621 active, 64-row
-// shape: 234 -> 212 us), and costs where the grid already takes rounds
-// (9830 active, 256-row shape: 558 -> 617 us; 4915, 128-row: 333 -> 341 us)
-// or is below one workgroup per CU (820 active: 35 -> 40 us).
-// FLASHLOOP_LAZY_SPLIT=0 or =1 turns it off or on wherever it is possible.
+// (a finer balance over the CUs) and no pipeline restart between the passes;
+// the two meet in the L2 of their XCD, which holds for >= 8 (sequence, head)
+// rows (whole heads per XCD).  Measured (16 or 55 heads): it pays on grids of
+// up to about 2.5 rounds of workgroups (32K workload, 2.4 / 1.2 / 0.64 rounds:
+// 549 -> 532, 330 -> 318, 233 -> 203 us; the deep workload's loops of 1.2-1.4
+// rounds 177 -> 159, 196 -> 182 us) and costs beyond (3.0-4.3 rounds:
+// 352 -> 377, 480 -> 502 us: the output rows are read back from HBM by the
+// second pass instead of from L2).  FLASHLOOP_LAZY_SPLIT=0 or =1 turns it off
+// or on wherever it is possible.
 static bool plan_lazy_split(int64_t n_sh, int64_t n_rows, int cfg) {
   if (n_sh < kXcds) return false;
   const char* e = getenv("FLASHLOOP_LAZY_SPLIT");
@@ -127,9 +128,8 @@ static bool plan_lazy_split(int64_t n_sh, int64_t n_rows, int cfg) {
   if (e && e[0] == '1') return true;
   const int64_t rows_per = lazy_cfg_rows(cfg);
   const int64_t wgs = n_sh * ((n_rows + rows_per - 1) / rows_per);
-  const int64_t per_cu = cfg == 0 ? 1 : cfg == 1 ? 2 : 4;            // resident workgroups per CU
-  const int64_t cus = kXcds * kCusPerXcd;
-  return wgs > cus && wgs < per_cu * cus;
+  const int64_t slots = (cfg == 0 ? 1 : cfg == 1 ? 2 : 4) * kXcds * kCusPerXcd;   // resident workgroups
+  return 2 * wgs < 5 * slots;
 }
 
 hipError_t launch_rows(const fl_attend_args& x, const KvView& kv, const AttendPlan& p, hipStream_t st);

@@ -219,22 +219,25 @@ class PrefillRun:
         wl, x = self.wl, self.inp[l]
         act, na, scores = self.act[l], wl.n_active(l), self.scores_l[l]
         t = self.timer
-        # the change of the candidate rows during loop l-1 (every row after the full loops)
+        # the change of the candidate rows during loop l-1 (every row after the full loops);
+        # on the second stream it runs beside the previous loop's attention and this
+        # loop's key selection, which do not depend on it
         if self.side is not None:
             with torch.cuda.stream(self.side), t(f"loop{l}.select_tokens"):
                 abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, scores, act, cand)
-            torch.cuda.current_stream().wait_stream(self.side)
         else:
             with t(f"loop{l}.select_tokens"):
                 abi.select_tokens(self.inp[l - 1]["h"][0], self.inp[l - 2]["h"][0], na, scores, act, cand)
-        if self.exit_flags is not None:          # early exit: no later library call touches the sequence
-            abi.exit_check(self.exit_flags, self.exit_threshold, scores=scores)
         first = wl.n_full + 1
         if self.freeze_keys and l > first:
             self.keys_l[l].copy_(self.keys_l[first])
         else:
             with t(f"loop{l}.select_keys"):
                 abi.select_keys(self.colmass, wl.n_keys, self.keys_l[l])
+        if self.side is not None:
+            torch.cuda.current_stream().wait_stream(self.side)
+        if self.exit_flags is not None:          # early exit: no later library call touches the sequence
+            abi.exit_check(self.exit_flags, self.exit_threshold, scores=scores)
         if not self.fuse:
             with t(f"loop{l}.kv_commit"):
                 abi.kv_commit(self.kv, l, act, x["k"], x["v"], exit_flags=self.exit_flags)
