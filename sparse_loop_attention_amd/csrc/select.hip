@@ -188,7 +188,7 @@ static hipError_t launch_topk_cand(const double* scores, const int32_t* cand, in
   bool done = false;
 #define FL_CAND_CASE(E)                                                                          \
   if (!done && per_c <= E) {                                                                     \
-    TimedLaunch t(st, "topk");                                                                   \
+    TimedLaunch t(st, "topk_tokens");                                                            \
     hipLaunchKernelGGL(k_topk_cand<E>, grid, block, 0, st, scores, cand, n_cand, k, out);       \
     done = true;                                                                                 \
   }
@@ -199,7 +199,7 @@ static hipError_t launch_topk_cand(const double* scores, const int32_t* cand, in
   if (e != hipSuccess) return e;
 #define FL_REST_CASE(E)                                                                          \
   if (per <= E) {                                                                                \
-    TimedLaunch t(st, "topk_rest");                                                              \
+    TimedLaunch t(st, "topk_tokens_rest");                                                              \
     hipLaunchKernelGGL(k_topk_rest<E>, grid, block, 0, st, scores, n, k, out);                  \
     return hipGetLastError();                                                                    \
   }
@@ -210,12 +210,12 @@ static hipError_t launch_topk_cand(const double* scores, const int32_t* cand, in
 
 template <typename ScoreT>
 static hipError_t launch_topk(const ScoreT* scores, int64_t n_seg, int64_t seg_len, int32_t k,
-                              int32_t* out, hipStream_t st) {
+                              int32_t* out, hipStream_t st, const char* label) {
   const int64_t per = (seg_len + kTopkThreads - 1) / kTopkThreads;
   dim3 grid(static_cast<unsigned>(n_seg)), block(kTopkThreads);
 #define FL_TOPK_CASE(E)                                                                    \
   if (per <= E) {                                                                          \
-    TimedLaunch t(st, "topk");                                                             \
+    TimedLaunch t(st, label);                                                              \
     hipLaunchKernelGGL((k_topk<ScoreT, E>), grid, block, 0, st, scores, seg_len, k, out);  \
     return hipGetLastError();                                                              \
   }
@@ -241,9 +241,9 @@ hipError_t launch_select(const fl_select_args& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     if (a.cand_idx && a.k > 0)
       return launch_topk_cand(a.scores, a.cand_idx, a.n_cand, a.n_rows, a.k, a.out_idx, st);
-    return launch_topk<double>(a.scores, 1, a.n_rows, a.k, a.out_idx, st);
+    return launch_topk<double>(a.scores, 1, a.n_rows, a.k, a.out_idx, st, "topk_tokens");
   }
-  return launch_topk<float>(a.key_scores, a.n_seg, a.seg_len, a.k, a.out_idx, st);
+  return launch_topk<float>(a.key_scores, a.n_seg, a.seg_len, a.k, a.out_idx, st, "topk_keys");
 }
 
 }  // namespace fl

@@ -102,14 +102,35 @@ def cmd_copy(a):
 def cmd_stats(a):
     with open(a.stats_csv) as fh:
         rows = list(csv.DictReader(fh))
-    out = [f"# {a.title}", "", "Command (from the repository root, one MI355X):", "", "```", a.command, "```", "",
-           "| kernel | calls | total ms | avg us | % |", "|---|---|---|---|---|"]
+    # per-dispatch durations from the trace beside the statistics, for the
+    # minimum, the median and the mean of each kernel's last `solo_last`
+    # dispatches (bench.py's one-stream timing passes come last)
+    trace = os.path.join(os.path.dirname(a.stats_csv), os.path.basename(a.stats_csv).replace("kernel_stats", "kernel_trace"))
+    durs = collections.defaultdict(list)
+    if os.path.exists(trace):
+        with open(trace) as fh:
+            for r in csv.DictReader(fh):
+                durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    solo = f" | last {a.solo_last} avg us" if a.solo_last else ""
+    out = [f"# {a.title}", "", "Command (from the repository root, one MI355X):", "", "```", a.command, "```", ""]
+    if a.solo_last:
+        out += [f"The last {a.solo_last} dispatches of each lazy-loop kernel are bench.py's one-stream timing passes "
+                "(per call, then per kernel); earlier dispatches of the lazy loops ran beside the token selection "
+                "on the second stream.", ""]
+    out += [f"| kernel | calls | total ms | avg us | min us | median us{solo} | % |",
+            "|---|---|---|---|---|---|" + ("---|" if a.solo_last else "") + "---|"]
     for r in rows[:a.top]:
         name = r["Name"]
-        if len(name) > 96:
-            name = name[:93] + "..."
-        out.append(f"| `{name}` | {r['Calls']} | {int(r['TotalDurationNs']) / 1e6:.3f} | "
-                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        d = sorted(durs.get(name, []))
+        mn = f"{d[0]:.1f}" if d else "-"
+        md = f"{d[len(d) // 2]:.1f}" if d else "-"
+        extra = ""
+        if a.solo_last:
+            seq = [x for x in durs.get(name, [])][-a.solo_last:]
+            extra = f" | {sum(seq) / len(seq):.1f}" if seq else " | -"
+        short = name if len(name) <= 96 else name[:93] + "..."
+        out.append(f"| `{short}` | {r['Calls']} | {int(r['TotalDurationNs']) / 1e6:.3f} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {mn} | {md}{extra} | {float(r['Percentage']):.2f} |")
     print("\n".join(out))
 
 
@@ -178,9 +199,23 @@ def cmd_counters(a):
             out.append(f"| {k} | {merged[k]:.4g} |")
         g = merged.get
         derived = []
+        # Units, from the counters' own consistency on this chip: GRBM_GUI_ACTIVE
+        # is summed over the 8 XCDs (per XCD it matches the kernel time at
+        # 1.8-2.1 GHz), SQ_BUSY_CU_CYCLES over the 256 CUs and
+        # SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs (MOPS x 512 / 1024 flops per
+        # cycle reproduces it)
+        if g("SQ_BUSY_CU_CYCLES") and g("GRBM_GUI_ACTIVE"):
+            derived.append(("CU busy fraction: SQ_BUSY_CU_CYCLES / (256 x GRBM_GUI_ACTIVE / 8)",
+                            g("SQ_BUSY_CU_CYCLES") / (256 * g("GRBM_GUI_ACTIVE") / 8)))
         if g("SQ_VALU_MFMA_BUSY_CYCLES") and g("SQ_BUSY_CU_CYCLES"):
-            # busy CU quad-cycles x 4 cycles x 4 SIMDs = busy SIMD cycles
-            derived.append(("MFMA busy / busy SIMD cycles", g("SQ_VALU_MFMA_BUSY_CYCLES") / (16 * g("SQ_BUSY_CU_CYCLES"))))
+            derived.append(("MFMA busy while the CU is busy: SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES)",
+                            g("SQ_VALU_MFMA_BUSY_CYCLES") / (4 * g("SQ_BUSY_CU_CYCLES"))))
+        if g("SQ_VALU_MFMA_BUSY_CYCLES") and g("GRBM_GUI_ACTIVE"):
+            derived.append(("MFMA busy over the kernel: SQ_VALU_MFMA_BUSY_CYCLES / (1024 x GRBM_GUI_ACTIVE / 8)",
+                            g("SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * g("GRBM_GUI_ACTIVE") / 8)))
+        if g("SQ_WAIT_INST_ANY") and g("SQ_WAVE_CYCLES"):
+            derived.append(("wave time waiting on a dependency: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+                            g("SQ_WAIT_INST_ANY") / g("SQ_WAVE_CYCLES")))
         if g("SQ_LDS_BANK_CONFLICT") and g("SQ_ACTIVE_INST_LDS"):
             derived.append(("LDS bank-conflict cycles / LDS active cycles",
                             g("SQ_LDS_BANK_CONFLICT") / (4 * g("SQ_ACTIVE_INST_LDS"))))
@@ -210,6 +245,7 @@ def main(argv=None):
     s.add_argument("--title", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--top", type=int, default=16)
+    s.add_argument("--solo-last", type=int, default=0)
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "cal_fetch", "cal_write", "kernel", "timer", "workload", "command"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
