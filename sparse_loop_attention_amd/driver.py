@@ -122,7 +122,9 @@ class PrefillRun:
         lazy loop's key group in every later lazy loop; exit_threshold enables
         the early exit (the sequence stops before the first lazy loop whose
         largest token change is below it); overlap runs the token selection on
-        a second stream (None: from 4096 tokens up)."""
+        a second stream (None: from 8192 tokens up; at 4096 tokens the lazy
+        loops measured 0.28 ms with it and 0.225 ms without, at 16384 and
+        32768 tokens 8.10 vs 8.33 ms and 2.36 vs 2.42 ms)."""
         assert wl.n_seq == 1 and not wl.decode
         self.wl, self.inp, self.dev, self.fuse = wl, inputs, device, fuse
         self.formula, self.freeze_keys = formula, freeze_keys
@@ -140,7 +142,7 @@ class PrefillRun:
         self.scores_l = {l: torch.empty(n, dtype=torch.float64, device=device)
                          for l in range(wl.n_full + 1, wl.n_loops + 1)}
         if overlap is None:
-            overlap = n >= 4096
+            overlap = n >= 8192
         self.side = torch.cuda.Stream(device=device) if overlap else None
         self.all_rows = torch.arange(n, dtype=torch.int32, device=device)
         self.act = {l: torch.empty(wl.n_active(l), dtype=torch.int32, device=device)
