@@ -1021,9 +1021,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
 // Key-major: a wave owns 32 key slots (K^ rows in registers, keys in lanes so
 // that column sums are lane-local) and streams tiles of 64 query rows through
 // LDS; S = Q K^T on the MFMA, p = 2^(s*c1 - b) with the row's final base-2
-// normaliser b, summed per key in a fixed order.  Software-pipelined like the
-// forward pass: the QK product of row tile t+1 runs on the matrix cores while
-// the VALU exponentiates tile t.  A lazy loop makes two passes: the previous
+// normaliser b, summed per key in a fixed order.  The kernel is bound by its
+// vector work (one exponential per pair), and four waves per SIMD overlap one
+// wave's exponentials with another's MFMAs, so a wave computes a tile's
+// logits and then its exponentials (a per-wave pipeline held a second logit
+// tile and cost more registers and copies than it hid).  A lazy loop makes two passes: the previous
 // loop's probabilities (b_prev, q_prev, K^ of version v-1) are subtracted, the
 // current ones added.  The rows can be split over several workgroups, whose
 // per-key partial sums a second kernel adds in a fixed order.
@@ -1134,27 +1136,19 @@ __device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H
   sstore(0, 0);
   if (n_tiles > 1) { gload(1); sstore(1, 1); }
   __syncthreads();
-  f32x16 S0[2], S1[2];
-  qk(0, S0);
-  __syncthreads();
+  // iteration t: logits and exponentials of tile t (the other waves of the
+  // SIMD keep the matrix cores busy meanwhile); query tile t+2 is loaded and,
+  // once every wave has read tile t's buffer, stored in its place.  Tile t+1
+  // was stored one iteration earlier, before that iteration's barrier.
+  f32x16 S[2];
   for (int t = 0; t < n_tiles; ++t) {
     gload(min(t + 2, n_tiles - 1));
-    mask(t, S0);
-    qk((t + 1) & 1, S1);
-    expsum(t, S0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
-    }
+    qk(t & 1, S);
+    mask(t, S);
+    expsum(t, S);
     asm volatile("" ::"v"(acc));
-    sstore(t & 1, t + 2);
     __syncthreads();
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) S0[qb] = S1[qb];
+    sstore(t & 1, t + 2);
   }
   __syncthreads();                                           // the buffers are reused by the next pass
 }
