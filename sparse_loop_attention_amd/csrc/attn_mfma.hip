@@ -1062,33 +1062,51 @@ __device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H
   float pb = INFINITY;
   int ptok = -1;
   // branch-free: rows past the range are read clamped and then neutralised
-  auto gload = [&](int tile) {
+  // this lane's chunk of a query row, and the distance between rows
+  const uint16_t* qlane = static_cast<const uint16_t*>(qsrc) + (static_cast<int64_t>(s) * rows_q * H + (sh % H)) * D +
+                          (tid % (D / 8)) * 8;
+  const int64_t qstride = static_cast<int64_t>(H) * D;
+  // Loads of a tile are issued early and used only when the tile is stored,
+  // at the end of the iteration (rows past the range, read clamped, are
+  // neutralised there), so a wave does not wait for them before its own work.
+  // The query rows' positions (row index, or token with by-token queries) of
+  // a tile are read one iteration before its query loads, so that those do
+  // not wait on a dependent load.
+  int qrow[T::QPER];
+  auto rload = [&](int tile) {
     const int q0 = r_begin + tile * QT;
 #pragma unroll
     for (int i = 0; i < T::QPER; ++i) {
       const int ch = min(tid + NT * i, T::QCH - 1);         // a partial last round repeats the last chunk
-      const int rr = q0 + ch / (D / 8);
-      const int rc = min(rr, r_end - 1);
-      const int64_t qr = a.q_compact ? rc : row_token(a, s, rc);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(qsrc) +
-                                                      ((static_cast<int64_t>(s) * rows_q + qr) * H + (sh % H)) * D +
-                                                      (ch % (D / 8)) * 8);
-      pq[i] = rr < r_end ? v : u32x4{0, 0, 0, 0};
+      const int rc = min(q0 + ch / (D / 8), r_end - 1);
+      qrow[i] = a.q_compact ? rc : row_token(a, s, rc);
     }
-    const int rr = q0 + (tid & 63);                         // every wave reads the tile's row statistics
-    const float4 st =
-        *reinterpret_cast<const float4*>(a.stat + (static_cast<int64_t>(sh) * a.n_rows + min(rr, r_end - 1)) * 4);
-    pb = rr < r_end ? (bsel ? st.y : st.x) : INFINITY;
-    ptok = rr < r_end ? __float_as_int(st.w) : -1;
   };
-  auto sstore = [&](int buf, int tile) {
+  auto gload = [&](int tile) {                              // the tile whose rows rload read last
+    const int q0 = r_begin + tile * QT;
 #pragma unroll
     for (int i = 0; i < T::QPER; ++i) {
       const int ch = min(tid + NT * i, T::QCH - 1);
-      *reinterpret_cast<u32x4*>(&sq[buf][(ch / (D / 8)) * QS + (ch % (D / 8)) * 8]) = pq[i];
+      pq[i] = *reinterpret_cast<const u32x4*>(qlane + static_cast<int64_t>(qrow[i]) * qstride +
+                                              (ch % (D / 8) - tid % (D / 8)) * 8);
     }
-    sb[tile & 3][tid & 63] = pb;                            // identical values from every wave
-    stok[tile & 3][tid & 63] = ptok;
+    const int rr = min(q0 + (tid & 63), r_end - 1);         // every wave reads the tile's row statistics
+    const float4 st = *reinterpret_cast<const float4*>(a.stat + (static_cast<int64_t>(sh) * a.n_rows + rr) * 4);
+    pb = bsel ? st.y : st.x;
+    ptok = __float_as_int(st.w);
+  };
+  // tile: the tile the last gload read, or a later one (past the end: never used)
+  auto sstore = [&](int buf, int tile) {
+    const int q0 = r_begin + tile * QT;
+#pragma unroll
+    for (int i = 0; i < T::QPER; ++i) {
+      const int ch = min(tid + NT * i, T::QCH - 1);
+      const bool ok = q0 + ch / (D / 8) < r_end;
+      *reinterpret_cast<u32x4*>(&sq[buf][(ch / (D / 8)) * QS + (ch % (D / 8)) * 8]) = ok ? pq[i] : u32x4{0, 0, 0, 0};
+    }
+    const bool ok = q0 + (tid & 63) < r_end;
+    sb[tile & 3][tid & 63] = ok ? pb : INFINITY;           // identical values from every wave
+    stok[tile & 3][tid & 63] = ok ? ptok : -1;
   };
   auto qk = [&](int buf, f32x16 (&S)[2]) {
 #pragma unroll
@@ -1132,17 +1150,21 @@ __device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H
     acc += SUB ? -part : part;
   };
 
+  rload(0);
   gload(0);
   sstore(0, 0);
-  if (n_tiles > 1) { gload(1); sstore(1, 1); }
+  if (n_tiles > 1) { rload(1); gload(1); sstore(1, 1); }
+  rload(min(2, n_tiles - 1));
   __syncthreads();
   // iteration t: logits and exponentials of tile t (the other waves of the
   // SIMD keep the matrix cores busy meanwhile); query tile t+2 is loaded and,
-  // once every wave has read tile t's buffer, stored in its place.  Tile t+1
-  // was stored one iteration earlier, before that iteration's barrier.
+  // once every wave has read tile t's buffer, stored in its place, and the
+  // row positions of tile t+3 are read.  Tile t+1 was stored one iteration
+  // earlier, before that iteration's barrier.
   f32x16 S[2];
   for (int t = 0; t < n_tiles; ++t) {
     gload(min(t + 2, n_tiles - 1));
+    rload(min(t + 3, n_tiles - 1));
     qk(t & 1, S);
     mask(t, S);
     expsum(t, S);
