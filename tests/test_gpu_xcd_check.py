@@ -2,13 +2,15 @@
 
 A full loop whose forward pass is cut into key parts, or whose column mass
 is cut into row ranges, merges the parts' partial results in the part that
-finishes last; this relies on every part of a head running on one XCD, whose
-L2 is where they meet.  Each part records its XCD; a mismatch sets
+finishes last, and a lazy loop whose two passes run as two workgroups meets
+them in the one that ends last; this relies on every part of a head running
+on one XCD, whose L2 is where they meet.  Each part records its XCD; a mismatch sets
 FL_DEV_XCD_SPLIT in the call's dev_status word.  After every loop of the
 prefill workloads at full size the word must be 0; with the host-set test
 flag (odd parts report another XCD) the check must fire, with the outputs
 unchanged.
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -64,4 +66,29 @@ def test_forced_mismatch_is_reported(S, H, N, d):
         del os.environ["FLASHLOOP_TEST_XCD_SPLIT"]
     assert int(status.item()) & abi.FL_DEV_XCD_SPLIT
     for x, y in zip(ref, got):
+        assert torch.equal(x, y)
+
+
+def test_forced_mismatch_is_reported_lazy():
+    """A lazy loop with its two passes as two workgroups (16 heads, 1229 of
+    4096 rows active: well under one round of workgroups)."""
+    wl = dataclasses.replace(configs.scaled(configs.LONG_PREFILL, 4096), n_loops=2, n_full=1)
+    assert wl.n_heads >= 8
+    inputs = driver.upload_loops(wl, SyntheticLoops(wl), DEV)
+    run = driver.PrefillRun(wl, inputs, DEV, overlap=False)
+    run.run(upto=1)
+    snap = run.snapshot()
+    run.run(start=2)
+    torch.cuda.synchronize()
+    assert int(run.dev_status.item()) == 0
+    ref = [x.clone() for x in (run.o, run.lse, run.colmass)]
+    run.restore(snap)
+    os.environ["FLASHLOOP_TEST_XCD_SPLIT"] = "1"
+    try:
+        run.run(start=2)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["FLASHLOOP_TEST_XCD_SPLIT"]
+    assert int(run.dev_status.item()) & abi.FL_DEV_XCD_SPLIT
+    for x, y in zip(ref, (run.o, run.lse, run.colmass)):
         assert torch.equal(x, y)
