@@ -199,6 +199,8 @@ __device__ __forceinline__ int vt_pos(int k16) {
 // U key slots of a 16-lane group walk their chains together (U = 4: four
 // times the loads in flight, for grids too small to fill the chip; U = 1
 // keeps the registers, and so the occupancy, of large grids).
+constexpr int kCommitRows = 2;                             // active rows per 16-lane group in a lazy commit
+
 template <int DT, int D, bool LAZY, bool FUSE, int U>
 __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArgs cm) {
   __shared__ uint16_t sv[2][64][D + 2];
@@ -212,22 +214,51 @@ __global__ __launch_bounds__(256) void k_gather(KvView kv, MfmaArgs a, CommitArg
   if (FUSE && b >= a.n_sh * n_tiles) {
     b -= a.n_sh * n_tiles;
     // lazy loops: blocks of their own write the active rows' records (the
-    // selected keys are other tokens); a full loop's key groups write them
-    const int64_t items = LAZY ? static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2 : 0;
+    // selected keys are other tokens); a full loop's key groups write them.
+    // A 16-lane group takes kCommitRows consecutive active rows of one head,
+    // K and V: their chains are walked together (one slot-row read per row
+    // for both) with every load in flight at once.
+    constexpr int CR = kCommitRows;
+    const int row_groups = (a.n_rows + CR - 1) / CR;
+    const int64_t items = LAZY ? static_cast<int64_t>(kv.n_seq) * kv.H * row_groups : 0;
     const int n_cb = static_cast<int>((items + 15) / 16);
     if (b < n_cb) {                                       // records of the active rows
       const int64_t item = static_cast<int64_t>(b) * 16 + g;
       if (item >= items) return;
-      const int which = static_cast<int>(item & 1);
-      const int h = static_cast<int>((item >> 1) % kv.H);
-      const int64_t sr = (item >> 1) / kv.H;
-      const int r = static_cast<int>(sr % a.n_rows), s = static_cast<int>(sr / a.n_rows);
+      const int h = static_cast<int>(item % kv.H);
+      const int64_t rest = item / kv.H;
+      const int r0 = static_cast<int>(rest % row_groups) * CR, s = static_cast<int>(rest / row_groups);
       if (kv.exited(s)) return;                           // uniform per 16-lane group
-      const int j = a.act ? a.act[static_cast<int64_t>(s) * a.n_rows + r] : r;
+      const bool live = 8 * p < D;
+      int jj[CR];
+      bool in[CR], ok[CR];
+#pragma unroll
+      for (int u = 0; u < CR; ++u) {
+        const int r = r0 + u;
+        in[u] = r < a.n_rows;                             // uniform per group
+        jj[u] = !in[u] ? 0 : a.act ? a.act[static_cast<int64_t>(s) * a.n_rows + r] : r;
+        ok[u] = in[u] && live;
+      }
+      float xk[CR][8], xv[CR][8], unused[CR][8];
+      recon_kv<DT, CR, false>(kv, s, h, jj, ok, a.version - 1, p, xk, xv, unused, unused);
       const int64_t src_rows = cm.src_compact ? a.n_rows : kv.N;
-      const int64_t src_elem = ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? r : j)) * kv.H + h) * D;
-      commit_row<DT>(kv, cm.arena, a.version, s, j, h, which, cm.slot_base + r, which ? cm.v_new : cm.k_new,
-                     src_elem, p);
+      float nk[CR][8], nv[CR][8];
+#pragma unroll
+      for (int u = 0; u < CR; ++u) {
+        if (ok[u]) {
+          const int64_t src =
+              ((static_cast<int64_t>(s) * src_rows + (cm.src_compact ? r0 + u : jj[u])) * kv.H + h) * D + 8 * p;
+          load8<DT>(cm.k_new, src, nk[u]);
+          load8<DT>(cm.v_new, src, nv[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CR; ++u) {
+        if (!in[u]) continue;
+        float out[8];
+        commit_advance8(kv, cm.arena, a.version, s, cm.slot_base + r0 + u, h, 0, nk[u], xk[u], live, p, out);
+        commit_advance8(kv, cm.arena, a.version, s, cm.slot_base + r0 + u, h, 1, nv[u], xv[u], live, p, out);
+      }
       return;
     }
     b -= n_cb;                                            // slot table column of layer `version`
@@ -1500,7 +1531,7 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     cm.k_new = x.k_new; cm.v_new = x.v_new;
     cm.src_compact = x.kv_layout == FL_ROWS_COMPACT;
     cm.slot_base = x.commit_slot_base; cm.reset = x.commit_reset;
-    const int64_t items = static_cast<int64_t>(kv.n_seq) * a.n_rows * kv.H * 2;
+    const int64_t items = static_cast<int64_t>(kv.n_seq) * kv.H * ((a.n_rows + kCommitRows - 1) / kCommitRows);
     if (lazy) gblocks += (items + 15) / 16;                                  // the active rows' records
     if (x.version >= 2) gblocks += static_cast<int64_t>(kv.n_seq) * ((kv.N + 255) / 256);   // slot column
   }
