@@ -84,6 +84,11 @@ struct MfmaArgs {
   // mass m per row [sh][n_rows]; fpart/fcount/f_tiles then hold the
   // current-loop pass's partials and the arrivals per row tile
   float* lmass;
+  // lazy loops: per-key sums of the previous-loop probabilities over each
+  // forward row tile's rows, [sh][row tiles][n_keys_pad] (row tiles of
+  // pcol_rows rows; written by the forward for the key tiles it visits)
+  float* pcol;
+  int32_t pcol_rows;
   int32_t fpair;            // full loops: workgroups per head taking an early and a late 128-row half (0 = off)
   int32_t* ccount;          // [2][sh][n_keys_pad / 256] column-mass ranges finished, then the XCDs they ran on
                             // (bit x: XCD x), zeroed by the gather; or null
@@ -406,6 +411,15 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t hadd2(uint32_t x, uint32_t y) {     // two fp16 sums
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, x) + __builtin_bit_cast(h2v, y));
+}
+
 // One wave owns 32 query rows (one per lane pair: lane c and c+32 hold the
 // two key halves of query c).  A workgroup of NW waves streams the key tiles
 // of one role through LDS; per tile the wave computes S^T = K Q^T (bf16
@@ -440,19 +454,24 @@ struct FwdTiles {
 // WLIM: the wave computes only its first my_n of the workgroup's n_tiles key
 // tiles (the rest lie past its rows' causal limit) and afterwards only helps
 // stage the tiles the other waves still use.
-template <int D, int NW, int KT_, bool FIXED, bool NOPV = false, bool WLIM = false>
+// COLS (fixed-normaliser pass): the per-key sums of the probabilities over
+// the workgroup's rows are written to col_dst[key slot] for every key tile
+// the workgroup visits (the waves' sums meet in scol, [2][NW][KT] floats,
+// and are added in wave order).
+template <int D, int NW, int KT_, bool FIXED, bool NOPV = false, bool WLIM = false, bool COLS = false>
 __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const uint16_t* kbase, const uint16_t* vbase,
                                          const int32_t* kx, uint16_t (*sk)[FwdTiles<D, NW, KT_>::KBUF],
                                          uint16_t (*sv)[FwdTiles<D, NW, KT_>::VBUF], int (*skx)[KT_],
                                          const bf16x8 (&qf)[D / 16], int tok, int tok_first, int tok_last, bool blk_full,
                                          float c1, float b_fix, f32x16 (&acc)[D / 32], float& ref, float& lsum,
-                                         int my_n = 0) {
+                                         int my_n = 0, float* col_dst = nullptr, float* scol = nullptr) {
+  static_assert(!COLS || (FIXED && !WLIM), "column sums: fixed-normaliser passes over every tile");
   using T = FwdTiles<D, NW, KT_>;
   constexpr int KT = T::KT, NT = T::NT, KS = T::KS, VS = T::VS;
   (void)NT;
   constexpr int DC = D / 16, DB = D / 32;
   constexpr int NKB = KT / 32, NCC = KT / 16;             // 32-key logit blocks, 16-key PV chunks
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, c = lane & 31;
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
@@ -603,9 +622,14 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
   // normaliser mass, whose terms can all lie below fp16's range and which
   // decides the row's validity and lse
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2v __attribute__((ext_vector_type(2)));
   auto convert = [&](f32x16 (&S)[NKB], int cc) {
+    u32x4 pw;                                             // one packed conversion per value pair
 #pragma unroll
-    for (int i = 0; i < 8; ++i) P[cc][i] = static_cast<_Float16>(S[cc >> 1][(cc & 1) * 8 + i]);
+    for (int i = 0; i < 4; ++i)
+      pw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v{S[cc >> 1][(cc & 1) * 8 + 2 * i],
+                                                                       S[cc >> 1][(cc & 1) * 8 + 2 * i + 1]}, h2));
+    P[cc] = __builtin_bit_cast(f16x8, pw);
     float ps = 0.0f;
     if (FIXED) {
 #pragma unroll
@@ -617,13 +641,68 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     }
     lsum += ps;
   };
+  // COLS: the per-key sums over the wave's 32 rows of the tile held in P (its
+  // fp16 probabilities, as the PV product uses them), in RP pieces that the
+  // next step interleaves with its QK products (P still holds the tile then).
+  // A reduce-scatter over the 32 lanes of each key half: at each level a lane
+  // keeps half of its value pairs and adds its partner's copy of that half
+  // (partners: the other 16-lane row, then the row, half-row and quad mirrors
+  // and swaps), so each value moves once.  The lane ends with the sum of one
+  // value index of the S list (block * 16 + element): its lane index c with
+  // two blocks; with one, 2 * (c >> 2) + (c & 1), also held by lane c ^ 2.
+  constexpr int MD = 8 * NKB;                             // dwords of P: value pairs (2d, 2d + 1)
+  constexpr int RP = NKB == 2 ? 16 : 9;
+  uint32_t rw[MD / 2];
+  float rsum = 0.0f;
+  const bool b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1;
+  auto pdw = [&](int d) -> uint32_t { return __builtin_bit_cast(u32x4, P[d >> 2])[d & 3]; };
+  auto rlevel = [&](int i, int n, bool hi, auto xchg) {
+    const uint32_t keep = hi ? rw[i + n] : rw[i], send = hi ? rw[i] : rw[i + n];
+    rw[i] = hadd2(keep, xchg(send));
+  };
+  auto rpiece = [&](int q) {
+    if (q < MD / 2) {                                     // 16-lane rows 0 <-> 1, 2 <-> 3
+      const auto r = __builtin_amdgcn_permlane16_swap(pdw(q), pdw(q + MD / 2), false, false);
+      rw[q] = hadd2(r[0], r[1]);                          // rows 0, 2: pair q; rows 1, 3: pair q + MD/2
+      return;
+    }
+    q -= MD / 2;
+    if (q < MD / 4) { rlevel(q, MD / 4, b3, [](uint32_t x) { return dpp_u32<kDppRowMirror>(x); }); return; }
+    q -= MD / 4;
+    if (q < MD / 8) { rlevel(q, MD / 8, b2, [](uint32_t x) { return dpp_u32<kDppRowHalfMirror>(x); }); return; }
+    q -= MD / 8;
+    if (q == 0) {
+      if (NKB == 2) rlevel(0, 1, b1, [](uint32_t x) { return dpp_u32<kDppQuadSwap2>(x); });
+      else rw[0] = hadd2(rw[0], dpp_u32<kDppQuadSwap2>(rw[0]));
+      return;
+    }
+    const uint32_t w = hadd2(rw[0], dpp_u32<kDppQuadSwap1>(rw[0]));   // both halves; the lane keeps one
+    rsum = static_cast<float>(__builtin_bit_cast(h2, b0 ? (w >> 16) : (w & 0xFFFFu))[0]);
+  };
+  // the sums of tile tt go to scol: every key of the tile once
+  auto rwrite = [&](int tt) {
+    const int idx = NKB == 2 ? c : 2 * (c >> 2) + (c & 1), kb = idx >> 4, e = idx & 15;
+    if (NKB == 2 || !b1) scol[((tt & 1) * NW + wave) * KT + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)] = rsum;
+  };
 
   // iteration t: QK(t+1) into Sn, PV(t-1) with P, softmax(t) of Sc into P;
   // K(t+2) and V(t) are loaded for the next iterations.  Tiles past the end
   // are computed on whatever the buffers hold and never used.
+  // the column sums of tile tt (in scol since the barrier that ended the
+  // next tile's step): one wave adds the NW waves' values and stores them
+  auto col_store = [&](int tt) {
+    if (wave == tt % NW && lane < KT) {
+      const float* sc = scol + (tt & 1) * NW * KT + lane;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += sc[w * KT];
+      col_dst[tt * KT + lane] = sum;
+    }
+  };
   auto step = [&](int t, f32x16 (&Sc)[NKB], f32x16 (&Sn)[NKB], bool first) {
     load_k(t & 1, min(t + 2, n_tiles - 1));
     if (!NOPV) load_v(t & 1, t);
+    if (COLS && t >= 2) col_store(t - 2);
     if (resc_prev) rescale(alpha_prev);
     mask(t, Sc);
     resc_cur = false;
@@ -634,7 +713,7 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     const uint16_t* V = sv[(t + 1) & 1];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) Sn[kb] = f32x16{};
-    int done = 0;
+    int done = 0, rdone = 0;
     // MFMA operands (K fragments, then V^T fragments) in a 3-entry register
     // ring, read two products ahead of their use
     const int n_mfma = pv ? NQK + NPV : NQK;
@@ -664,6 +743,8 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
       const int slots = pv ? NQK + NPV : NQK;
       const int target = min(kPieces, (m + 1) * kPieces / slots);
       for (; done < target; ++done) piece(Sc, done);
+      if (COLS && !first && m < NQK)
+        for (; rdone < min(RP, (m + 1) * RP / NQK); ++rdone) rpiece(rdone);
       if (pv && m >= NQK && (m - NQK) % DB == DB - 1) {  // the last PV product that reads P[cc]
         const int cc = (m - NQK) / DB;
         for (; done < kExpBase + 4 * (cc + 1); ++done) piece(Sc, done);
@@ -674,6 +755,10 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
     }
     for (; done < kPieces; ++done) piece(Sc, done);
+    if (COLS && !first) {                                 // tile t-1's sums, before P takes tile t
+      for (; rdone < RP; ++rdone) rpiece(rdone);
+      rwrite(t - 1);
+    }
     if (!pv) {
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) convert(Sc, cc);
@@ -714,6 +799,14 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     run(t + 1, S0, S1, false);
   }
   if (t < n_tiles) run(t, S1, S0, false);
+  if (COLS) {                                              // the last two tiles' sums
+    if (n_tiles >= 2) col_store(n_tiles - 2);
+#pragma unroll
+    for (int q = 0; q < RP; ++q) rpiece(q);
+    rwrite(n_tiles - 1);
+    __syncthreads();
+    col_store(n_tiles - 1);
+  }
   if (NOPV || (WLIM && my_n < n_tiles)) return;
   if (resc_prev) rescale(alpha_prev);                      // PV of the last tile
   pv_acc((n_tiles - 1) & 1, P);
@@ -739,6 +832,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   __shared__ __attribute__((aligned(16))) int skx[4][KT];
   __shared__ int s_last, s_arrived;
   __shared__ int s_wcount[NW];
+  __shared__ float scol[LAZY ? 2 * NW * KT : 1];          // lazy: the previous-loop pass's column sums
   constexpr int NT = 64 * NW;
   // the key split serves full loops in the 256-row, 64-key-tile shape
   constexpr bool kSplit = !LAZY && ROWS == 256 && KT == 64 && !PAIR;
@@ -918,6 +1012,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   // lse_prev gives the mass m and contribution a; o_prev - a is written back
   // at once, and pass 2 (current loop, online softmax) adds m * otilde.
   const float b_prev = vrow ? a.lse[(static_cast<int64_t>(s) * rows_o + orow) * H + h] * kLog2e : 0.0f;
+  // the previous-loop probabilities' per-key sums over this row tile's rows
+  float* col_dst = a.pcol + (static_cast<int64_t>(sh) * ((a.n_rows + ROWS - 1) / ROWS) + qtile) * a.n_keys_pad;
   // o <- o_prev - a (or (1 - m) o_prev), from o as read by ld
   auto prev_update = [&](bool valid, float m, auto ld) {
     if (!valid) return;
@@ -993,8 +1089,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
     bool valid;
     if (lrole == 1) {
       load_q(a.q_prev, qf);
-      fwd_pass<D, NW, KT_, true, MIX>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok, tok_first,
-                                      tok_last, blk_full, c1, b_prev, acc, ref, lsum);
+      fwd_pass<D, NW, KT_, true, MIX, false, true>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok,
+                                                   tok_first, tok_last, blk_full, c1, b_prev, acc, ref, lsum, 0,
+                                                   col_dst, scol);
       m = lsum + __shfl_xor(lsum, 32, 64);
       valid = vrow && m > 0.0f;
       prev_update(valid, m, ld_plain);
@@ -1036,8 +1133,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
     return;
   }
   load_q(a.q_prev, qf);
-  fwd_pass<D, NW, KT_, true, MIX>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok, tok_first,
-                                  tok_last, blk_full, c1, b_prev, acc, ref, lsum);
+  fwd_pass<D, NW, KT_, true, MIX, false, true>(a, n_tiles, a.kp + kofs, a.vtp + kofs, kx, sk, sv, skx, qf, tok,
+                                               tok_first, tok_last, blk_full, c1, b_prev, acc, ref, lsum, 0, col_dst,
+                                               scol);
   const float m = lsum + __shfl_xor(lsum, 32, 64);
   const bool valid = vrow && m > 0.0f;
   prev_update(valid, m, ld_plain);
@@ -1056,9 +1154,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
 // vector work (one exponential per pair), and four waves per SIMD overlap one
 // wave's exponentials with another's MFMAs, so a wave computes a tile's
 // logits and then its exponentials (a per-wave pipeline held a second logit
-// tile and cost more registers and copies than it hid).  A lazy loop makes two passes: the previous
-// loop's probabilities (b_prev, q_prev, K^ of version v-1) are subtracted, the
-// current ones added.  The rows can be split over several workgroups, whose
+// tile and cost more registers and copies than it hid).  A lazy loop adds
+// the current probabilities and subtracts the previous loop's, which the
+// forward's fixed-normaliser pass already summed per key and row tile (it
+// holds them in registers, so the logits and exponentials of version v-1 are
+// not computed twice).  The rows can be split over several workgroups, whose
 // per-key partial sums a second kernel adds in a fixed order.
 //
 // stat rows hold (b_prev, b_cur, valid, token); rows that did not update
@@ -1072,9 +1172,9 @@ struct ColTiles {
   static constexpr int QPER = (QCH + NT - 1) / NT;
 };
 
-template <int D, bool SUB>
+template <int D>
 __device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H, int N, int r_begin, int r_end,
-                                         const void* qsrc, const uint16_t* krow, int bsel, int kj, int kmax,
+                                         const void* qsrc, const uint16_t* krow, int kj, int kmax,
                                          uint16_t (*sq)[ColTiles<D>::QT * ColTiles<D>::QS], float (*sb)[64],
                                          int (*stok)[64], float c1, float& acc) {
   using T = ColTiles<D>;
@@ -1123,7 +1223,7 @@ __device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H
     }
     const int rr = min(q0 + (tid & 63), r_end - 1);         // every wave reads the tile's row statistics
     const float4 st = *reinterpret_cast<const float4*>(a.stat + (static_cast<int64_t>(sh) * a.n_rows + rr) * 4);
-    pb = bsel ? st.y : st.x;
+    pb = st.y;
     ptok = __float_as_int(st.w);
   };
   // tile: the tile the last gload read, or a later one (past the end: never used)
@@ -1178,7 +1278,7 @@ __device__ __forceinline__ void col_pass(const MfmaArgs& a, int s, int sh, int H
         part += ex2(fmaf(S[qb][4 * q4 + 2], c1, -b4.z));
         part += ex2(fmaf(S[qb][4 * q4 + 3], c1, -b4.w));
       }
-    acc += SUB ? -part : part;
+    acc += part;
   };
 
   rload(0);
@@ -1287,11 +1387,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512), amdgpu_waves_per_
   const int r_begin = max(c_lo, (s_start / QT) * QT);
   const int64_t kofs = (static_cast<int64_t>(sh) * a.n_keys_pad + t) * D + 8 * hh;
   float acc = 0.0f;
-  if (LAZY) {
-    col_pass<D, true>(a, s, sh, H, N, r_begin, r_end, a.q_prev, a.kp + kofs, 0, kj, kmax, sq, sb, stok, c1, acc);
-    col_pass<D, false>(a, s, sh, H, N, r_begin, r_end, a.q_cur, a.kc + kofs, 1, kj, kmax, sq, sb, stok, c1, acc);
-  } else {
-    col_pass<D, false>(a, s, sh, H, N, r_begin, r_end, a.q_cur, a.kc + kofs, 1, kj, kmax, sq, sb, stok, c1, acc);
+  col_pass<D>(a, s, sh, H, N, r_begin, r_end, a.q_cur, a.kc + kofs, kj, kmax, sq, sb, stok, c1, acc);
+  if (LAZY && hh == 0) {
+    // the previous loop's probabilities, summed by the forward per row tile,
+    // are subtracted: each range takes the tiles that start in it, in order
+    // (a tile whose last row precedes the key saw none of it, and its entry
+    // was not written)
+    const int pr = a.pcol_rows, rt = (a.n_rows + pr - 1) / pr;
+    const int t_lo = (c_lo + pr - 1) / pr, t_hi = min(rt, (min(a.n_rows, c_lo + a.col_rows) + pr - 1) / pr);
+    const float* pc = a.pcol + static_cast<int64_t>(sh) * rt * a.n_keys_pad + t;
+    float prev = 0.0f;
+#pragma unroll 4
+    for (int r = t_lo; r < t_hi; ++r) {
+      const float v = pc[static_cast<int64_t>(r) * a.n_keys_pad];
+      prev += kj <= row_token(a, s, min((r + 1) * pr, a.n_rows) - 1) ? v : 0.0f;
+    }
+    acc -= prev;
   }
   acc += __shfl_xor(acc, 32, 64);
   if (hh != 0) return;
@@ -1522,6 +1633,10 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
     a.fpart = reinterpret_cast<float4*>(ws + p.off_fpart);
     a.fcount = reinterpret_cast<int32_t*>(ws + p.off_fcount);
     a.lmass = reinterpret_cast<float*>(ws + p.off_lmass);
+  }
+  if (lazy) {
+    a.pcol = reinterpret_cast<float*>(ws + p.off_pcol);
+    a.pcol_rows = lazy_cfg_rows(p.lazy_cfg);
   }
   const bool fuse = x.fuse_commit;
   CommitArgs cm{};

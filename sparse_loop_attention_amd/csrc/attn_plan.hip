@@ -223,6 +223,11 @@ AttendPlan plan_attend(const fl_attend_args& a) {
       p.off_fcount = off;                                // counters, then as many XCD masks
       off = align256(off + 2 * sh * p.f_tiles * 4);
     }
+    p.off_pcol = off;
+    if (lazy) {
+      const uint64_t rows_per = lazy_cfg_rows(p.lazy_cfg);
+      off = align256(off + sh * ((rows + rows_per - 1) / rows_per) * kpad * 4);
+    }
     p.off_total = off;
     return p;
   }

@@ -38,8 +38,9 @@ struct AttendPlan {
   // off_lmass)
   int lazy_cfg;
   bool lsplit;
-  // byte offsets in the workspace
-  uint64_t off_part, off_logit, off_stat, off_gather, off_fpart, off_fcount, off_ccount, off_lmass, off_total;
+  // byte offsets in the workspace (off_pcol: lazy loops, the previous-loop
+  // probabilities' per-key sums of each forward row tile)
+  uint64_t off_part, off_logit, off_stat, off_gather, off_fpart, off_fcount, off_ccount, off_lmass, off_pcol, off_total;
   bool col_fused;       // several row ranges: the last range to finish adds them (no reduction launch)
 };
 // Forward key split of a full loop (0 = none) for n_sh (sequence, head) rows of
