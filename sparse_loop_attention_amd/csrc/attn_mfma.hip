@@ -411,13 +411,39 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ uint32_t hadd2(uint32_t x, uint32_t y) {     // two fp16 sums
-  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, x) + __builtin_bit_cast(h2v, y));
+// Per-key sums over a wave's 32 query rows of one key tile's probabilities,
+// held as the forward holds them (S^T blocks: lane c and c + 32 have query c
+// of the two key halves, 16 keys each per 32-key block), in float32.  A
+// reduce-scatter over the 32 lanes of each half: at every level a lane keeps
+// half of its values and adds its partner's copy of that half (partners: the
+// other 16-lane row, then the row, half-row and quad mirrors and swaps), so
+// each value moves once.  The lane ends with the sum of one value index of
+// the S list (block * 16 + element): its lane index c with two blocks, c / 2
+// with one (lanes c and c ^ 1 then hold the same sum).
+template <int NKB>
+__device__ __forceinline__ float col_reduce(const f32x16 (&S)[NKB], int lane) {
+  constexpr int M = 16 * NKB;
+  float v[M / 2];
+#pragma unroll
+  for (int m = 0; m < M / 2; ++m) {
+    const int i = m, j = m + M / 2;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(S[i >> 4][i & 15]),
+                                                    __float_as_uint(S[j >> 4][j & 15]), false, false);
+    v[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);   // rows 0, 2: value m; rows 1, 3: value m + M/2
+  }
+  auto level = [&](int n, bool hi, auto xchg) {
+#pragma unroll
+    for (int m = 0; m < n; ++m) {
+      const float keep = hi ? v[m + n] : v[m], send = hi ? v[m] : v[m + n];
+      v[m] = keep + xchg(send);
+    }
+  };
+  level(M / 4, (lane >> 3) & 1, [](float x) { return dpp_mov<kDppRowMirror>(x); });
+  level(M / 8, (lane >> 2) & 1, [](float x) { return dpp_mov<kDppRowHalfMirror>(x); });
+  level(M / 16, (lane >> 1) & 1, [](float x) { return dpp_mov<kDppQuadSwap2>(x); });
+  if constexpr (M == 32) level(1, lane & 1, [](float x) { return dpp_mov<kDppQuadSwap1>(x); });
+  else v[0] += dpp_mov<kDppQuadSwap1>(v[0]);
+  return v[0];
 }
 
 // One wave owns 32 query rows (one per lane pair: lane c and c+32 hold the
@@ -641,55 +667,11 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     }
     lsum += ps;
   };
-  // COLS: the per-key sums over the wave's 32 rows of the tile held in P (its
-  // fp16 probabilities, as the PV product uses them), in RP pieces that the
-  // next step interleaves with its QK products (P still holds the tile then).
-  // A reduce-scatter over the 32 lanes of each key half: at each level a lane
-  // keeps half of its value pairs and adds its partner's copy of that half
-  // (partners: the other 16-lane row, then the row, half-row and quad mirrors
-  // and swaps), so each value moves once.  The lane ends with the sum of one
-  // value index of the S list (block * 16 + element): its lane index c with
-  // two blocks; with one, 2 * (c >> 2) + (c & 1), also held by lane c ^ 2.
-  constexpr int MD = 8 * NKB;                             // dwords of P: value pairs (2d, 2d + 1)
-  constexpr int RP = NKB == 2 ? 16 : 9;
-  uint32_t rw[MD / 2];
-  float rsum = 0.0f;
-  const bool b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1;
-  auto pdw = [&](int d) -> uint32_t { return __builtin_bit_cast(u32x4, P[d >> 2])[d & 3]; };
-  auto rlevel = [&](int i, int n, bool hi, auto xchg) {
-    const uint32_t keep = hi ? rw[i + n] : rw[i], send = hi ? rw[i] : rw[i + n];
-    rw[i] = hadd2(keep, xchg(send));
-  };
-  auto rpiece = [&](int q) {
-    if (q < MD / 2) {                                     // 16-lane rows 0 <-> 1, 2 <-> 3
-      const auto r = __builtin_amdgcn_permlane16_swap(pdw(q), pdw(q + MD / 2), false, false);
-      rw[q] = hadd2(r[0], r[1]);                          // rows 0, 2: pair q; rows 1, 3: pair q + MD/2
-      return;
-    }
-    q -= MD / 2;
-    if (q < MD / 4) { rlevel(q, MD / 4, b3, [](uint32_t x) { return dpp_u32<kDppRowMirror>(x); }); return; }
-    q -= MD / 4;
-    if (q < MD / 8) { rlevel(q, MD / 8, b2, [](uint32_t x) { return dpp_u32<kDppRowHalfMirror>(x); }); return; }
-    q -= MD / 8;
-    if (q == 0) {
-      if (NKB == 2) rlevel(0, 1, b1, [](uint32_t x) { return dpp_u32<kDppQuadSwap2>(x); });
-      else rw[0] = hadd2(rw[0], dpp_u32<kDppQuadSwap2>(rw[0]));
-      return;
-    }
-    const uint32_t w = hadd2(rw[0], dpp_u32<kDppQuadSwap1>(rw[0]));   // both halves; the lane keeps one
-    rsum = static_cast<float>(__builtin_bit_cast(h2, b0 ? (w >> 16) : (w & 0xFFFFu))[0]);
-  };
-  // the sums of tile tt go to scol: every key of the tile once
-  auto rwrite = [&](int tt) {
-    const int idx = NKB == 2 ? c : 2 * (c >> 2) + (c & 1), kb = idx >> 4, e = idx & 15;
-    if (NKB == 2 || !b1) scol[((tt & 1) * NW + wave) * KT + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)] = rsum;
-  };
-
   // iteration t: QK(t+1) into Sn, PV(t-1) with P, softmax(t) of Sc into P;
   // K(t+2) and V(t) are loaded for the next iterations.  Tiles past the end
   // are computed on whatever the buffers hold and never used.
-  // the column sums of tile tt (in scol since the barrier that ended the
-  // next tile's step): one wave adds the NW waves' values and stores them
+  // the column sums of tile tt (in scol since the barrier that ended its
+  // step): one wave adds the NW waves' values and stores them
   auto col_store = [&](int tt) {
     if (wave == tt % NW && lane < KT) {
       const float* sc = scol + (tt & 1) * NW * KT + lane;
@@ -702,7 +684,7 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
   auto step = [&](int t, f32x16 (&Sc)[NKB], f32x16 (&Sn)[NKB], bool first) {
     load_k(t & 1, min(t + 2, n_tiles - 1));
     if (!NOPV) load_v(t & 1, t);
-    if (COLS && t >= 2) col_store(t - 2);
+    if (COLS && !first) col_store(t - 1);
     if (resc_prev) rescale(alpha_prev);
     mask(t, Sc);
     resc_cur = false;
@@ -713,7 +695,7 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     const uint16_t* V = sv[(t + 1) & 1];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) Sn[kb] = f32x16{};
-    int done = 0, rdone = 0;
+    int done = 0;
     // MFMA operands (K fragments, then V^T fragments) in a 3-entry register
     // ring, read two products ahead of their use
     const int n_mfma = pv ? NQK + NPV : NQK;
@@ -743,8 +725,6 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
       const int slots = pv ? NQK + NPV : NQK;
       const int target = min(kPieces, (m + 1) * kPieces / slots);
       for (; done < target; ++done) piece(Sc, done);
-      if (COLS && !first && m < NQK)
-        for (; rdone < min(RP, (m + 1) * RP / NQK); ++rdone) rpiece(rdone);
       if (pv && m >= NQK && (m - NQK) % DB == DB - 1) {  // the last PV product that reads P[cc]
         const int cc = (m - NQK) / DB;
         for (; done < kExpBase + 4 * (cc + 1); ++done) piece(Sc, done);
@@ -755,10 +735,6 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
     }
     for (; done < kPieces; ++done) piece(Sc, done);
-    if (COLS && !first) {                                 // tile t-1's sums, before P takes tile t
-      for (; rdone < RP; ++rdone) rpiece(rdone);
-      rwrite(t - 1);
-    }
     if (!pv) {
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) convert(Sc, cc);
@@ -767,6 +743,11 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     // into the next iteration, away from the MFMAs it should overlap)
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) asm volatile("" ::"v"(P[cc]));
+    if (COLS) {                                           // this tile's per-key sums (S is free now)
+      const float cs = col_reduce<NKB>(Sc, lane);
+      const int idx = NKB == 2 ? c : c >> 1, kb = idx >> 4, e = idx & 15;
+      if (NKB == 2 || (c & 1) == 0) scol[((t & 1) * NW + wave) * KT + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)] = cs;
+    }
     flush_k();
     if (!NOPV) flush_v();
     store_kx(t + 2);
@@ -799,14 +780,7 @@ __device__ __forceinline__ void fwd_pass(const MfmaArgs& a, int n_tiles, const u
     run(t + 1, S0, S1, false);
   }
   if (t < n_tiles) run(t, S1, S0, false);
-  if (COLS) {                                              // the last two tiles' sums
-    if (n_tiles >= 2) col_store(n_tiles - 2);
-#pragma unroll
-    for (int q = 0; q < RP; ++q) rpiece(q);
-    rwrite(n_tiles - 1);
-    __syncthreads();
-    col_store(n_tiles - 1);
-  }
+  if (COLS) col_store(n_tiles - 1);                        // the last tile's sums
   if (NOPV || (WLIM && my_n < n_tiles)) return;
   if (resc_prev) rescale(alpha_prev);                      // PV of the last tile
   pv_acc((n_tiles - 1) & 1, P);
