@@ -441,7 +441,7 @@ def per_call_and_kernel_times(run, wl, snap, reps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1 "
                                    "(the multi-GPU sharding is a design note, not code)"}))
         sys.exit(2)
     import torch
