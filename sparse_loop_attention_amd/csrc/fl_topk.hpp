@@ -6,14 +6,16 @@
 // keeps the tokens whose hidden state changed most, paragraph 2 the keys with
 // the most previous-loop attention mass; both are this selection.
 //
-// One workgroup of NT threads selects from one segment; thread t owns
-// elements [t*EPT, (t+1)*EPT), so the final compaction is in index order.
-// Keys are order-preserving bit patterns (larger score -> larger unsigned
-// key, -0.0 == +0.0), selected 8 bits at a time from the top with
-// wave-aggregated LDS histograms; the selection ends as soon as the crossing
-// bin is taken whole.  Keys stay in registers as 32-bit words: the whole key
-// of a float, the high word of a double's; a double's low word is reloaded
-// through `load` only for keys whose high word ties the selected prefix.
+// One workgroup of NT threads selects from one segment; element i belongs
+// to thread i mod NT (slot i / NT), so that every load of the workgroup is
+// one contiguous run of the segment.  Keys are order-preserving bit patterns
+// (larger score -> larger unsigned key, -0.0 == +0.0), selected 8 bits at a
+// time from the top with wave-aggregated LDS histograms; the selection ends
+// as soon as the crossing bin is taken whole.  Keys stay in registers as
+// 32-bit words: the whole key of a float, the high word of a double's; a
+// double's low word is reloaded through `load` only for keys whose high word
+// ties the selected prefix.  Output positions are ranks in index order, from
+// per-(slot, wave) ballot counts scanned once.
 #pragma once
 #include "fl_common.hpp"
 
@@ -36,54 +38,77 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 // atomics on one counter serialise; with the copies at most 64 /
 // kTopkReplicas lanes of a wave meet on one address.
 constexpr int kTopkReplicas = 8;
+constexpr int kTopkMaxSlots = 64;                     // elements per thread
 
 template <int NT>
 struct TopkLds {
   int hist[256 * kTopkReplicas];
-  int scan_tmp[NT / 64 + 1];
+  int rank[kTopkMaxSlots * (NT / 64)];                // per (slot, wave) counts, then their exclusive prefix
+  int rank_total;
   int sel_bin, sel_above, sel_count;
 };
 
-// Exclusive scan of one int per thread across the NT-thread workgroup;
-// `total` receives the sum.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* lds_waves, int& total) {
-  constexpr int kWaves = NT / 64;
+// Ranks in index order of the flagged elements: element (slot e, thread t)
+// is index e * NT + t, so the order is slot, then wave, then lane.  flags:
+// bit e of a thread's mask flags its slot-e element.  fn(e, rank) is called
+// for every flagged element with the number of flagged elements before it;
+// the return value is their total.  Every thread of the workgroup calls it.
+template <int EPT, int NT, class Fn>
+__device__ __forceinline__ int block_rank(uint64_t flags, TopkLds<NT>& s, Fn fn) {
+  constexpr int kWaves = NT / 64, kTot = EPT * kWaves, kPer = (kTot + 63) / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
+  for (int e = 0; e < EPT; ++e) {
+    const uint64_t b = __ballot((flags >> e) & 1);
+    if (lane == 0) s.rank[e * kWaves + wave] = __popcll(b);
   }
-  if (lane == 63) lds_waves[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    const int w = lane < kWaves ? lds_waves[lane] : 0;
-    int wi = w;
+  if (wave == 0) {                                    // exclusive scan of the kTot counts in order
+    int v[kPer], sum = 0;
 #pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const int t = __shfl_up(wi, o, 64);
-      if (lane >= o) wi += t;
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = lane * kPer + j;
+      v[j] = idx < kTot ? s.rank[idx] : 0;
+      sum += v[j];
     }
-    if (lane < kWaves) lds_waves[lane] = wi - w;      // exclusive wave offsets
-    if (lane == kWaves - 1) lds_waves[kWaves] = wi;
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = lane * kPer + j;
+      if (idx < kTot) s.rank[idx] = run;
+      run += v[j];
+    }
+    if (lane == 63) s.rank_total = incl;
   }
   __syncthreads();
-  const int res = lds_waves[wave] + incl - v;
-  total = lds_waves[kWaves];
-  __syncthreads();
-  return res;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint64_t b = __ballot((flags >> e) & 1);
+    const int before = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0));
+    if ((flags >> e) & 1) fn(e, s.rank[e * kWaves + wave] + before);
+  }
+  const int total = s.rank_total;
+  __syncthreads();                                    // s.rank is free again
+  return total;
 }
 
 // Every thread of the workgroup calls it.  load(i) returns score i (0 <= i <
 // n); out(pos, i) stores the pos-th selected position (pos < k).  n <= NT*EPT.
 template <typename ScoreT, int EPT, int NT, class Load, class Out>
 __device__ __forceinline__ void topk_block(int64_t n, int32_t k, Load load, Out out, TopkLds<NT>& s) {
+  static_assert(EPT <= kTopkMaxSlots, "at most 64 elements per thread");
   constexpr bool WIDE = sizeof(ScoreT) == 8;
   constexpr int kBits = WIDE ? 64 : 32;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int64_t first = static_cast<int64_t>(tid) * EPT;
+  const int n32 = static_cast<int>(n);                // n <= NT * EPT
+  auto index = [&](int e) -> int { return e * NT + tid; };
 
   if (k == 0) return;
   if (k >= n) {                                       // everything, already ascending
@@ -94,12 +119,15 @@ __device__ __forceinline__ void topk_block(int64_t n, int32_t k, Load load, Out 
   // flight together; a guarded load per element makes each wait for the last
   ScoreT raw[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) raw[e] = load(min(first + e, n - 1));
+  for (int e = 0; e < EPT; ++e) raw[e] = load(min(index(e), n32 - 1));
   uint32_t hi[EPT];
+  uint64_t valid = 0;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    hi[e] = first + e < n ? static_cast<uint32_t>(order_key(raw[e]) >> (WIDE ? 32 : 0)) : 0u;
-  auto lo_of = [&](int e) -> uint32_t { return static_cast<uint32_t>(order_key(load(first + e))); };
+  for (int e = 0; e < EPT; ++e) {
+    hi[e] = index(e) < n32 ? static_cast<uint32_t>(order_key(raw[e]) >> (WIDE ? 32 : 0)) : 0u;
+    valid |= static_cast<uint64_t>(index(e) < n32) << e;
+  }
+  auto lo_of = [&](int e) -> uint32_t { return static_cast<uint32_t>(order_key(load(index(e)))); };
 
   if (tid == 0) { s.sel_bin = 0; s.sel_above = 0; s.sel_count = 0; }
   uint32_t pre_hi = 0, msk_hi = 0, pre_lo = 0, msk_lo = 0;   // the selected prefix and its bits
@@ -111,7 +139,7 @@ __device__ __forceinline__ void topk_block(int64_t n, int32_t k, Load load, Out 
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      bool act = (first + e < n) && ((hi[e] & msk_hi) == pre_hi);
+      bool act = ((valid >> e) & 1) && ((hi[e] & msk_hi) == pre_hi);
       uint32_t word = hi[e];
       if (low && act) {
         word = lo_of(e);
@@ -122,7 +150,7 @@ __device__ __forceinline__ void topk_block(int64_t n, int32_t k, Load load, Out 
       const uint64_t m = __ballot(act);
       if (m == 0) continue;
       const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
-      const int lbin = __shfl(bin, leader, 64);
+      const int lbin = __builtin_amdgcn_readlane(bin, leader);   // leader is wave-uniform
       const uint64_t same = __ballot(act && bin == lbin);
       if (same == m) {
         if (lane == leader) atomicAdd(&s.hist[lbin * kTopkReplicas], __popcll(m));
@@ -170,47 +198,26 @@ __device__ __forceinline__ void topk_block(int64_t n, int32_t k, Load load, Out 
   }
   // The prefix is the k-th largest key on the bits fixed so far (all of them
   // unless the crossing bin was taken whole); take every key above it there
-  // and the first k_rem keys equal to it in index order.  cmp: +1 above, 0
-  // equal, -1 below.
-  auto cmp = [&](int e) -> int {
+  // and the first k_rem keys equal to it in index order.
+  uint64_t above = 0, equal = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (!((valid >> e) & 1)) continue;
     const uint32_t h = hi[e] & msk_hi;
-    if (h != pre_hi) return h > pre_hi ? 1 : -1;
-    if (!WIDE || msk_lo == 0) return 0;
-    const uint32_t l = lo_of(e) & msk_lo;
-    return l > pre_lo ? 1 : (l == pre_lo ? 0 : -1);
-  };
-  int n_eq = 0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) n_eq += (first + e < n && cmp(e) == 0) ? 1 : 0;
-  int tot;
-  const int eq_before = block_excl_scan<NT>(n_eq, s.scan_tmp, tot);
-  int n_sel = 0;
-  {
-    int eq_rank = eq_before;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      if (first + e >= n) continue;
-      const int c = cmp(e);
-      if (c > 0) ++n_sel;
-      else if (c == 0) { if (eq_rank < k_rem) ++n_sel; ++eq_rank; }
+    int c = 0;
+    if (h != pre_hi) c = h > pre_hi ? 1 : -1;
+    else if (WIDE && msk_lo != 0) {
+      const uint32_t l = lo_of(e) & msk_lo;
+      c = l > pre_lo ? 1 : (l == pre_lo ? 0 : -1);
     }
+    above |= static_cast<uint64_t>(c > 0) << e;
+    equal |= static_cast<uint64_t>(c == 0) << e;
   }
-  int pos = block_excl_scan<NT>(n_sel, s.scan_tmp, tot);
-  {
-    int eq_rank = eq_before;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      if (first + e >= n) continue;
-      const int c = cmp(e);
-      bool take = false;
-      if (c > 0) take = true;
-      else if (c == 0) { take = eq_rank < k_rem; ++eq_rank; }
-      if (take) {
-        if (pos < k) out(pos, static_cast<int32_t>(first + e));
-        ++pos;
-      }
-    }
-  }
+  uint64_t take = above;
+  block_rank<EPT, NT>(equal, s, [&](int e, int rank) { take |= static_cast<uint64_t>(rank < k_rem) << e; });
+  block_rank<EPT, NT>(take, s, [&](int e, int rank) {
+    if (rank < k) out(rank, static_cast<int32_t>(index(e)));
+  });
 }
 
 }  // namespace fl

@@ -117,9 +117,13 @@ hipError_t launch_exit_check(const fl_exit_args& a, hipStream_t st) {
 // top-k by radix select (fl_topk.hpp): one 1024-thread workgroup per segment.
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024;
+// Key workgroups of at most 8 elements per thread keep to 64 VGPRs, so that
+// two fit on a CU: the decode batch's 512 key segments then run in one round.
+template <typename ScoreT, int EPT>
+constexpr int kTopkWavesPerEu = sizeof(ScoreT) == 4 && EPT <= 8 ? 8 : 1;
 
 template <typename ScoreT, int EPT>
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const ScoreT* __restrict__ scores,
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(kTopkWavesPerEu<ScoreT, EPT>))) void k_topk(const ScoreT* __restrict__ scores,
                                                        int64_t seg_len, int32_t k,
                                                        int32_t* __restrict__ out_idx) {
   __shared__ TopkLds<kTopkThreads> lds;
