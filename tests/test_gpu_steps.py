@@ -117,6 +117,40 @@ def test_select_tokens_candidates(n, hidden, n_cand, n_still, ks):
         assert np.array_equal(out.cpu().numpy(), oracle.topk_ascending(u_ref, k)), k
 
 
+@pytest.mark.parametrize("n,k,cand_every", [(32768, 9831, 0), (32768, 4915, 3), (3000, 1500, 0), (3000, 700, 2),
+                                             (1000, 999, 0)])
+def test_select_tokens_low_word_ties(n, k, cand_every):
+    """Token scores whose float64 high words all tie (1 + m 2^-22 + small
+    terms, m < 4, share their top 20 mantissa bits): the selection must
+    decide on the low words, and rows with equal scores go to the lower
+    index.  h_prev = 0 and h_cur = (1 + m 2^-23, j 2^-24, 0, ...), so every
+    score x^2 + y^2 is exact in float64 (49 significant bits) on both sides."""
+    rng = np.random.default_rng(n + k + cand_every)
+    hidden = 8
+    h_prev = np.zeros((n, hidden), np.float32)
+    h_cur = np.zeros((n, hidden), np.float32)
+    m = rng.integers(0, 4, n)
+    j = rng.integers(0, 40, n)                                     # repeats: exact ties
+    h_cur[:, 0] = (1.0 + m * 2.0 ** -23).astype(np.float32)
+    h_cur[:, 1] = (j * 2.0 ** -24).astype(np.float32)
+    u_ref = oracle.token_scores(h_cur, h_prev)
+    assert len(np.unique((u_ref.view(np.uint64) >> 32))) == 1      # one high word
+    cand = None
+    if cand_every:
+        cand = np.arange(0, n, cand_every, dtype=np.int32)          # the other rows are carried: score 0
+        keep = np.zeros(n, bool)
+        keep[cand] = True
+        h_cur[~keep] = h_prev[~keep]
+        u_ref = oracle.token_scores(h_cur, h_prev)
+    scores = torch.empty(n, dtype=torch.float64, device=DEV)
+    out = torch.full((k,), -7, dtype=torch.int32, device=DEV)
+    abi.select_tokens(to_dev(h_cur, torch.float32), to_dev(h_prev, torch.float32), k, scores, out,
+                      None if cand is None else torch.from_numpy(cand).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(scores.cpu().numpy(), u_ref)              # one rounding each: identical
+    assert np.array_equal(out.cpu().numpy(), oracle.topk_ascending(u_ref, k))
+
+
 @pytest.mark.parametrize("n_seg,seg_len,k", [(1, 1, 1), (1, 256, 26), (16, 4096, 410), (3, 32768, 3277),
                                              (512, 8192, 820), (55, 16384, 1639), (2, 1000, 1000), (2, 700, 0),
                                              (1, 65536, 6554), (4, 65536, 1)])
