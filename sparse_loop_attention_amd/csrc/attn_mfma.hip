@@ -1668,6 +1668,7 @@ static hipError_t launch_d(const fl_attend_args& x, const KvView& kv, const Atte
   } while (0)
     if (a.fpair > 0) hipLaunchKernelGGL((k_mfma_fwd<D, 8, 64, false, false, true>), gf, dim3(512), 0, st, kv.H, kv.N, a);
     else if (cfg == 0) FL_FWD(8, 64, 512);
+    else if (cfg == 1 && D <= 96) FL_FWD(4, 64, 256);   // 64-key tiles fit the registers below head_dim 128
     else if (cfg == 1) FL_FWD(4, 32, 256);
     else FL_FWD(2, 32, 128);
 #undef FL_FWD

@@ -103,8 +103,10 @@ int plan_fwd_pair(int64_t n_sh, int64_t n_rows) {
 }
 
 // 256-row workgroups with 64-key tiles for lazy loops that fill the chip,
-// else 128-row workgroups with 32-key tiles, or 64-row ones for grids too
-// small even for those (more, lighter workgroups).
+// else 128-row workgroups (64-key tiles up to head_dim 96, 32-key tiles at
+// 128, whose four staged K and V chunks per thread would not fit the
+// registers), or 64-row ones with 32-key tiles for grids too small even for
+// those (more, lighter workgroups).
 int plan_lazy_cfg(int64_t n_sh, int64_t n_rows) {
   const int64_t wg256 = n_sh * ((n_rows + 255) / 256);
   const int64_t wg128 = n_sh * ((n_rows + 127) / 128);
